@@ -1,0 +1,324 @@
+"""CPU oracle for the rotated W4A4 linear data path.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  The HIP library never
+calls it, and it shares no code with the HIP path; the only common module is
+the seeded input generator (``workloads``), which computes no step of the
+method.
+
+Plain, slow, obviously correct NumPy.  Floating-point stages run in float64;
+the quantizer runs in float32 because its integer decisions must be taken in
+the precision the kernel uses (the pages fix no precision for it).
+
+Sources (web pages; cited as [key, section]):
+
+* [RSQ]  "ReSpinQuant: Efficient Layer-Wise LLM Quantization via Subspace
+  Residual Rotation Approximation" -- paper notes (m0rtzz).  Sections
+  "整体框架" (framework flowchart) and "关键设计" 1-3.
+* [QS]   "QuaRot 与 SpinQuant" (lizn-zn scholia log).  §1.2 (rotation as a basis
+  change), §1.3 (worked 4x4 Hadamard example), §2.2 (why Hadamard).
+* [IQ2]  "Infra Quant II" (taking-lying-flat).  QuaRot "Background" and
+  "Method" (online Hadamard before the down projection; activation, weight
+  and GEMM quantization), SpinQuant "MOTIVATION" (symmetric quantizer),
+  FlatQuant "Preliminaries" (signed b-bit grid, Y = (XH)(H^T W^T)).
+
+Readings where the pages are silent or ambiguous are listed in the design doc;
+the ones that shape code here are restated next to the code.
+
+Pins: every function below is pinned by ``tests/test_oracle_pins.py`` against
+something other than itself (worked example, closed forms, library routines,
+invariants, brute force).  ``silu_gate`` is pinned only by closed-form
+identities of SiLU; the pages give no SiLU value ("parity unpinned" against
+the pages).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "bf16_to_f64", "f64_to_bf16", "align", "align_dense", "t_hat", "fwht", "hadamard",
+    "quant_sym", "quant_int4", "pack_int4", "unpack_int4", "gemm_int", "gemm_int_loop",
+    "epilogue", "silu_gate", "prep_weight", "prequant", "rotated_linear", "residual", "layer",
+    "FLAG_ALIGN", "FLAG_FWHT", "FLAG_SWIGLU",
+]
+
+FLAG_ALIGN = 1
+FLAG_FWHT = 2
+FLAG_SWIGLU = 4
+
+
+# ----------------------------------------------------------------------------
+# bf16 values
+# ----------------------------------------------------------------------------
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64, exactly (bf16 is the top half of fp32)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16(v: np.ndarray) -> np.ndarray:
+    """float64 -> nearest bf16 (ties to even) in one rounding, as uint16 bit patterns.
+
+    bf16 keeps 8 significant bits and fp32's exponent range; below 2^-126 the
+    spacing is fixed at 2^-133.  Finite inputs only.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    m, e = np.frexp(v)                         # v = m * 2^e, 0.5 <= |m| < 1
+    e = np.maximum(e, -125)                    # subnormal range: fixed spacing 2^-133
+    q = np.rint(np.ldexp(v, 8 - e))            # integer count of units 2^(e-8); half-even
+    r = np.ldexp(q, e - 8)
+    r32 = r.astype(np.float32)                 # exact: r has <= 8 significant bits
+    return (r32.view(np.uint32) >> 16).astype(np.uint16)
+
+
+# ----------------------------------------------------------------------------
+# S1: low-rank residual alignment  [RSQ 关键设计 2, 3; framework flowchart]
+# ----------------------------------------------------------------------------
+def align(x: np.ndarray, Q: np.ndarray, M: np.ndarray) -> np.ndarray:
+    """Online residual alignment, the three-step path of [RSQ 关键设计 3].
+
+    Per token (rows of ``x``): project to the r-dim subspace y = Q^T x, apply
+    the small matrix z = (M - I_r) y, lift and add: out = x + Q z.
+
+    ``M`` is the orthogonal sub-rotation R_sub; the page folds the identity
+    into its small matrix (its M is R_sub - I_r), so the step applies M - I.
+    With r = 0 the path is the identity.
+    """
+    x = np.asarray(x, np.float64)
+    Q = np.asarray(Q, np.float64)
+    M = np.asarray(M, np.float64)
+    r = Q.shape[1]
+    y = x @ Q                                   # row t: (Q^T x_t)^T
+    z = y @ (M - np.eye(r)).T                   # row t: ((M - I) y_t)^T
+    return x + z @ Q.T                          # row t: x_t + Q z_t
+
+
+def t_hat(Q: np.ndarray, M: np.ndarray) -> np.ndarray:
+    """Dense aligned transition T_hat = I + Q (M - I) Q^T  [RSQ 关键设计 2]."""
+    Q = np.asarray(Q, np.float64)
+    M = np.asarray(M, np.float64)
+    D, r = Q.shape
+    return np.eye(D) + Q @ (M - np.eye(r)) @ Q.T
+
+
+def align_dense(x: np.ndarray, Q: np.ndarray, M: np.ndarray) -> np.ndarray:
+    """Brute force: materialize T_hat and multiply every token by it."""
+    return np.asarray(x, np.float64) @ t_hat(Q, M).T
+
+
+# ----------------------------------------------------------------------------
+# S2: Walsh-Hadamard transform  [QS §2.2; IQ2 QuaRot Background]
+# ----------------------------------------------------------------------------
+def hadamard(D: int) -> np.ndarray:
+    """Normalized Walsh-Hadamard matrix of order D = 2^n, natural (Sylvester) order.
+
+    Entry (i, j) is (-1)^popcount(i & j) / sqrt(D)  (entries +-1/sqrt(D) per
+    [IQ2 QuaRot Background]; Sylvester order as in the printed H_4 of [QS §1.3]).
+    """
+    i = np.arange(D)
+    bits = np.bitwise_and.outer(i, i)
+    par = np.zeros_like(bits)
+    while bits.any():
+        par ^= bits & 1
+        bits >>= 1
+    return np.where(par == 1, -1.0, 1.0) / np.sqrt(D)
+
+
+def fwht(v: np.ndarray) -> np.ndarray:
+    """Fast Walsh-Hadamard transform of every row, normalized: H_D v / sqrt(D).
+
+    Butterflies (a, b) -> (a + b, a - b) on index pairs (i, i + h) inside
+    blocks of 2h, for h = 1, 2, 4, ..., D/2; O(D log D)  [QS §2.2;
+    IQ2 QuaRot Background].  The last dimension must be a power of two.
+    """
+    a = np.array(v, dtype=np.float64, copy=True)
+    D = a.shape[-1]
+    if D & (D - 1) or D < 1:
+        raise ValueError("FWHT size must be a power of two")
+    lead = a.shape[:-1]
+    h = 1
+    while h < D:
+        b = a.reshape(lead + (D // (2 * h), 2, h))
+        lo = b[..., 0, :].copy()
+        hi = b[..., 1, :].copy()
+        b[..., 0, :] = lo + hi
+        b[..., 1, :] = lo - hi
+        h *= 2
+    return a / np.sqrt(D)
+
+
+# ----------------------------------------------------------------------------
+# S3: symmetric absmax quantization  [IQ2 SpinQuant MOTIVATION; QuaRot Method]
+# ----------------------------------------------------------------------------
+def quant_sym(v: np.ndarray, bits: int = 4):
+    """Per-row symmetric absmax quantization to signed ``bits``-bit integers.
+
+    Step alpha = max|row| / (2^(bits-1) - 1)  [IQ2 SpinQuant MOTIVATION,
+    symmetric case]; code = round(row / alpha)  [IQ2 QuaRot Method: per-token,
+    absmax / 7 for 4 bits]; projected onto the signed grid
+    {-2^(bits-1), ..., 2^(bits-1) - 1}  [IQ2 FlatQuant Preliminaries].
+
+    Decided in float32 (the kernel's precision): alpha = fl32(absmax / qmax)
+    with IEEE division; quotient fl32(v / alpha) rounded to fp32 before it is
+    rounded to an integer; integer rounding is half-to-even.  An all-zero row
+    gets alpha = 0 and codes 0.
+    Returns (codes int8 [..., D], alpha float32 [...]).
+    """
+    v = np.asarray(v, dtype=np.float32)
+    qmax = (1 << (bits - 1)) - 1
+    qmin = -(1 << (bits - 1))
+    a = np.max(np.abs(v), axis=-1)                          # exact in fp32
+    s = (a / np.float32(qmax)).astype(np.float32)           # IEEE fp32 division
+    safe = np.where(s == 0, np.float32(1), s).astype(np.float32)
+    qf = (v / safe[..., None]).astype(np.float32)           # fp32 quotient
+    q = np.clip(np.rint(qf), qmin, qmax)
+    q = np.where((s == 0)[..., None], 0, q)
+    return q.astype(np.int8), s
+
+
+def quant_int4(v: np.ndarray):
+    """4-bit case of ``quant_sym``: step absmax / 7, grid {-8..7}."""
+    return quant_sym(v, 4)
+
+
+def pack_int4(q: np.ndarray) -> np.ndarray:
+    """Two's-complement nibbles, element 2j in the low nibble of byte j."""
+    q = np.asarray(q, dtype=np.int16)
+    if q.shape[-1] % 2:
+        raise ValueError("row length must be even")
+    lo = (q[..., 0::2] & 0xF).astype(np.uint8)
+    hi = (q[..., 1::2] & 0xF).astype(np.uint8)
+    return (lo | (hi << 4)).astype(np.uint8)
+
+
+def unpack_int4(p: np.ndarray) -> np.ndarray:
+    p = np.asarray(p, dtype=np.uint8).astype(np.int16)
+    lo = p & 0xF
+    hi = p >> 4
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), np.int8)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
+# ----------------------------------------------------------------------------
+# S4: integer GEMM and dequantization  [IQ2 QuaRot Method]
+# ----------------------------------------------------------------------------
+def gemm_int(qa: np.ndarray, qw: np.ndarray) -> np.ndarray:
+    """acc[t, n] = sum_k qa[t, k] * qw[n, k], exact, as int32.
+
+    A float64 matrix product of integer-valued matrices is exact here: every
+    partial sum is an integer of magnitude <= 64 K < 2^53.
+    """
+    qa = np.asarray(qa)
+    qw = np.asarray(qw)
+    if qa.shape[-1] * 64 >= 2 ** 53:
+        raise ValueError("K too large for exact float64 accumulation")
+    acc = qa.astype(np.float64) @ qw.astype(np.float64).T
+    return acc.astype(np.int64).astype(np.int32)
+
+
+def gemm_int_loop(qa: np.ndarray, qw: np.ndarray) -> np.ndarray:
+    """Triple loop over integers (tiny shapes only)."""
+    T, K = qa.shape
+    N = qw.shape[0]
+    out = np.zeros((T, N), np.int64)
+    for t in range(T):
+        for n in range(N):
+            s = 0
+            for k in range(K):
+                s += int(qa[t, k]) * int(qw[n, k])
+            out[t, n] = s
+    return out.astype(np.int32)
+
+
+def epilogue(acc: np.ndarray, s_a: np.ndarray, s_w: np.ndarray) -> np.ndarray:
+    """Dequantize: acc * (row scale of the activation) * (column scale of the weight),
+    then one rounding to bf16  [IQ2 QuaRot Method; bf16 output]."""
+    y = (np.asarray(acc, np.float64) * np.asarray(s_a, np.float64)[:, None]
+         * np.asarray(s_w, np.float64)[None, :])
+    return f64_to_bf16(y)
+
+
+# ----------------------------------------------------------------------------
+# S5: gated FFN front  (SiLU(gate) * up; the Hadamard goes after the gating)
+# ----------------------------------------------------------------------------
+def silu_gate(gu: np.ndarray) -> np.ndarray:
+    """h = SiLU(g) * u with g, u the first and second halves of each row, float64.
+
+    SiLU(g) = g / (1 + exp(-g)).  A rotation cannot cross the SiLU [QS §2.1],
+    so the online Hadamard is applied to h, before the down projection
+    [IQ2 QuaRot Method].
+    """
+    gu = np.asarray(gu, np.float64)
+    F = gu.shape[-1] // 2
+    g = gu[..., :F]
+    u = gu[..., F:]
+    return g / (1.0 + np.exp(-g)) * u
+
+
+# ----------------------------------------------------------------------------
+# chains
+# ----------------------------------------------------------------------------
+def prep_weight(W: np.ndarray, rotate: bool, bits: int = 4):
+    """Offline weight preparation: optional Hadamard rotation of every row along K
+    (the online Hadamard's inverse folded into the weight, [IQ2 QuaRot Method]),
+    then per-output-channel symmetric quantization (rows of W [N][K]).
+    Returns (codes int8 [N][K], s_w float32 [N], the fp32 values that were quantized)."""
+    Wr = fwht(W).astype(np.float32) if rotate else np.asarray(W, np.float32)
+    q, s = quant_sym(Wr, bits)
+    return q, s, Wr
+
+
+def prequant(x: np.ndarray, flags: int, Q=None, M=None) -> np.ndarray:
+    """float64 values that reach the activation quantizer.
+
+    ``x`` is float64 [T][D] (or [T][2D] gate|up with FLAG_SWIGLU).  Order:
+    align -> gate -> Hadamard, as selected by ``flags``.
+    """
+    v = np.asarray(x, np.float64)
+    if flags & FLAG_ALIGN:
+        v = align(v, Q, M)
+    if flags & FLAG_SWIGLU:
+        v = silu_gate(v)
+    if flags & FLAG_FWHT:
+        v = fwht(v)
+    return v
+
+
+def rotated_linear(x_bits: np.ndarray, flags: int, wq: np.ndarray, s_w: np.ndarray,
+                   Q=None, M=None):
+    """Whole unit on bf16 input bits: pre-quant values -> fp32 -> per-token INT4
+    -> integer GEMM -> dequantized bf16.  Returns a dict of every stage."""
+    v = prequant(bf16_to_f64(x_bits), flags, Q, M)
+    v32 = v.astype(np.float32)
+    qa, s_a = quant_int4(v32)
+    acc = gemm_int(qa, wq)
+    y = epilogue(acc, s_a, s_w)
+    return {"prequant": v, "prequant32": v32, "codes": qa, "s_a": s_a, "acc": acc, "y": y}
+
+
+def residual(x_bits: np.ndarray, Q, M, addend_bits: np.ndarray) -> np.ndarray:
+    """bf16(align(x) + addend): the aligned skip plus the block output, one rounding."""
+    return f64_to_bf16(align(bf16_to_f64(x_bits), Q, M) + bf16_to_f64(addend_bits))
+
+
+def layer(x0_bits, basis, wq: dict, s_w: dict, D: int):
+    """One decoder layer's quantized data path on bf16 input bits.
+
+    qkv = L(x0); o = L(V part of qkv) (each token attends only to itself);
+    x1 = bf16(align1(x0) + o); gu = L(x1); d = L_down(FWHT(SiLU(g) * u));
+    x2 = bf16(align2(x1) + d).  Returns every stage."""
+    (Q1, M1), (Q2, M2) = basis
+    st = {}
+    st["qkv"] = rotated_linear(x0_bits, 0, wq["qkv"], s_w["qkv"])
+    v_bits = st["qkv"]["y"][:, 2 * D:3 * D]
+    st["o"] = rotated_linear(v_bits, 0, wq["o"], s_w["o"])
+    st["x1"] = residual(x0_bits, Q1, M1, st["o"]["y"])
+    st["gate_up"] = rotated_linear(st["x1"], 0, wq["gate_up"], s_w["gate_up"])
+    st["down"] = rotated_linear(st["gate_up"]["y"], FLAG_SWIGLU | FLAG_FWHT, wq["down"],
+                                s_w["down"])
+    st["x2"] = residual(st["x1"], Q2, M2, st["down"]["y"])
+    return st
