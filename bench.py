@@ -1,0 +1,230 @@
+"""Benchmark of the rotated W4A4 linear on one MI355X.
+
+One step = one rotated_linear call (align -> FWHT -> per-token INT4 -> W4A4 GEMM
+-> bf16) over the 4096-wide prefill workload (D=4096, T=2048 tokens, r=32,
+K=N=4096), synthetic seeded inputs already resident in HBM. Several copies of
+all operands are rotated so that the per-step working set does not stay in the
+256 MB last-level cache.
+
+Prints ONE JSON line (rank 0): tokens/s, the dominant kernel's roofline
+(W4A4 GEMM, int8 MFMA), and the CPU oracle timed on a bounded token sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_I8_TOPS = 5000.0          # MI355X dense int8 MFMA, TOP/s
+PEAK_HBM_GBS = 8000.0
+METRIC = "rotated W4A4 linear tokens/s; GEMM int8-MFMA TOPS and align/quant GB/s vs peak"
+GEMM_SRC = os.path.join(ROOT, "rotation_w4a4_quantized_amd", "csrc", "gemm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w4a4_gemm_D4096_T2048_traffic.json")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--config", type=int, default=1)
+    p.add_argument("--buffers", type=int, default=8, help="operand sets rotated per step")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain 256 MiB device copy (counter calibration)")
+    return p.parse_args()
+
+
+def _src_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_bytes():
+    """HBM bytes per GEMM launch from committed counter runs, or None when the
+    kernel source changed since they were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        rec = json.load(f)
+    if rec.get("gemm_src_sha256_16") != _src_hash(GEMM_SRC):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, inp, seconds):
+    """The oracle, as it stands, on a bounded token sample of the same workload."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max(int(i.get("num_threads", 1)) for i in threadpool_info()) if threadpool_info() else 1
+    except Exception:
+        threads = 1
+    Q, M = inp["basis"][0]
+    qw, s_w, _ = O.prep_weight(inp["W"]["lin"], rotate=True)      # offline, untimed
+    sample = 128
+    x = inp["x"]
+    done, t_total, i = 0, 0.0, 0
+    while t_total < seconds and done < wl.T * 4:
+        rows = x[(i * sample) % wl.T:(i * sample) % wl.T + sample]
+        t0 = time.perf_counter()
+        O.rotated_linear(rows, O.FLAG_ALIGN | O.FLAG_FWHT, qw, s_w, Q, M)
+        t_total += time.perf_counter() - t0
+        done += rows.shape[0]
+        i += 1
+    return {"value": done / t_total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} tokens of the same workload in {sample}-token batches "
+                      f"(float64 align+FWHT, fp32 quant, float64-BLAS integer GEMM), "
+                      f"{t_total:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+
+    import rotation_w4a4_quantized_amd as rw
+    import workloads as W
+
+    rw.lib()
+    wl = W.CONFIGS[args.config]
+    if wl.is_layer:
+        raise SystemExit("bench workloads are the single-linear configs (0, 1, 4)")
+    dev = torch.device("cuda:0")
+    inp = W.workload_inputs(wl)
+    Q, M = inp["basis"][0]
+    T, D, r = wl.T, wl.D, wl.r
+    N = wl.linears[0].N
+    flags = rw.RW4_ALIGN | rw.RW4_FWHT
+
+    def g(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    Qg, Mg = g(Q), g(M)
+    x0 = g(inp["x"])
+    Wg = g(inp["W"]["lin"])
+    codes0, sw0, _ = rw.prep_weight(Wg, True)
+    del Wg
+    nb = max(1, args.buffers)
+    sets = []
+    ws_bytes = rw.rotated_linear_workspace_size(T, D, flags)
+    for i in range(nb):
+        sets.append({
+            "x": x0.clone(), "w": codes0.clone(), "sw": sw0.clone(),
+            "y": torch.empty((T, N), dtype=torch.bfloat16, device=dev),
+            "ws": torch.empty((ws_bytes,), dtype=torch.uint8, device=dev),
+        })
+    torch.cuda.synchronize()
+
+    def step(i):
+        s = sets[i % nb]
+        rw.rotated_linear(s["x"], s["w"], s["sw"], flags, Qg, Mg, out=s["y"], workspace=s["ws"])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record()
+        step(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    step_ms_ev = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    # The dominant kernel alone: the GEMM entry point on the same operands and
+    # launch configuration, HIP events around every launch on the same stream.
+    def gemm(i):
+        s = sets[i % nb]
+        codes, s_a = rw.workspace_views(s["ws"], T, D)
+        rw.w4a4_gemm(codes, s_a, s["w"], s["sw"], out=s["y"])
+
+    for i in range(args.warmup):
+        gemm(i)
+    gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        gev[i][0].record()
+        gemm(i)
+        gev[i][1].record()
+    torch.cuda.synchronize()
+    gemm_ms = float(np.mean([a.elapsed_time(b) for a, b in gev]))
+    gemm_ops = 2.0 * T * D * N
+    achieved = gemm_ops / (gemm_ms * 1e-3) / 1e12
+
+    # stage split of the prologue (same entry points the unit uses)
+    s0 = sets[0]
+    tmp = torch.empty((T, D), dtype=torch.float32, device=dev)
+    codes_t, sa_t = rw.workspace_views(s0["ws"], T, D)
+
+    def timed(fn, n=20):
+        for _ in range(3):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    align_ms = timed(lambda: rw.respin_align(s0["x"], Qg, Mg, out=tmp))
+    fwht_ms = timed(lambda: rw.fwht(tmp, out=tmp))
+    quant_ms = timed(lambda: rw.quant_act_int4(tmp, codes_t, sa_t))
+
+    if args.copy_calibration:
+        src = torch.empty((256 << 20,), dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    traffic = traffic_bytes()
+    out = {
+        "metric": METRIC,
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "D": D, "T": T, "r": r, "K": D, "N": N,
+                   "flags": "align|fwht", "operand_sets_rotated": nb},
+        "roofline": {"bound": "mfma", "kernel": "w4a4_gemm (gemm_kernel)",
+                     "achieved": achieved, "peak": PEAK_I8_TOPS, "unit": "TFLOP/s",
+                     "unit_note": "integer ops (2 per int4 multiply-add), TOP/s",
+                     "frac": achieved / PEAK_I8_TOPS, "traffic": traffic,
+                     "avg_launch_us": gemm_ms * 1e3, "ops_per_launch": gemm_ops},
+        "stages_us": {"step_events": step_ms_ev * 1e3, "align": align_ms * 1e3,
+                      "fwht": fwht_ms * 1e3, "quant": quant_ms * 1e3, "gemm": gemm_ms * 1e3},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

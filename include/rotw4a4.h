@@ -1,0 +1,174 @@
+/*
+ * rotw4a4.h -- C ABI of the MI355X (gfx950) rotated W4A4 linear data path.
+ *
+ * The online path of a rotation-quantized transformer linear layer:
+ *   low-rank residual alignment  x + Q ((M - I) (Q^T x))
+ *   online Walsh-Hadamard transform
+ *   per-token symmetric absmax INT4 activation quantization
+ *   W4A4 GEMM (int32 accumulation) with per-token x per-channel scale epilogue.
+ *
+ * Sources (web pages):
+ *   [RSQ] "ReSpinQuant: Efficient Layer-Wise LLM Quantization via Subspace
+ *         Residual Rotation Approximation" (paper notes), framework flowchart
+ *         and key designs 2-3 (T_hat = I + Q(R_sub - I)Q^T; three-step path).
+ *   [QS]  "QuaRot 与 SpinQuant", §1.3 (normalized Hadamard) and §2.2 (fast
+ *         Walsh-Hadamard transform, power-of-two sizes).
+ *   [IQ2] "Infra Quant II", QuaRot "Background" (entries +-1/sqrt(d)) and
+ *         "Method" (online Hadamard before the down projection; per-token
+ *         absmax/7 activation quantization; INT4 GEMM to INT32, then row scale
+ *         x column scale), SpinQuant "MOTIVATION" (symmetric step).
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer is a DEVICE pointer (HIP global memory on the current
+ *     device) unless stated otherwise. The caller owns every buffer; the
+ *     library never allocates or frees device memory.
+ *   - Matrices are row-major. Activations are [T][D] (token rows).
+ *   - bf16 is IEEE-754 binary32's upper 16 bits; conversions to bf16 round to
+ *     nearest, ties to even.
+ *   - INT4 codes: two's-complement nibbles, two per byte, element 2j in the
+ *     low nibble of byte j, rows K-contiguous ([rows][K/2] bytes).
+ *   - `stream` is a hipStream_t passed as void* (NULL = default stream). All
+ *     work is enqueued on it; calls return after launch. Argument errors are
+ *     detected on the host before anything is launched; launch failures
+ *     return RW4_ERR_HIP; asynchronous device faults surface at the caller's
+ *     next synchronization.
+ *   - Pointers to bf16/fp32/int32 arrays, codes and scales must be 16-byte
+ *     aligned (RW4_ERR_MISALIGNED otherwise), except M (4-byte).
+ *   - T = 0 is a valid empty call (returns RW4_OK, launches nothing).
+ *   - The library holds no state between calls and is thread-safe; calls that
+ *     write overlapping buffers must be ordered by the caller.
+ *   - Floating point is IEEE: no fast-math; fp32 division is correctly
+ *     rounded; denormals are kept.
+ */
+#ifndef ROTW4A4_H
+#define ROTW4A4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rw4_status {
+  RW4_OK = 0,
+  RW4_ERR_INVALID_ARG = -1, /* null pointer, negative size, bad dtype or flag */
+  RW4_ERR_UNSUPPORTED = -2, /* valid but outside what the kernels implement */
+  RW4_ERR_MISALIGNED = -3,  /* pointer not 16-byte aligned */
+  RW4_ERR_WORKSPACE = -4,   /* workspace missing or too small */
+  RW4_ERR_HIP = -5          /* the HIP runtime reported an error at launch */
+} rw4_status;
+
+typedef enum rw4_dtype { RW4_BF16 = 0, RW4_F32 = 1, RW4_I32 = 2 } rw4_dtype;
+
+/* flags of rotated_linear */
+enum { RW4_ALIGN = 1, RW4_FWHT = 2, RW4_SWIGLU = 4 };
+
+/*
+ * respin_align -- online low-rank residual alignment [RSQ key design 3].
+ *   out[t] = x[t] + Q ((M - I_r) (Q^T x[t]))  (+ addend[t])
+ * which equals T_hat x[t] with T_hat = I + Q (M - I) Q^T in SO(D) [RSQ key
+ * design 2]. M is the orthogonal r x r sub-rotation (R_sub); the page's small
+ * matrix is M - I, which the kernel forms exactly while staging M.
+ *   x      [T][D], dtype x_dt (RW4_BF16 or RW4_F32)
+ *   out    [T][D], dtype out_dt (RW4_BF16 or RW4_F32); must not alias x
+ *   Q      fp32 [D][r], orthonormal columns (not checked)
+ *   M      fp32 [r][r]
+ *   addend nullable, [T][D] of dtype out_dt, added after the alignment (the
+ *          block output of a residual connection); one rounding to out_dt
+ * Constraints: 0 <= r <= min(D, 128), r % 4 == 0 (r = 0: out = x (+ addend));
+ * D >= 1, D % 8 == 0. Arithmetic is fp32.
+ */
+rw4_status respin_align(const void* x, rw4_dtype x_dt, void* out, rw4_dtype out_dt,
+                        const float* Q, const float* M, const void* addend,
+                        int64_t T, int64_t D, int64_t r, void* stream);
+
+/*
+ * fwht -- normalized Walsh-Hadamard transform of every row [QS §2.2; IQ2
+ * QuaRot Background]: y[t] = H_D x[t], H_D = Sylvester (natural-order)
+ * Hadamard / sqrt(D), entries (-1)^popcount(i&j) / sqrt(D). fp32 butterflies;
+ * the scale is one multiply by fl32(1/sqrt(D)) after the last stage.
+ *   x  [T][D], dtype x_dt (RW4_BF16 or RW4_F32)
+ *   y  fp32 [T][D]; may alias x when x_dt == RW4_F32 (in place)
+ * Constraints: D a power of two, 2 <= D <= 32768.
+ */
+rw4_status fwht(const void* x, rw4_dtype x_dt, float* y, int64_t T, int64_t D, void* stream);
+
+/*
+ * quant_act_int4 -- per-row symmetric absmax INT4 quantization [IQ2 QuaRot
+ * Method; SpinQuant MOTIVATION]:
+ *   scales[t] = fl32(max_i |x[t][i]| / 7)            (IEEE fp32 division)
+ *   q         = clamp(rint(fl32(x[t][i] / scales[t])), -8, 7)   (half-even)
+ *   all-zero row: scales[t] = 0, codes 0.
+ * Rows of a weight matrix [N][K] use the same call (per-output-channel).
+ *   x       [T][D], dtype x_dt (RW4_BF16 or RW4_F32)
+ *   codes   uint8 [T][D/2] (packed INT4, see conventions)
+ *   scales  fp32 [T]
+ * Constraints: D even, 2 <= D <= 1048576.
+ */
+rw4_status quant_act_int4(const void* x, rw4_dtype x_dt, uint8_t* codes, float* scales,
+                          int64_t T, int64_t D, void* stream);
+
+/*
+ * w4a4_gemm -- INT4 x INT4 GEMM with int32 accumulation and dequantization
+ * [IQ2 QuaRot Method]:
+ *   acc[t][n] = sum_k a[t][k] * w[n][k]                  (exact int32)
+ *   y[t][n]   = bf16( (fp32(acc) * s_a[t]) * s_w[n] )    (y_dt = RW4_BF16)
+ *   y[t][n]   = acc[t][n]                                (y_dt = RW4_I32)
+ *   a    uint8 [T][K/2]   packed activation codes;  s_a fp32 [T]
+ *   w    uint8 [N][K/2]   packed weight codes;      s_w fp32 [N]
+ *   y    [T][N], bf16 or int32 (s_a, s_w unused for RW4_I32 and may be NULL)
+ * Constraints: K % 32 == 0, 32 <= K <= 131072; N >= 1.
+ */
+rw4_status w4a4_gemm(const uint8_t* a, const float* s_a, const uint8_t* w, const float* s_w,
+                     void* y, rw4_dtype y_dt, int64_t T, int64_t K, int64_t N, void* stream);
+
+/*
+ * rotated_linear -- the whole unit: [align] -> [SiLU gate] -> [FWHT] ->
+ * per-token INT4 quantization -> W4A4 GEMM -> bf16.
+ *   flags  RW4_ALIGN: align the D-wide input with (Q, M, r) first.
+ *          RW4_SWIGLU: the input row is a gate|up pair of width 2D; the
+ *            quantized vector is SiLU(gate) * up in fp32 (SiLU(g) = g/(1+e^-g)).
+ *          RW4_FWHT: Hadamard transform of size D before quantization.
+ *          flags = 0: quantize x as is. ALIGN and SWIGLU are exclusive.
+ *   x        bf16, T rows of D (or 2D with SWIGLU) values, row stride ldx
+ *            elements (ldx >= width, ldx % 8 == 0)
+ *   Q, M, r  as respin_align (ignored without RW4_ALIGN)
+ *   w, s_w   weight codes uint8 [N][D/2] and fp32 scales [N]; the weights must
+ *            already carry the inverse of every rotation applied here (e.g.
+ *            rows Hadamard-transformed along K when RW4_FWHT is set)
+ *   y        bf16 [T][N]
+ *   workspace device memory of at least rotated_linear_workspace_size(T, D,
+ *            flags) bytes, 256-byte aligned. After the call it holds the
+ *            activation codes uint8 [T][D/2] at offset 0 and the per-token
+ *            scales fp32 [T] at offset rw4_align256(T * D / 2); the rest is
+ *            internal.
+ *   dbg_prequant nullable fp32 [T][D]: if given, receives the fp32 values that
+ *            were quantized (for stage-wise checking).
+ * Constraints: D % 32 == 0; with RW4_FWHT, D a power of two <= 32768.
+ */
+rw4_status rotated_linear(const void* x, int64_t ldx, int64_t T, int64_t D,
+                          const float* Q, const float* M, int64_t r, unsigned flags,
+                          const uint8_t* w, const float* s_w, int64_t N, void* y,
+                          void* workspace, size_t ws_bytes, float* dbg_prequant,
+                          void* stream);
+
+/* bytes of workspace rotated_linear needs for (T, D, flags); 0 on bad input */
+size_t rotated_linear_workspace_size(int64_t T, int64_t D, unsigned flags);
+
+/* n rounded up to a multiple of 256 (workspace offsets) */
+size_t rw4_align256(size_t n);
+
+/* static, human-readable name of a status code */
+const char* rw4_status_string(rw4_status s);
+
+/* ABI version of this header (bumped on any signature change) */
+int rw4_abi_version(void);
+
+#define RW4_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ROTW4A4_H */

@@ -1,0 +1,243 @@
+"""Python binding of librotw4a4 (gfx950): the rotated W4A4 linear data path.
+
+Argument marshalling only: every step runs in the HIP library behind the C ABI
+declared in include/rotw4a4.h. PyTorch provides device memory and streams.
+The functions keep the ABI's names; they take CUDA (HIP) tensors and enqueue
+on torch's current stream. There is no CPU fallback: without the built
+library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+__all__ = [
+    "RW4_ALIGN", "RW4_FWHT", "RW4_SWIGLU", "Rw4Error", "lib", "library_path",
+    "respin_align", "fwht", "quant_act_int4", "w4a4_gemm", "rotated_linear",
+    "rotated_linear_workspace_size", "prep_weight", "layer",
+]
+
+RW4_ALIGN, RW4_FWHT, RW4_SWIGLU = 1, 2, 4
+_BF16, _F32, _I32 = 0, 1, 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "librotw4a4.so")
+_lib = None
+
+EXPORTS = ("respin_align", "fwht", "quant_act_int4", "w4a4_gemm", "rotated_linear",
+           "rotated_linear_workspace_size", "rw4_align256", "rw4_status_string",
+           "rw4_abi_version")
+
+
+class Rw4Error(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {msg} (status {status})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (built in-tree); raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise RuntimeError(
+            f"{library_path} is missing: build it with "
+            "`python -m rotation_w4a4_quantized_amd.build` (no CPU fallback exists)")
+    L = ctypes.CDLL(library_path)
+    vp, i64, u32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint, ctypes.c_size_t
+    i32 = ctypes.c_int
+    L.respin_align.argtypes = [vp, i32, vp, i32, vp, vp, vp, i64, i64, i64, vp]
+    L.fwht.argtypes = [vp, i32, vp, i64, i64, vp]
+    L.quant_act_int4.argtypes = [vp, i32, vp, vp, i64, i64, vp]
+    L.w4a4_gemm.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp]
+    L.rotated_linear.argtypes = [vp, i64, i64, i64, vp, vp, i64, u32, vp, vp, i64, vp, vp, sz,
+                                 vp, vp]
+    L.rotated_linear_workspace_size.argtypes = [i64, i64, u32]
+    L.rotated_linear_workspace_size.restype = sz
+    L.rw4_align256.argtypes = [sz]
+    L.rw4_align256.restype = sz
+    L.rw4_status_string.argtypes = [i32]
+    L.rw4_status_string.restype = ctypes.c_char_p
+    L.rw4_abi_version.restype = i32
+    for f in ("respin_align", "fwht", "quant_act_int4", "w4a4_gemm", "rotated_linear"):
+        getattr(L, f).restype = i32
+    _lib = L
+    return L
+
+
+# ---------------------------------------------------------------- helpers
+def _torch():
+    import torch
+    return torch
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+def _check(fn: str, st: int):
+    if st != 0:
+        raise Rw4Error(fn, st, lib().rw4_status_string(st).decode())
+
+
+def _fdt(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return _BF16
+    if t.dtype == torch.float32:
+        return _F32
+    raise TypeError(f"expected bf16 or fp32 tensor, got {t.dtype}")
+
+
+def _rows(x):
+    if x.dim() != 2 or not x.is_cuda:
+        raise ValueError("expected a 2-D CUDA tensor [T][D]")
+    if x.stride(1) != 1:
+        raise ValueError("rows must be contiguous")
+
+
+def _contig(x):
+    _rows(x)
+    if not x.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+
+
+# ---------------------------------------------------------------- entry points
+def respin_align(x, Q, M, out=None, addend=None, out_dtype=None):
+    """out = x + Q (M - I) Q^T x (+ addend), per token row; see include/rotw4a4.h."""
+    torch = _torch()
+    _contig(x)
+    T, D = x.shape
+    r = Q.shape[1] if Q is not None else 0
+    if out is None:
+        out = torch.empty((T, D), dtype=out_dtype or torch.float32, device=x.device)
+    if addend is not None:
+        _contig(addend)
+        if addend.dtype != out.dtype or addend.shape != out.shape:
+            raise ValueError("addend must match out in dtype and shape")
+    if r > 0:
+        if Q.dtype != torch.float32 or M.dtype != torch.float32:
+            raise TypeError("Q and M must be fp32")
+        Q, M = Q.contiguous(), M.contiguous()
+    st = lib().respin_align(_p(x), _fdt(x), _p(out), _fdt(out), _p(Q) if r else None,
+                            _p(M) if r else None, _p(addend), T, D, r, _stream())
+    _check("respin_align", st)
+    return out
+
+
+def fwht(x, out=None):
+    """Normalized Walsh-Hadamard transform of every row -> fp32 (in place if out is x)."""
+    torch = _torch()
+    _contig(x)
+    T, D = x.shape
+    if out is None:
+        out = torch.empty((T, D), dtype=torch.float32, device=x.device)
+    st = lib().fwht(_p(x), _fdt(x), _p(out), T, D, _stream())
+    _check("fwht", st)
+    return out
+
+
+def quant_act_int4(x, codes=None, scales=None) -> Tuple:
+    """Per-row absmax INT4: (codes uint8 [T][D/2], scales fp32 [T])."""
+    torch = _torch()
+    _contig(x)
+    T, D = x.shape
+    if codes is None:
+        codes = torch.empty((T, D // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((T,), dtype=torch.float32, device=x.device)
+    st = lib().quant_act_int4(_p(x), _fdt(x), _p(codes), _p(scales), T, D, _stream())
+    _check("quant_act_int4", st)
+    return codes, scales
+
+
+def w4a4_gemm(a, s_a, w, s_w, out=None, out_dtype=None):
+    """y = bf16(acc * s_a[t] * s_w[n]) or raw int32 acc (out_dtype=torch.int32)."""
+    torch = _torch()
+    _contig(a)
+    _contig(w)
+    T, KB = a.shape
+    N = w.shape[0]
+    if w.shape[1] != KB:
+        raise ValueError("a and w must have the same K")
+    odt = out_dtype or (out.dtype if out is not None else torch.bfloat16)
+    if out is None:
+        out = torch.empty((T, N), dtype=odt, device=a.device)
+    ydt = _I32 if odt == torch.int32 else _BF16
+    st = lib().w4a4_gemm(_p(a), _p(s_a), _p(w), _p(s_w), _p(out), ydt, T, 2 * KB, N, _stream())
+    _check("w4a4_gemm", st)
+    return out
+
+
+def rotated_linear_workspace_size(T: int, D: int, flags: int) -> int:
+    return int(lib().rotated_linear_workspace_size(T, D, flags))
+
+
+def rotated_linear(x, w, s_w, flags: int, Q=None, M=None, out=None, workspace=None,
+                   dbg_prequant=None):
+    """[align] -> [SiLU gate] -> [FWHT] -> INT4 quant -> W4A4 GEMM -> bf16 [T][N].
+
+    ``x`` is bf16 [T][D] (or [T][2D] with RW4_SWIGLU); a row-strided view is
+    allowed. Returns (y, workspace); the workspace holds the activation codes
+    and scales after the call (layout in include/rotw4a4.h).
+    """
+    torch = _torch()
+    _rows(x)
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bf16")
+    T = x.shape[0]
+    D = x.shape[1] // 2 if flags & RW4_SWIGLU else x.shape[1]
+    N = w.shape[0]
+    r = Q.shape[1] if (flags & RW4_ALIGN) and Q is not None else 0
+    need = rotated_linear_workspace_size(T, D, flags)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    st = lib().rotated_linear(_p(x), x.stride(0), T, D, _p(Q) if r else None,
+                              _p(M) if r else None, r, flags, _p(w), _p(s_w), N, _p(out),
+                              _p(workspace), workspace.numel() * workspace.element_size(),
+                              _p(dbg_prequant), _stream())
+    _check("rotated_linear", st)
+    return out, workspace
+
+
+def workspace_views(workspace, T: int, D: int):
+    """(codes uint8 [T][D/2], scales fp32 [T]) inside a rotated_linear workspace."""
+    off = int(lib().rw4_align256(T * D // 2))
+    codes = workspace[: T * D // 2].view(T, D // 2)
+    scales = workspace[off: off + 4 * T].view(_torch().float32)
+    return codes, scales
+
+
+def prep_weight(W, rotate: bool):
+    """Offline weight preparation on the GPU: optional row-wise Hadamard along K
+    (fwht), then per-output-channel INT4 (quant_act_int4). W fp32 [N][K]."""
+    _contig(W)
+    src = fwht(W) if rotate else W
+    codes, s_w = quant_act_int4(src)
+    return codes, s_w, src
+
+
+def layer(x0, basis, weights, D: int, ws=None):
+    """One decoder layer's quantized path (each token attends only to itself):
+    qkv = L(x0); o = L(V part of qkv); x1 = bf16(align1(x0) + o);
+    gu = L(x1); d = L_down(FWHT(SiLU(g) * u)); x2 = bf16(align2(x1) + d).
+    ``weights``: name -> (codes, s_w) for qkv, o, gate_up, down. Returns a dict
+    of every stage's output tensor."""
+    torch = _torch()
+    (Q1, M1), (Q2, M2) = basis
+    st = {}
+    st["qkv"], _ = rotated_linear(x0, *weights["qkv"], flags=0)
+    st["o"], _ = rotated_linear(st["qkv"][:, 2 * D:3 * D], *weights["o"], flags=0)
+    st["x1"] = respin_align(x0, Q1, M1, addend=st["o"], out_dtype=torch.bfloat16)
+    st["gate_up"], _ = rotated_linear(st["x1"], *weights["gate_up"], flags=0)
+    st["down"], _ = rotated_linear(st["gate_up"], *weights["down"], flags=RW4_SWIGLU | RW4_FWHT)
+    st["x2"] = respin_align(st["x1"], Q2, M2, addend=st["down"], out_dtype=torch.bfloat16)
+    return st

@@ -1,0 +1,149 @@
+// C ABI of the rotated W4A4 path: host-side argument validation, then launch.
+// Every check runs before any HIP call, so invalid arguments never touch the
+// device (and can be tested without one).
+#include <hip/hip_runtime.h>
+
+#include "../../include/rotw4a4.h"
+#include "launch.hpp"
+
+namespace {
+
+inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+inline bool fdt(rw4_dtype d) { return d == RW4_BF16 || d == RW4_F32; }
+inline rw4_status hip_status(hipError_t e) { return e == hipSuccess ? RW4_OK : RW4_ERR_HIP; }
+inline hipStream_t strm(void* s) { return static_cast<hipStream_t>(s); }
+
+rw4_status check_align_args(const void* x, rw4_dtype x_dt, const void* out, rw4_dtype out_dt,
+                            const float* Q, const float* M, int64_t T, int64_t D, int64_t r) {
+  if (!x || !out || T < 0 || D < 1 || r < 0) return RW4_ERR_INVALID_ARG;
+  if (!fdt(x_dt) || !fdt(out_dt)) return RW4_ERR_INVALID_ARG;
+  if (r > 0 && (!Q || !M)) return RW4_ERR_INVALID_ARG;
+  if (r > D || r > 128 || (r % 4) != 0 || (D % 8) != 0) return RW4_ERR_UNSUPPORTED;
+  if (D > (int64_t(1) << 30)) return RW4_ERR_UNSUPPORTED;
+  if (!al16(x) || !al16(out) || (r > 0 && !al16(Q))) return RW4_ERR_MISALIGNED;
+  if (r > 0 && (reinterpret_cast<uintptr_t>(M) & 3u)) return RW4_ERR_MISALIGNED;
+  return RW4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rw4_abi_version(void) { return RW4_ABI_VERSION; }
+
+size_t rw4_align256(size_t n) { return (n + 255u) & ~static_cast<size_t>(255u); }
+
+const char* rw4_status_string(rw4_status s) {
+  switch (s) {
+    case RW4_OK: return "ok";
+    case RW4_ERR_INVALID_ARG: return "invalid argument";
+    case RW4_ERR_UNSUPPORTED: return "unsupported shape or parameter";
+    case RW4_ERR_MISALIGNED: return "pointer not 16-byte aligned";
+    case RW4_ERR_WORKSPACE: return "workspace missing or too small";
+    case RW4_ERR_HIP: return "HIP runtime error at launch";
+  }
+  return "unknown status";
+}
+
+rw4_status respin_align(const void* x, rw4_dtype x_dt, void* out, rw4_dtype out_dt,
+                        const float* Q, const float* M, const void* addend, int64_t T, int64_t D,
+                        int64_t r, void* stream) {
+  rw4_status st = check_align_args(x, x_dt, out, out_dt, Q, M, T, D, r);
+  if (st != RW4_OK) return st;
+  if (addend && !al16(addend)) return RW4_ERR_MISALIGNED;
+  if (x == out) return RW4_ERR_INVALID_ARG;
+  if (T == 0) return RW4_OK;
+  return hip_status(rw4::launch_align(x, x_dt == RW4_F32, out, out_dt == RW4_F32, Q, M, addend, T,
+                                      D, r, strm(stream)));
+}
+
+rw4_status fwht(const void* x, rw4_dtype x_dt, float* y, int64_t T, int64_t D, void* stream) {
+  if (!x || !y || T < 0 || !fdt(x_dt)) return RW4_ERR_INVALID_ARG;
+  if (!pow2(D) || D < 2 || D > 32768) return RW4_ERR_UNSUPPORTED;
+  if (!al16(x) || !al16(y)) return RW4_ERR_MISALIGNED;
+  if (x == static_cast<const void*>(y) && x_dt != RW4_F32) return RW4_ERR_INVALID_ARG;
+  if (T == 0) return RW4_OK;
+  return hip_status(rw4::launch_row(x, x_dt == RW4_F32 ? rw4::IN_F32 : rw4::IN_BF16, D, T, D, true,
+                                    y, nullptr, nullptr, nullptr, strm(stream)));
+}
+
+rw4_status quant_act_int4(const void* x, rw4_dtype x_dt, uint8_t* codes, float* scales, int64_t T,
+                          int64_t D, void* stream) {
+  if (!x || !codes || !scales || T < 0 || !fdt(x_dt)) return RW4_ERR_INVALID_ARG;
+  if (D < 2 || (D % 2) != 0 || D > (int64_t(1) << 20)) return RW4_ERR_UNSUPPORTED;
+  if (!al16(x) || !al16(codes) || !al16(scales)) return RW4_ERR_MISALIGNED;
+  if (T == 0) return RW4_OK;
+  const int in = x_dt == RW4_F32 ? rw4::IN_F32 : rw4::IN_BF16;
+  if (pow2(D) && D <= 32768)
+    return hip_status(rw4::launch_row(x, in, D, T, D, false, nullptr, codes, scales, nullptr,
+                                      strm(stream)));
+  return hip_status(rw4::launch_quant_generic(x, in, D, T, D, codes, scales, strm(stream)));
+}
+
+rw4_status w4a4_gemm(const uint8_t* a, const float* s_a, const uint8_t* w, const float* s_w,
+                     void* y, rw4_dtype y_dt, int64_t T, int64_t K, int64_t N, void* stream) {
+  if (!a || !w || !y || T < 0 || N < 1) return RW4_ERR_INVALID_ARG;
+  if (y_dt != RW4_BF16 && y_dt != RW4_I32) return RW4_ERR_INVALID_ARG;
+  if (y_dt == RW4_BF16 && (!s_a || !s_w)) return RW4_ERR_INVALID_ARG;
+  if (K < 32 || (K % 32) != 0 || K > 131072) return RW4_ERR_UNSUPPORTED;
+  if (T > (int64_t(1) << 31) - 1 || N > (int64_t(1) << 31) - 1) return RW4_ERR_UNSUPPORTED;
+  if (!al16(a) || !al16(w) || !al16(y)) return RW4_ERR_MISALIGNED;
+  if (y_dt == RW4_BF16 && (!al16(s_a) || !al16(s_w))) return RW4_ERR_MISALIGNED;
+  if (T == 0) return RW4_OK;
+  return hip_status(rw4::launch_gemm(a, s_a, w, s_w, y, y_dt == RW4_I32, T, K, N, strm(stream)));
+}
+
+size_t rotated_linear_workspace_size(int64_t T, int64_t D, unsigned flags) {
+  if (T < 0 || D < 2 || (D % 2) != 0) return 0;
+  size_t n = rw4_align256(static_cast<size_t>(T) * static_cast<size_t>(D) / 2) +
+             rw4_align256(4u * static_cast<size_t>(T));
+  if (flags & RW4_ALIGN) n += rw4_align256(4u * static_cast<size_t>(T) * static_cast<size_t>(D));
+  return n;
+}
+
+rw4_status rotated_linear(const void* x, int64_t ldx, int64_t T, int64_t D, const float* Q,
+                          const float* M, int64_t r, unsigned flags, const uint8_t* w,
+                          const float* s_w, int64_t N, void* y, void* workspace, size_t ws_bytes,
+                          float* dbg_prequant, void* stream) {
+  if (!x || !w || !s_w || !y || T < 0 || N < 1) return RW4_ERR_INVALID_ARG;
+  if (flags & ~static_cast<unsigned>(RW4_ALIGN | RW4_FWHT | RW4_SWIGLU)) return RW4_ERR_INVALID_ARG;
+  if ((flags & RW4_ALIGN) && (flags & RW4_SWIGLU)) return RW4_ERR_INVALID_ARG;
+  if (!pow2(D) || D < 32 || D > 32768) return RW4_ERR_UNSUPPORTED;
+  const int64_t width = (flags & RW4_SWIGLU) ? 2 * D : D;
+  if (ldx < width || (ldx % 8) != 0) return RW4_ERR_INVALID_ARG;
+  if (flags & RW4_ALIGN) {
+    rw4_status st = check_align_args(x, RW4_BF16, x, RW4_F32, Q, M, T, D, r);
+    if (st != RW4_OK) return st;
+    if (ldx != D) return RW4_ERR_UNSUPPORTED;
+  }
+  if (T > (int64_t(1) << 31) - 1 || N > (int64_t(1) << 31) - 1) return RW4_ERR_UNSUPPORTED;
+  if (!al16(x) || !al16(w) || !al16(s_w) || !al16(y)) return RW4_ERR_MISALIGNED;
+  if (dbg_prequant && !al16(dbg_prequant)) return RW4_ERR_MISALIGNED;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return RW4_ERR_WORKSPACE;
+  if (ws_bytes < rotated_linear_workspace_size(T, D, flags)) return RW4_ERR_WORKSPACE;
+  if (T == 0) return RW4_OK;
+
+  hipStream_t s = strm(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint8_t* codes = ws;
+  float* s_a = reinterpret_cast<float*>(ws + rw4_align256(static_cast<size_t>(T) * D / 2));
+  const void* src = x;
+  int in = (flags & RW4_SWIGLU) ? rw4::IN_SWIGLU : rw4::IN_BF16;
+  int64_t ld = ldx;
+  if (flags & RW4_ALIGN) {
+    float* tmp = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(s_a) +
+                                          rw4_align256(4u * static_cast<size_t>(T)));
+    hipError_t e = rw4::launch_align(x, 0, tmp, 1, Q, M, nullptr, T, D, r, s);
+    if (e != hipSuccess) return RW4_ERR_HIP;
+    src = tmp;
+    in = rw4::IN_F32;
+    ld = D;
+  }
+  hipError_t e = rw4::launch_row(src, in, ld, T, D, (flags & RW4_FWHT) != 0, nullptr, codes, s_a,
+                                 dbg_prequant, s);
+  if (e != hipSuccess) return RW4_ERR_HIP;
+  return hip_status(rw4::launch_gemm(codes, s_a, w, s_w, y, false, T, D, N, s));
+}
+
+}  // extern "C"

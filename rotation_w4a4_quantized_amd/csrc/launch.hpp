@@ -1,0 +1,30 @@
+// Host-side launchers of the gfx950 kernels (called by the C ABI after validation).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rw4 {
+
+enum InMode { IN_BF16 = 0, IN_F32 = 1, IN_SWIGLU = 2 };
+
+// Per-row transform: [SiLU gate] -> [Walsh-Hadamard] -> output.
+// Output either fp32 values (yf) or INT4 codes + scales (+ optional fp32 dump).
+// D must be a power of two in [2, 32768] when do_fwht is set.
+hipError_t launch_row(const void* x, int in_mode, int64_t ldx, int64_t T, int64_t D, bool do_fwht,
+                      float* yf, uint8_t* codes, float* scales, float* dbg, hipStream_t s);
+
+// Per-row INT4 quantization for any even D (no transform).
+hipError_t launch_quant_generic(const void* x, int in_mode, int64_t ldx, int64_t T, int64_t D,
+                                uint8_t* codes, float* scales, hipStream_t s);
+
+// Low-rank residual alignment out = x + Q (M - I) Q^T x (+ addend).
+hipError_t launch_align(const void* x, int x_f32, void* out, int out_f32, const float* Q,
+                        const float* M, const void* addend, int64_t T, int64_t D, int64_t r,
+                        hipStream_t s);
+
+// W4A4 GEMM, bf16 (dequantized) or raw int32 output.
+hipError_t launch_gemm(const uint8_t* a, const float* s_a, const uint8_t* w, const float* s_w,
+                       void* y, bool i32_out, int64_t T, int64_t K, int64_t N, hipStream_t s);
+
+}  // namespace rw4

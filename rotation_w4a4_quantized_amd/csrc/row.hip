@@ -1,0 +1,351 @@
+// Per-token row kernels: gated front, Walsh-Hadamard transform, INT4 quantization.
+//
+// Walsh-Hadamard transform ("QuaRot 与 SpinQuant" §2.2; "Infra Quant II",
+// QuaRot Background): H_D = H_2 (x) ... (x) H_2, so the transform is one
+// butterfly stage per index bit and the stages commute. A row of D = 2^N fp32
+// values is split over P = D / EPT threads (EPT = 2^E values each). Pass 0
+// butterflies the low E index bits in registers right after a contiguous
+// vector load; every further pass takes the next group of at most E bits: the
+// row goes through LDS (padded one word per 16 to spread banks), each thread
+// reads the values whose indices differ only in that group, butterflies them
+// in registers and writes them back. The 1/sqrt(D) scale is one multiply after
+// the last stage.
+//
+// Quantization ("Infra Quant II", QuaRot Method; SpinQuant MOTIVATION):
+// per row, step = fl32(absmax / 7), code = clamp(rint(fl32(v / step)), -8, 7),
+// packed two per byte (element 2j in the low nibble).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace rw4 {
+namespace {
+
+__device__ __forceinline__ int padi(int i) { return i + (i >> 4); }
+
+template <int N, int E>
+struct Sched {
+  static constexpr int REM = N - E;
+  static constexpr int NP = REM > 0 ? (REM + E - 1) / E : 0;
+  static constexpr int gsize(int p) { return REM / NP + (p < REM % NP ? 1 : 0); }
+  static constexpr int gbase(int p) {
+    int b = E;
+    for (int i = 0; i < p; ++i) b += gsize(i);
+    return b;
+  }
+};
+
+// butterflies over G index bits for each of the 2^(E-G) sub-vectors held in v
+template <int E, int G>
+__device__ __forceinline__ void butterflies(float (&v)[1 << E]) {
+  constexpr int SV = 1 << G;
+#pragma unroll
+  for (int s = 0; s < (1 << (E - G)); ++s) {
+#pragma unroll
+    for (int h = 1; h < SV; h <<= 1) {
+#pragma unroll
+      for (int j = 0; j < SV; ++j) {
+        if ((j & h) == 0) {
+          const float a = v[s * SV + j];
+          const float b = v[s * SV + j + h];
+          v[s * SV + j] = a + b;
+          v[s * SV + j + h] = a - b;
+        }
+      }
+    }
+  }
+}
+
+// element index of entry j of the group [b, b+G) for free index f
+__device__ __forceinline__ int gidx(int f, int j, int b, int G) {
+  return (f & ((1 << b) - 1)) | (j << b) | ((f >> b) << (b + G));
+}
+
+template <int E, int G, int B>
+__device__ __forceinline__ void lds_pass(float (&v)[1 << E], float* rowlds, int t, bool last,
+                                         float norm) {
+  constexpr int SV = 1 << G;
+  constexpr int NS = 1 << (E - G);
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+#pragma unroll
+    for (int j = 0; j < SV; ++j) v[s * SV + j] = rowlds[padi(gidx(t * NS + s, j, B, G))];
+  butterflies<E, G>(v);
+  if (last) {
+#pragma unroll
+    for (int i = 0; i < (1 << E); ++i) v[i] *= norm;
+  }
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+#pragma unroll
+    for (int j = 0; j < SV; ++j) rowlds[padi(gidx(t * NS + s, j, B, G))] = v[s * SV + j];
+}
+
+template <int N, int E, int P>
+__device__ __forceinline__ void run_passes(float (&v)[1 << E], float* rowlds, int t, float norm) {
+  using S = Sched<N, E>;
+  if constexpr (S::NP >= 1) {
+    lds_pass<E, S::gsize(0), S::gbase(0)>(v, rowlds, t, S::NP == 1, norm);
+    __syncthreads();
+  }
+  if constexpr (S::NP >= 2) {
+    lds_pass<E, S::gsize(1), S::gbase(1)>(v, rowlds, t, S::NP == 2, norm);
+    __syncthreads();
+  }
+  if constexpr (S::NP >= 3) {
+    lds_pass<E, S::gsize(2), S::gbase(2)>(v, rowlds, t, S::NP == 3, norm);
+    __syncthreads();
+  }
+  static_assert(S::NP <= 3, "at most three LDS passes");
+}
+
+// load EPT contiguous inputs of a row starting at element e0 as fp32
+template <int IN, int EPT>
+__device__ __forceinline__ void load_row(float (&v)[EPT], const void* x, int64_t rowoff, int e0,
+                                         int D, bool active) {
+  if (!active) {
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) v[i] = 0.0f;
+    return;
+  }
+  if constexpr (IN == IN_F32) {
+    const float* p = static_cast<const float*>(x) + rowoff + e0;
+    if constexpr (EPT >= 4) {
+#pragma unroll
+      for (int i = 0; i < EPT / 4; ++i) {
+        const float4 q = reinterpret_cast<const float4*>(p)[i];
+        v[4 * i] = q.x; v[4 * i + 1] = q.y; v[4 * i + 2] = q.z; v[4 * i + 3] = q.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) v[i] = p[i];
+    }
+  } else {
+    const uint16_t* p = static_cast<const uint16_t*>(x) + rowoff + e0;
+    float g[EPT];
+    if constexpr (EPT >= 8) {
+#pragma unroll
+      for (int i = 0; i < EPT / 8; ++i) {
+        const uint4 q = reinterpret_cast<const uint4*>(p)[i];
+        g[8 * i + 0] = bf16lo(q.x); g[8 * i + 1] = bf16hi(q.x);
+        g[8 * i + 2] = bf16lo(q.y); g[8 * i + 3] = bf16hi(q.y);
+        g[8 * i + 4] = bf16lo(q.z); g[8 * i + 5] = bf16hi(q.z);
+        g[8 * i + 6] = bf16lo(q.w); g[8 * i + 7] = bf16hi(q.w);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) g[i] = bf16_to_f32(p[i]);
+    }
+    if constexpr (IN == IN_SWIGLU) {
+      // gate = first D values of the row, up = next D values
+      const uint16_t* pu = p + D;
+      float u[EPT];
+      if constexpr (EPT >= 8) {
+#pragma unroll
+        for (int i = 0; i < EPT / 8; ++i) {
+          const uint4 q = reinterpret_cast<const uint4*>(pu)[i];
+          u[8 * i + 0] = bf16lo(q.x); u[8 * i + 1] = bf16hi(q.x);
+          u[8 * i + 2] = bf16lo(q.y); u[8 * i + 3] = bf16hi(q.y);
+          u[8 * i + 4] = bf16lo(q.z); u[8 * i + 5] = bf16hi(q.z);
+          u[8 * i + 6] = bf16lo(q.w); u[8 * i + 7] = bf16hi(q.w);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) u[i] = bf16_to_f32(pu[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) v[i] = g[i] / (1.0f + expf(-g[i])) * u[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) v[i] = g[i];
+    }
+  }
+}
+
+template <int EPT>
+__device__ __forceinline__ void store_f32(float* p, const float (&v)[EPT]) {
+  if constexpr (EPT >= 4) {
+#pragma unroll
+    for (int i = 0; i < EPT / 4; ++i)
+      reinterpret_cast<float4*>(p)[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) p[i] = v[i];
+  }
+}
+
+template <int EPT>
+__device__ __forceinline__ void store_codes(uint8_t* p, const float (&v)[EPT], float s) {
+  uint32_t wds[(EPT + 7) / 8];
+#pragma unroll
+  for (int i = 0; i < (EPT + 7) / 8; ++i) wds[i] = 0;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const int q = s > 0.0f ? quant4(v[i], s) : 0;
+    wds[i / 8] |= nib(q) << (4 * (i % 8));
+  }
+  if constexpr (EPT == 32) {
+    reinterpret_cast<uint4*>(p)[0] = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+  } else if constexpr (EPT == 16) {
+    reinterpret_cast<uint2*>(p)[0] = make_uint2(wds[0], wds[1]);
+  } else if constexpr (EPT == 8) {
+    reinterpret_cast<uint32_t*>(p)[0] = wds[0];
+  } else if constexpr (EPT == 4) {
+    reinterpret_cast<uint16_t*>(p)[0] = static_cast<uint16_t>(wds[0]);
+  } else {
+    p[0] = static_cast<uint8_t>(wds[0]);
+  }
+}
+
+constexpr int kRowThreads = 256;
+
+template <int N, int E, int IN, bool FW, bool QOUT>
+__global__ void __launch_bounds__(1024)
+row_kernel(const void* __restrict__ x, int64_t ldx, int64_t T, float* __restrict__ yf,
+           uint8_t* __restrict__ codes, float* __restrict__ scales, float* __restrict__ dbg,
+           float norm) {
+  constexpr int D = 1 << N;
+  constexpr int EPT = 1 << E;
+  constexpr int P = D >> E;                         // threads per row
+  constexpr int ROWS = P >= kRowThreads ? 1 : kRowThreads / P;
+  constexpr int PADD = D + (D >> 4);
+  constexpr int WPR = P > 64 ? P / 64 : 1;          // waves per row
+  __shared__ float lds[FW ? ROWS * PADD : 1];
+  __shared__ float red[ROWS * WPR];
+
+  const int tid = threadIdx.x;
+  const int rl = tid / P;
+  const int t = tid % P;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * ROWS + rl;
+  const bool active = row < T;
+
+  float v[EPT];
+  load_row<IN, EPT>(v, x, row * ldx, t * EPT, D, active);
+
+  if constexpr (FW) {
+    float* rowlds = lds + rl * PADD;
+    butterflies<E, E>(v);
+    if constexpr (Sched<N, E>::NP == 0) {
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) v[i] *= norm;
+    } else {
+#pragma unroll
+      for (int j = 0; j < EPT; ++j) rowlds[padi(t * EPT + j)] = v[j];
+      __syncthreads();
+      run_passes<N, E, P>(v, rowlds, t, norm);
+      // back to the contiguous layout for the output phase
+#pragma unroll
+      for (int j = 0; j < EPT; ++j) v[j] = rowlds[padi(t * EPT + j)];
+    }
+  }
+
+  if constexpr (!QOUT) {
+    if (active) store_f32<EPT>(yf + row * D + t * EPT, v);
+    return;
+  } else {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) m = fmaxf(m, fabsf(v[i]));
+    if constexpr (P <= 64) {
+      m = group_max<P>(m);
+    } else {
+      m = wave_max(m);
+      if ((tid & 63) == 0) red[rl * WPR + t / 64] = m;
+      __syncthreads();
+      m = red[rl * WPR];
+#pragma unroll
+      for (int i = 1; i < WPR; ++i) m = fmaxf(m, red[rl * WPR + i]);
+    }
+    if (!active) return;
+    const float s = m / 7.0f;
+    if (t == 0) scales[row] = s;
+    store_codes<EPT>(codes + row * (D / 2) + t * (EPT / 2), v, s);
+    if (dbg) store_f32<EPT>(dbg + row * D + t * EPT, v);
+  }
+}
+
+template <int N, int IN, bool FW, bool QOUT>
+hipError_t launch_row_n(const void* x, int64_t ldx, int64_t T, float* yf, uint8_t* codes,
+                        float* scales, float* dbg, hipStream_t s) {
+  constexpr int E = N >= 15 ? 5 : (N < 4 ? N : 4);
+  constexpr int P = (1 << N) >> E;
+  constexpr int ROWS = P >= kRowThreads ? 1 : kRowThreads / P;
+  const float norm = static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(1 << N)));
+  const int64_t blocks = (T + ROWS - 1) / ROWS;
+  hipLaunchKernelGGL((row_kernel<N, E, IN, FW, QOUT>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(P * ROWS), 0, s, x, ldx, T, yf, codes, scales, dbg, norm);
+  return hipGetLastError();
+}
+
+template <int IN, bool FW, bool QOUT>
+hipError_t dispatch_n(int n, const void* x, int64_t ldx, int64_t T, float* yf, uint8_t* codes,
+                      float* scales, float* dbg, hipStream_t s) {
+  switch (n) {
+#define RW4_CASE(k) \
+  case k: return launch_row_n<k, IN, FW, QOUT>(x, ldx, T, yf, codes, scales, dbg, s);
+    RW4_CASE(1) RW4_CASE(2) RW4_CASE(3) RW4_CASE(4) RW4_CASE(5) RW4_CASE(6) RW4_CASE(7)
+    RW4_CASE(8) RW4_CASE(9) RW4_CASE(10) RW4_CASE(11) RW4_CASE(12) RW4_CASE(13) RW4_CASE(14)
+    RW4_CASE(15)
+#undef RW4_CASE
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// ---------------------------------------------------------------- any even D
+template <int IN>
+__global__ void __launch_bounds__(256)
+quant_generic_kernel(const void* __restrict__ x, int64_t ldx, int64_t D,
+                     uint8_t* __restrict__ codes, float* __restrict__ scales) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  auto val = [&](int64_t i) -> float {
+    if constexpr (IN == IN_F32) return static_cast<const float*>(x)[row * ldx + i];
+    else return bf16_to_f32(static_cast<const uint16_t*>(x)[row * ldx + i]);
+  };
+  float m = 0.0f;
+  for (int64_t i = tid; i < D; i += 256) m = fmaxf(m, fabsf(val(i)));
+  m = wave_max(m);
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = m / 7.0f;
+  if (tid == 0) scales[row] = s;
+  for (int64_t j = tid; j < D / 2; j += 256) {
+    const int q0 = s > 0.0f ? quant4(val(2 * j), s) : 0;
+    const int q1 = s > 0.0f ? quant4(val(2 * j + 1), s) : 0;
+    codes[row * (D / 2) + j] = static_cast<uint8_t>(nib(q0) | (nib(q1) << 4));
+  }
+}
+
+}  // namespace
+
+hipError_t launch_row(const void* x, int in_mode, int64_t ldx, int64_t T, int64_t D, bool do_fwht,
+                      float* yf, uint8_t* codes, float* scales, float* dbg, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  int n = 0;
+  while ((int64_t(1) << n) < D) ++n;
+  const bool q = codes != nullptr;
+#define RW4_SEL(INM, FW, Q) \
+  if (in_mode == INM && do_fwht == FW && q == Q) \
+    return dispatch_n<INM, FW, Q>(n, x, ldx, T, yf, codes, scales, dbg, s);
+  RW4_SEL(IN_BF16, true, true) RW4_SEL(IN_BF16, true, false)
+  RW4_SEL(IN_F32, true, true) RW4_SEL(IN_F32, true, false)
+  RW4_SEL(IN_SWIGLU, true, true) RW4_SEL(IN_SWIGLU, false, true)
+  RW4_SEL(IN_BF16, false, true) RW4_SEL(IN_F32, false, true)
+#undef RW4_SEL
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_quant_generic(const void* x, int in_mode, int64_t ldx, int64_t T, int64_t D,
+                                uint8_t* codes, float* scales, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (in_mode == IN_F32)
+    hipLaunchKernelGGL(quant_generic_kernel<IN_F32>, dim3(static_cast<unsigned>(T)), dim3(256), 0,
+                       s, x, ldx, D, codes, scales);
+  else
+    hipLaunchKernelGGL(quant_generic_kernel<IN_BF16>, dim3(static_cast<unsigned>(T)), dim3(256), 0,
+                       s, x, ldx, D, codes, scales);
+  return hipGetLastError();
+}
+
+}  // namespace rw4

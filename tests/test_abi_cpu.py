@@ -1,0 +1,136 @@
+"""The C ABI library on the CPU: it loads, exports what the header declares, and
+rejects invalid arguments on the host before any device work (no GPU calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import rotation_w4a4_quantized_amd as rw
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rotw4a4.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while", "return")))
+
+
+def test_library_built_and_loads():
+    assert os.path.exists(rw.library_path), "build the HIP library first"
+    L = rw.lib()
+    assert L.rw4_abi_version() == 1
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert set(names) == set(rw.EXPORTS), names
+    L = ctypes.CDLL(rw.library_path)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    L = rw.lib()
+    for code, text in [(0, b"ok"), (-1, b"invalid argument"), (-3, b"pointer not 16-byte aligned"),
+                       (-4, b"workspace missing or too small"), (-5, b"HIP runtime error at launch")]:
+        assert L.rw4_status_string(code) == text
+    assert L.rw4_status_string(7) == b"unknown status"
+
+
+def test_workspace_size():
+    L = rw.lib()
+    assert L.rw4_align256(1) == 256 and L.rw4_align256(256) == 256 and L.rw4_align256(0) == 0
+    T, D = 2048, 4096
+    base = L.rw4_align256(T * D // 2) + L.rw4_align256(4 * T)
+    assert L.rotated_linear_workspace_size(T, D, 0) == base
+    assert L.rotated_linear_workspace_size(T, D, 2) == base
+    assert L.rotated_linear_workspace_size(T, D, 3) == base + 4 * T * D
+    assert L.rotated_linear_workspace_size(-1, D, 0) == 0
+    assert L.rotated_linear_workspace_size(4, 7, 0) == 0
+
+
+# fake, 256-byte aligned addresses: validation must reject before dereferencing
+A = ctypes.c_void_p(0x10000)
+B = ctypes.c_void_p(0x20000)
+C = ctypes.c_void_p(0x30000)
+Dp = ctypes.c_void_p(0x40000)
+ODD = ctypes.c_void_p(0x10004)
+NUL = None
+INV, UNS, MIS, WSE = -1, -2, -3, -4
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((NUL, 0, B, 1, C, Dp, NUL, 4, 64, 8, NUL), INV),        # null x
+    ((A, 0, B, 1, NUL, Dp, NUL, 4, 64, 8, NUL), INV),        # null Q with r > 0
+    ((A, 5, B, 1, C, Dp, NUL, 4, 64, 8, NUL), INV),          # bad dtype
+    ((A, 0, B, 1, C, Dp, NUL, -1, 64, 8, NUL), INV),         # negative T
+    ((A, 0, B, 1, C, Dp, NUL, 4, 64, 6, NUL), UNS),          # r % 4
+    ((A, 0, B, 1, C, Dp, NUL, 4, 64, 132, NUL), UNS),        # r > 128
+    ((A, 0, B, 1, C, Dp, NUL, 4, 60, 8, NUL), UNS),          # D % 8
+    ((ODD, 0, B, 1, C, Dp, NUL, 4, 64, 8, NUL), MIS),        # misaligned x
+    ((A, 0, A, 1, C, Dp, NUL, 4, 64, 8, NUL), INV),          # out aliases x
+    ((A, 0, B, 1, C, Dp, NUL, 0, 64, 8, NUL), 0),            # T = 0: valid, nothing launched
+])
+def test_respin_align_validation(args, expect):
+    assert rw.lib().respin_align(*args) == expect
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((A, 0, B, 4, 12, NUL), UNS),            # D not a power of two
+    ((A, 0, B, 4, 65536, NUL), UNS),         # D too large
+    ((A, 0, B, 4, 1, NUL), UNS),             # D too small
+    ((A, 0, A, 4, 64, NUL), INV),            # in place needs fp32 input
+    ((A, 2, B, 4, 64, NUL), INV),            # int32 input
+    ((ODD, 1, B, 4, 64, NUL), MIS),
+    ((A, 1, A, 0, 64, NUL), 0),              # T = 0 in place
+])
+def test_fwht_validation(args, expect):
+    assert rw.lib().fwht(*args) == expect
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((A, 0, B, NUL, 4, 64, NUL), INV),
+    ((A, 0, B, C, 4, 63, NUL), UNS),
+    ((A, 0, B, C, 4, 0, NUL), UNS),
+    ((A, 0, ODD, C, 4, 64, NUL), MIS),
+    ((A, 0, B, C, 0, 64, NUL), 0),
+])
+def test_quant_validation(args, expect):
+    assert rw.lib().quant_act_int4(*args) == expect
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((A, B, C, Dp, A, 0, 4, 48, 16, NUL), UNS),     # K % 32
+    ((A, B, C, Dp, A, 0, 4, 262144, 16, NUL), UNS), # K too large for int32 accumulators
+    ((A, NUL, C, Dp, A, 0, 4, 64, 16, NUL), INV),   # bf16 output needs scales
+    ((A, NUL, C, NUL, A, 2, 0, 64, 16, NUL), 0),    # int32 output needs none; T = 0
+    ((A, B, C, Dp, A, 1, 4, 64, 16, NUL), INV),     # fp32 output not offered
+    ((A, B, C, Dp, A, 0, 4, 64, 0, NUL), INV),      # N = 0
+    ((A, B, ODD, Dp, A, 0, 4, 64, 16, NUL), MIS),
+])
+def test_gemm_validation(args, expect):
+    assert rw.lib().w4a4_gemm(*args) == expect
+
+
+def _rl(x=A, ldx=64, T=4, D=64, Q=B, M=C, r=8, flags=3, w=Dp, sw=A, N=16, y=B, ws=C,
+        wsb=1 << 20, dbg=NUL):
+    return rw.lib().rotated_linear(x, ldx, T, D, Q, M, r, flags, w, sw, N, y, ws, wsb, dbg, NUL)
+
+
+def test_rotated_linear_validation():
+    assert _rl(flags=8) == INV                     # unknown flag
+    assert _rl(flags=1 | 4) == INV                 # align + swiglu
+    assert _rl(D=48) == UNS                        # not a power of two
+    assert _rl(ldx=32) == INV                      # stride below width
+    assert _rl(flags=4, ldx=64) == INV             # swiglu needs 2D wide rows
+    assert _rl(r=6) == UNS
+    assert _rl(ldx=128) == UNS                     # align needs contiguous rows
+    assert _rl(ws=ctypes.c_void_p(0x30010)) == WSE # workspace alignment
+    assert _rl(wsb=100) == WSE
+    assert _rl(ws=NUL) == WSE
+    assert _rl(x=ODD) == MIS
+    assert _rl(T=0) == 0

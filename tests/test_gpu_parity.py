@@ -1,0 +1,321 @@
+"""Stage parity of the HIP path against the CPU oracle (needs an MI355X).
+
+Every call goes through the C ABI (via the ctypes binding). Inputs come from
+the seeded generators; expected values come only from the oracle.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+from gpu_util import BF16_TOL, FP32_TOL, bf16_rel, dev, host, normwise, say, torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def rw():
+    import rotation_w4a4_quantized_amd as m
+    m.lib()
+    return m
+
+
+def _sync():
+    torch().cuda.synchronize()
+
+
+# ---------------------------------------------------------------- quantizer
+def _quant_input(T, D, seed, special=True):
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((T, D)) * rng.uniform(0.01, 50, (T, 1))).astype(np.float32)
+    if special and T >= 4:
+        x[0] = 0.0                                     # all-zero row
+        x[1] = 0.0
+        x[1, D // 3] = -5.0                            # one nonzero (negative) entry
+        # ties: absmax 7 -> step exactly 1, values on k + 1/2
+        x[2] = (rng.integers(-7, 7, D) + 0.5).astype(np.float32)
+        x[2, 0] = 7.0
+        x[3] = np.float32(1e-40) * rng.standard_normal(D).astype(np.float32)   # denormal row
+    return x
+
+
+@pytest.mark.parametrize("T,D", [(1, 2), (4, 6), (64, 256), (300, 4096), (5, 16384), (3, 32768),
+                                 (7, 12288), (2, 65536), (0, 64)])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_quant_act_int4(rw, T, D, dt):
+    say(f"quant_act_int4 T={T} D={D} {dt}")
+    x = _quant_input(T, D, seed=T * 7 + D)
+    if dt == "bf16":
+        xb = W.f32_to_bf16_bits(x)
+        xg = dev(xb)
+        x = W.bf16_bits_to_f32(xb)
+    else:
+        xg = dev(x)
+    codes, scales = rw.quant_act_int4(xg)
+    _sync()
+    if T == 0:
+        return
+    q, s = O.quant_int4(x)
+    np.testing.assert_array_equal(host(scales), s)
+    np.testing.assert_array_equal(host(codes), O.pack_int4(q))
+
+
+# ---------------------------------------------------------------- Hadamard
+def test_fwht_worked_example(rw):
+    x = dev(np.array([[20, 0, 0, 0], [10, 10, 10, 10]], np.float32))
+    y = host(rw.fwht(x))
+    np.testing.assert_array_equal(y, np.array([[10, 10, 10, 10], [20, 0, 0, 0]], np.float32))
+
+
+@pytest.mark.parametrize("D", [2 ** k for k in range(1, 16)])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_fwht(rw, D, dt):
+    T = 37 if D <= 4096 else 5
+    say(f"fwht T={T} D={D} {dt}")
+    x32 = W.bf16_bits_to_f32(W.gen_x(D, T, D, min(8, D // 2), 80.0))
+    xg = dev(W.f32_to_bf16_bits(x32)) if dt == "bf16" else dev(x32)
+    y = host(rw.fwht(xg))
+    assert normwise(y, O.fwht(x32)) <= FP32_TOL
+
+
+def test_fwht_in_place_and_involution(rw):
+    x = W.bf16_bits_to_f32(W.gen_x(9, 16, 4096, 8, 80.0))
+    g = dev(x)
+    rw.fwht(g, out=g)
+    rw.fwht(g, out=g)
+    assert normwise(host(g), x) <= 2 * FP32_TOL
+
+
+# ---------------------------------------------------------------- alignment
+@pytest.mark.parametrize("T,D,r", [(64, 256, 8), (37, 4096, 32), (19, 8192, 64), (9, 4096, 128),
+                                   (13, 1000, 12), (1, 64, 4)])
+@pytest.mark.parametrize("xdt", ["bf16", "f32"])
+def test_respin_align_f32(rw, T, D, r, xdt):
+    say(f"respin_align T={T} D={D} r={r} x={xdt}")
+    Q, M = W.gen_basis(D + r, D, r)
+    xb = W.gen_x(D, T, D, 8, 80.0)
+    x = W.bf16_bits_to_f32(xb)
+    xg = dev(xb) if xdt == "bf16" else dev(x)
+    out = host(rw.respin_align(xg, dev(Q), dev(M)))
+    assert normwise(out, O.align(x, Q, M)) <= FP32_TOL
+
+
+def test_respin_align_identity_cases(rw):
+    T, D = 20, 4096
+    Q, M = W.gen_basis(5, D, 32)
+    xb = W.gen_x(5, T, D, 8, 80.0)
+    x = W.bf16_bits_to_f32(xb)
+    # M = I: M - I is exactly zero, the output equals the input bit for bit
+    out = host(rw.respin_align(dev(xb), dev(Q), dev(np.eye(32, dtype=np.float32))))
+    np.testing.assert_array_equal(out, x)
+    outb = host(rw.respin_align(dev(xb), dev(Q), dev(np.eye(32, dtype=np.float32)),
+                                out_dtype=torch().bfloat16))
+    np.testing.assert_array_equal(outb, xb)
+    # r = 0: identity
+    out0 = host(rw.respin_align(dev(x), None, None))
+    np.testing.assert_array_equal(out0, x)
+    # norm preserved (T_hat is orthogonal)
+    out = host(rw.respin_align(dev(xb), dev(Q), dev(M))).astype(np.float64)
+    np.testing.assert_allclose(np.linalg.norm(out, axis=1), np.linalg.norm(x, axis=1), rtol=1e-5)
+
+
+@pytest.mark.parametrize("T,D,r", [(33, 4096, 32), (8, 4096, 32)])
+def test_respin_align_bf16_residual(rw, T, D, r):
+    Q, M = W.gen_basis(77, D, r)
+    xb = W.gen_x(77, T, D, 8, 80.0)
+    ab = W.gen_x(78, T, D, 0, 1.0)
+    out = host(rw.respin_align(dev(xb), dev(Q), dev(M), addend=dev(ab),
+                               out_dtype=torch().bfloat16))
+    ref = O.residual(xb, Q, M, ab)
+    # one rounding each side from fp32 / float64 sums: at most one bf16 ulp apart
+    diff = np.abs(out.astype(np.int32) - ref.astype(np.int32))
+    assert diff.max() <= 1
+    assert (diff > 0).mean() < 0.01
+
+
+# ---------------------------------------------------------------- GEMM
+def _codes(seed, rows, K):
+    rng = np.random.default_rng(seed)
+    return rng.integers(0, 256, (rows, K // 2), dtype=np.uint8)   # every byte is two valid codes
+
+
+@pytest.mark.parametrize("T,K,N", [(1, 32, 1), (64, 256, 256), (300, 512, 384), (129, 4096, 130),
+                                   (17, 16384, 64), (8, 4096, 12288), (257, 96, 1000)])
+def test_w4a4_gemm(rw, T, K, N):
+    say(f"w4a4_gemm T={T} K={K} N={N}")
+    a = _codes(T + K, T, K)
+    w = _codes(N + K + 1, N, K)
+    rng = np.random.default_rng(K)
+    s_a = rng.uniform(1e-3, 1.0, T).astype(np.float32)
+    s_w = rng.uniform(1e-3, 0.1, N).astype(np.float32)
+    acc = host(rw.w4a4_gemm(dev(a), None, dev(w), None, out_dtype=torch().int32))
+    ref = O.gemm_int(O.unpack_int4(a), O.unpack_int4(w))
+    np.testing.assert_array_equal(acc, ref)
+    y = host(rw.w4a4_gemm(dev(a), dev(s_a), dev(w), dev(s_w)))
+    nbad, worst = bf16_rel(y, O.epilogue(ref, s_a, s_w))
+    assert nbad == 0, worst
+
+
+def test_w4a4_gemm_extremes(rw):
+    T, K, N = 40, 16384, 72
+    a = np.full((T, K // 2), 0x88, np.uint8)            # all codes -8
+    w = np.full((N, K // 2), 0x88, np.uint8)
+    acc = host(rw.w4a4_gemm(dev(a), None, dev(w), None, out_dtype=torch().int32))
+    assert np.all(acc == 64 * K)
+    w[:, :] = 0x77                                      # all codes +7
+    acc = host(rw.w4a4_gemm(dev(a), None, dev(w), None, out_dtype=torch().int32))
+    assert np.all(acc == -56 * K)
+
+
+# ---------------------------------------------------------------- weight prep and the unit
+def _prep(rw, Wf, rotate):
+    codes, s_w, src = rw.prep_weight(dev(Wf), rotate)
+    src_h = host(src)
+    if rotate:
+        assert normwise(src_h, O.fwht(Wf)) <= FP32_TOL
+    q, s = O.quant_int4(src_h)
+    np.testing.assert_array_equal(host(s_w), s)
+    np.testing.assert_array_equal(host(codes), O.pack_int4(q))
+    return codes, s_w, q, s
+
+
+def _check_unit(rw, xb, Q, M, flags, codes_w, s_w, qw, sw_h, rows=None):
+    """Run rotated_linear on the GPU and check every stage against the oracle.
+    rows: optional token sample for the expensive float checks."""
+    t = torch()
+    T = xb.shape[0]
+    D = xb.shape[1] // 2 if flags & O.FLAG_SWIGLU else xb.shape[1]
+    dbg = t.empty((T, D), dtype=t.float32, device="cuda")
+    y, ws = rw.rotated_linear(dev(xb), codes_w, s_w, flags, dev(Q) if Q is not None else None,
+                              dev(M) if M is not None else None, dbg_prequant=dbg)
+    _sync()
+    codes_g, sa_g = (host(v) for v in rw.workspace_views(ws, T, D))
+    pre = host(dbg)
+    y = host(y)
+    sel = np.arange(T) if rows is None else rows
+    # 1. pre-quant fp32 values vs the float64 chain
+    ref_pre = O.prequant(O.bf16_to_f64(xb[sel]), flags, Q, M)
+    assert normwise(pre[sel], ref_pre) <= FP32_TOL
+    # 2. codes and scales: bit-exact on the GPU's own fp32 values
+    q, s = O.quant_int4(pre[sel])
+    np.testing.assert_array_equal(sa_g[sel], s)
+    np.testing.assert_array_equal(codes_g[sel], O.pack_int4(q))
+    # 3. GEMM + epilogue on those codes
+    ref_y = O.epilogue(O.gemm_int(q, qw), s, sw_h)
+    nbad, worst = bf16_rel(y[sel], ref_y)
+    assert nbad == 0, worst
+    # 4. end to end against the oracle's own chain: rare code flips only
+    q_own, _ = O.quant_int4(ref_pre.astype(np.float32))
+    flips = float((q_own != q).mean())
+    say(f"   end-to-end code flips vs float64 chain: {flips:.2e}")
+    assert flips < 1e-3
+    return y
+
+
+@pytest.mark.parametrize("cid", [0, 1])
+def test_rotated_linear_config(rw, cid):
+    wl = W.CONFIGS[cid]
+    say(f"rotated_linear {wl.name}")
+    inp = W.workload_inputs(wl)
+    Q, M = inp["basis"][0]
+    lin = wl.linears[0]
+    codes_w, s_w, qw, sw_h = _prep(rw, inp["W"]["lin"], lin.rotate)
+    _check_unit(rw, inp["x"], Q, M, O.FLAG_ALIGN | O.FLAG_FWHT, codes_w, s_w, qw, sw_h)
+
+
+def test_rotated_linear_config4_sampled(rw):
+    """Full 70B-shaped size (T=8192, D=8192, r=64, N=28672); float and GEMM checks
+    on 48 sampled tokens (every stage is per token, so the sample is exact)."""
+    wl = W.CONFIGS[4]
+    say(f"rotated_linear {wl.name} (sampled)")
+    inp = W.workload_inputs(wl)
+    Q, M = inp["basis"][0]
+    codes_w, s_w, src = rw.prep_weight(dev(inp["W"]["lin"]), True)
+    rows_w = np.random.default_rng(4).choice(wl.linears[0].N, 64, replace=False)
+    src_h = host(src[torch().from_numpy(rows_w).cuda()])
+    assert normwise(src_h, O.fwht(inp["W"]["lin"][rows_w])) <= FP32_TOL
+    q_s, s_s = O.quant_int4(src_h)
+    np.testing.assert_array_equal(host(codes_w)[rows_w], O.pack_int4(q_s))
+    qw = O.unpack_int4(host(codes_w))
+    sw_h = host(s_w)
+    rows = np.sort(np.random.default_rng(5).choice(wl.T, 48, replace=False))
+    _check_unit(rw, inp["x"], Q, M, O.FLAG_ALIGN | O.FLAG_FWHT, codes_w, s_w, qw, sw_h, rows=rows)
+
+
+@pytest.mark.parametrize("T,D,N,flags", [(77, 512, 200, 0), (77, 512, 200, 2), (50, 256, 64, 4 | 2),
+                                         (33, 1024, 96, 4), (130, 2048, 260, 1),
+                                         (1, 4096, 4096, 3)])
+def test_rotated_linear_flags(rw, T, D, N, flags):
+    say(f"rotated_linear T={T} D={D} N={N} flags={flags}")
+    width = 2 * D if flags & 4 else D
+    xb = W.gen_x(T + D, T, width, 4, 30.0)
+    Q, M = W.gen_basis(T + D, D, 16) if flags & 1 else (None, None)
+    Wf = W.gen_weight(N, N, D, 0.02)
+    codes_w, s_w, qw, sw_h = _prep(rw, Wf, bool(flags & 2))
+    _check_unit(rw, xb, Q, M, flags, codes_w, s_w, qw, sw_h)
+
+
+def test_rotated_linear_strided_input(rw):
+    """Row-strided bf16 input (the V third of a QKV output)."""
+    T, D, N = 24, 256, 64
+    big = W.gen_x(3, T, 3 * D, 2, 10.0)
+    Wf = W.gen_weight(4, N, D, 0.02)
+    codes_w, s_w, qw, sw_h = _prep(rw, Wf, False)
+    g = dev(big)[:, 2 * D:3 * D]
+    y, ws = rw.rotated_linear(g, codes_w, s_w, 0)
+    q, s = O.quant_int4(W.bf16_bits_to_f32(big[:, 2 * D:]))
+    ref = O.epilogue(O.gemm_int(q, qw), s, sw_h)
+    nbad, worst = bf16_rel(host(y), ref)
+    assert nbad == 0, worst
+
+
+# ---------------------------------------------------------------- decoder layer
+def _layer_check(rw, cid, sample=None):
+    wl = W.CONFIGS[cid]
+    say(f"layer {wl.name}")
+    D = wl.D
+    inp = W.workload_inputs(wl)
+    weights, qws, sws = {}, {}, {}
+    for lin in wl.linears:
+        c, s, src = rw.prep_weight(dev(inp["W"][lin.name]), lin.rotate)
+        weights[lin.name] = (c, s)
+        qws[lin.name] = O.unpack_int4(host(c))
+        sws[lin.name] = host(s)
+    basis = [(dev(Q), dev(M)) for Q, M in inp["basis"]]
+    st = rw.layer(dev(inp["x"]), basis, weights, D)
+    _sync()
+    g = {k: host(v) for k, v in st.items()}
+    rows = np.arange(wl.T) if sample is None else sample
+    # identical-input stage parity: every oracle stage is fed the GPU's previous stage
+    def lin_check(name, xin_bits, flags, out_bits):
+        pre = O.prequant(O.bf16_to_f64(xin_bits), flags)
+        q, s = O.quant_int4(pre.astype(np.float32))
+        ref = O.epilogue(O.gemm_int(q, qws[name]), s, sws[name])
+        nbad, worst = bf16_rel(out_bits, ref)
+        assert nbad == 0, (name, worst)
+    x0 = inp["x"][rows]
+    lin_check("qkv", x0, 0, g["qkv"][rows])
+    lin_check("o", g["qkv"][rows][:, 2 * D:3 * D], 0, g["o"][rows])
+    (Q1, M1), (Q2, M2) = inp["basis"]
+    for name, xin, add, Qm, Mm in (("x1", x0, g["o"][rows], Q1, M1),
+                                   ("x2", g["x1"][rows], g["down"][rows], Q2, M2)):
+        ref = O.residual(xin, Qm, Mm, add)
+        diff = np.abs(g[name][rows].astype(np.int32) - ref.astype(np.int32))
+        assert diff.max() <= 1, name
+    lin_check("gate_up", g["x1"][rows], 0, g["gate_up"][rows])
+    # the down projection's pre-quant values are fp32 (SiLU, FWHT): codes can flip
+    # at rounding boundaries, so check floats and the GEMM on the oracle's codes
+    pre = O.prequant(O.bf16_to_f64(g["gate_up"][rows]), O.FLAG_SWIGLU | O.FLAG_FWHT)
+    q, s = O.quant_int4(pre.astype(np.float32))
+    ref = O.epilogue(O.gemm_int(q, qws["down"]), s, sws["down"])
+    gd = O.bf16_to_f64(g["down"][rows])
+    rd = O.bf16_to_f64(ref)
+    assert normwise(gd, rd) < 0.02
+
+
+def test_layer_decode_config2(rw):
+    _layer_check(rw, 2)
+
+
+def test_layer_prefill_config3_sampled(rw):
+    _layer_check(rw, 3, sample=np.sort(np.random.default_rng(3).choice(4096, 32, replace=False)))
