@@ -74,7 +74,7 @@ def cpu_baseline(wl, inp, seconds):
     sample = 128
     x = inp["x"]
     done, t_total, i = 0, 0.0, 0
-    while t_total < seconds and done < wl.T * 4:
+    while t_total < seconds and done < wl.T * 64:
         rows = x[(i * sample) % wl.T:(i * sample) % wl.T + sample]
         t0 = time.perf_counter()
         O.rotated_linear(rows, O.FLAG_ALIGN | O.FLAG_FWHT, qw, s_w, Q, M)
@@ -120,7 +120,7 @@ def main():
     del Wg
     nb = max(1, args.buffers)
     sets = []
-    ws_bytes = rw.rotated_linear_workspace_size(T, D, flags)
+    ws_bytes = rw.rotated_linear_workspace_size(T, D, r, flags)
     for i in range(nb):
         sets.append({
             "x": x0.clone(), "w": codes0.clone(), "sw": sw0.clone(),
@@ -186,7 +186,8 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / n
 
-    align_ms = timed(lambda: rw.respin_align(s0["x"], Qg, Mg, out=tmp))
+    aws = torch.empty((rw.respin_align_workspace_size(T, D, r),), dtype=torch.uint8, device=dev)
+    align_ms = timed(lambda: rw.respin_align(s0["x"], Qg, Mg, out=tmp, workspace=aws))
     fwht_ms = timed(lambda: rw.fwht(tmp, out=tmp))
     quant_ms = timed(lambda: rw.quant_act_int4(tmp, codes_t, sa_t))
 

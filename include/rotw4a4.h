@@ -34,7 +34,8 @@
  *     next synchronization.
  *   - Pointers to bf16/fp32/int32 arrays, codes and scales must be 16-byte
  *     aligned (RW4_ERR_MISALIGNED otherwise), except M (4-byte).
- *   - T = 0 is a valid empty call (returns RW4_OK, launches nothing).
+ *   - T = 0 is a valid empty call: once the sizes, dtypes and flags are
+ *     valid it returns RW4_OK without inspecting any pointer or launching.
  *   - The library holds no state between calls and is thread-safe; calls that
  *     write overlapping buffers must be ordered by the caller.
  *   - Floating point is IEEE: no fast-math; fp32 division is correctly
@@ -76,12 +77,21 @@ enum { RW4_ALIGN = 1, RW4_FWHT = 2, RW4_SWIGLU = 4 };
  *   M      fp32 [r][r]
  *   addend nullable, [T][D] of dtype out_dt, added after the alignment (the
  *          block output of a residual connection); one rounding to out_dt
+ *   workspace, ws_bytes: device scratch of respin_align_workspace_size(T, D, r)
+ *          bytes (256-byte aligned). With it, bf16 x and D % 32 == 0 run on
+ *          bf16 matrix cores (Q and z split into two bf16 terms, fp32
+ *          accumulation). NULL / 0 selects the direct fp32-FMA kernel (any
+ *          supported shape, slower).
  * Constraints: 0 <= r <= min(D, 128), r % 4 == 0 (r = 0: out = x (+ addend));
  * D >= 1, D % 8 == 0. Arithmetic is fp32.
  */
 rw4_status respin_align(const void* x, rw4_dtype x_dt, void* out, rw4_dtype out_dt,
                         const float* Q, const float* M, const void* addend,
-                        int64_t T, int64_t D, int64_t r, void* stream);
+                        int64_t T, int64_t D, int64_t r, void* workspace, size_t ws_bytes,
+                        void* stream);
+
+/* bytes of workspace respin_align needs for its matrix-core path */
+size_t respin_align_workspace_size(int64_t T, int64_t D, int64_t r);
 
 /*
  * fwht -- normalized Walsh-Hadamard transform of every row [QS §2.2; IQ2
@@ -139,7 +149,7 @@ rw4_status w4a4_gemm(const uint8_t* a, const float* s_a, const uint8_t* w, const
  *            rows Hadamard-transformed along K when RW4_FWHT is set)
  *   y        bf16 [T][N]
  *   workspace device memory of at least rotated_linear_workspace_size(T, D,
- *            flags) bytes, 256-byte aligned. After the call it holds the
+ *            r, flags) bytes, 256-byte aligned. After the call it holds the
  *            activation codes uint8 [T][D/2] at offset 0 and the per-token
  *            scales fp32 [T] at offset rw4_align256(T * D / 2); the rest is
  *            internal.
@@ -153,8 +163,8 @@ rw4_status rotated_linear(const void* x, int64_t ldx, int64_t T, int64_t D,
                           void* workspace, size_t ws_bytes, float* dbg_prequant,
                           void* stream);
 
-/* bytes of workspace rotated_linear needs for (T, D, flags); 0 on bad input */
-size_t rotated_linear_workspace_size(int64_t T, int64_t D, unsigned flags);
+/* bytes of workspace rotated_linear needs for (T, D, r, flags); 0 on bad input */
+size_t rotated_linear_workspace_size(int64_t T, int64_t D, int64_t r, unsigned flags);
 
 /* n rounded up to a multiple of 256 (workspace offsets) */
 size_t rw4_align256(size_t n);
@@ -165,7 +175,7 @@ const char* rw4_status_string(rw4_status s);
 /* ABI version of this header (bumped on any signature change) */
 int rw4_abi_version(void);
 
-#define RW4_ABI_VERSION 1
+#define RW4_ABI_VERSION 2
 
 #ifdef __cplusplus
 }

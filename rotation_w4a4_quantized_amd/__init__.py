@@ -15,7 +15,8 @@ from typing import Optional, Tuple
 __all__ = [
     "RW4_ALIGN", "RW4_FWHT", "RW4_SWIGLU", "Rw4Error", "lib", "library_path",
     "respin_align", "fwht", "quant_act_int4", "w4a4_gemm", "rotated_linear",
-    "rotated_linear_workspace_size", "prep_weight", "layer",
+    "rotated_linear_workspace_size", "respin_align_workspace_size", "workspace_views",
+    "prep_weight", "layer",
 ]
 
 RW4_ALIGN, RW4_FWHT, RW4_SWIGLU = 1, 2, 4
@@ -25,8 +26,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "librotw4a4.so")
 _lib = None
 
-EXPORTS = ("respin_align", "fwht", "quant_act_int4", "w4a4_gemm", "rotated_linear",
-           "rotated_linear_workspace_size", "rw4_align256", "rw4_status_string",
+EXPORTS = ("respin_align", "respin_align_workspace_size", "fwht", "quant_act_int4", "w4a4_gemm",
+           "rotated_linear", "rotated_linear_workspace_size", "rw4_align256", "rw4_status_string",
            "rw4_abi_version")
 
 
@@ -48,13 +49,15 @@ def lib() -> ctypes.CDLL:
     L = ctypes.CDLL(library_path)
     vp, i64, u32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint, ctypes.c_size_t
     i32 = ctypes.c_int
-    L.respin_align.argtypes = [vp, i32, vp, i32, vp, vp, vp, i64, i64, i64, vp]
+    L.respin_align.argtypes = [vp, i32, vp, i32, vp, vp, vp, i64, i64, i64, vp, sz, vp]
+    L.respin_align_workspace_size.argtypes = [i64, i64, i64]
+    L.respin_align_workspace_size.restype = sz
     L.fwht.argtypes = [vp, i32, vp, i64, i64, vp]
     L.quant_act_int4.argtypes = [vp, i32, vp, vp, i64, i64, vp]
     L.w4a4_gemm.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp]
     L.rotated_linear.argtypes = [vp, i64, i64, i64, vp, vp, i64, u32, vp, vp, i64, vp, vp, sz,
                                  vp, vp]
-    L.rotated_linear_workspace_size.argtypes = [i64, i64, u32]
+    L.rotated_linear_workspace_size.argtypes = [i64, i64, i64, u32]
     L.rotated_linear_workspace_size.restype = sz
     L.rw4_align256.argtypes = [sz]
     L.rw4_align256.restype = sz
@@ -98,19 +101,26 @@ def _fdt(t) -> int:
 def _rows(x):
     if x.dim() != 2 or not x.is_cuda:
         raise ValueError("expected a 2-D CUDA tensor [T][D]")
-    if x.stride(1) != 1:
+    if x.numel() and x.stride(1) != 1:
         raise ValueError("rows must be contiguous")
 
 
 def _contig(x):
     _rows(x)
-    if not x.is_contiguous():
+    if x.numel() and not x.is_contiguous():
         raise ValueError("expected a contiguous tensor")
 
 
 # ---------------------------------------------------------------- entry points
-def respin_align(x, Q, M, out=None, addend=None, out_dtype=None):
-    """out = x + Q (M - I) Q^T x (+ addend), per token row; see include/rotw4a4.h."""
+def respin_align_workspace_size(T: int, D: int, r: int) -> int:
+    return int(lib().respin_align_workspace_size(T, D, r))
+
+
+def respin_align(x, Q, M, out=None, addend=None, out_dtype=None, workspace=None, direct=False):
+    """out = x + Q (M - I) Q^T x (+ addend), per token row; see include/rotw4a4.h.
+
+    With bf16 x (and D % 32 == 0) it runs on matrix cores using ``workspace``
+    (allocated here if not given); ``direct=True`` selects the fp32-FMA kernel."""
     torch = _torch()
     _contig(x)
     T, D = x.shape
@@ -125,8 +135,15 @@ def respin_align(x, Q, M, out=None, addend=None, out_dtype=None):
         if Q.dtype != torch.float32 or M.dtype != torch.float32:
             raise TypeError("Q and M must be fp32")
         Q, M = Q.contiguous(), M.contiguous()
+    need = 0 if direct else respin_align_workspace_size(T, D, r)
+    if need and workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=x.device)
+    if not need:
+        workspace = None
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib().respin_align(_p(x), _fdt(x), _p(out), _fdt(out), _p(Q) if r else None,
-                            _p(M) if r else None, _p(addend), T, D, r, _stream())
+                            _p(M) if r else None, _p(addend), T, D, r, _p(workspace), nbytes,
+                            _stream())
     _check("respin_align", st)
     return out
 
@@ -175,8 +192,8 @@ def w4a4_gemm(a, s_a, w, s_w, out=None, out_dtype=None):
     return out
 
 
-def rotated_linear_workspace_size(T: int, D: int, flags: int) -> int:
-    return int(lib().rotated_linear_workspace_size(T, D, flags))
+def rotated_linear_workspace_size(T: int, D: int, r: int, flags: int) -> int:
+    return int(lib().rotated_linear_workspace_size(T, D, r, flags))
 
 
 def rotated_linear(x, w, s_w, flags: int, Q=None, M=None, out=None, workspace=None,
@@ -195,7 +212,7 @@ def rotated_linear(x, w, s_w, flags: int, Q=None, M=None, out=None, workspace=No
     D = x.shape[1] // 2 if flags & RW4_SWIGLU else x.shape[1]
     N = w.shape[0]
     r = Q.shape[1] if (flags & RW4_ALIGN) and Q is not None else 0
-    need = rotated_linear_workspace_size(T, D, flags)
+    need = rotated_linear_workspace_size(T, D, r, flags)
     if workspace is None:
         workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=x.device)
     if out is None:

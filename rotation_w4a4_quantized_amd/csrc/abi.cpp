@@ -46,21 +46,37 @@ const char* rw4_status_string(rw4_status s) {
   return "unknown status";
 }
 
+size_t respin_align_workspace_size(int64_t T, int64_t D, int64_t r) {
+  if (T < 0 || D < 1 || r < 0 || r > 128) return 0;
+  if (!rw4::align_mfma_supported(D, r)) return 0;
+  return rw4::align_mfma_workspace(T, D, r);
+}
+
 rw4_status respin_align(const void* x, rw4_dtype x_dt, void* out, rw4_dtype out_dt,
                         const float* Q, const float* M, const void* addend, int64_t T, int64_t D,
-                        int64_t r, void* stream) {
+                        int64_t r, void* workspace, size_t ws_bytes, void* stream) {
+  if (T == 0 && D >= 1 && r >= 0 && fdt(x_dt) && fdt(out_dt)) return RW4_OK;
   rw4_status st = check_align_args(x, x_dt, out, out_dt, Q, M, T, D, r);
   if (st != RW4_OK) return st;
   if (addend && !al16(addend)) return RW4_ERR_MISALIGNED;
   if (x == out) return RW4_ERR_INVALID_ARG;
+  if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u)) return RW4_ERR_WORKSPACE;
+  const bool mfma = workspace && x_dt == RW4_BF16 && rw4::align_mfma_supported(D, r);
+  if (mfma && ws_bytes < rw4::align_mfma_workspace(T, D, r)) return RW4_ERR_WORKSPACE;
   if (T == 0) return RW4_OK;
+  if (mfma)
+    return hip_status(rw4::launch_align_mfma(static_cast<const uint16_t*>(x), out,
+                                             out_dt == RW4_F32, Q, M, addend, T, D, r, workspace,
+                                             strm(stream)));
   return hip_status(rw4::launch_align(x, x_dt == RW4_F32, out, out_dt == RW4_F32, Q, M, addend, T,
                                       D, r, strm(stream)));
 }
 
 rw4_status fwht(const void* x, rw4_dtype x_dt, float* y, int64_t T, int64_t D, void* stream) {
-  if (!x || !y || T < 0 || !fdt(x_dt)) return RW4_ERR_INVALID_ARG;
+  if (T < 0 || !fdt(x_dt)) return RW4_ERR_INVALID_ARG;
   if (!pow2(D) || D < 2 || D > 32768) return RW4_ERR_UNSUPPORTED;
+  if (T == 0) return RW4_OK;
+  if (!x || !y) return RW4_ERR_INVALID_ARG;
   if (!al16(x) || !al16(y)) return RW4_ERR_MISALIGNED;
   if (x == static_cast<const void*>(y) && x_dt != RW4_F32) return RW4_ERR_INVALID_ARG;
   if (T == 0) return RW4_OK;
@@ -70,8 +86,10 @@ rw4_status fwht(const void* x, rw4_dtype x_dt, float* y, int64_t T, int64_t D, v
 
 rw4_status quant_act_int4(const void* x, rw4_dtype x_dt, uint8_t* codes, float* scales, int64_t T,
                           int64_t D, void* stream) {
-  if (!x || !codes || !scales || T < 0 || !fdt(x_dt)) return RW4_ERR_INVALID_ARG;
+  if (T < 0 || !fdt(x_dt)) return RW4_ERR_INVALID_ARG;
   if (D < 2 || (D % 2) != 0 || D > (int64_t(1) << 20)) return RW4_ERR_UNSUPPORTED;
+  if (T == 0) return RW4_OK;
+  if (!x || !codes || !scales) return RW4_ERR_INVALID_ARG;
   if (!al16(x) || !al16(codes) || !al16(scales)) return RW4_ERR_MISALIGNED;
   if (T == 0) return RW4_OK;
   const int in = x_dt == RW4_F32 ? rw4::IN_F32 : rw4::IN_BF16;
@@ -83,8 +101,10 @@ rw4_status quant_act_int4(const void* x, rw4_dtype x_dt, uint8_t* codes, float* 
 
 rw4_status w4a4_gemm(const uint8_t* a, const float* s_a, const uint8_t* w, const float* s_w,
                      void* y, rw4_dtype y_dt, int64_t T, int64_t K, int64_t N, void* stream) {
-  if (!a || !w || !y || T < 0 || N < 1) return RW4_ERR_INVALID_ARG;
+  if (T < 0 || N < 1) return RW4_ERR_INVALID_ARG;
   if (y_dt != RW4_BF16 && y_dt != RW4_I32) return RW4_ERR_INVALID_ARG;
+  if (T == 0 && K >= 32 && K % 32 == 0 && K <= 131072) return RW4_OK;
+  if (!a || !w || !y) return RW4_ERR_INVALID_ARG;
   if (y_dt == RW4_BF16 && (!s_a || !s_w)) return RW4_ERR_INVALID_ARG;
   if (K < 32 || (K % 32) != 0 || K > 131072) return RW4_ERR_UNSUPPORTED;
   if (T > (int64_t(1) << 31) - 1 || N > (int64_t(1) << 31) - 1) return RW4_ERR_UNSUPPORTED;
@@ -94,11 +114,15 @@ rw4_status w4a4_gemm(const uint8_t* a, const float* s_a, const uint8_t* w, const
   return hip_status(rw4::launch_gemm(a, s_a, w, s_w, y, y_dt == RW4_I32, T, K, N, strm(stream)));
 }
 
-size_t rotated_linear_workspace_size(int64_t T, int64_t D, unsigned flags) {
-  if (T < 0 || D < 2 || (D % 2) != 0) return 0;
+size_t rotated_linear_workspace_size(int64_t T, int64_t D, int64_t r, unsigned flags) {
+  if (T < 0 || D < 2 || (D % 2) != 0 || r < 0) return 0;
   size_t n = rw4_align256(static_cast<size_t>(T) * static_cast<size_t>(D) / 2) +
              rw4_align256(4u * static_cast<size_t>(T));
-  if (flags & RW4_ALIGN) n += rw4_align256(4u * static_cast<size_t>(T) * static_cast<size_t>(D));
+  if ((flags & RW4_ALIGN) && r > 0) {
+    if (!rw4::align_mfma_supported(D, r)) return 0;
+    n += rw4_align256(4u * static_cast<size_t>(T) * static_cast<size_t>(D));
+    n += rw4::align_mfma_workspace(T, D, r);
+  }
   return n;
 }
 
@@ -106,10 +130,12 @@ rw4_status rotated_linear(const void* x, int64_t ldx, int64_t T, int64_t D, cons
                           const float* M, int64_t r, unsigned flags, const uint8_t* w,
                           const float* s_w, int64_t N, void* y, void* workspace, size_t ws_bytes,
                           float* dbg_prequant, void* stream) {
-  if (!x || !w || !s_w || !y || T < 0 || N < 1) return RW4_ERR_INVALID_ARG;
+  if (T < 0 || N < 1) return RW4_ERR_INVALID_ARG;
   if (flags & ~static_cast<unsigned>(RW4_ALIGN | RW4_FWHT | RW4_SWIGLU)) return RW4_ERR_INVALID_ARG;
   if ((flags & RW4_ALIGN) && (flags & RW4_SWIGLU)) return RW4_ERR_INVALID_ARG;
   if (!pow2(D) || D < 32 || D > 32768) return RW4_ERR_UNSUPPORTED;
+  if (T == 0) return RW4_OK;
+  if (!x || !w || !s_w || !y) return RW4_ERR_INVALID_ARG;
   const int64_t width = (flags & RW4_SWIGLU) ? 2 * D : D;
   if (ldx < width || (ldx % 8) != 0) return RW4_ERR_INVALID_ARG;
   if (flags & RW4_ALIGN) {
@@ -121,7 +147,8 @@ rw4_status rotated_linear(const void* x, int64_t ldx, int64_t T, int64_t D, cons
   if (!al16(x) || !al16(w) || !al16(s_w) || !al16(y)) return RW4_ERR_MISALIGNED;
   if (dbg_prequant && !al16(dbg_prequant)) return RW4_ERR_MISALIGNED;
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return RW4_ERR_WORKSPACE;
-  if (ws_bytes < rotated_linear_workspace_size(T, D, flags)) return RW4_ERR_WORKSPACE;
+  if (ws_bytes < rotated_linear_workspace_size(T, D, (flags & RW4_ALIGN) ? r : 0, flags))
+    return RW4_ERR_WORKSPACE;
   if (T == 0) return RW4_OK;
 
   hipStream_t s = strm(stream);
@@ -131,10 +158,12 @@ rw4_status rotated_linear(const void* x, int64_t ldx, int64_t T, int64_t D, cons
   const void* src = x;
   int in = (flags & RW4_SWIGLU) ? rw4::IN_SWIGLU : rw4::IN_BF16;
   int64_t ld = ldx;
-  if (flags & RW4_ALIGN) {
-    float* tmp = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(s_a) +
-                                          rw4_align256(4u * static_cast<size_t>(T)));
-    hipError_t e = rw4::launch_align(x, 0, tmp, 1, Q, M, nullptr, T, D, r, s);
+  if ((flags & RW4_ALIGN) && r > 0) {
+    uint8_t* tmpb = reinterpret_cast<uint8_t*>(s_a) + rw4_align256(4u * static_cast<size_t>(T));
+    float* tmp = reinterpret_cast<float*>(tmpb);
+    void* aws = tmpb + rw4_align256(4u * static_cast<size_t>(T) * static_cast<size_t>(D));
+    hipError_t e = rw4::launch_align_mfma(static_cast<const uint16_t*>(x), tmp, 1, Q, M, nullptr,
+                                          T, D, r, aws, s);
     if (e != hipSuccess) return RW4_ERR_HIP;
     src = tmp;
     in = rw4::IN_F32;

@@ -23,6 +23,13 @@ hipError_t launch_align(const void* x, int x_f32, void* out, int out_f32, const 
                         const float* M, const void* addend, int64_t T, int64_t D, int64_t r,
                         hipStream_t s);
 
+// Alignment on bf16 MFMA (bf16 x only); workspace from align_mfma_workspace().
+bool align_mfma_supported(int64_t D, int64_t r);
+size_t align_mfma_workspace(int64_t T, int64_t D, int64_t r);
+hipError_t launch_align_mfma(const uint16_t* x, void* out, int out_f32, const float* Q,
+                             const float* M, const void* addend, int64_t T, int64_t D, int64_t r,
+                             void* ws, hipStream_t s);
+
 // W4A4 GEMM, bf16 (dequantized) or raw int32 output.
 hipError_t launch_gemm(const uint8_t* a, const float* s_a, const uint8_t* w, const float* s_w,
                        void* y, bool i32_out, int64_t T, int64_t K, int64_t N, hipStream_t s);

@@ -22,7 +22,7 @@ def _declared():
 def test_library_built_and_loads():
     assert os.path.exists(rw.library_path), "build the HIP library first"
     L = rw.lib()
-    assert L.rw4_abi_version() == 1
+    assert L.rw4_abi_version() == 2
 
 
 def test_exports_every_declared_symbol():
@@ -46,11 +46,16 @@ def test_workspace_size():
     assert L.rw4_align256(1) == 256 and L.rw4_align256(256) == 256 and L.rw4_align256(0) == 0
     T, D = 2048, 4096
     base = L.rw4_align256(T * D // 2) + L.rw4_align256(4 * T)
-    assert L.rotated_linear_workspace_size(T, D, 0) == base
-    assert L.rotated_linear_workspace_size(T, D, 2) == base
-    assert L.rotated_linear_workspace_size(T, D, 3) == base + 4 * T * D
-    assert L.rotated_linear_workspace_size(-1, D, 0) == 0
-    assert L.rotated_linear_workspace_size(4, 7, 0) == 0
+    assert L.rotated_linear_workspace_size(T, D, 32, 0) == base
+    assert L.rotated_linear_workspace_size(T, D, 32, 2) == base
+    aws = L.respin_align_workspace_size(T, D, 32)
+    assert aws > 0
+    assert L.rotated_linear_workspace_size(T, D, 32, 3) == base + 4 * T * D + aws
+    assert L.rotated_linear_workspace_size(T, D, 0, 3) == base
+    assert L.rotated_linear_workspace_size(-1, D, 0, 0) == 0
+    assert L.rotated_linear_workspace_size(4, 7, 0, 0) == 0
+    # matrix-core alignment needs D % 32 == 0
+    assert L.respin_align_workspace_size(4, 1000, 12) == 0
 
 
 # fake, 256-byte aligned addresses: validation must reject before dereferencing
@@ -64,16 +69,18 @@ INV, UNS, MIS, WSE = -1, -2, -3, -4
 
 
 @pytest.mark.parametrize("args,expect", [
-    ((NUL, 0, B, 1, C, Dp, NUL, 4, 64, 8, NUL), INV),        # null x
-    ((A, 0, B, 1, NUL, Dp, NUL, 4, 64, 8, NUL), INV),        # null Q with r > 0
-    ((A, 5, B, 1, C, Dp, NUL, 4, 64, 8, NUL), INV),          # bad dtype
-    ((A, 0, B, 1, C, Dp, NUL, -1, 64, 8, NUL), INV),         # negative T
-    ((A, 0, B, 1, C, Dp, NUL, 4, 64, 6, NUL), UNS),          # r % 4
-    ((A, 0, B, 1, C, Dp, NUL, 4, 64, 132, NUL), UNS),        # r > 128
-    ((A, 0, B, 1, C, Dp, NUL, 4, 60, 8, NUL), UNS),          # D % 8
-    ((ODD, 0, B, 1, C, Dp, NUL, 4, 64, 8, NUL), MIS),        # misaligned x
-    ((A, 0, A, 1, C, Dp, NUL, 4, 64, 8, NUL), INV),          # out aliases x
-    ((A, 0, B, 1, C, Dp, NUL, 0, 64, 8, NUL), 0),            # T = 0: valid, nothing launched
+    ((NUL, 0, B, 1, C, Dp, NUL, 4, 64, 8, NUL, 0, NUL), INV),        # null x
+    ((A, 0, B, 1, NUL, Dp, NUL, 4, 64, 8, NUL, 0, NUL), INV),        # null Q with r > 0
+    ((A, 5, B, 1, C, Dp, NUL, 4, 64, 8, NUL, 0, NUL), INV),          # bad dtype
+    ((A, 0, B, 1, C, Dp, NUL, -1, 64, 8, NUL, 0, NUL), INV),         # negative T
+    ((A, 0, B, 1, C, Dp, NUL, 4, 64, 6, NUL, 0, NUL), UNS),          # r % 4
+    ((A, 0, B, 1, C, Dp, NUL, 4, 64, 132, NUL, 0, NUL), UNS),        # r > 128
+    ((A, 0, B, 1, C, Dp, NUL, 4, 60, 8, NUL, 0, NUL), UNS),          # D % 8
+    ((ODD, 0, B, 1, C, Dp, NUL, 4, 64, 8, NUL, 0, NUL), MIS),        # misaligned x
+    ((A, 0, A, 1, C, Dp, NUL, 4, 64, 8, NUL, 0, NUL), INV),          # out aliases x
+    ((A, 0, B, 1, C, Dp, NUL, 0, 64, 8, NUL, 0, NUL), 0),            # T = 0: valid, nothing launched
+    ((A, 0, B, 1, C, Dp, NUL, 4, 64, 8, C, 16, NUL), WSE),           # workspace too small
+    ((A, 0, B, 1, C, Dp, NUL, 4, 64, 8, ODD, 1 << 20, NUL), WSE),    # workspace misaligned
 ])
 def test_respin_align_validation(args, expect):
     assert rw.lib().respin_align(*args) == expect
@@ -87,6 +94,7 @@ def test_respin_align_validation(args, expect):
     ((A, 2, B, 4, 64, NUL), INV),            # int32 input
     ((ODD, 1, B, 4, 64, NUL), MIS),
     ((A, 1, A, 0, 64, NUL), 0),              # T = 0 in place
+    ((NUL, 1, NUL, 0, 64, NUL), 0),          # empty call: pointers not inspected
 ])
 def test_fwht_validation(args, expect):
     assert rw.lib().fwht(*args) == expect
@@ -98,6 +106,7 @@ def test_fwht_validation(args, expect):
     ((A, 0, B, C, 4, 0, NUL), UNS),
     ((A, 0, ODD, C, 4, 64, NUL), MIS),
     ((A, 0, B, C, 0, 64, NUL), 0),
+    ((NUL, 0, NUL, NUL, 0, 64, NUL), 0),     # empty call: pointers not inspected
 ])
 def test_quant_validation(args, expect):
     assert rw.lib().quant_act_int4(*args) == expect
@@ -108,6 +117,7 @@ def test_quant_validation(args, expect):
     ((A, B, C, Dp, A, 0, 4, 262144, 16, NUL), UNS), # K too large for int32 accumulators
     ((A, NUL, C, Dp, A, 0, 4, 64, 16, NUL), INV),   # bf16 output needs scales
     ((A, NUL, C, NUL, A, 2, 0, 64, 16, NUL), 0),    # int32 output needs none; T = 0
+    ((NUL, NUL, NUL, NUL, NUL, 0, 0, 64, 16, NUL), 0),  # empty call: pointers not inspected
     ((A, B, C, Dp, A, 1, 4, 64, 16, NUL), INV),     # fp32 output not offered
     ((A, B, C, Dp, A, 0, 4, 64, 0, NUL), INV),      # N = 0
     ((A, B, ODD, Dp, A, 0, 4, 64, 16, NUL), MIS),
@@ -134,3 +144,4 @@ def test_rotated_linear_validation():
     assert _rl(ws=NUL) == WSE
     assert _rl(x=ODD) == MIS
     assert _rl(T=0) == 0
+    assert _rl(T=0, x=NUL, w=NUL, sw=NUL, y=NUL) == 0

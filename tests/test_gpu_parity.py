@@ -90,14 +90,26 @@ def test_fwht_in_place_and_involution(rw):
 @pytest.mark.parametrize("T,D,r", [(64, 256, 8), (37, 4096, 32), (19, 8192, 64), (9, 4096, 128),
                                    (13, 1000, 12), (1, 64, 4)])
 @pytest.mark.parametrize("xdt", ["bf16", "f32"])
-def test_respin_align_f32(rw, T, D, r, xdt):
-    say(f"respin_align T={T} D={D} r={r} x={xdt}")
+@pytest.mark.parametrize("direct", [False, True])
+def test_respin_align_f32(rw, T, D, r, xdt, direct):
+    """bf16 x with D % 32 == 0 runs the matrix-core path unless direct=True."""
+    say(f"respin_align T={T} D={D} r={r} x={xdt} direct={direct}")
     Q, M = W.gen_basis(D + r, D, r)
     xb = W.gen_x(D, T, D, 8, 80.0)
     x = W.bf16_bits_to_f32(xb)
     xg = dev(xb) if xdt == "bf16" else dev(x)
-    out = host(rw.respin_align(xg, dev(Q), dev(M)))
+    out = host(rw.respin_align(xg, dev(Q), dev(M), direct=direct))
     assert normwise(out, O.align(x, Q, M)) <= FP32_TOL
+
+
+@pytest.mark.parametrize("T,D,r", [(2048, 4096, 32), (8, 4096, 32), (4096, 4096, 32)])
+def test_respin_align_workload_sizes(rw, T, D, r):
+    """The alignment at the workload sizes (prefill linear, decode, prefill layer)."""
+    say(f"respin_align workload T={T} D={D} r={r}")
+    Q, M = W.gen_basis(1001, D, r)
+    xb = W.gen_x(1001, T, D, 8, 80.0)
+    out = host(rw.respin_align(dev(xb), dev(Q), dev(M)))
+    assert normwise(out, O.align(W.bf16_bits_to_f32(xb), Q, M)) <= FP32_TOL
 
 
 def test_respin_align_identity_cases(rw):
@@ -111,6 +123,8 @@ def test_respin_align_identity_cases(rw):
     outb = host(rw.respin_align(dev(xb), dev(Q), dev(np.eye(32, dtype=np.float32)),
                                 out_dtype=torch().bfloat16))
     np.testing.assert_array_equal(outb, xb)
+    out = host(rw.respin_align(dev(xb), dev(Q), dev(np.eye(32, dtype=np.float32)), direct=True))
+    np.testing.assert_array_equal(out, x)
     # r = 0: identity
     out0 = host(rw.respin_align(dev(x), None, None))
     np.testing.assert_array_equal(out0, x)
@@ -119,17 +133,25 @@ def test_respin_align_identity_cases(rw):
     np.testing.assert_allclose(np.linalg.norm(out, axis=1), np.linalg.norm(x, axis=1), rtol=1e-5)
 
 
-@pytest.mark.parametrize("T,D,r", [(33, 4096, 32), (8, 4096, 32)])
-def test_respin_align_bf16_residual(rw, T, D, r):
+@pytest.mark.parametrize("T,D,r", [(33, 4096, 32), (8, 4096, 32), (70, 256, 8)])
+@pytest.mark.parametrize("direct", [False, True])
+def test_respin_align_bf16_residual(rw, T, D, r, direct):
     Q, M = W.gen_basis(77, D, r)
     xb = W.gen_x(77, T, D, 8, 80.0)
     ab = W.gen_x(78, T, D, 0, 1.0)
     out = host(rw.respin_align(dev(xb), dev(Q), dev(M), addend=dev(ab),
-                               out_dtype=torch().bfloat16))
+                               out_dtype=torch().bfloat16, direct=direct))
     ref = O.residual(xb, Q, M, ab)
-    # one rounding each side from fp32 / float64 sums: at most one bf16 ulp apart
+    # fp32 alignment + fp32 add, one bf16 rounding, against float64 + one rounding:
+    # apart by at most one bf16 ulp plus an fp32-level error of the summands
+    # (where align(x) + addend cancels, that error spans several ulps of the tiny sum)
+    aligned = O.align(W.bf16_bits_to_f32(xb), Q, M)
+    addv = W.bf16_bits_to_f32(ab).astype(np.float64)
+    g, o = O.bf16_to_f64(out), O.bf16_to_f64(ref)
+    ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(o), 2.0 ** -126))[1] - 8)
+    bound = ulp + 2.0 ** -20 * (np.abs(aligned) + np.abs(addv))
+    assert np.all(np.abs(g - o) <= bound)
     diff = np.abs(out.astype(np.int32) - ref.astype(np.int32))
-    assert diff.max() <= 1
     assert (diff > 0).mean() < 0.01
 
 
