@@ -78,7 +78,7 @@ enum { RW4_ALIGN = 1, RW4_FWHT = 2, RW4_SWIGLU = 4 };
  *   addend nullable, [T][D] of dtype out_dt, added after the alignment (the
  *          block output of a residual connection); one rounding to out_dt
  *   workspace, ws_bytes: device scratch of respin_align_workspace_size(T, D, r)
- *          bytes (256-byte aligned). With it, bf16 x and D % 32 == 0 run on
+ *          bytes (256-byte aligned). With it, bf16 x and D % 64 == 0 run on
  *          bf16 matrix cores (Q and z split into two bf16 terms, fp32
  *          accumulation). NULL / 0 selects the direct fp32-FMA kernel (any
  *          supported shape, slower).
@@ -155,7 +155,8 @@ rw4_status w4a4_gemm(const uint8_t* a, const float* s_a, const uint8_t* w, const
  *            internal.
  *   dbg_prequant nullable fp32 [T][D]: if given, receives the fp32 values that
  *            were quantized (for stage-wise checking).
- * Constraints: D % 32 == 0; with RW4_FWHT, D a power of two <= 32768.
+ * Constraints: D a power of two, 32 <= D <= 32768; with RW4_ALIGN and r > 0,
+ * D >= 64 (the alignment runs on matrix cores).
  */
 rw4_status rotated_linear(const void* x, int64_t ldx, int64_t T, int64_t D,
                           const float* Q, const float* M, int64_t r, unsigned flags,

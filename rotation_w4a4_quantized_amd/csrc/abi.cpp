@@ -142,6 +142,7 @@ rw4_status rotated_linear(const void* x, int64_t ldx, int64_t T, int64_t D, cons
     rw4_status st = check_align_args(x, RW4_BF16, x, RW4_F32, Q, M, T, D, r);
     if (st != RW4_OK) return st;
     if (ldx != D) return RW4_ERR_UNSUPPORTED;
+    if (r > 0 && !rw4::align_mfma_supported(D, r)) return RW4_ERR_UNSUPPORTED;
   }
   if (T > (int64_t(1) << 31) - 1 || N > (int64_t(1) << 31) - 1) return RW4_ERR_UNSUPPORTED;
   if (!al16(x) || !al16(w) || !al16(s_w) || !al16(y)) return RW4_ERR_MISALIGNED;

@@ -9,15 +9,21 @@
 // running on v_mfma_f32_16x16x32_bf16 instead of fp32 FMAs. With M = I, z is
 // exactly zero and the output equals the input.
 //
-// Three launches, each over (token block of 16) x (D part of <= 512):
+// Three launches:
 //   prep : Qh/Ql in both orientations ([r][D] for the projection, [D][r] for
-//          the lift), zero-padded in r; M - I in fp32.
-//   yproj: partial y over one D part (four waves split the part's 32-wide
-//          k-steps, reduced through LDS) -> Ypart[part][t][j].
-//   lift : sums the parts, forms z = (M - I) y and its bf16 split in LDS, then
-//          out = x + Q z for its D part. The MFMA's row order is permuted so a
-//          lane's accumulator covers the same 8 consecutive columns of one
-//          token that its 16-byte x load holds: the accumulator starts as x.
+//          the lift), zero-padded in r; (M - I) transposed, fp32.
+//   yproj: per (64 tokens, 512-column D part): partial y of the part on the
+//          matrix cores, reduced over the four waves in LDS, then the partial
+//          z = (M - I) y_part (z is linear in y) -> Zpart[part][t][i].
+//   lift : per (64 tokens, D part): z = sum of the parts in a fixed order
+//          (deterministic), its bf16 split in LDS, then out = x + Q z. The
+//          MFMA's row order is permuted so a lane's accumulator covers the same
+//          16 consecutive columns of one token that its x load holds: the
+//          accumulator starts as x. Results go out through LDS as whole rows.
+// Every global load is unconditional (clamped indices, masked values): loads
+// inside branches whose values are used after the join read stale registers
+// with this toolchain, and a short drain separates the last MFMA from the
+// first non-MFMA read of its result.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -30,161 +36,325 @@ constexpr int TB = 16;          // tokens per workgroup (MFMA rows)
 constexpr int NW = 4;           // waves per workgroup
 
 __device__ __forceinline__ v8bf ld8(const uint16_t* p) { return *reinterpret_cast<const v8bf*>(p); }
+__device__ __forceinline__ v8bf as8(uint4 u) { return __builtin_bit_cast(v8bf, u); }
 
 __device__ __forceinline__ v4f mfma(v8bf a, v8bf b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Let the last matrix-core results land before anything else reads them: no
+// instruction may be scheduled across, and the wave sleeps ~64 cycles (longer
+// than the instruction's pipeline) in between.
+__device__ __forceinline__ void mfma_drain() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_sleep(1);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One workgroup per 64 (d) x 32 (j) tile of Q: coalesced fp32 reads, the
+// bf16 split, [D][RK] rows written directly and [RP][D] rows through an LDS
+// transpose. Columns j >= r are zero padding.
 __global__ void __launch_bounds__(256)
 basis_prep_kernel(const float* __restrict__ Q, const float* __restrict__ M, int D, int r, int RP,
                   int RK, uint16_t* __restrict__ QtH, uint16_t* __restrict__ QtL,
                   uint16_t* __restrict__ QH, uint16_t* __restrict__ QL, float* __restrict__ Mm) {
-  const int64_t nthreads = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  const int64_t tid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  for (int64_t i = tid; i < static_cast<int64_t>(D) * RK; i += nthreads) {
-    const int d = static_cast<int>(i / RK);
-    const int j = static_cast<int>(i % RK);
-    const float q = j < r ? Q[static_cast<int64_t>(d) * r + j] : 0.0f;
-    const uint16_t h = f32_to_bf16(q);
-    QH[i] = h;
-    QL[i] = f32_to_bf16(q - bf16_to_f32(h));
+  __shared__ uint16_t th[32][64 + 2];
+  __shared__ uint16_t tlo[32][64 + 2];
+  const int tid = threadIdx.x;
+  const int d0 = blockIdx.x * 64;
+  const int j0 = blockIdx.y * 32;
+  // 64 x 32 tile: thread -> (row dd = tid / 4, 8 columns jj = 8 * (tid % 4) + 0..7)
+  const int dd = tid >> 2;
+  const int jb = (tid & 3) * 8;
+  const int d = d0 + dd;
+  uint16_t h[8], l[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int j = j0 + jb + e;
+    const float q = (d < D && j < r) ? Q[static_cast<int64_t>(d) * r + j] : 0.0f;
+    h[e] = f32_to_bf16(q);
+    l[e] = f32_to_bf16(q - bf16_to_f32(h[e]));
+    th[jb + e][dd] = h[e];
+    tlo[jb + e][dd] = l[e];
   }
-  for (int64_t i = tid; i < static_cast<int64_t>(D) * RP; i += nthreads) {
-    const int j = static_cast<int>(i / D);
-    const int d = static_cast<int>(i % D);
-    const float q = j < r ? Q[static_cast<int64_t>(d) * r + j] : 0.0f;
-    const uint16_t h = f32_to_bf16(q);
-    QtH[i] = h;
-    QtL[i] = f32_to_bf16(q - bf16_to_f32(h));
+  if (d < D && j0 + jb < RK) {
+    uint4 vh, vl;
+    vh.x = h[0] | (uint32_t(h[1]) << 16); vh.y = h[2] | (uint32_t(h[3]) << 16);
+    vh.z = h[4] | (uint32_t(h[5]) << 16); vh.w = h[6] | (uint32_t(h[7]) << 16);
+    vl.x = l[0] | (uint32_t(l[1]) << 16); vl.y = l[2] | (uint32_t(l[3]) << 16);
+    vl.z = l[4] | (uint32_t(l[5]) << 16); vl.w = l[6] | (uint32_t(l[7]) << 16);
+    *reinterpret_cast<uint4*>(QH + static_cast<int64_t>(d) * RK + j0 + jb) = vh;
+    *reinterpret_cast<uint4*>(QL + static_cast<int64_t>(d) * RK + j0 + jb) = vl;
   }
-  for (int64_t i = tid; i < static_cast<int64_t>(r) * r; i += nthreads) {
-    const int a = static_cast<int>(i / r);
-    const int b = static_cast<int>(i % r);
-    Mm[i] = a == b ? M[i] - 1.0f : M[i];
+  __syncthreads();
+  // transposed rows: thread -> (row j = tid / 8, 8 consecutive d)
+  const int jr = tid >> 3;
+  const int db = (tid & 7) * 8;
+  const int j = j0 + jr;
+  if (j < RP && d0 + db < D) {
+    uint4 vh, vl;
+    vh.x = th[jr][db] | (uint32_t(th[jr][db + 1]) << 16); vh.y = th[jr][db + 2] | (uint32_t(th[jr][db + 3]) << 16);
+    vh.z = th[jr][db + 4] | (uint32_t(th[jr][db + 5]) << 16); vh.w = th[jr][db + 6] | (uint32_t(th[jr][db + 7]) << 16);
+    vl.x = tlo[jr][db] | (uint32_t(tlo[jr][db + 1]) << 16); vl.y = tlo[jr][db + 2] | (uint32_t(tlo[jr][db + 3]) << 16);
+    vl.z = tlo[jr][db + 4] | (uint32_t(tlo[jr][db + 5]) << 16); vl.w = tlo[jr][db + 6] | (uint32_t(tlo[jr][db + 7]) << 16);
+    *reinterpret_cast<uint4*>(QtH + static_cast<int64_t>(j) * D + d0 + db) = vh;
+    *reinterpret_cast<uint4*>(QtL + static_cast<int64_t>(j) * D + d0 + db) = vl;
+  }
+  // (M - I) stored transposed: Mm[j * r + i] = M[i][j] - [i == j]
+  if (blockIdx.x == 0 && blockIdx.y == 0) {
+    for (int i = tid; i < r * r; i += 256) {
+      const int a = i / r, b = i % r;
+      Mm[b * r + a] = a == b ? M[i] - 1.0f : M[i];
+    }
   }
 }
+
+// A D part of 512 columns is 8 double steps of 64 columns; each of the 4
+// waves takes 2. Inside a double step lane group g (lane / 16) owns the 16
+// contiguous columns [16g, 16g + 16): its first 8 feed one MFMA, the next 8 a
+// second one. The k order of a dot product is free, so both operands use this
+// same order, and every lane reads 32 contiguous bytes per row.
+// A workgroup aligns TBW blocks of 16 tokens: every Q fragment it loads is
+// used by TBW MFMA blocks, which keeps the L2 traffic for Q at 1/TBW of the
+// token count.
+constexpr int DPW = 2;                    // double steps per wave
+constexpr int kPart = NW * DPW * 64;
+constexpr int TBW = 4;                    // 16-token blocks per workgroup
+constexpr int TPW = TBW * TB;             // tokens per workgroup
 
 template <int RP>
 __global__ void __launch_bounds__(256)
-yproj_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P,
+yproj_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int r,
              const uint16_t* __restrict__ QtH, const uint16_t* __restrict__ QtL,
-             float* __restrict__ Ypart) {
-  __shared__ float red[NW][TB][RP];
+             const float* __restrict__ MmT, float* __restrict__ Zpart) {
+  constexpr int RK = (RP + 31) / 32 * 32;
+  constexpr bool MLDS = RK <= 64;                      // (M - I)^T staged in LDS when small
+  __shared__ float red[NW][TPW][RP + 1];
+  __shared__ float mt[MLDS ? RK * RK : 1];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TB;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TPW;
   const int part = blockIdx.y;
   const int dbeg = part * P;
   const int dend = min(D, dbeg + P);
-  const int nks = (dend - dbeg) / 32;
+  const int nds = (dend - dbeg) / 64;                 // whole double steps in this part
   const int g = lane >> 4;
   const int tl = lane & 15;
-  const int64_t trow = min(t0 + tl, T - 1);
-  const uint16_t* xrow = x + trow * D + 8 * g;
+  constexpr int NBC = (RP / 16) % 2 == 0 ? 2 : 1;     // basis blocks per load batch (divides RP/16)
 
-  v4f acc[RP / 16];
+  // loads are unconditional: double steps past the part's end re-read its last
+  // one and their x is zeroed; tokens past T re-read the last token
+  v8bf xa[TBW][DPW][2];
 #pragma unroll
-  for (int nb = 0; nb < RP / 16; ++nb) acc[nb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  for (int ks = wave; ks < nks; ks += NW) {
-    const int d0 = dbeg + 32 * ks;
-    const v8bf a = ld8(xrow + d0);
+  for (int b = 0; b < TBW; ++b) {
+    const int64_t trow = min(t0 + 16 * b + tl, T - 1);
+    const uint16_t* xrow = x + trow * D + 16 * g;
 #pragma unroll
-    for (int nb = 0; nb < RP / 16; ++nb) {
-      const int64_t qo = static_cast<int64_t>(16 * nb + tl) * D + d0 + 8 * g;
-      acc[nb] = mfma(a, ld8(QtH + qo), acc[nb]);
-      acc[nb] = mfma(a, ld8(QtL + qo), acc[nb]);
+    for (int u = 0; u < DPW; ++u) {
+      const int ds = wave * DPW + u;
+      const int dsc = ds < nds ? ds : nds - 1;
+      const uint4* px = reinterpret_cast<const uint4*>(xrow + dbeg + 64 * dsc);
+      uint4 a0 = px[0], a1 = px[1];
+      const uint32_t keep = ds < nds ? 0xFFFFFFFFu : 0u;
+      a0.x &= keep; a0.y &= keep; a0.z &= keep; a0.w &= keep;
+      a1.x &= keep; a1.y &= keep; a1.z &= keep; a1.w &= keep;
+      xa[b][u][0] = as8(a0);
+      xa[b][u][1] = as8(a1);
     }
   }
-  // C layout: lane holds rows 4g + v (tokens), column tl (basis index in the block)
+  v4f acc[TBW][RP / 16];
 #pragma unroll
-  for (int nb = 0; nb < RP / 16; ++nb)
+  for (int b = 0; b < TBW; ++b)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) red[wave][4 * g + v][16 * nb + tl] = acc[nb][v];
-  __syncthreads();
-  for (int o = tid; o < TB * RP; o += 256) {
-    const int t = o / RP;
-    const int j = o % RP;
-    if (t0 + t < T) {
-      const float s = (red[0][t][j] + red[1][t][j]) + (red[2][t][j] + red[3][t][j]);
-      Ypart[(static_cast<int64_t>(part) * T + t0 + t) * RP + j] = s;
+    for (int nb = 0; nb < RP / 16; ++nb) acc[b][nb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int nb0 = 0; nb0 < RP / 16; nb0 += NBC) {
+    v8bf bh[DPW][NBC][2], bl[DPW][NBC][2];
+#pragma unroll
+    for (int u = 0; u < DPW; ++u) {
+      const int ds = wave * DPW + u;
+      const int dsc = ds < nds ? ds : nds - 1;
+#pragma unroll
+      for (int c = 0; c < NBC; ++c) {
+        const int64_t qo = static_cast<int64_t>(16 * (nb0 + c) + tl) * D + dbeg + 64 * dsc + 16 * g;
+        bh[u][c][0] = ld8(QtH + qo);
+        bh[u][c][1] = ld8(QtH + qo + 8);
+        bl[u][c][0] = ld8(QtL + qo);
+        bl[u][c][1] = ld8(QtL + qo + 8);
+      }
     }
+#pragma unroll
+    for (int u = 0; u < DPW; ++u)
+#pragma unroll
+      for (int c = 0; c < NBC; ++c)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int b = 0; b < TBW; ++b) {
+            acc[b][nb0 + c] = mfma(xa[b][u][h], bh[u][c][h], acc[b][nb0 + c]);
+            acc[b][nb0 + c] = mfma(xa[b][u][h], bl[u][c][h], acc[b][nb0 + c]);
+          }
   }
-}
-
-template <int RP, int RK, bool OF32, bool ADD>
-__global__ void __launch_bounds__(256)
-lift_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int S, int r,
-            const float* __restrict__ Ypart, const float* __restrict__ Mm,
-            const uint16_t* __restrict__ QH, const uint16_t* __restrict__ QL,
-            const void* __restrict__ addend, void* __restrict__ out) {
-  __shared__ float ys[TB][RP];
-  __shared__ __attribute__((aligned(16))) uint16_t zh[TB][RK];
-  __shared__ __attribute__((aligned(16))) uint16_t zl[TB][RK];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TB;
-  const int part = blockIdx.y;
-  const int dbeg = part * P;
-  const int dend = min(D, dbeg + P);
-  const int nks = (dend - dbeg) / 32;
-
-  for (int o = tid; o < TB * RP; o += 256) {
+  mfma_drain();
+  // C layout: lane holds rows 4g + v (tokens of block b), column tl (basis index)
+#pragma unroll
+  for (int b = 0; b < TBW; ++b)
+#pragma unroll
+    for (int nb = 0; nb < RP / 16; ++nb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[wave][16 * b + 4 * g + v][16 * nb + tl] = acc[b][nb][v];
+  if constexpr (MLDS)
+    for (int o = tid; o < r * r; o += 256) mt[o] = MmT[o];
+  __syncthreads();
+  // partial y of this D part for the workgroup's tokens, into red[0]
+  for (int o = tid; o < TPW * RP; o += 256) {
     const int t = o / RP;
     const int j = o % RP;
-    float s = 0.0f;
-    if (t0 + t < T)
-      for (int p = 0; p < S; ++p) s += Ypart[(static_cast<int64_t>(p) * T + t0 + t) * RP + j];
-    ys[t][j] = s;
+    red[0][t][j] = (red[0][t][j] + red[1][t][j]) + (red[2][t][j] + red[3][t][j]);
   }
   __syncthreads();
-  for (int o = tid; o < TB * RK; o += 256) {
+  // partial z = (M - I) (partial y): z is linear in y, so the lift only sums
+  // the parts. (M - I) is stored transposed: consecutive i read consecutive words.
+  for (int o = tid; o < TPW * RK; o += 256) {
     const int t = o / RK;
     const int i = o % RK;
     float z = 0.0f;
     if (i < r)
-      for (int j = 0; j < r; ++j) z = fmaf(Mm[i * r + j], ys[t][j], z);
-    const uint16_t h = f32_to_bf16(z);
-    zh[t][i] = h;
-    zl[t][i] = f32_to_bf16(z - bf16_to_f32(h));
+      for (int j = 0; j < r; ++j) z = fmaf(MLDS ? mt[j * r + i] : MmT[j * r + i], red[0][t][j], z);
+    if (t0 + t < T) Zpart[(static_cast<int64_t>(part) * T + t0 + t) * RK + i] = z;
+  }
+}
+
+// The lift runs 8 waves per workgroup, one 64-column double step each, so a
+// 512-column part of 64 tokens keeps two waves per SIMD busy.
+constexpr int LNW = 8;
+
+template <int RP, int RK, bool OF32, bool ADD>
+__global__ void __launch_bounds__(LNW * 64)
+lift_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int S, int r,
+            const float* __restrict__ Zpart, const uint16_t* __restrict__ QH,
+            const uint16_t* __restrict__ QL, const void* __restrict__ addend,
+            void* __restrict__ out) {
+  constexpr int NT = LNW * 64;
+  __shared__ __attribute__((aligned(16))) uint16_t zh[TPW][RK + 8];
+  __shared__ __attribute__((aligned(16))) uint16_t zl[TPW][RK + 8];
+  // one 16-token block of results, written out as whole row segments
+  __shared__ __attribute__((aligned(16))) float stage[TB][kPart + 4];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TPW;
+  const int part = blockIdx.y;
+  const int dbeg = part * P;
+  const int dend = min(D, dbeg + P);
+  const int nds = (dend - dbeg) / 64;
+  const int g = lane >> 4;
+  const int tl = lane & 15;
+  constexpr int KQ = RK / 32 < 2 ? RK / 32 : 2;       // Q k-chunks loaded up front
+  const bool live = wave < nds;                       // this wave's double step exists
+  const int d0 = dbeg + 64 * (live ? wave : nds - 1);
+  static_assert(TPW * RK % (4 * NT) == 0 || TPW * RK < 4 * NT, "z chunks");
+
+  // 1. every load of the lift, issued up front and unconditional (a wave past
+  // the part's end re-reads its last double step and stores nothing; tokens
+  // past T re-read the last token). Block b of the double step covers columns
+  // 16g + 4b + v for lane group g, so A's row i = 4g' + v of block b is column
+  // 16g' + 4b + v. Each thread also fetches 4 consecutive z entries of every
+  // D part (TPW * RK / 4 float4 chunks over the workgroup).
+  v8bf qh[4][KQ], ql[4][KQ];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int drow = d0 + 16 * (tl >> 2) + 4 * b + (tl & 3);
+#pragma unroll
+    for (int kk = 0; kk < KQ; ++kk) {
+      const int64_t qo = static_cast<int64_t>(drow) * RK + 32 * kk + 8 * g;
+      qh[b][kk] = ld8(QH + qo);
+      ql[b][kk] = ld8(QL + qo);
+    }
+  }
+  uint4 xv[TBW][2];
+#pragma unroll
+  for (int tb = 0; tb < TBW; ++tb) {
+    const int64_t trow = min(t0 + 16 * tb + tl, T - 1);
+    const uint4* px = reinterpret_cast<const uint4*>(x + trow * D + d0 + 16 * g);
+    xv[tb][0] = px[0];
+    xv[tb][1] = px[1];
+  }
+  // 2. z = sum over D parts (fixed order), its bf16 split into LDS
+  constexpr int ZC = TPW * RK / 4;                     // float4 chunks of z
+  for (int c = tid; c < ZC; c += NT) {
+    const int tt = (4 * c) / RK;
+    const int i = (4 * c) % RK;
+    const int64_t trow = min(t0 + tt, T - 1);
+    float4 z = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int p = 0; p < S; ++p) {
+      const float4 zp = *reinterpret_cast<const float4*>(Zpart + (static_cast<int64_t>(p) * T + trow) * RK + i);
+      z.x += zp.x; z.y += zp.y; z.z += zp.z; z.w += zp.w;
+    }
+    const float zz[4] = {z.x, z.y, z.z, z.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint16_t h = f32_to_bf16(zz[e]);
+      zh[tt][i + e] = h;
+      zl[tt][i + e] = f32_to_bf16(zz[e] - bf16_to_f32(h));
+    }
   }
   __syncthreads();
 
-  const int g = lane >> 4;
-  const int tl = lane & 15;
-  const int64_t t = t0 + tl;
-  const int64_t trow = min(t, T - 1);
-  const uint16_t* xrow = x + trow * D + 8 * g;
-  for (int ks = wave; ks < nks; ks += NW) {
-    const int d0 = dbeg + 32 * ks;
-    const uint4 xv = *reinterpret_cast<const uint4*>(xrow + d0);
-    v4f acc[2];
-    acc[0] = v4f{bf16lo(xv.x), bf16hi(xv.x), bf16lo(xv.y), bf16hi(xv.y)};
-    acc[1] = v4f{bf16lo(xv.z), bf16hi(xv.z), bf16lo(xv.w), bf16hi(xv.w)};
+  // 4. out = x + Q z per token block; the accumulators start at x. Each block's
+  // results are staged in LDS, then all threads write them as contiguous row
+  // segments (the MFMA layout would scatter 16-byte pieces over 16 rows).
+  const int ncols = dend - dbeg;
+#pragma unroll 1
+  for (int tb = 0; tb < TBW; ++tb) {
+    if (live) {
+      v4f acc[4];
+      acc[0] = v4f{bf16lo(xv[tb][0].x), bf16hi(xv[tb][0].x), bf16lo(xv[tb][0].y), bf16hi(xv[tb][0].y)};
+      acc[1] = v4f{bf16lo(xv[tb][0].z), bf16hi(xv[tb][0].z), bf16lo(xv[tb][0].w), bf16hi(xv[tb][0].w)};
+      acc[2] = v4f{bf16lo(xv[tb][1].x), bf16hi(xv[tb][1].x), bf16lo(xv[tb][1].y), bf16hi(xv[tb][1].y)};
+      acc[3] = v4f{bf16lo(xv[tb][1].z), bf16hi(xv[tb][1].z), bf16lo(xv[tb][1].w), bf16hi(xv[tb][1].w)};
 #pragma unroll
-    for (int kk = 0; kk < RK / 32; ++kk) {
-      const v8bf bh = *reinterpret_cast<const v8bf*>(&zh[tl][32 * kk + 8 * g]);
-      const v8bf bl = *reinterpret_cast<const v8bf*>(&zl[tl][32 * kk + 8 * g]);
+      for (int kk = 0; kk < RK / 32; ++kk) {
+        const v8bf bh = *reinterpret_cast<const v8bf*>(&zh[16 * tb + tl][32 * kk + 8 * g]);
+        const v8bf bl = *reinterpret_cast<const v8bf*>(&zl[16 * tb + tl][32 * kk + 8 * g]);
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int drow = d0 + 8 * (tl >> 2) + 4 * b + (tl & 3);
-        const int64_t qo = static_cast<int64_t>(drow) * RK + 32 * kk + 8 * g;
-        const v8bf ah = ld8(QH + qo);
-        const v8bf al = ld8(QL + qo);
-        acc[b] = mfma(ah, bh, acc[b]);
-        acc[b] = mfma(al, bh, acc[b]);
-        acc[b] = mfma(ah, bl, acc[b]);
+        for (int b = 0; b < 4; ++b) {
+          v8bf ah, al;
+          if (kk < KQ) {
+            ah = qh[b][kk < KQ ? kk : 0];
+            al = ql[b][kk < KQ ? kk : 0];
+          } else {
+            const int drow = d0 + 16 * (tl >> 2) + 4 * b + (tl & 3);
+            const int64_t qo = static_cast<int64_t>(drow) * RK + 32 * kk + 8 * g;
+            ah = ld8(QH + qo);
+            al = ld8(QL + qo);
+          }
+          acc[b] = mfma(ah, bh, acc[b]);
+          acc[b] = mfma(al, bh, acc[b]);
+          acc[b] = mfma(ah, bl, acc[b]);
+        }
       }
+      mfma_drain();
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        *reinterpret_cast<float4*>(&stage[tl][64 * wave + 16 * g + 4 * b]) =
+            make_float4(acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
     }
-    if (t < T) {
-      const int64_t off = t * D + d0 + 8 * g;
-      float o[8] = {acc[0][0], acc[0][1], acc[0][2], acc[0][3],
-                    acc[1][0], acc[1][1], acc[1][2], acc[1][3]};
+    __syncthreads();
+    for (int c = tid; c < TB * (ncols / 8); c += NT) {
+      const int row = c / (ncols / 8);
+      const int col = (c % (ncols / 8)) * 8;
+      const int64_t t = t0 + 16 * tb + row;
+      if (t >= T) continue;
+      const float4 s0 = *reinterpret_cast<const float4*>(&stage[row][col]);
+      const float4 s1 = *reinterpret_cast<const float4*>(&stage[row][col + 4]);
+      float o[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+      const int64_t off = t * D + dbeg + col;
       if constexpr (ADD) {
         if constexpr (OF32) {
-          const float4 a0 = *reinterpret_cast<const float4*>(static_cast<const float*>(addend) + off);
-          const float4 a1 = *reinterpret_cast<const float4*>(static_cast<const float*>(addend) + off + 4);
+          const float4* ap = reinterpret_cast<const float4*>(static_cast<const float*>(addend) + off);
+          const float4 a0 = ap[0], a1 = ap[1];
           o[0] += a0.x; o[1] += a0.y; o[2] += a0.z; o[3] += a0.w;
           o[4] += a1.x; o[5] += a1.y; o[6] += a1.z; o[7] += a1.w;
         } else {
@@ -194,9 +364,9 @@ lift_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int S, int 
         }
       }
       if constexpr (OF32) {
-        float* op = static_cast<float*>(out) + off;
-        reinterpret_cast<float4*>(op)[0] = make_float4(o[0], o[1], o[2], o[3]);
-        reinterpret_cast<float4*>(op)[1] = make_float4(o[4], o[5], o[6], o[7]);
+        float4* op = reinterpret_cast<float4*>(static_cast<float*>(out) + off);
+        op[0] = make_float4(o[0], o[1], o[2], o[3]);
+        op[1] = make_float4(o[4], o[5], o[6], o[7]);
       } else {
         uint32_t w[4];
 #pragma unroll
@@ -205,32 +375,32 @@ lift_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int S, int 
         *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + off) = make_uint4(w[0], w[1], w[2], w[3]);
       }
     }
+    __syncthreads();
   }
 }
 
 inline int rp_of(int64_t r) { return static_cast<int>((r + 15) / 16 * 16); }
 inline int rk_of(int64_t r) { return static_cast<int>((r + 31) / 32 * 32); }
 inline size_t a256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
-constexpr int kPart = 512;
 
 template <int RP>
-hipError_t run_yproj(const uint16_t* x, int64_t T, int D, int P, int S, const uint16_t* QtH,
-                     const uint16_t* QtL, float* Ypart, hipStream_t s) {
-  hipLaunchKernelGGL(yproj_kernel<RP>, dim3(static_cast<unsigned>((T + TB - 1) / TB), S), dim3(256),
-                     0, s, x, T, D, P, QtH, QtL, Ypart);
+hipError_t run_yproj(const uint16_t* x, int64_t T, int D, int P, int S, int r, const uint16_t* QtH,
+                     const uint16_t* QtL, const float* MmT, float* Zpart, hipStream_t s) {
+  hipLaunchKernelGGL(yproj_kernel<RP>, dim3(static_cast<unsigned>((T + TPW - 1) / TPW), S), dim3(256),
+                     0, s, x, T, D, P, r, QtH, QtL, MmT, Zpart);
   return hipGetLastError();
 }
 
 template <int RP, int RK>
-hipError_t run_lift(const uint16_t* x, int64_t T, int D, int P, int S, int r, const float* Ypart,
-                    const float* Mm, const uint16_t* QH, const uint16_t* QL, const void* addend,
-                    void* out, bool of32, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>((T + TB - 1) / TB), S);
-#define RW4_LIFT(OF, AD)                                                                         \
-  if (of32 == OF && (addend != nullptr) == AD) {                                                 \
-    hipLaunchKernelGGL((lift_kernel<RP, RK, OF, AD>), grid, dim3(256), 0, s, x, T, D, P, S, r,   \
-                       Ypart, Mm, QH, QL, addend, out);                                          \
-    return hipGetLastError();                                                                    \
+hipError_t run_lift(const uint16_t* x, int64_t T, int D, int P, int S, int r, const float* Zpart,
+                    const uint16_t* QH, const uint16_t* QL, const void* addend, void* out, bool of32,
+                    hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((T + TPW - 1) / TPW), S);
+#define RW4_LIFT(OF, AD)                                                                          \
+  if (of32 == OF && (addend != nullptr) == AD) {                                                  \
+    hipLaunchKernelGGL((lift_kernel<RP, RK, OF, AD>), grid, dim3(LNW * 64), 0, s, x, T, D, P, S,  \
+                       r, Zpart, QH, QL, addend, out);                                            \
+    return hipGetLastError();                                                                     \
   }
   RW4_LIFT(true, false) RW4_LIFT(true, true) RW4_LIFT(false, false) RW4_LIFT(false, true)
 #undef RW4_LIFT
@@ -239,13 +409,13 @@ hipError_t run_lift(const uint16_t* x, int64_t T, int D, int P, int S, int r, co
 
 }  // namespace
 
-bool align_mfma_supported(int64_t D, int64_t r) { return r > 0 && r <= 128 && D % 32 == 0; }
+bool align_mfma_supported(int64_t D, int64_t r) { return r > 0 && r <= 128 && D % 64 == 0; }
 
 size_t align_mfma_workspace(int64_t T, int64_t D, int64_t r) {
   const int RP = rp_of(r), RK = rk_of(r);
   const int64_t S = (D + kPart - 1) / kPart;
   return 2 * a256(static_cast<size_t>(RP) * D * 2) + 2 * a256(static_cast<size_t>(D) * RK * 2) +
-         a256(static_cast<size_t>(r) * r * 4) + a256(static_cast<size_t>(S) * T * RP * 4);
+         a256(static_cast<size_t>(r) * r * 4) + a256(static_cast<size_t>(S) * T * RK * 4);
 }
 
 hipError_t launch_align_mfma(const uint16_t* x, void* out, int out_f32, const float* Q,
@@ -253,7 +423,7 @@ hipError_t launch_align_mfma(const uint16_t* x, void* out, int out_f32, const fl
                              void* ws, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int RP = rp_of(r), RK = rk_of(r);
-  const int P = static_cast<int>(D < kPart ? D : kPart);
+  const int P = kPart;
   const int S = static_cast<int>((D + P - 1) / P);
   uint8_t* p = static_cast<uint8_t*>(ws);
   uint16_t* QtH = reinterpret_cast<uint16_t*>(p); p += a256(static_cast<size_t>(RP) * D * 2);
@@ -261,18 +431,17 @@ hipError_t launch_align_mfma(const uint16_t* x, void* out, int out_f32, const fl
   uint16_t* QH = reinterpret_cast<uint16_t*>(p);  p += a256(static_cast<size_t>(D) * RK * 2);
   uint16_t* QL = reinterpret_cast<uint16_t*>(p);  p += a256(static_cast<size_t>(D) * RK * 2);
   float* Mm = reinterpret_cast<float*>(p);        p += a256(static_cast<size_t>(r) * r * 4);
-  float* Ypart = reinterpret_cast<float*>(p);
+  float* Zpart = reinterpret_cast<float*>(p);
 
-  const int64_t work = D * RK;
-  const unsigned pblocks = static_cast<unsigned>(work / 256 < 1024 ? (work + 255) / 256 : 1024);
-  hipLaunchKernelGGL(basis_prep_kernel, dim3(pblocks), dim3(256), 0, s, Q, M, static_cast<int>(D),
+  const dim3 pgrid(static_cast<unsigned>((D + 63) / 64), static_cast<unsigned>(RK / 32));
+  hipLaunchKernelGGL(basis_prep_kernel, pgrid, dim3(256), 0, s, Q, M, static_cast<int>(D),
                      static_cast<int>(r), RP, RK, QtH, QtL, QH, QL, Mm);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int Di = static_cast<int>(D);
   const int ri = static_cast<int>(r);
   switch (RP) {
-#define RW4_Y(V) case V: e = run_yproj<V>(x, T, Di, P, S, QtH, QtL, Ypart, s); break;
+#define RW4_Y(V) case V: e = run_yproj<V>(x, T, Di, P, S, ri, QtH, QtL, Mm, Zpart, s); break;
     RW4_Y(16) RW4_Y(32) RW4_Y(48) RW4_Y(64) RW4_Y(80) RW4_Y(96) RW4_Y(112) RW4_Y(128)
 #undef RW4_Y
     default: return hipErrorInvalidValue;
@@ -280,7 +449,7 @@ hipError_t launch_align_mfma(const uint16_t* x, void* out, int out_f32, const fl
   if (e != hipSuccess) return e;
   const bool of32 = out_f32 != 0;
   switch (RP) {
-#define RW4_L(V, K) case V: return run_lift<V, K>(x, T, Di, P, S, ri, Ypart, Mm, QH, QL, addend, out, of32, s);
+#define RW4_L(V, K) case V: return run_lift<V, K>(x, T, Di, P, S, ri, Zpart, QH, QL, addend, out, of32, s);
     RW4_L(16, 32) RW4_L(32, 32) RW4_L(48, 64) RW4_L(64, 64) RW4_L(80, 96) RW4_L(96, 96)
     RW4_L(112, 128) RW4_L(128, 128)
 #undef RW4_L

@@ -12,9 +12,10 @@
 // operands use the same order, so each MFMA still pairs equal k.
 //
 // Tile: NWW x NWT waves, each wave BW x BT blocks of 32 x 32 outputs (BW along
-// the weight rows, BT along the tokens). K advances 128 codes (64 bytes) per
-// step through double-buffered LDS holding the packed codes (row pitch 80
-// bytes). MFMA A = weight rows, B = token rows, so each lane's accumulators
+// the weight rows, BT along the tokens). K advances 256 codes (128 bytes) per
+// step through double-buffered LDS holding the packed codes (row pitch 144
+// bytes), global loads running two steps ahead and each 64-code fragment read
+// from LDS one sub-step before its MFMAs. MFMA A = weight rows, B = token rows, so each lane's accumulators
 // hold 4 consecutive output columns of one token (8-byte bf16 stores).
 // Workgroups are renumbered so that the eight XCDs (which receive workgroups
 // round-robin) each work on a contiguous band of weight tiles.
@@ -24,8 +25,9 @@
 namespace rw4 {
 namespace gemm {
 
-constexpr int BKB = 64;     // packed bytes per k-step (128 codes)
-constexpr int PITCH = 80;   // LDS row pitch (bytes)
+constexpr int BKB = 128;    // packed bytes per k-step (256 codes), one barrier each
+constexpr int PITCH = 144;  // LDS row pitch (bytes): 128 + 16 keeps 16-lane b128 reads conflict-free
+constexpr int KSUB = BKB / 32;  // 64-code sub-steps per k-step (two MFMAs each)
 
 __device__ __forceinline__ void widen(const uint4 p, v4i& m0, v4i& m1) {
   const uint32_t H = 0xF0F0F0F0u;
@@ -40,9 +42,10 @@ struct Cfg {
   static constexpr int TW = NWW * BW * 32;        // weight rows per tile
   static constexpr int TT = NWT * BT * 32;        // tokens per tile
   static constexpr int NTH = 64 * NWW * NWT;
-  static constexpr int LW = TW * 4 / NTH;         // 16-byte chunks per thread per k-step
-  static constexpr int LA = TT * 4 / NTH;
-  static_assert(LW >= 1 && LA >= 1 && TW * 4 % NTH == 0 && TT * 4 % NTH == 0, "tile/threads");
+  static constexpr int CPR = BKB / 16;            // 16-byte chunks per row per k-step
+  static constexpr int LW = TW * CPR / NTH;       // chunks per thread per k-step
+  static constexpr int LA = TT * CPR / NTH;
+  static_assert(LW >= 1 && LA >= 1 && TW * CPR % NTH == 0 && TT * CPR % NTH == 0, "tile/threads");
 };
 
 template <int NWW, int NWT, int BW, int BT, bool I32OUT>
@@ -74,37 +77,55 @@ gemm_kernel(const uint8_t* __restrict__ a, const float* __restrict__ s_a,
   const int KB = K / 2;
   const int nk = (KB + BKB - 1) / BKB;
 
+  // per-thread global source rows (clamped: rows past T or N load valid
+  // memory and only feed outputs that are never stored)
+  const uint8_t* gw[C::LW];
+  const uint8_t* ga[C::LA];
+  int cw[C::LW], ca[C::LA];
+#pragma unroll
+  for (int i = 0; i < C::LW; ++i) {
+    const int c = tid + C::NTH * i;
+    cw[i] = (c % C::CPR) * 16;
+    gw[i] = w + static_cast<int64_t>(min(n0 + c / C::CPR, N - 1)) * KB + cw[i];
+  }
+#pragma unroll
+  for (int i = 0; i < C::LA; ++i) {
+    const int c = tid + C::NTH * i;
+    ca[i] = (c % C::CPR) * 16;
+    ga[i] = a + static_cast<int64_t>(min(t0 + c / C::CPR, T - 1)) * KB + ca[i];
+  }
   uint4 rw_[C::LW], ra_[C::LA];
+  // loads are unconditional (no exec-masked branches around them): chunks
+  // past the end of K read the row's first chunk and are zeroed by a mask
   auto gload = [&](int ks) {
+    const int kb = ks * BKB;
 #pragma unroll
     for (int i = 0; i < C::LW; ++i) {
-      const int c = tid + C::NTH * i;
-      const int row = c >> 2;
-      const int kb = ks * BKB + (c & 3) * 16;
-      const int tn = min(n0 + row, N - 1);
-      rw_[i] = kb < KB ? *reinterpret_cast<const uint4*>(w + static_cast<int64_t>(tn) * KB + kb)
-                       : make_uint4(0, 0, 0, 0);
+      const bool ok = kb + cw[i] < KB;
+      uint4 v = *reinterpret_cast<const uint4*>(gw[i] + (ok ? kb : -cw[i]));
+      const uint32_t m = ok ? 0xFFFFFFFFu : 0u;
+      v.x &= m; v.y &= m; v.z &= m; v.w &= m;
+      rw_[i] = v;
     }
 #pragma unroll
     for (int i = 0; i < C::LA; ++i) {
-      const int c = tid + C::NTH * i;
-      const int row = c >> 2;
-      const int kb = ks * BKB + (c & 3) * 16;
-      const int ta = min(t0 + row, T - 1);
-      ra_[i] = kb < KB ? *reinterpret_cast<const uint4*>(a + static_cast<int64_t>(ta) * KB + kb)
-                       : make_uint4(0, 0, 0, 0);
+      const bool ok = kb + ca[i] < KB;
+      uint4 v = *reinterpret_cast<const uint4*>(ga[i] + (ok ? kb : -ca[i]));
+      const uint32_t m = ok ? 0xFFFFFFFFu : 0u;
+      v.x &= m; v.y &= m; v.z &= m; v.w &= m;
+      ra_[i] = v;
     }
   };
   auto lstore = [&](int st) {
 #pragma unroll
     for (int i = 0; i < C::LW; ++i) {
       const int c = tid + C::NTH * i;
-      *reinterpret_cast<uint4*>(&lw[st][(c >> 2) * PITCH + (c & 3) * 16]) = rw_[i];
+      *reinterpret_cast<uint4*>(&lw[st][(c / C::CPR) * PITCH + cw[i]]) = rw_[i];
     }
 #pragma unroll
     for (int i = 0; i < C::LA; ++i) {
       const int c = tid + C::NTH * i;
-      *reinterpret_cast<uint4*>(&la[st][(c >> 2) * PITCH + (c & 3) * 16]) = ra_[i];
+      *reinterpret_cast<uint4*>(&la[st][(c / C::CPR) * PITCH + ca[i]]) = ra_[i];
     }
   };
 
@@ -116,29 +137,36 @@ gemm_kernel(const uint8_t* __restrict__ a, const float* __restrict__ s_a,
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0;
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
   const int lrow = lane & 31;
   const int lgrp = (lane >> 5) * 16;
+  const int wofs = ((ww * BW) * 32 + lrow) * PITCH + lgrp;
+  const int aofs = ((wt * BT) * 32 + lrow) * PITCH + lgrp;
+  auto frags = [&](int st, int kk, uint4 (&pw)[BW], uint4 (&pa)[BT]) {
+#pragma unroll
+    for (int i = 0; i < BW; ++i)
+      pw[i] = *reinterpret_cast<const uint4*>(&lw[st][wofs + i * 32 * PITCH + kk * 32]);
+#pragma unroll
+    for (int j = 0; j < BT; ++j)
+      pa[j] = *reinterpret_cast<const uint4*>(&la[st][aofs + j * 32 * PITCH + kk * 32]);
+  };
+
+  gload(0);
+  lstore(0);
+  if (nk > 1) gload(1);
+  __syncthreads();
   for (int ks = 0; ks < nk; ++ks) {
     const int st = ks & 1;
-    if (ks + 1 < nk) gload(ks + 1);
+    uint4 pw[BW], pa[BT];
+    frags(st, 0, pw, pa);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < KSUB; ++kk) {
+      uint4 qw[BW], qa[BT];
+      if (kk + 1 < KSUB) frags(st, kk + 1, qw, qa);
       v4i w0[BW], w1[BW], a0[BT], a1[BT];
 #pragma unroll
-      for (int i = 0; i < BW; ++i) {
-        const uint4 p = *reinterpret_cast<const uint4*>(
-            &lw[st][((ww * BW + i) * 32 + lrow) * PITCH + kk * 32 + lgrp]);
-        widen(p, w0[i], w1[i]);
-      }
+      for (int i = 0; i < BW; ++i) widen(pw[i], w0[i], w1[i]);
 #pragma unroll
-      for (int j = 0; j < BT; ++j) {
-        const uint4 p = *reinterpret_cast<const uint4*>(
-            &la[st][((wt * BT + j) * 32 + lrow) * PITCH + kk * 32 + lgrp]);
-        widen(p, a0[j], a1[j]);
-      }
+      for (int j = 0; j < BT; ++j) widen(pa[j], a0[j], a1[j]);
 #pragma unroll
       for (int i = 0; i < BW; ++i)
 #pragma unroll
@@ -149,53 +177,91 @@ gemm_kernel(const uint8_t* __restrict__ a, const float* __restrict__ s_a,
 #pragma unroll
         for (int j = 0; j < BT; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(w1[i], a1[j], acc[i][j], 0, 0, 0);
+      if (kk + 1 < KSUB) {
+#pragma unroll
+        for (int i = 0; i < BW; ++i) pw[i] = qw[i];
+#pragma unroll
+        for (int j = 0; j < BT; ++j) pa[j] = qa[j];
+      }
     }
     if (ks + 1 < nk) lstore(st ^ 1);
     __syncthreads();
+    if (ks + 2 < nk) gload(ks + 2);
   }
 
   // epilogue: lane holds, for token t = .. + (lane & 31), output columns
   // n = .. + 8*(v/4) + 4*(lane/32) + v%4, v = 0..15
+  if constexpr (!I32OUT) {
+    // bf16 results go through LDS (the k-loop buffers are free now) so that the
+    // tile is written as whole contiguous row segments: 16 lanes per 256 bytes
+    constexpr int SP = C::TW + 8;                       // staging row pitch (bf16)
+    static_assert(C::TT * SP * 2 <= 2 * (C::TW + C::TT) * PITCH, "staging fits the k-loop LDS");
+    uint16_t* stage = reinterpret_cast<uint16_t*>(&lw[0][0]);
 #pragma unroll
-  for (int j = 0; j < BT; ++j) {
-    const int t = t0 + (wt * BT + j) * 32 + (lane & 31);
-    if (t >= T) continue;
-    const float sa = I32OUT ? 0.0f : s_a[t];
+    for (int j = 0; j < BT; ++j) {
+      const int tt = (wt * BT + j) * 32 + (lane & 31);
+      const float sa = s_a[min(t0 + tt, T - 1)];
 #pragma unroll
-    for (int i = 0; i < BW; ++i) {
+      for (int i = 0; i < BW; ++i) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = n0 + (ww * BW + i) * 32 + 8 * q + 4 * (lane >> 5);
-        int vals[4];
+        for (int q = 0; q < 4; ++q) {
+          const int nn = (ww * BW + i) * 32 + 8 * q + 4 * (lane >> 5);
+          // clamped, unconditional scale loads (columns past N are never stored)
+          float swv[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) vals[c] = acc[i][j][4 * q + c] >> 8;
-        const int64_t off = static_cast<int64_t>(t) * N + n;
-        const bool full = n + 3 < N && (N & 3) == 0;
-        if constexpr (I32OUT) {
-          int* yp = static_cast<int*>(y) + off;
-          if (full) {
+          for (int c = 0; c < 4; ++c) swv[c] = s_w[min(n0 + nn + c, N - 1)];
+          uint16_t o[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            o[c] = f32_to_bf16((static_cast<float>(acc[i][j][4 * q + c] >> 8) * sa) * swv[c]);
+          *reinterpret_cast<uint2*>(&stage[tt * SP + nn]) =
+              make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16));
+        }
+      }
+    }
+    __syncthreads();
+    constexpr int CPRW = C::TW / 8;                     // 16-byte chunks per staged row
+    uint16_t* yb = static_cast<uint16_t*>(y);
+    for (int c = tid; c < C::TT * CPRW; c += C::NTH) {
+      const int tt = c / CPRW;
+      const int nn = (c % CPRW) * 8;
+      const int t = t0 + tt;
+      const int n = n0 + nn;
+      if (t >= T) continue;
+      const uint4 v = *reinterpret_cast<const uint4*>(&stage[tt * SP + nn]);
+      uint16_t* yp = yb + static_cast<int64_t>(t) * N + n;
+      if (n + 7 < N && (N & 7) == 0) {
+        *reinterpret_cast<uint4*>(yp) = v;
+      } else {
+        const uint16_t e[8] = {static_cast<uint16_t>(v.x), static_cast<uint16_t>(v.x >> 16),
+                               static_cast<uint16_t>(v.y), static_cast<uint16_t>(v.y >> 16),
+                               static_cast<uint16_t>(v.z), static_cast<uint16_t>(v.z >> 16),
+                               static_cast<uint16_t>(v.w), static_cast<uint16_t>(v.w >> 16)};
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (n + k < N) yp[k] = e[k];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < BT; ++j) {
+      const int t = t0 + (wt * BT + j) * 32 + (lane & 31);
+      if (t >= T) continue;
+#pragma unroll
+      for (int i = 0; i < BW; ++i) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + (ww * BW + i) * 32 + 8 * q + 4 * (lane >> 5);
+          int vals[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) vals[c] = acc[i][j][4 * q + c] >> 8;
+          int* yp = static_cast<int*>(y) + static_cast<int64_t>(t) * N + n;
+          if (n + 3 < N && (N & 3) == 0) {
             *reinterpret_cast<int4*>(yp) = make_int4(vals[0], vals[1], vals[2], vals[3]);
           } else {
 #pragma unroll
             for (int c = 0; c < 4; ++c)
               if (n + c < N) yp[c] = vals[c];
-          }
-        } else {
-          uint16_t* yp = static_cast<uint16_t*>(y) + off;
-          uint16_t o[4];
-          if (full) {
-            const float4 sw = *reinterpret_cast<const float4*>(s_w + n);
-            o[0] = f32_to_bf16((static_cast<float>(vals[0]) * sa) * sw.x);
-            o[1] = f32_to_bf16((static_cast<float>(vals[1]) * sa) * sw.y);
-            o[2] = f32_to_bf16((static_cast<float>(vals[2]) * sa) * sw.z);
-            o[3] = f32_to_bf16((static_cast<float>(vals[3]) * sa) * sw.w);
-            *reinterpret_cast<uint2*>(yp) =
-                make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16),
-                           o[2] | (static_cast<uint32_t>(o[3]) << 16));
-          } else {
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-              if (n + c < N) yp[c] = f32_to_bf16((static_cast<float>(vals[c]) * sa) * s_w[n + c]);
           }
         }
       }

@@ -99,14 +99,24 @@ __device__ __forceinline__ void run_passes(float (&v)[1 << E], float* rowlds, in
 }
 
 // load EPT contiguous inputs of a row starting at element e0 as fp32
+// Loads are unconditional: a row past T reads the last row (rowoff is
+// clamped by the caller) and its values are zeroed afterwards, so no load sits
+// inside a branch whose result is used after the branch.
+template <int IN, int EPT>
+__device__ __forceinline__ void load_row_raw(float (&v)[EPT], const void* x, int64_t rowoff, int e0,
+                                             int D);
+
 template <int IN, int EPT>
 __device__ __forceinline__ void load_row(float (&v)[EPT], const void* x, int64_t rowoff, int e0,
                                          int D, bool active) {
-  if (!active) {
+  load_row_raw<IN, EPT>(v, x, rowoff, e0, D);
 #pragma unroll
-    for (int i = 0; i < EPT; ++i) v[i] = 0.0f;
-    return;
-  }
+  for (int i = 0; i < EPT; ++i) v[i] = active ? v[i] : 0.0f;
+}
+
+template <int IN, int EPT>
+__device__ __forceinline__ void load_row_raw(float (&v)[EPT], const void* x, int64_t rowoff, int e0,
+                                             int D) {
   if constexpr (IN == IN_F32) {
     const float* p = static_cast<const float*>(x) + rowoff + e0;
     if constexpr (EPT >= 4) {
@@ -219,7 +229,7 @@ row_kernel(const void* __restrict__ x, int64_t ldx, int64_t T, float* __restrict
   const bool active = row < T;
 
   float v[EPT];
-  load_row<IN, EPT>(v, x, row * ldx, t * EPT, D, active);
+  load_row<IN, EPT>(v, x, (active ? row : T - 1) * ldx, t * EPT, D, active);
 
   if constexpr (FW) {
     float* rowlds = lds + rl * PADD;

@@ -54,7 +54,7 @@ def test_workspace_size():
     assert L.rotated_linear_workspace_size(T, D, 0, 3) == base
     assert L.rotated_linear_workspace_size(-1, D, 0, 0) == 0
     assert L.rotated_linear_workspace_size(4, 7, 0, 0) == 0
-    # matrix-core alignment needs D % 32 == 0
+    # matrix-core alignment needs D % 64 == 0
     assert L.respin_align_workspace_size(4, 1000, 12) == 0
 
 
