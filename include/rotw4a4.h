@@ -134,6 +134,56 @@ rw4_status w4a4_gemm(const uint8_t* a, const float* s_a, const uint8_t* w, const
                      void* y, rw4_dtype y_dt, int64_t T, int64_t K, int64_t N, void* stream);
 
 /*
+ * FP6 operand tiles -- the operand format of the matrix-core W4A4 GEMM.
+ *
+ * gfx950's f8f6f4 matrix instruction multiplies FP6 E2M3 numbers, and E2M3
+ * represents every integer in [-7, 7] exactly (the range of a symmetric
+ * absmax INT4 quantizer, step absmax / 7 [IQ2 QuaRot Method; SpinQuant
+ * MOTIVATION]). A code q is stored as the E2M3 number q: sign bit 5,
+ * exponent bits 4..3 (bias 1), mantissa bits 2..0; magnitudes 0..7 encode as
+ * 0, 8, 16, 20, 24, 26, 28, 30. With fp32 accumulation every partial sum is an
+ * integer below 2^24 (K <= 131072), so the result equals the INT32 sum.
+ *
+ * Layout of a tiled matrix [R][K] (K % 64 == 0): rows are padded to
+ * Rp = ceil(R / 256) * 256 (padding rows hold code 0 when written by
+ * w4a4_tile_codes; the GEMM never stores results of padding rows). Tiles of
+ * 32 rows x 64 codes, 1536 bytes each; tile (rt, kt) starts at byte
+ * (rt * (K / 64) + kt) * 1536. Within a tile, "lane" l (0..63) owns row
+ * 32 rt + l % 32 and codes k = 64 kt + 32 (l / 32) + e for e = 0..31, as
+ * six-bit fields, field e at bit 6 e of a 192-bit little-endian string whose
+ * bytes 0..15 sit at 16 l and bytes 16..23 at 1024 + 8 l within the tile.
+ */
+
+/* bytes of the tiled form of an [R][K] code matrix; 0 on bad input.
+ * Constraints: R >= 0; K % 64 == 0, 64 <= K <= 131072. */
+size_t w4a4_tiles_size(int64_t R, int64_t K);
+
+/*
+ * w4a4_tile_codes -- packed INT4 rows (uint8 [R][K/2], conventions above) ->
+ * FP6 tiles (w4a4_tiles_size(R, K) bytes, caller-allocated). Offline weight
+ * preparation; also usable for activations. A code of -8 has no E2M3 value:
+ * it is stored as 0 and, if `bad` (device int, nullable, 4-byte aligned) is
+ * given, *bad is set to 1 (the caller clears it before and reads it after).
+ * Constraints: as w4a4_tiles_size; R < 2^31 - 256.
+ */
+rw4_status w4a4_tile_codes(const uint8_t* codes, int64_t R, int64_t K, uint8_t* tiles, int* bad,
+                           void* stream);
+
+/*
+ * w4a4_gemm_tiles -- the W4A4 GEMM on FP6 tiles [IQ2 QuaRot Method]:
+ *   acc[t][n] = sum_k a[t][k] * w[n][k]          (exact)
+ *   y[t][n]   = bf16( (fp32(acc) * s_a[t]) * s_w[n] )   or int32 acc
+ *   a  tiles of [T][K] (w4a4_tiles_size(T, K) bytes);  s_a fp32 [T]
+ *   w  tiles of [N][K] (w4a4_tiles_size(N, K) bytes);  s_w fp32 [N]
+ *   y  [T][N] bf16 or int32 (s_a, s_w unused for RW4_I32 and may be NULL)
+ * Results equal w4a4_gemm on the same codes bit for bit.
+ * Constraints: K % 64 == 0, 64 <= K <= 131072; 1 <= N, T < 2^31 - 256.
+ */
+rw4_status w4a4_gemm_tiles(const uint8_t* a, const float* s_a, const uint8_t* w,
+                           const float* s_w, void* y, rw4_dtype y_dt, int64_t T, int64_t K,
+                           int64_t N, void* stream);
+
+/*
  * rotated_linear -- the whole unit: [align] -> [SiLU gate] -> [FWHT] ->
  * per-token INT4 quantization -> W4A4 GEMM -> bf16.
  *   flags  RW4_ALIGN: align the D-wide input with (Q, M, r) first.
@@ -144,19 +194,20 @@ rw4_status w4a4_gemm(const uint8_t* a, const float* s_a, const uint8_t* w, const
  *   x        bf16, T rows of D (or 2D with SWIGLU) values, row stride ldx
  *            elements (ldx >= width, ldx % 8 == 0)
  *   Q, M, r  as respin_align (ignored without RW4_ALIGN)
- *   w, s_w   weight codes uint8 [N][D/2] and fp32 scales [N]; the weights must
- *            already carry the inverse of every rotation applied here (e.g.
- *            rows Hadamard-transformed along K when RW4_FWHT is set)
+ *   w, s_w   weight codes as FP6 tiles of [N][D] (w4a4_tile_codes) and fp32
+ *            scales [N]; the weights must already carry the inverse of every
+ *            rotation applied here (e.g. rows Hadamard-transformed along K
+ *            when RW4_FWHT is set) and hold no code -8
  *   y        bf16 [T][N]
  *   workspace device memory of at least rotated_linear_workspace_size(T, D,
  *            r, flags) bytes, 256-byte aligned. After the call it holds the
- *            activation codes uint8 [T][D/2] at offset 0 and the per-token
- *            scales fp32 [T] at offset rw4_align256(T * D / 2); the rest is
+ *            activation codes as FP6 tiles of [T][D] at offset 0
+ *            (w4a4_tiles_size(T, D) bytes) and the per-token scales fp32 [T]
+ *            at offset rw4_align256(w4a4_tiles_size(T, D)); the rest is
  *            internal.
  *   dbg_prequant nullable fp32 [T][D]: if given, receives the fp32 values that
  *            were quantized (for stage-wise checking).
- * Constraints: D a power of two, 32 <= D <= 32768; with RW4_ALIGN and r > 0,
- * D >= 64 (the alignment runs on matrix cores).
+ * Constraints: D a power of two, 64 <= D <= 32768; 1 <= N, T < 2^31 - 256.
  */
 rw4_status rotated_linear(const void* x, int64_t ldx, int64_t T, int64_t D,
                           const float* Q, const float* M, int64_t r, unsigned flags,
@@ -176,7 +227,7 @@ const char* rw4_status_string(rw4_status s);
 /* ABI version of this header (bumped on any signature change) */
 int rw4_abi_version(void);
 
-#define RW4_ABI_VERSION 2
+#define RW4_ABI_VERSION 3
 
 #ifdef __cplusplus
 }

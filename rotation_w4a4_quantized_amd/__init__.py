@@ -16,7 +16,7 @@ __all__ = [
     "RW4_ALIGN", "RW4_FWHT", "RW4_SWIGLU", "Rw4Error", "lib", "library_path",
     "respin_align", "fwht", "quant_act_int4", "w4a4_gemm", "rotated_linear",
     "rotated_linear_workspace_size", "respin_align_workspace_size", "workspace_views",
-    "prep_weight", "layer",
+    "w4a4_tiles_size", "w4a4_tile_codes", "w4a4_gemm_tiles", "prep_weight", "layer",
 ]
 
 RW4_ALIGN, RW4_FWHT, RW4_SWIGLU = 1, 2, 4
@@ -27,8 +27,8 @@ library_path = os.path.join(_HERE, "librotw4a4.so")
 _lib = None
 
 EXPORTS = ("respin_align", "respin_align_workspace_size", "fwht", "quant_act_int4", "w4a4_gemm",
-           "rotated_linear", "rotated_linear_workspace_size", "rw4_align256", "rw4_status_string",
-           "rw4_abi_version")
+           "w4a4_tiles_size", "w4a4_tile_codes", "w4a4_gemm_tiles", "rotated_linear",
+           "rotated_linear_workspace_size", "rw4_align256", "rw4_status_string", "rw4_abi_version")
 
 
 class Rw4Error(RuntimeError):
@@ -55,6 +55,10 @@ def lib() -> ctypes.CDLL:
     L.fwht.argtypes = [vp, i32, vp, i64, i64, vp]
     L.quant_act_int4.argtypes = [vp, i32, vp, vp, i64, i64, vp]
     L.w4a4_gemm.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp]
+    L.w4a4_tiles_size.argtypes = [i64, i64]
+    L.w4a4_tiles_size.restype = sz
+    L.w4a4_tile_codes.argtypes = [vp, i64, i64, vp, vp, vp]
+    L.w4a4_gemm_tiles.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp]
     L.rotated_linear.argtypes = [vp, i64, i64, i64, vp, vp, i64, u32, vp, vp, i64, vp, vp, sz,
                                  vp, vp]
     L.rotated_linear_workspace_size.argtypes = [i64, i64, i64, u32]
@@ -64,7 +68,8 @@ def lib() -> ctypes.CDLL:
     L.rw4_status_string.argtypes = [i32]
     L.rw4_status_string.restype = ctypes.c_char_p
     L.rw4_abi_version.restype = i32
-    for f in ("respin_align", "fwht", "quant_act_int4", "w4a4_gemm", "rotated_linear"):
+    for f in ("respin_align", "fwht", "quant_act_int4", "w4a4_gemm", "w4a4_tile_codes",
+              "w4a4_gemm_tiles", "rotated_linear"):
         getattr(L, f).restype = i32
     _lib = L
     return L
@@ -192,6 +197,46 @@ def w4a4_gemm(a, s_a, w, s_w, out=None, out_dtype=None):
     return out
 
 
+def w4a4_tiles_size(R: int, K: int) -> int:
+    """Bytes of the FP6 tile form of an [R][K] code matrix (layout in include/rotw4a4.h)."""
+    return int(lib().w4a4_tiles_size(R, K))
+
+
+def w4a4_tile_codes(codes, tiles=None, check: bool = True):
+    """Packed INT4 rows uint8 [R][K/2] -> FP6 tiles (flat uint8). With ``check``
+    the call synchronizes and raises if any code was -8 (no FP6 value)."""
+    torch = _torch()
+    _contig(codes)
+    R, KB = codes.shape
+    K = 2 * KB
+    n = w4a4_tiles_size(R, K)
+    if n == 0 and R > 0:
+        raise Rw4Error("w4a4_tile_codes", -2, lib().rw4_status_string(-2).decode())
+    if tiles is None:
+        tiles = torch.empty((max(n, 16),), dtype=torch.uint8, device=codes.device)
+    bad = torch.zeros((1,), dtype=torch.int32, device=codes.device) if check else None
+    st = lib().w4a4_tile_codes(_p(codes), R, K, _p(tiles), _p(bad), _stream())
+    _check("w4a4_tile_codes", st)
+    if check and int(bad.item()) != 0:
+        raise ValueError("w4a4_tile_codes: code -8 has no FP6 value (codes must lie in [-7, 7])")
+    return tiles
+
+
+def w4a4_gemm_tiles(a, s_a, w, s_w, T: int, K: int, N: int, out=None, out_dtype=None):
+    """The W4A4 GEMM on FP6 tiles: bf16(acc * s_a[t] * s_w[n]) or int32 acc."""
+    torch = _torch()
+    for name, t, R in (("a", a, T), ("w", w, N)):
+        if t.numel() * t.element_size() < w4a4_tiles_size(R, K):
+            raise ValueError(f"{name}: tile buffer too small")
+    odt = out_dtype or (out.dtype if out is not None else torch.bfloat16)
+    if out is None:
+        out = torch.empty((T, N), dtype=odt, device=a.device)
+    ydt = _I32 if odt == torch.int32 else _BF16
+    st = lib().w4a4_gemm_tiles(_p(a), _p(s_a), _p(w), _p(s_w), _p(out), ydt, T, K, N, _stream())
+    _check("w4a4_gemm_tiles", st)
+    return out
+
+
 def rotated_linear_workspace_size(T: int, D: int, r: int, flags: int) -> int:
     return int(lib().rotated_linear_workspace_size(T, D, r, flags))
 
@@ -201,8 +246,10 @@ def rotated_linear(x, w, s_w, flags: int, Q=None, M=None, out=None, workspace=No
     """[align] -> [SiLU gate] -> [FWHT] -> INT4 quant -> W4A4 GEMM -> bf16 [T][N].
 
     ``x`` is bf16 [T][D] (or [T][2D] with RW4_SWIGLU); a row-strided view is
-    allowed. Returns (y, workspace); the workspace holds the activation codes
-    and scales after the call (layout in include/rotw4a4.h).
+    allowed. ``w`` holds the weight codes as FP6 tiles (``prep_weight`` /
+    ``w4a4_tile_codes``), ``s_w`` their fp32 scales [N]. Returns (y,
+    workspace); the workspace holds the activation tiles and scales after the
+    call (layout in include/rotw4a4.h).
     """
     torch = _torch()
     _rows(x)
@@ -210,7 +257,9 @@ def rotated_linear(x, w, s_w, flags: int, Q=None, M=None, out=None, workspace=No
         raise TypeError("x must be bf16")
     T = x.shape[0]
     D = x.shape[1] // 2 if flags & RW4_SWIGLU else x.shape[1]
-    N = w.shape[0]
+    N = s_w.shape[0]
+    if w.numel() * w.element_size() < w4a4_tiles_size(N, D):
+        raise ValueError("w: weight tile buffer too small for [N][D]")
     r = Q.shape[1] if (flags & RW4_ALIGN) and Q is not None else 0
     need = rotated_linear_workspace_size(T, D, r, flags)
     if workspace is None:
@@ -226,27 +275,30 @@ def rotated_linear(x, w, s_w, flags: int, Q=None, M=None, out=None, workspace=No
 
 
 def workspace_views(workspace, T: int, D: int):
-    """(codes uint8 [T][D/2], scales fp32 [T]) inside a rotated_linear workspace."""
-    off = int(lib().rw4_align256(T * D // 2))
-    codes = workspace[: T * D // 2].view(T, D // 2)
+    """(activation tiles, flat uint8, and scales fp32 [T]) inside a rotated_linear workspace."""
+    n = w4a4_tiles_size(T, D)
+    off = int(lib().rw4_align256(n))
+    tiles = workspace[:n]
     scales = workspace[off: off + 4 * T].view(_torch().float32)
-    return codes, scales
+    return tiles, scales
 
 
 def prep_weight(W, rotate: bool):
     """Offline weight preparation on the GPU: optional row-wise Hadamard along K
-    (fwht), then per-output-channel INT4 (quant_act_int4). W fp32 [N][K]."""
+    (fwht), per-output-channel INT4 (quant_act_int4), then FP6 tiles.
+    W fp32 [N][K]. Returns (tiles, s_w, codes [N][K/2], rotated W)."""
     _contig(W)
     src = fwht(W) if rotate else W
     codes, s_w = quant_act_int4(src)
-    return codes, s_w, src
+    tiles = w4a4_tile_codes(codes)
+    return tiles, s_w, codes, src
 
 
 def layer(x0, basis, weights, D: int, ws=None):
     """One decoder layer's quantized path (each token attends only to itself):
     qkv = L(x0); o = L(V part of qkv); x1 = bf16(align1(x0) + o);
     gu = L(x1); d = L_down(FWHT(SiLU(g) * u)); x2 = bf16(align2(x1) + d).
-    ``weights``: name -> (codes, s_w) for qkv, o, gate_up, down. Returns a dict
+    ``weights``: name -> (tiles, s_w) for qkv, o, gate_up, down. Returns a dict
     of every stage's output tensor."""
     torch = _torch()
     (Q1, M1), (Q2, M2) = basis

@@ -13,6 +13,7 @@ inline bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 inline bool fdt(rw4_dtype d) { return d == RW4_BF16 || d == RW4_F32; }
 inline rw4_status hip_status(hipError_t e) { return e == hipSuccess ? RW4_OK : RW4_ERR_HIP; }
 inline hipStream_t strm(void* s) { return static_cast<hipStream_t>(s); }
+inline bool tiles_k_ok(int64_t K) { return K >= 64 && K % 64 == 0 && K <= 131072; }
 
 rw4_status check_align_args(const void* x, rw4_dtype x_dt, const void* out, rw4_dtype out_dt,
                             const float* Q, const float* M, int64_t T, int64_t D, int64_t r) {
@@ -81,7 +82,7 @@ rw4_status fwht(const void* x, rw4_dtype x_dt, float* y, int64_t T, int64_t D, v
   if (x == static_cast<const void*>(y) && x_dt != RW4_F32) return RW4_ERR_INVALID_ARG;
   if (T == 0) return RW4_OK;
   return hip_status(rw4::launch_row(x, x_dt == RW4_F32 ? rw4::IN_F32 : rw4::IN_BF16, D, T, D, true,
-                                    y, nullptr, nullptr, nullptr, strm(stream)));
+                                    y, nullptr, false, nullptr, nullptr, strm(stream)));
 }
 
 rw4_status quant_act_int4(const void* x, rw4_dtype x_dt, uint8_t* codes, float* scales, int64_t T,
@@ -94,8 +95,8 @@ rw4_status quant_act_int4(const void* x, rw4_dtype x_dt, uint8_t* codes, float* 
   if (T == 0) return RW4_OK;
   const int in = x_dt == RW4_F32 ? rw4::IN_F32 : rw4::IN_BF16;
   if (pow2(D) && D <= 32768)
-    return hip_status(rw4::launch_row(x, in, D, T, D, false, nullptr, codes, scales, nullptr,
-                                      strm(stream)));
+    return hip_status(rw4::launch_row(x, in, D, T, D, false, nullptr, codes, false, scales,
+                                      nullptr, strm(stream)));
   return hip_status(rw4::launch_quant_generic(x, in, D, T, D, codes, scales, strm(stream)));
 }
 
@@ -114,10 +115,42 @@ rw4_status w4a4_gemm(const uint8_t* a, const float* s_a, const uint8_t* w, const
   return hip_status(rw4::launch_gemm(a, s_a, w, s_w, y, y_dt == RW4_I32, T, K, N, strm(stream)));
 }
 
+size_t w4a4_tiles_size(int64_t R, int64_t K) {
+  if (R < 0 || !tiles_k_ok(K)) return 0;
+  return rw4::tiles_bytes(R, K);
+}
+
+rw4_status w4a4_tile_codes(const uint8_t* codes, int64_t R, int64_t K, uint8_t* tiles, int* bad,
+                           void* stream) {
+  if (R < 0) return RW4_ERR_INVALID_ARG;
+  if (!tiles_k_ok(K)) return RW4_ERR_UNSUPPORTED;
+  if (R > (int64_t(1) << 31) - 256) return RW4_ERR_UNSUPPORTED;
+  if (R == 0) return RW4_OK;
+  if (!codes || !tiles) return RW4_ERR_INVALID_ARG;
+  if (!al16(codes) || !al16(tiles)) return RW4_ERR_MISALIGNED;
+  if (bad && (reinterpret_cast<uintptr_t>(bad) & 3u)) return RW4_ERR_MISALIGNED;
+  return hip_status(rw4::launch_tile_codes(codes, R, K, tiles, bad, strm(stream)));
+}
+
+rw4_status w4a4_gemm_tiles(const uint8_t* a, const float* s_a, const uint8_t* w,
+                           const float* s_w, void* y, rw4_dtype y_dt, int64_t T, int64_t K,
+                           int64_t N, void* stream) {
+  if (T < 0 || N < 1) return RW4_ERR_INVALID_ARG;
+  if (y_dt != RW4_BF16 && y_dt != RW4_I32) return RW4_ERR_INVALID_ARG;
+  if (!tiles_k_ok(K)) return RW4_ERR_UNSUPPORTED;
+  if (T > (int64_t(1) << 31) - 256 || N > (int64_t(1) << 31) - 256) return RW4_ERR_UNSUPPORTED;
+  if (T == 0) return RW4_OK;
+  if (!a || !w || !y) return RW4_ERR_INVALID_ARG;
+  if (y_dt == RW4_BF16 && (!s_a || !s_w)) return RW4_ERR_INVALID_ARG;
+  if (!al16(a) || !al16(w) || !al16(y)) return RW4_ERR_MISALIGNED;
+  if (y_dt == RW4_BF16 && (!al16(s_a) || !al16(s_w))) return RW4_ERR_MISALIGNED;
+  return hip_status(
+      rw4::launch_gemm_tiles(a, s_a, w, s_w, y, y_dt == RW4_I32, T, K, N, strm(stream)));
+}
+
 size_t rotated_linear_workspace_size(int64_t T, int64_t D, int64_t r, unsigned flags) {
-  if (T < 0 || D < 2 || (D % 2) != 0 || r < 0) return 0;
-  size_t n = rw4_align256(static_cast<size_t>(T) * static_cast<size_t>(D) / 2) +
-             rw4_align256(4u * static_cast<size_t>(T));
+  if (T < 0 || !pow2(D) || D < 64 || D > 32768 || r < 0) return 0;
+  size_t n = rw4_align256(rw4::tiles_bytes(T, D)) + rw4_align256(4u * static_cast<size_t>(T));
   if ((flags & RW4_ALIGN) && r > 0) {
     if (!rw4::align_mfma_supported(D, r)) return 0;
     n += rw4_align256(4u * static_cast<size_t>(T) * static_cast<size_t>(D));
@@ -133,7 +166,7 @@ rw4_status rotated_linear(const void* x, int64_t ldx, int64_t T, int64_t D, cons
   if (T < 0 || N < 1) return RW4_ERR_INVALID_ARG;
   if (flags & ~static_cast<unsigned>(RW4_ALIGN | RW4_FWHT | RW4_SWIGLU)) return RW4_ERR_INVALID_ARG;
   if ((flags & RW4_ALIGN) && (flags & RW4_SWIGLU)) return RW4_ERR_INVALID_ARG;
-  if (!pow2(D) || D < 32 || D > 32768) return RW4_ERR_UNSUPPORTED;
+  if (!pow2(D) || D < 64 || D > 32768) return RW4_ERR_UNSUPPORTED;
   if (T == 0) return RW4_OK;
   if (!x || !w || !s_w || !y) return RW4_ERR_INVALID_ARG;
   const int64_t width = (flags & RW4_SWIGLU) ? 2 * D : D;
@@ -144,18 +177,17 @@ rw4_status rotated_linear(const void* x, int64_t ldx, int64_t T, int64_t D, cons
     if (ldx != D) return RW4_ERR_UNSUPPORTED;
     if (r > 0 && !rw4::align_mfma_supported(D, r)) return RW4_ERR_UNSUPPORTED;
   }
-  if (T > (int64_t(1) << 31) - 1 || N > (int64_t(1) << 31) - 1) return RW4_ERR_UNSUPPORTED;
+  if (T > (int64_t(1) << 31) - 256 || N > (int64_t(1) << 31) - 256) return RW4_ERR_UNSUPPORTED;
   if (!al16(x) || !al16(w) || !al16(s_w) || !al16(y)) return RW4_ERR_MISALIGNED;
   if (dbg_prequant && !al16(dbg_prequant)) return RW4_ERR_MISALIGNED;
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return RW4_ERR_WORKSPACE;
   if (ws_bytes < rotated_linear_workspace_size(T, D, (flags & RW4_ALIGN) ? r : 0, flags))
     return RW4_ERR_WORKSPACE;
-  if (T == 0) return RW4_OK;
 
   hipStream_t s = strm(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint8_t* codes = ws;
-  float* s_a = reinterpret_cast<float*>(ws + rw4_align256(static_cast<size_t>(T) * D / 2));
+  float* s_a = reinterpret_cast<float*>(ws + rw4_align256(rw4::tiles_bytes(T, D)));
   const void* src = x;
   int in = (flags & RW4_SWIGLU) ? rw4::IN_SWIGLU : rw4::IN_BF16;
   int64_t ld = ldx;
@@ -170,10 +202,10 @@ rw4_status rotated_linear(const void* x, int64_t ldx, int64_t T, int64_t D, cons
     in = rw4::IN_F32;
     ld = D;
   }
-  hipError_t e = rw4::launch_row(src, in, ld, T, D, (flags & RW4_FWHT) != 0, nullptr, codes, s_a,
-                                 dbg_prequant, s);
+  hipError_t e = rw4::launch_row(src, in, ld, T, D, (flags & RW4_FWHT) != 0, nullptr, codes, true,
+                                 s_a, dbg_prequant, s);
   if (e != hipSuccess) return RW4_ERR_HIP;
-  return hip_status(rw4::launch_gemm(codes, s_a, w, s_w, y, false, T, D, N, s));
+  return hip_status(rw4::launch_gemm_tiles(codes, s_a, w, s_w, y, false, T, D, N, s));
 }
 
 }  // extern "C"

@@ -342,32 +342,31 @@ lift_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int S, int 
             make_float4(acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
     }
     __syncthreads();
-    for (int c = tid; c < TB * (ncols / 8); c += NT) {
-      const int row = c / (ncols / 8);
-      const int col = (c % (ncols / 8)) * 8;
+    // one 16-byte store per thread and chunk, so that every store instruction
+    // of a wave covers 1 KiB of one row segment
+    constexpr int CW = OF32 ? 4 : 8;
+    for (int c = tid; c < TB * (ncols / CW); c += NT) {
+      const int row = c / (ncols / CW);
+      const int col = (c % (ncols / CW)) * CW;
       const int64_t t = t0 + 16 * tb + row;
       if (t >= T) continue;
-      const float4 s0 = *reinterpret_cast<const float4*>(&stage[row][col]);
-      const float4 s1 = *reinterpret_cast<const float4*>(&stage[row][col + 4]);
-      float o[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
       const int64_t off = t * D + dbeg + col;
-      if constexpr (ADD) {
-        if constexpr (OF32) {
-          const float4* ap = reinterpret_cast<const float4*>(static_cast<const float*>(addend) + off);
-          const float4 a0 = ap[0], a1 = ap[1];
-          o[0] += a0.x; o[1] += a0.y; o[2] += a0.z; o[3] += a0.w;
-          o[4] += a1.x; o[5] += a1.y; o[6] += a1.z; o[7] += a1.w;
-        } else {
+      if constexpr (OF32) {
+        float4 o = *reinterpret_cast<const float4*>(&stage[row][col]);
+        if constexpr (ADD) {
+          const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(addend) + off);
+          o.x += a.x; o.y += a.y; o.z += a.z; o.w += a.w;
+        }
+        *reinterpret_cast<float4*>(static_cast<float*>(out) + off) = o;
+      } else {
+        const float4 s0 = *reinterpret_cast<const float4*>(&stage[row][col]);
+        const float4 s1 = *reinterpret_cast<const float4*>(&stage[row][col + 4]);
+        float o[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+        if constexpr (ADD) {
           const uint4 av = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(addend) + off);
           o[0] += bf16lo(av.x); o[1] += bf16hi(av.x); o[2] += bf16lo(av.y); o[3] += bf16hi(av.y);
           o[4] += bf16lo(av.z); o[5] += bf16hi(av.z); o[6] += bf16lo(av.w); o[7] += bf16hi(av.w);
         }
-      }
-      if constexpr (OF32) {
-        float4* op = reinterpret_cast<float4*>(static_cast<float*>(out) + off);
-        op[0] = make_float4(o[0], o[1], o[2], o[3]);
-        op[1] = make_float4(o[4], o[5], o[6], o[7]);
-      } else {
         uint32_t w[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)

@@ -10,9 +10,11 @@ enum InMode { IN_BF16 = 0, IN_F32 = 1, IN_SWIGLU = 2 };
 
 // Per-row transform: [SiLU gate] -> [Walsh-Hadamard] -> output.
 // Output either fp32 values (yf) or INT4 codes + scales (+ optional fp32 dump).
-// D must be a power of two in [2, 32768] when do_fwht is set.
+// Codes go to packed INT4 rows, or (tiled, D >= 64) to FP6 operand tiles.
+// D must be a power of two in [2, 32768].
 hipError_t launch_row(const void* x, int in_mode, int64_t ldx, int64_t T, int64_t D, bool do_fwht,
-                      float* yf, uint8_t* codes, float* scales, float* dbg, hipStream_t s);
+                      float* yf, uint8_t* codes, bool tiled, float* scales, float* dbg,
+                      hipStream_t s);
 
 // Per-row INT4 quantization for any even D (no transform).
 hipError_t launch_quant_generic(const void* x, int in_mode, int64_t ldx, int64_t T, int64_t D,
@@ -33,5 +35,15 @@ hipError_t launch_align_mfma(const uint16_t* x, void* out, int out_f32, const fl
 // W4A4 GEMM, bf16 (dequantized) or raw int32 output.
 hipError_t launch_gemm(const uint8_t* a, const float* s_a, const uint8_t* w, const float* s_w,
                        void* y, bool i32_out, int64_t T, int64_t K, int64_t N, hipStream_t s);
+
+// FP6 operand tiles (layout in common.hpp): rows padded to a multiple of 256.
+int64_t tiles_rows(int64_t R);
+size_t tiles_bytes(int64_t R, int64_t K);
+hipError_t launch_tile_codes(const uint8_t* codes, int64_t R, int64_t K, uint8_t* tiles, int* bad,
+                             hipStream_t s);
+// W4A4 GEMM on FP6 tiles, bf16 (dequantized) or raw int32 output.
+hipError_t launch_gemm_tiles(const uint8_t* a, const float* s_a, const uint8_t* w,
+                             const float* s_w, void* y, bool i32_out, int64_t T, int64_t K,
+                             int64_t N, hipStream_t s);
 
 }  // namespace rw4

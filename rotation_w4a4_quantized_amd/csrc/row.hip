@@ -208,7 +208,22 @@ __device__ __forceinline__ void store_codes(uint8_t* p, const float (&v)[EPT], f
 
 constexpr int kRowThreads = 256;
 
-template <int N, int E, int IN, bool FW, bool QOUT>
+// codes of EPT (a multiple of 16) consecutive values starting at column k0 of
+// row `row`, written as FP6 E2M3 fields into the tiled layout (common.hpp)
+template <int EPT>
+__device__ __forceinline__ void store_tiled(uint8_t* tiles, int64_t row, int64_t k0, int64_t K,
+                                            const float (&v)[EPT], float s) {
+  static_assert(EPT % 16 == 0, "tiled output needs 16-value groups");
+#pragma unroll
+  for (int h = 0; h < EPT / 16; ++h) {
+    uint32_t f[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) f[e] = e2m3(s > 0.0f ? quant4(v[16 * h + e], s) : 0);
+    store_fields16(tiles, row, k0 + 16 * h, K, pack_fields16(f));
+  }
+}
+
+template <int N, int E, int IN, bool FW, bool QOUT, bool TILED>
 __global__ void __launch_bounds__(1024)
 row_kernel(const void* __restrict__ x, int64_t ldx, int64_t T, float* __restrict__ yf,
            uint8_t* __restrict__ codes, float* __restrict__ scales, float* __restrict__ dbg,
@@ -225,7 +240,11 @@ row_kernel(const void* __restrict__ x, int64_t ldx, int64_t T, float* __restrict
   const int tid = threadIdx.x;
   const int rl = tid / P;
   const int t = tid % P;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * ROWS + rl;
+  // tiled output: give each XCD (workgroups go to XCDs round-robin) a
+  // contiguous band of rows, so a tile's 32 rows are written through one L2
+  int64_t blk = blockIdx.x;
+  if (TILED && (gridDim.x & 7) == 0) blk = (blk & 7) * (gridDim.x >> 3) + (blk >> 3);
+  const int64_t row = blk * ROWS + rl;
   const bool active = row < T;
 
   float v[EPT];
@@ -268,12 +287,15 @@ row_kernel(const void* __restrict__ x, int64_t ldx, int64_t T, float* __restrict
     if (!active) return;
     const float s = m / 7.0f;
     if (t == 0) scales[row] = s;
-    store_codes<EPT>(codes + row * (D / 2) + t * (EPT / 2), v, s);
+    if constexpr (TILED)
+      store_tiled<EPT>(codes, row, static_cast<int64_t>(t) * EPT, D, v, s);
+    else
+      store_codes<EPT>(codes + row * (D / 2) + t * (EPT / 2), v, s);
     if (dbg) store_f32<EPT>(dbg + row * D + t * EPT, v);
   }
 }
 
-template <int N, int IN, bool FW, bool QOUT>
+template <int N, int IN, bool FW, bool QOUT, bool TILED>
 hipError_t launch_row_n(const void* x, int64_t ldx, int64_t T, float* yf, uint8_t* codes,
                         float* scales, float* dbg, hipStream_t s) {
   constexpr int E = N >= 15 ? 5 : (N < 4 ? N : 4);
@@ -281,17 +303,19 @@ hipError_t launch_row_n(const void* x, int64_t ldx, int64_t T, float* yf, uint8_
   constexpr int ROWS = P >= kRowThreads ? 1 : kRowThreads / P;
   const float norm = static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(1 << N)));
   const int64_t blocks = (T + ROWS - 1) / ROWS;
-  hipLaunchKernelGGL((row_kernel<N, E, IN, FW, QOUT>), dim3(static_cast<unsigned>(blocks)),
+  if constexpr (TILED && (1 << E) < 16) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((row_kernel<N, E, IN, FW, QOUT, TILED && (1 << E) >= 16>),
+                     dim3(static_cast<unsigned>(blocks)),
                      dim3(P * ROWS), 0, s, x, ldx, T, yf, codes, scales, dbg, norm);
   return hipGetLastError();
 }
 
-template <int IN, bool FW, bool QOUT>
+template <int IN, bool FW, bool QOUT, bool TILED>
 hipError_t dispatch_n(int n, const void* x, int64_t ldx, int64_t T, float* yf, uint8_t* codes,
                       float* scales, float* dbg, hipStream_t s) {
   switch (n) {
 #define RW4_CASE(k) \
-  case k: return launch_row_n<k, IN, FW, QOUT>(x, ldx, T, yf, codes, scales, dbg, s);
+  case k: return launch_row_n<k, IN, FW, QOUT, TILED>(x, ldx, T, yf, codes, scales, dbg, s);
     RW4_CASE(1) RW4_CASE(2) RW4_CASE(3) RW4_CASE(4) RW4_CASE(5) RW4_CASE(6) RW4_CASE(7)
     RW4_CASE(8) RW4_CASE(9) RW4_CASE(10) RW4_CASE(11) RW4_CASE(12) RW4_CASE(13) RW4_CASE(14)
     RW4_CASE(15)
@@ -330,18 +354,23 @@ quant_generic_kernel(const void* __restrict__ x, int64_t ldx, int64_t D,
 }  // namespace
 
 hipError_t launch_row(const void* x, int in_mode, int64_t ldx, int64_t T, int64_t D, bool do_fwht,
-                      float* yf, uint8_t* codes, float* scales, float* dbg, hipStream_t s) {
+                      float* yf, uint8_t* codes, bool tiled, float* scales, float* dbg,
+                      hipStream_t s) {
   if (T == 0) return hipSuccess;
   int n = 0;
   while ((int64_t(1) << n) < D) ++n;
   const bool q = codes != nullptr;
-#define RW4_SEL(INM, FW, Q) \
-  if (in_mode == INM && do_fwht == FW && q == Q) \
-    return dispatch_n<INM, FW, Q>(n, x, ldx, T, yf, codes, scales, dbg, s);
-  RW4_SEL(IN_BF16, true, true) RW4_SEL(IN_BF16, true, false)
-  RW4_SEL(IN_F32, true, true) RW4_SEL(IN_F32, true, false)
-  RW4_SEL(IN_SWIGLU, true, true) RW4_SEL(IN_SWIGLU, false, true)
-  RW4_SEL(IN_BF16, false, true) RW4_SEL(IN_F32, false, true)
+  if (tiled && (!q || D < 64)) return hipErrorInvalidValue;
+#define RW4_SEL(INM, FW, Q, TL) \
+  if (in_mode == INM && do_fwht == FW && q == Q && tiled == TL) \
+    return dispatch_n<INM, FW, Q, TL>(n, x, ldx, T, yf, codes, scales, dbg, s);
+  RW4_SEL(IN_BF16, true, true, false) RW4_SEL(IN_BF16, true, false, false)
+  RW4_SEL(IN_F32, true, true, false) RW4_SEL(IN_F32, true, false, false)
+  RW4_SEL(IN_SWIGLU, true, true, false) RW4_SEL(IN_SWIGLU, false, true, false)
+  RW4_SEL(IN_BF16, false, true, false) RW4_SEL(IN_F32, false, true, false)
+  RW4_SEL(IN_BF16, true, true, true) RW4_SEL(IN_F32, true, true, true)
+  RW4_SEL(IN_SWIGLU, true, true, true) RW4_SEL(IN_SWIGLU, false, true, true)
+  RW4_SEL(IN_BF16, false, true, true) RW4_SEL(IN_F32, false, true, true)
 #undef RW4_SEL
   return hipErrorInvalidValue;
 }

@@ -22,7 +22,7 @@ def _declared():
 def test_library_built_and_loads():
     assert os.path.exists(rw.library_path), "build the HIP library first"
     L = rw.lib()
-    assert L.rw4_abi_version() == 2
+    assert L.rw4_abi_version() == 3
 
 
 def test_exports_every_declared_symbol():
@@ -45,7 +45,12 @@ def test_workspace_size():
     L = rw.lib()
     assert L.rw4_align256(1) == 256 and L.rw4_align256(256) == 256 and L.rw4_align256(0) == 0
     T, D = 2048, 4096
-    base = L.rw4_align256(T * D // 2) + L.rw4_align256(4 * T)
+    assert L.w4a4_tiles_size(T, D) == T * D * 3 // 4          # 2048 rows: already a multiple of 256
+    assert L.w4a4_tiles_size(1, 64) == 256 * 64 * 3 // 4      # rows padded to 256
+    assert L.w4a4_tiles_size(257, 128) == 512 * 128 * 3 // 4
+    assert L.w4a4_tiles_size(4, 96) == 0 and L.w4a4_tiles_size(4, 32) == 0
+    assert L.w4a4_tiles_size(-1, 64) == 0 and L.w4a4_tiles_size(0, 64) == 0
+    base = L.rw4_align256(L.w4a4_tiles_size(T, D)) + L.rw4_align256(4 * T)
     assert L.rotated_linear_workspace_size(T, D, 32, 0) == base
     assert L.rotated_linear_workspace_size(T, D, 32, 2) == base
     aws = L.respin_align_workspace_size(T, D, 32)
@@ -54,6 +59,7 @@ def test_workspace_size():
     assert L.rotated_linear_workspace_size(T, D, 0, 3) == base
     assert L.rotated_linear_workspace_size(-1, D, 0, 0) == 0
     assert L.rotated_linear_workspace_size(4, 7, 0, 0) == 0
+    assert L.rotated_linear_workspace_size(4, 32, 0, 0) == 0   # tiles need D >= 64
     # matrix-core alignment needs D % 64 == 0
     assert L.respin_align_workspace_size(4, 1000, 12) == 0
 
@@ -126,6 +132,33 @@ def test_gemm_validation(args, expect):
     assert rw.lib().w4a4_gemm(*args) == expect
 
 
+@pytest.mark.parametrize("args,expect", [
+    ((A, 4, 96, B, NUL, NUL), UNS),                 # K % 64
+    ((A, 4, 32, B, NUL, NUL), UNS),                 # K < 64
+    ((A, -1, 64, B, NUL, NUL), INV),
+    ((NUL, 4, 64, B, NUL, NUL), INV),
+    ((ODD, 4, 64, B, NUL, NUL), MIS),
+    ((A, 4, 64, B, ctypes.c_void_p(0x20002), NUL), MIS),   # flag word alignment
+    ((NUL, 0, 64, NUL, NUL, NUL), 0),               # empty call
+])
+def test_tile_codes_validation(args, expect):
+    assert rw.lib().w4a4_tile_codes(*args) == expect
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((A, B, C, Dp, A, 0, 4, 96, 16, NUL), UNS),     # K % 64
+    ((A, B, C, Dp, A, 0, 4, 262144, 16, NUL), UNS), # K too large for exact fp32 sums
+    ((A, NUL, C, Dp, A, 0, 4, 64, 16, NUL), INV),   # bf16 output needs scales
+    ((A, NUL, C, NUL, A, 2, 0, 64, 16, NUL), 0),    # T = 0
+    ((NUL, NUL, NUL, NUL, NUL, 0, 0, 64, 16, NUL), 0),
+    ((A, B, C, Dp, A, 1, 4, 64, 16, NUL), INV),     # fp32 output not offered
+    ((A, B, C, Dp, A, 0, 4, 64, 0, NUL), INV),      # N = 0
+    ((A, B, ODD, Dp, A, 0, 4, 64, 16, NUL), MIS),
+])
+def test_gemm_tiles_validation(args, expect):
+    assert rw.lib().w4a4_gemm_tiles(*args) == expect
+
+
 def _rl(x=A, ldx=64, T=4, D=64, Q=B, M=C, r=8, flags=3, w=Dp, sw=A, N=16, y=B, ws=C,
         wsb=1 << 20, dbg=NUL):
     return rw.lib().rotated_linear(x, ldx, T, D, Q, M, r, flags, w, sw, N, y, ws, wsb, dbg, NUL)
@@ -135,6 +168,7 @@ def test_rotated_linear_validation():
     assert _rl(flags=8) == INV                     # unknown flag
     assert _rl(flags=1 | 4) == INV                 # align + swiglu
     assert _rl(D=48) == UNS                        # not a power of two
+    assert _rl(D=32, ldx=32, flags=0) == UNS       # below the 64-code tile width
     assert _rl(ldx=32) == INV                      # stride below width
     assert _rl(flags=4, ldx=64) == INV             # swiglu needs 2D wide rows
     assert _rl(r=6) == UNS

@@ -6,6 +6,7 @@ the seeded generators; expected values come only from the oracle.
 import numpy as np
 import pytest
 
+import fp6_layout as F
 import oracle as O
 import workloads as W
 from gpu_util import BF16_TOL, FP32_TOL, bf16_rel, dev, host, normwise, say, torch
@@ -191,16 +192,82 @@ def test_w4a4_gemm_extremes(rw):
     assert np.all(acc == -56 * K)
 
 
+# ---------------------------------------------------------------- FP6 tiles and the tiled GEMM
+def _codes7(seed, rows, K):
+    """packed INT4 rows with codes in [-7, 7] (the symmetric quantizer's range)"""
+    q = np.random.default_rng(seed).integers(-7, 8, (rows, K))
+    return O.pack_int4(q), q
+
+
+@pytest.mark.parametrize("R,K", [(1, 64), (33, 128), (300, 192), (256, 4096), (70, 16384)])
+def test_tile_codes(rw, R, K):
+    say(f"w4a4_tile_codes R={R} K={K}")
+    packed, q = _codes7(R * 3 + K, R, K)
+    tiles = host(rw.w4a4_tile_codes(dev(packed)))
+    assert len(tiles) == F.tiles_size(R, K) == rw.w4a4_tiles_size(R, K)
+    np.testing.assert_array_equal(tiles, F.tile(q))
+
+
+def test_tile_codes_rejects_minus8(rw):
+    packed, _ = _codes7(9, 40, 128)
+    packed[17, 5] = 0x8F                                 # codes -1 and -8
+    with pytest.raises(ValueError):
+        rw.w4a4_tile_codes(dev(packed))
+
+
+@pytest.mark.parametrize("T,K,N", [(1, 64, 1), (64, 256, 256), (300, 512, 384), (129, 4096, 130),
+                                   (17, 16384, 64), (8, 4096, 12288), (257, 192, 1000),
+                                   (4096, 4096, 4096), (4100, 1024, 4104)])
+def test_w4a4_gemm_tiles(rw, T, K, N):
+    say(f"w4a4_gemm_tiles T={T} K={K} N={N}")
+    a, qa = _codes7(T + K, T, K)
+    w, qw = _codes7(N + K + 1, N, K)
+    rng = np.random.default_rng(K)
+    s_a = rng.uniform(1e-3, 1.0, T).astype(np.float32)
+    s_w = rng.uniform(1e-3, 0.1, N).astype(np.float32)
+    at = rw.w4a4_tile_codes(dev(a))
+    wt = rw.w4a4_tile_codes(dev(w))
+    acc = host(rw.w4a4_gemm_tiles(at, None, wt, None, T, K, N, out_dtype=torch().int32))
+    if T * N <= 1 << 22:
+        ref = O.gemm_int(qa, qw)
+        np.testing.assert_array_equal(acc, ref)
+    else:                                                # sampled exact dot products
+        ts = np.random.default_rng(1).integers(0, T, 512)
+        ns = np.random.default_rng(2).integers(0, N, 512)
+        ref_s = (qa[ts].astype(np.int64) * qw[ns].astype(np.int64)).sum(axis=1)
+        np.testing.assert_array_equal(acc[ts, ns], ref_s)
+        ref = None
+    y = host(rw.w4a4_gemm_tiles(at, dev(s_a), wt, dev(s_w), T, K, N))
+    # the same codes through the int8 path give the same bits
+    y8 = host(rw.w4a4_gemm(dev(a), dev(s_a), dev(w), dev(s_w)))
+    np.testing.assert_array_equal(y, y8)
+    if ref is not None:
+        nbad, worst = bf16_rel(y, O.epilogue(ref, s_a, s_w))
+        assert nbad == 0, worst
+
+
+def test_w4a4_gemm_tiles_extremes(rw):
+    T, K, N = 40, 16384, 72
+    qa = np.full((T, K), -7)
+    for wv, expect in ((-7, 49 * K), (7, -49 * K)):
+        qw = np.full((N, K), wv)
+        at = rw.w4a4_tile_codes(dev(O.pack_int4(qa)))
+        wt = rw.w4a4_tile_codes(dev(O.pack_int4(qw)))
+        acc = host(rw.w4a4_gemm_tiles(at, None, wt, None, T, K, N, out_dtype=torch().int32))
+        assert np.all(acc == expect)
+
+
 # ---------------------------------------------------------------- weight prep and the unit
 def _prep(rw, Wf, rotate):
-    codes, s_w, src = rw.prep_weight(dev(Wf), rotate)
+    tiles, s_w, codes, src = rw.prep_weight(dev(Wf), rotate)
     src_h = host(src)
     if rotate:
         assert normwise(src_h, O.fwht(Wf)) <= FP32_TOL
     q, s = O.quant_int4(src_h)
     np.testing.assert_array_equal(host(s_w), s)
     np.testing.assert_array_equal(host(codes), O.pack_int4(q))
-    return codes, s_w, q, s
+    np.testing.assert_array_equal(host(tiles), F.tile(q))
+    return tiles, s_w, q, s
 
 
 def _check_unit(rw, xb, Q, M, flags, codes_w, s_w, qw, sw_h, rows=None):
@@ -213,7 +280,8 @@ def _check_unit(rw, xb, Q, M, flags, codes_w, s_w, qw, sw_h, rows=None):
     y, ws = rw.rotated_linear(dev(xb), codes_w, s_w, flags, dev(Q) if Q is not None else None,
                               dev(M) if M is not None else None, dbg_prequant=dbg)
     _sync()
-    codes_g, sa_g = (host(v) for v in rw.workspace_views(ws, T, D))
+    tiles_g, sa_g = (host(v) for v in rw.workspace_views(ws, T, D))
+    codes_g = F.untile(tiles_g, T, D)
     pre = host(dbg)
     y = host(y)
     sel = np.arange(T) if rows is None else rows
@@ -223,7 +291,7 @@ def _check_unit(rw, xb, Q, M, flags, codes_w, s_w, qw, sw_h, rows=None):
     # 2. codes and scales: bit-exact on the GPU's own fp32 values
     q, s = O.quant_int4(pre[sel])
     np.testing.assert_array_equal(sa_g[sel], s)
-    np.testing.assert_array_equal(codes_g[sel], O.pack_int4(q))
+    np.testing.assert_array_equal(codes_g[sel], q)
     # 3. GEMM + epilogue on those codes
     ref_y = O.epilogue(O.gemm_int(q, qw), s, sw_h)
     nbad, worst = bf16_rel(y[sel], ref_y)
@@ -254,7 +322,7 @@ def test_rotated_linear_config4_sampled(rw):
     say(f"rotated_linear {wl.name} (sampled)")
     inp = W.workload_inputs(wl)
     Q, M = inp["basis"][0]
-    codes_w, s_w, src = rw.prep_weight(dev(inp["W"]["lin"]), True)
+    tiles_w, s_w, codes_w, src = rw.prep_weight(dev(inp["W"]["lin"]), True)
     rows_w = np.random.default_rng(4).choice(wl.linears[0].N, 64, replace=False)
     src_h = host(src[torch().from_numpy(rows_w).cuda()])
     assert normwise(src_h, O.fwht(inp["W"]["lin"][rows_w])) <= FP32_TOL
@@ -263,7 +331,7 @@ def test_rotated_linear_config4_sampled(rw):
     qw = O.unpack_int4(host(codes_w))
     sw_h = host(s_w)
     rows = np.sort(np.random.default_rng(5).choice(wl.T, 48, replace=False))
-    _check_unit(rw, inp["x"], Q, M, O.FLAG_ALIGN | O.FLAG_FWHT, codes_w, s_w, qw, sw_h, rows=rows)
+    _check_unit(rw, inp["x"], Q, M, O.FLAG_ALIGN | O.FLAG_FWHT, tiles_w, s_w, qw, sw_h, rows=rows)
 
 
 @pytest.mark.parametrize("T,D,N,flags", [(77, 512, 200, 0), (77, 512, 200, 2), (50, 256, 64, 4 | 2),
@@ -301,8 +369,8 @@ def _layer_check(rw, cid, sample=None):
     inp = W.workload_inputs(wl)
     weights, qws, sws = {}, {}, {}
     for lin in wl.linears:
-        c, s, src = rw.prep_weight(dev(inp["W"][lin.name]), lin.rotate)
-        weights[lin.name] = (c, s)
+        tl, s, c, src = rw.prep_weight(dev(inp["W"][lin.name]), lin.rotate)
+        weights[lin.name] = (tl, s)
         qws[lin.name] = O.unpack_int4(host(c))
         sws[lin.name] = host(s)
     basis = [(dev(Q), dev(M)) for Q, M in inp["basis"]]
