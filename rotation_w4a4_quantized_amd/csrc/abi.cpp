@@ -195,8 +195,16 @@ rw4_status rotated_linear(const void* x, int64_t ldx, int64_t T, int64_t D, cons
     uint8_t* tmpb = reinterpret_cast<uint8_t*>(s_a) + rw4_align256(4u * static_cast<size_t>(T));
     float* tmp = reinterpret_cast<float*>(tmpb);
     void* aws = tmpb + rw4_align256(4u * static_cast<size_t>(T) * static_cast<size_t>(D));
-    hipError_t e = rw4::launch_align_mfma(static_cast<const uint16_t*>(x), tmp, 1, Q, M, nullptr,
-                                          T, D, r, aws, s);
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    if (rw4::lfq_supported(D, r)) {
+      // projection, then lift + transform + quantization on chip
+      if (rw4::launch_align_prep_proj(xb, Q, M, T, D, r, aws, s) != hipSuccess) return RW4_ERR_HIP;
+      if (rw4::launch_lift_fwht_quant(xb, T, D, r, aws, (flags & RW4_FWHT) != 0, codes, s_a,
+                                      dbg_prequant, s) != hipSuccess)
+        return RW4_ERR_HIP;
+      return hip_status(rw4::launch_gemm_tiles(codes, s_a, w, s_w, y, false, T, D, N, s));
+    }
+    hipError_t e = rw4::launch_align_mfma(xb, tmp, 1, Q, M, nullptr, T, D, r, aws, s);
     if (e != hipSuccess) return RW4_ERR_HIP;
     src = tmp;
     in = rw4::IN_F32;

@@ -13,7 +13,7 @@
 //   prep : Qh/Ql in both orientations ([r][D] for the projection, [D][r] for
 //          the lift), zero-padded in r; (M - I) transposed, fp32.
 //   yproj: per (64 tokens, 512-column D part): partial y of the part on the
-//          matrix cores, reduced over the four waves in LDS, then the partial
+//          matrix cores, reduced over the eight waves in LDS, then the partial
 //          z = (M - I) y_part (z is linear in y) -> Zpart[part][t][i].
 //   lift : per (64 tokens, D part): z = sum of the parts in a fixed order
 //          (deterministic), its bf16 split in LDS, then out = x + Q z. The
@@ -30,26 +30,8 @@
 namespace rw4 {
 namespace {
 
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-
 constexpr int TB = 16;          // tokens per workgroup (MFMA rows)
 constexpr int NW = 4;           // waves per workgroup
-
-__device__ __forceinline__ v8bf ld8(const uint16_t* p) { return *reinterpret_cast<const v8bf*>(p); }
-__device__ __forceinline__ v8bf as8(uint4 u) { return __builtin_bit_cast(v8bf, u); }
-
-__device__ __forceinline__ v4f mfma(v8bf a, v8bf b, v4f c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// Let the last matrix-core results land before anything else reads them: no
-// instruction may be scheduled across, and the wave sleeps ~64 cycles (longer
-// than the instruction's pipeline) in between.
-__device__ __forceinline__ void mfma_drain() {
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_sleep(1);
-  __builtin_amdgcn_sched_barrier(0);
-}
 
 // One workgroup per 64 (d) x 32 (j) tile of Q: coalesced fp32 reads, the
 // bf16 split, [D][RK] rows written directly and [RP][D] rows through an LDS
@@ -109,27 +91,29 @@ basis_prep_kernel(const float* __restrict__ Q, const float* __restrict__ M, int 
   }
 }
 
-// A D part of 512 columns is 8 double steps of 64 columns; each of the 4
-// waves takes 2. Inside a double step lane group g (lane / 16) owns the 16
+// A D part of 512 columns is 8 double steps of 64 columns; each of the 8
+// waves takes 1. Inside a double step lane group g (lane / 16) owns the 16
 // contiguous columns [16g, 16g + 16): its first 8 feed one MFMA, the next 8 a
 // second one. The k order of a dot product is free, so both operands use this
 // same order, and every lane reads 32 contiguous bytes per row.
 // A workgroup aligns TBW blocks of 16 tokens: every Q fragment it loads is
 // used by TBW MFMA blocks, which keeps the L2 traffic for Q at 1/TBW of the
 // token count.
-constexpr int DPW = 2;                    // double steps per wave
-constexpr int kPart = NW * DPW * 64;
+constexpr int YNW = 8;                    // projection waves per workgroup
+constexpr int DPW = 1;                    // double steps per wave
+constexpr int kPart = YNW * DPW * 64;
 constexpr int TBW = 4;                    // 16-token blocks per workgroup
 constexpr int TPW = TBW * TB;             // tokens per workgroup
 
 template <int RP>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(YNW * 64)
 yproj_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int r,
              const uint16_t* __restrict__ QtH, const uint16_t* __restrict__ QtL,
              const float* __restrict__ MmT, float* __restrict__ Zpart) {
   constexpr int RK = (RP + 31) / 32 * 32;
   constexpr bool MLDS = RK <= 64;                      // (M - I)^T staged in LDS when small
-  __shared__ float red[NW][TPW][RP + 1];
+  constexpr int NT = YNW * 64;
+  __shared__ float red[4][TPW][RP + 1];
   __shared__ float mt[MLDS ? RK * RK : 1];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -198,17 +182,32 @@ yproj_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int r,
   }
   mfma_drain();
   // C layout: lane holds rows 4g + v (tokens of block b), column tl (basis index)
+  // waves 4..7 park their sums in red[wave - 4]; waves 0..3 add theirs
+  if (wave >= 4) {
 #pragma unroll
-  for (int b = 0; b < TBW; ++b)
+    for (int b = 0; b < TBW; ++b)
 #pragma unroll
-    for (int nb = 0; nb < RP / 16; ++nb)
+      for (int nb = 0; nb < RP / 16; ++nb)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) red[wave][16 * b + 4 * g + v][16 * nb + tl] = acc[b][nb][v];
+        for (int v = 0; v < 4; ++v) red[wave - 4][16 * b + 4 * g + v][16 * nb + tl] = acc[b][nb][v];
+  }
   if constexpr (MLDS)
-    for (int o = tid; o < r * r; o += 256) mt[o] = MmT[o];
+    for (int o = tid; o < r * r; o += NT) mt[o] = MmT[o];
+  __syncthreads();
+  if (wave < 4) {
+#pragma unroll
+    for (int b = 0; b < TBW; ++b)
+#pragma unroll
+      for (int nb = 0; nb < RP / 16; ++nb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float& slot = red[wave][16 * b + 4 * g + v][16 * nb + tl];
+          slot = acc[b][nb][v] + slot;
+        }
+  }
   __syncthreads();
   // partial y of this D part for the workgroup's tokens, into red[0]
-  for (int o = tid; o < TPW * RP; o += 256) {
+  for (int o = tid; o < TPW * RP; o += NT) {
     const int t = o / RP;
     const int j = o % RP;
     red[0][t][j] = (red[0][t][j] + red[1][t][j]) + (red[2][t][j] + red[3][t][j]);
@@ -216,7 +215,7 @@ yproj_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int r,
   __syncthreads();
   // partial z = (M - I) (partial y): z is linear in y, so the lift only sums
   // the parts. (M - I) is stored transposed: consecutive i read consecutive words.
-  for (int o = tid; o < TPW * RK; o += 256) {
+  for (int o = tid; o < TPW * RK; o += NT) {
     const int t = o / RK;
     const int i = o % RK;
     float z = 0.0f;
@@ -385,7 +384,7 @@ inline size_t a256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 template <int RP>
 hipError_t run_yproj(const uint16_t* x, int64_t T, int D, int P, int S, int r, const uint16_t* QtH,
                      const uint16_t* QtL, const float* MmT, float* Zpart, hipStream_t s) {
-  hipLaunchKernelGGL(yproj_kernel<RP>, dim3(static_cast<unsigned>((T + TPW - 1) / TPW), S), dim3(256),
+  hipLaunchKernelGGL(yproj_kernel<RP>, dim3(static_cast<unsigned>((T + TPW - 1) / TPW), S), dim3(YNW * 64),
                      0, s, x, T, D, P, r, QtH, QtL, MmT, Zpart);
   return hipGetLastError();
 }
@@ -417,38 +416,55 @@ size_t align_mfma_workspace(int64_t T, int64_t D, int64_t r) {
          a256(static_cast<size_t>(r) * r * 4) + a256(static_cast<size_t>(S) * T * RK * 4);
 }
 
-hipError_t launch_align_mfma(const uint16_t* x, void* out, int out_f32, const float* Q,
-                             const float* M, const void* addend, int64_t T, int64_t D, int64_t r,
-                             void* ws, hipStream_t s) {
-  if (T == 0) return hipSuccess;
+AlignParts align_parts(void* ws, int64_t T, int64_t D, int64_t r) {
   const int RP = rp_of(r), RK = rk_of(r);
-  const int P = kPart;
-  const int S = static_cast<int>((D + P - 1) / P);
+  AlignParts a;
+  a.RP = RP;
+  a.RK = RK;
+  a.S = static_cast<int>((D + kPart - 1) / kPart);
   uint8_t* p = static_cast<uint8_t*>(ws);
-  uint16_t* QtH = reinterpret_cast<uint16_t*>(p); p += a256(static_cast<size_t>(RP) * D * 2);
-  uint16_t* QtL = reinterpret_cast<uint16_t*>(p); p += a256(static_cast<size_t>(RP) * D * 2);
-  uint16_t* QH = reinterpret_cast<uint16_t*>(p);  p += a256(static_cast<size_t>(D) * RK * 2);
-  uint16_t* QL = reinterpret_cast<uint16_t*>(p);  p += a256(static_cast<size_t>(D) * RK * 2);
-  float* Mm = reinterpret_cast<float*>(p);        p += a256(static_cast<size_t>(r) * r * 4);
-  float* Zpart = reinterpret_cast<float*>(p);
+  a.QtH = reinterpret_cast<uint16_t*>(p); p += a256(static_cast<size_t>(RP) * D * 2);
+  a.QtL = reinterpret_cast<uint16_t*>(p); p += a256(static_cast<size_t>(RP) * D * 2);
+  a.QH = reinterpret_cast<uint16_t*>(p);  p += a256(static_cast<size_t>(D) * RK * 2);
+  a.QL = reinterpret_cast<uint16_t*>(p);  p += a256(static_cast<size_t>(D) * RK * 2);
+  a.Mm = reinterpret_cast<float*>(p);     p += a256(static_cast<size_t>(r) * r * 4);
+  a.Zpart = reinterpret_cast<float*>(p);
+  (void)T;
+  return a;
+}
 
-  const dim3 pgrid(static_cast<unsigned>((D + 63) / 64), static_cast<unsigned>(RK / 32));
+hipError_t launch_align_prep_proj(const uint16_t* x, const float* Q, const float* M, int64_t T,
+                                  int64_t D, int64_t r, void* ws, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const AlignParts a = align_parts(ws, T, D, r);
+  const dim3 pgrid(static_cast<unsigned>((D + 63) / 64), static_cast<unsigned>(a.RK / 32));
   hipLaunchKernelGGL(basis_prep_kernel, pgrid, dim3(256), 0, s, Q, M, static_cast<int>(D),
-                     static_cast<int>(r), RP, RK, QtH, QtL, QH, QL, Mm);
+                     static_cast<int>(r), a.RP, a.RK, a.QtH, a.QtL, a.QH, a.QL, a.Mm);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int Di = static_cast<int>(D);
   const int ri = static_cast<int>(r);
-  switch (RP) {
-#define RW4_Y(V) case V: e = run_yproj<V>(x, T, Di, P, S, ri, QtH, QtL, Mm, Zpart, s); break;
+  switch (a.RP) {
+#define RW4_Y(V) case V: return run_yproj<V>(x, T, Di, kPart, a.S, ri, a.QtH, a.QtL, a.Mm, a.Zpart, s);
     RW4_Y(16) RW4_Y(32) RW4_Y(48) RW4_Y(64) RW4_Y(80) RW4_Y(96) RW4_Y(112) RW4_Y(128)
 #undef RW4_Y
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_align_mfma(const uint16_t* x, void* out, int out_f32, const float* Q,
+                             const float* M, const void* addend, int64_t T, int64_t D, int64_t r,
+                             void* ws, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  hipError_t e = launch_align_prep_proj(x, Q, M, T, D, r, ws, s);
   if (e != hipSuccess) return e;
+  const AlignParts a = align_parts(ws, T, D, r);
+  const int Di = static_cast<int>(D);
+  const int ri = static_cast<int>(r);
   const bool of32 = out_f32 != 0;
-  switch (RP) {
-#define RW4_L(V, K) case V: return run_lift<V, K>(x, T, Di, P, S, ri, Zpart, QH, QL, addend, out, of32, s);
+  switch (a.RP) {
+#define RW4_L(V, K) \
+  case V: return run_lift<V, K>(x, T, Di, kPart, a.S, ri, a.Zpart, a.QH, a.QL, addend, out, of32, s);
     RW4_L(16, 32) RW4_L(32, 32) RW4_L(48, 64) RW4_L(64, 64) RW4_L(80, 96) RW4_L(96, 96)
     RW4_L(112, 128) RW4_L(128, 128)
 #undef RW4_L

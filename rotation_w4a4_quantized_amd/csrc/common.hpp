@@ -9,6 +9,26 @@ namespace rw4 {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ v8bf ld8(const uint16_t* p) { return *reinterpret_cast<const v8bf*>(p); }
+__device__ __forceinline__ v8bf as8(uint4 u) { return __builtin_bit_cast(v8bf, u); }
+
+// D (16 x 16, fp32) += A (16 x 32, bf16) B (32 x 16, bf16). Lane l holds
+// A[l % 16][8 (l / 16) + 0..7], B[8 (l / 16) + 0..7][l % 16] and
+// D[4 (l / 16) + 0..3][l % 16].
+__device__ __forceinline__ v4f mfma(v8bf a, v8bf b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Let the last matrix-core results land before anything else reads them: no
+// instruction may be scheduled across, and the wave sleeps ~64 cycles (longer
+// than the instruction's pipeline) in between.
+__device__ __forceinline__ void mfma_drain() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_sleep(1);
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 // bf16 bits -> fp32 (exact)
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
@@ -67,29 +87,23 @@ __device__ __forceinline__ uint32_t nib(int q) { return static_cast<uint32_t>(q)
 constexpr int kTileBytes = 1536;
 constexpr int kPlane1 = 1024;
 
-// E2M3 encoding of an integer in [-7, 7]
-__device__ __forceinline__ uint32_t e2m3(int q) {
-  constexpr uint64_t kMag = (8ull << 6) | (16ull << 12) | (20ull << 18) | (24ull << 24) |
-                            (26ull << 30) | (28ull << 36) | (30ull << 42);
-  const uint32_t a = static_cast<uint32_t>(q < 0 ? -q : q);
-  return static_cast<uint32_t>((kMag >> (6 * a)) & 63u) | (q < 0 ? 32u : 0u);
-}
-
 // 16 six-bit fields packed into three words, field e at bit 6e
 struct Field12 { uint32_t w0, w1, w2; };
-__device__ __forceinline__ Field12 pack_fields16(const uint32_t (&f)[16]) {
-  uint64_t a = 0, b = 0;
-#pragma unroll
-  for (int e = 0; e < 10; ++e) a |= static_cast<uint64_t>(f[e]) << (6 * e);
-#pragma unroll
-  for (int e = 10; e < 16; ++e) b |= static_cast<uint64_t>(f[e]) << (6 * (e - 10));
-  return Field12{static_cast<uint32_t>(a), static_cast<uint32_t>(a >> 32) | static_cast<uint32_t>(b << 28),
-                 static_cast<uint32_t>(b >> 4)};
-}
 
 // store the 16 fields of codes [k0, k0 + 16) of row t (k0 % 16 == 0) into a
 // tiled matrix with K columns: they are words 0..2 (k0 % 32 == 0) or words
 // 3..5 of the owning lane
+// store the 32 fields of codes [k0, k0 + 32) of row t (k0 % 32 == 0): the six
+// words of the owning lane, as one 16-byte and one 8-byte store
+__device__ __forceinline__ void store_fields32(uint8_t* tiles, int64_t t, int64_t k0, int64_t K,
+                                               Field12 a, Field12 b) {
+  const int64_t tile = (t >> 5) * (K >> 6) + (k0 >> 6);
+  const int lane = static_cast<int>(((k0 >> 5) & 1) * 32 + (t & 31));
+  uint8_t* base = tiles + tile * kTileBytes;
+  *reinterpret_cast<uint4*>(base + lane * 16) = make_uint4(a.w0, a.w1, a.w2, b.w0);
+  *reinterpret_cast<uint2*>(base + kPlane1 + lane * 8) = make_uint2(b.w1, b.w2);
+}
+
 __device__ __forceinline__ void store_fields16(uint8_t* tiles, int64_t t, int64_t k0, int64_t K,
                                                Field12 v) {
   const int64_t tile = (t >> 5) * (K >> 6) + (k0 >> 6);
@@ -102,6 +116,57 @@ __device__ __forceinline__ void store_fields16(uint8_t* tiles, int64_t t, int64_
     p0[3] = v.w0;
     *reinterpret_cast<uint2*>(base + kPlane1 + lane * 8) = make_uint2(v.w1, v.w2);
   }
+}
+
+// Per-row quantizer with the step's reciprocal. For a row with step s
+// (s = fl32(absmax / 7), normal) and y = fl32(1 / s) (correctly rounded),
+// t = fl32(v * y) differs from v / s by at most 2^-23 |v / s| <= 8.4e-7 and
+// fl32(v / s) from v / s by at most 4.2e-7. So when t is at least 2^-18 away
+// from every half-integer, fl32(v / s) lies strictly between the same two
+// half-integers as t and rint(fl32(v / s)) == rint(t); otherwise the exact
+// quotient decides. Codes equal quant4(v, s) for every v.
+struct RowQuant {
+  float s, y;
+  bool fast;  // s normal: y finite and the bound above holds
+  __device__ __forceinline__ explicit RowQuant(float step)
+      : s(step), y(step > 0.0f ? 1.0f / step : 0.0f), fast(step >= 1.17549435e-38f) {}
+  // integer-valued code in [-8, 7]; zero is +0 (never -0)
+  __device__ __forceinline__ float code(float v) const {
+    if (!(s > 0.0f)) return 0.0f;
+    if (fast) {
+      const float t = v * y;               // |t| <= 7.0000009, so |rint(t)| <= 7
+      const float q = rintf(t);
+      if (0.5f - fabsf(t - q) >= 3.814697265625e-06f)  // 2^-18
+        return q + 0.0f;
+    }
+    return static_cast<float>(quant4(v, s));
+  }
+};
+
+// Packed E2M3 fields from integer-valued floats in [-7, 7] (no -0) with the
+// gfx950 conversion instruction: with scale 1.0 it converts exactly, and it
+// places element i of its first source in field 2i and element i of its
+// second source in field 2i + 1 of a 192-bit result (field e at bit 6e).
+typedef float v16f_t __attribute__((ext_vector_type(16)));
+typedef uint32_t v6u_t __attribute__((ext_vector_type(6)));
+
+// fields 0..31 = q[0..31]: the six words of one lane
+__device__ __forceinline__ v6u_t pack_fp6_32(const float (&q)[32]) {
+  v16f_t a, b;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) { a[i] = q[2 * i]; b[i] = q[2 * i + 1]; }
+  return __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(a, b, 1.0f);
+}
+
+// fields 0..15 = q[0..15]: three words
+__device__ __forceinline__ Field12 pack_fp6_16(const float (&q)[16]) {
+  v16f_t a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { a[i] = q[2 * i]; b[i] = q[2 * i + 1]; }
+#pragma unroll
+  for (int i = 8; i < 16; ++i) { a[i] = 0.0f; b[i] = 0.0f; }
+  const v6u_t w = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(a, b, 1.0f);
+  return Field12{w[0], w[1], w[2]};
 }
 
 }  // namespace rw4

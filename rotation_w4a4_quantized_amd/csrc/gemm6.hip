@@ -188,7 +188,7 @@ tile_kernel(const uint8_t* __restrict__ codes, int64_t R, int64_t Rp, int64_t K,
   // unconditional load (row clamped), masked afterwards
   const bool live = row < R;
   const uint2 p = *reinterpret_cast<const uint2*>(codes + (live ? row : R - 1) * (K / 2) + k0 / 2);
-  uint32_t f[16];
+  float f[16];
   bool neg8 = false;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
@@ -196,9 +196,9 @@ tile_kernel(const uint8_t* __restrict__ codes, int64_t R, int64_t Rp, int64_t K,
     int q = static_cast<int>((w >> (4 * (e & 7))) & 15u);
     q = live ? (q >= 8 ? q - 16 : q) : 0;
     neg8 |= q == -8;
-    f[e] = q == -8 ? 0u : e2m3(q);
+    f[e] = q == -8 ? 0.0f : static_cast<float>(q);
   }
-  store_fields16(tiles, row, k0, K, pack_fields16(f));
+  store_fields16(tiles, row, k0, K, pack_fp6_16(f));
   if (neg8 && bad) atomicOr(bad, 1);
 }
 

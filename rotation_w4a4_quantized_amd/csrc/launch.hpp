@@ -32,6 +32,25 @@ hipError_t launch_align_mfma(const uint16_t* x, void* out, int out_f32, const fl
                              const float* M, const void* addend, int64_t T, int64_t D, int64_t r,
                              void* ws, hipStream_t s);
 
+// Pieces of the matrix-core alignment workspace: the prepared basis (bf16
+// hi/lo Q in both orientations, (M - I) transposed) and the per-part z sums.
+struct AlignParts {
+  uint16_t* QtH; uint16_t* QtL; uint16_t* QH; uint16_t* QL;
+  float* Mm; float* Zpart;
+  int RP, RK, S;   // r padded to 16 and to 32; number of D parts of Zpart
+};
+AlignParts align_parts(void* ws, int64_t T, int64_t D, int64_t r);
+// basis preparation and the projection z = sum over parts of (M - I) Q_part^T x_part
+hipError_t launch_align_prep_proj(const uint16_t* x, const float* Q, const float* M, int64_t T,
+                                  int64_t D, int64_t r, void* ws, hipStream_t s);
+
+// Fused lift + [Walsh-Hadamard] + INT4 quantization into FP6 tiles, after
+// launch_align_prep_proj: per token, v = x + Q z, [v = H v], codes of v.
+bool lfq_supported(int64_t D, int64_t r);
+hipError_t launch_lift_fwht_quant(const uint16_t* x, int64_t T, int64_t D, int64_t r, void* ws,
+                                  bool do_fwht, uint8_t* tiles, float* s_a, float* dbg,
+                                  hipStream_t s);
+
 // W4A4 GEMM, bf16 (dequantized) or raw int32 output.
 hipError_t launch_gemm(const uint8_t* a, const float* s_a, const uint8_t* w, const float* s_w,
                        void* y, bool i32_out, int64_t T, int64_t K, int64_t N, hipStream_t s);

@@ -188,9 +188,10 @@ __device__ __forceinline__ void store_codes(uint8_t* p, const float (&v)[EPT], f
   uint32_t wds[(EPT + 7) / 8];
 #pragma unroll
   for (int i = 0; i < (EPT + 7) / 8; ++i) wds[i] = 0;
+  const RowQuant rq(s);
 #pragma unroll
   for (int i = 0; i < EPT; ++i) {
-    const int q = s > 0.0f ? quant4(v[i], s) : 0;
+    const int q = static_cast<int>(rq.code(v[i]));
     wds[i / 8] |= nib(q) << (4 * (i % 8));
   }
   if constexpr (EPT == 32) {
@@ -214,12 +215,13 @@ template <int EPT>
 __device__ __forceinline__ void store_tiled(uint8_t* tiles, int64_t row, int64_t k0, int64_t K,
                                             const float (&v)[EPT], float s) {
   static_assert(EPT % 16 == 0, "tiled output needs 16-value groups");
+  const RowQuant rq(s);
 #pragma unroll
   for (int h = 0; h < EPT / 16; ++h) {
-    uint32_t f[16];
+    float q[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) f[e] = e2m3(s > 0.0f ? quant4(v[16 * h + e], s) : 0);
-    store_fields16(tiles, row, k0 + 16 * h, K, pack_fields16(f));
+    for (int e = 0; e < 16; ++e) q[e] = rq.code(v[16 * h + e]);
+    store_fields16(tiles, row, k0 + 16 * h, K, pack_fp6_16(q));
   }
 }
 

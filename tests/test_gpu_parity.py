@@ -61,6 +61,39 @@ def test_quant_act_int4(rw, T, D, dt):
     np.testing.assert_array_equal(host(codes), O.pack_int4(q))
 
 
+def test_quant_near_half_integers(rw):
+    """Values whose quotient by the step sits within a few ulps of k + 1/2, the
+    case where the fp32 quotient's rounding decides the code (R6)."""
+    rng = np.random.default_rng(11)
+    T, D = 48, 4096
+    x = np.zeros((T, D), np.float32)
+    for t in range(T):
+        m = np.float32(rng.uniform(0.1, 100.0))
+        s = np.float32(m / np.float32(7))
+        k = rng.integers(-7, 7, D).astype(np.float32) + np.float32(0.5)
+        base = (k.astype(np.float64) * np.float64(s)).astype(np.float32)
+        steps = rng.integers(-3, 4, D).astype(np.int32)
+        v = base.view(np.int32) + steps                    # a few ulps either way
+        x[t] = v.view(np.float32)
+        x[t] = np.clip(x[t], -m, m)
+        x[t, 0] = m                                        # absmax: step is fl(m / 7)
+    codes, scales = rw.quant_act_int4(dev(x))
+    q, s = O.quant_int4(x)
+    np.testing.assert_array_equal(host(scales), s)
+    np.testing.assert_array_equal(host(codes), O.pack_int4(q))
+    # the tiled writer of the unit takes the same decisions
+    Wq = np.random.default_rng(12).integers(-7, 8, (64, D))
+    wt = rw.w4a4_tile_codes(dev(O.pack_int4(Wq)))
+    dbg = torch().empty((T, D), dtype=torch().float32, device="cuda")
+    y, ws = rw.rotated_linear(dev(W.f32_to_bf16_bits(x)), wt, dev(np.ones(64, np.float32)), 0,
+                              dbg_prequant=dbg)
+    pre = host(dbg)
+    tiles_g, sa_g = (host(v) for v in rw.workspace_views(ws, T, D))
+    q2, s2 = O.quant_int4(pre)
+    np.testing.assert_array_equal(sa_g, s2)
+    np.testing.assert_array_equal(F.untile(tiles_g, T, D), q2)
+
+
 # ---------------------------------------------------------------- Hadamard
 def test_fwht_worked_example(rw):
     x = dev(np.array([[20, 0, 0, 0], [10, 10, 10, 10]], np.float32))
