@@ -96,14 +96,17 @@ basis_prep_kernel(const float* __restrict__ Q, const float* __restrict__ M, int 
 // contiguous columns [16g, 16g + 16): its first 8 feed one MFMA, the next 8 a
 // second one. The k order of a dot product is free, so both operands use this
 // same order, and every lane reads 32 contiguous bytes per row.
-// A workgroup aligns TBW blocks of 16 tokens: every Q fragment it loads is
-// used by TBW MFMA blocks, which keeps the L2 traffic for Q at 1/TBW of the
-// token count.
+// A lift workgroup aligns TBW blocks of 16 tokens: every Q fragment it loads
+// is used by TBW MFMA blocks, which keeps the L2 traffic for Q at 1/TBW of
+// the token count; the projection uses the same 64-token blocks (16-token
+// blocks measured slower: four times the Q traffic outweighs the overlap).
 constexpr int YNW = 8;                    // projection waves per workgroup
 constexpr int DPW = 1;                    // double steps per wave
 constexpr int kPart = YNW * DPW * 64;
-constexpr int TBW = 4;                    // 16-token blocks per workgroup
-constexpr int TPW = TBW * TB;             // tokens per workgroup
+constexpr int TBW = 4;                    // 16-token blocks per lift workgroup
+constexpr int TPW = TBW * TB;             // tokens per lift workgroup
+constexpr int YTBW = 4;                   // 16-token blocks per projection workgroup
+constexpr int YTPW = YTBW * TB;
 
 template <int RP>
 __global__ void __launch_bounds__(YNW * 64)
@@ -113,12 +116,12 @@ yproj_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int r,
   constexpr int RK = (RP + 31) / 32 * 32;
   constexpr bool MLDS = RK <= 64;                      // (M - I)^T staged in LDS when small
   constexpr int NT = YNW * 64;
-  __shared__ float red[4][TPW][RP + 1];
+  __shared__ float red[4][YTPW][RP + 1];
   __shared__ float mt[MLDS ? RK * RK : 1];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TPW;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * YTPW;
   const int part = blockIdx.y;
   const int dbeg = part * P;
   const int dend = min(D, dbeg + P);
@@ -129,9 +132,9 @@ yproj_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int r,
 
   // loads are unconditional: double steps past the part's end re-read its last
   // one and their x is zeroed; tokens past T re-read the last token
-  v8bf xa[TBW][DPW][2];
+  v8bf xa[YTBW][DPW][2];
 #pragma unroll
-  for (int b = 0; b < TBW; ++b) {
+  for (int b = 0; b < YTBW; ++b) {
     const int64_t trow = min(t0 + 16 * b + tl, T - 1);
     const uint16_t* xrow = x + trow * D + 16 * g;
 #pragma unroll
@@ -147,9 +150,9 @@ yproj_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int r,
       xa[b][u][1] = as8(a1);
     }
   }
-  v4f acc[TBW][RP / 16];
+  v4f acc[YTBW][RP / 16];
 #pragma unroll
-  for (int b = 0; b < TBW; ++b)
+  for (int b = 0; b < YTBW; ++b)
 #pragma unroll
     for (int nb = 0; nb < RP / 16; ++nb) acc[b][nb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -175,7 +178,7 @@ yproj_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int r,
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int b = 0; b < TBW; ++b) {
+          for (int b = 0; b < YTBW; ++b) {
             acc[b][nb0 + c] = mfma(xa[b][u][h], bh[u][c][h], acc[b][nb0 + c]);
             acc[b][nb0 + c] = mfma(xa[b][u][h], bl[u][c][h], acc[b][nb0 + c]);
           }
@@ -185,7 +188,7 @@ yproj_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int r,
   // waves 4..7 park their sums in red[wave - 4]; waves 0..3 add theirs
   if (wave >= 4) {
 #pragma unroll
-    for (int b = 0; b < TBW; ++b)
+    for (int b = 0; b < YTBW; ++b)
 #pragma unroll
       for (int nb = 0; nb < RP / 16; ++nb)
 #pragma unroll
@@ -196,7 +199,7 @@ yproj_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int r,
   __syncthreads();
   if (wave < 4) {
 #pragma unroll
-    for (int b = 0; b < TBW; ++b)
+    for (int b = 0; b < YTBW; ++b)
 #pragma unroll
       for (int nb = 0; nb < RP / 16; ++nb)
 #pragma unroll
@@ -207,7 +210,7 @@ yproj_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int r,
   }
   __syncthreads();
   // partial y of this D part for the workgroup's tokens, into red[0]
-  for (int o = tid; o < TPW * RP; o += NT) {
+  for (int o = tid; o < YTPW * RP; o += NT) {
     const int t = o / RP;
     const int j = o % RP;
     red[0][t][j] = (red[0][t][j] + red[1][t][j]) + (red[2][t][j] + red[3][t][j]);
@@ -215,7 +218,7 @@ yproj_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int r,
   __syncthreads();
   // partial z = (M - I) (partial y): z is linear in y, so the lift only sums
   // the parts. (M - I) is stored transposed: consecutive i read consecutive words.
-  for (int o = tid; o < TPW * RK; o += NT) {
+  for (int o = tid; o < YTPW * RK; o += NT) {
     const int t = o / RK;
     const int i = o % RK;
     float z = 0.0f;
@@ -384,7 +387,7 @@ inline size_t a256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 template <int RP>
 hipError_t run_yproj(const uint16_t* x, int64_t T, int D, int P, int S, int r, const uint16_t* QtH,
                      const uint16_t* QtL, const float* MmT, float* Zpart, hipStream_t s) {
-  hipLaunchKernelGGL(yproj_kernel<RP>, dim3(static_cast<unsigned>((T + TPW - 1) / TPW), S), dim3(YNW * 64),
+  hipLaunchKernelGGL(yproj_kernel<RP>, dim3(static_cast<unsigned>((T + YTPW - 1) / YTPW), S), dim3(YNW * 64),
                      0, s, x, T, D, P, r, QtH, QtL, MmT, Zpart);
   return hipGetLastError();
 }
