@@ -217,7 +217,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "D": D, "T": T, "r": r, "K": D, "N": N,
                    "flags": "align|fwht", "operand_sets_rotated": nb},
-        "roofline": {"bound": "mfma", "kernel": "w4a4_gemm_tiles (gemm6_kernel, FP6 E2M3 operands)",
+        "roofline": {"bound": "mfma", "kernel": "w4a4_gemm_tiles (gemm6_lds_kernel, FP6 E2M3 operands)",
                      "achieved": achieved, "peak": PEAK_FP6_TFLOPS, "unit": "TFLOP/s",
                      "unit_note": "2 ops per int4 multiply-add; codes run as exact FP6 E2M3 "
                                   "numbers, so the peak is the FP6 one",

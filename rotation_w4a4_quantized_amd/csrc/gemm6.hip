@@ -12,12 +12,23 @@
 // and equals the INT32 accumulator. No VALU widening of nibbles is needed, and
 // the FP6 rate is twice the int8 rate on this chip.
 //
-// Each workgroup is one wave computing BW x BT blocks of 32 x 32 outputs (BW
-// along the weight rows, BT along the tokens). A fragment (32 rows x 64 codes)
-// is one 1536-byte tile, read straight from global memory into registers with
-// a 16-byte and an 8-byte load per lane (no LDS in the k-loop); PD tiles per operand are
-// in flight. Workgroups are renumbered so that each XCD works on a contiguous
-// band of weight tiles. The bf16 epilogue is staged in LDS for 16-byte stores.
+// Two kernels:
+//
+// * gemm6_lds_kernel (K % 128 == 0, T >= 128): a workgroup of WW x WT waves
+//   computes a (WW FW 32) x (WT FT 32) output block; each wave owns FW x FT
+//   32 x 32 fragments. Operand tiles for two k-tiles (128 k) at a time are
+//   copied straight from global memory into LDS with the gfx950 global->LDS
+//   loads (no VGPR staging), into a ring of S stage buffers, and every wave
+//   reads its fragments from LDS. Sharing the block's tiles among its waves
+//   cuts the L2 traffic per MFMA by the wave-grid factor, which is what bounds
+//   a one-wave-per-tile kernel on this chip.
+// * gemm6_kernel (any K % 64 == 0, and small T): one wave per workgroup,
+//   BW x BT fragments, tiles read straight into registers, PD k-tiles in
+//   flight.
+//
+// In both, workgroups are renumbered so that each XCD works on a contiguous
+// band of weight tiles, and the bf16 epilogue is staged in LDS so that rows
+// are written with 16-byte stores.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -174,6 +185,242 @@ gemm6_kernel(const uint8_t* __restrict__ at, const float* __restrict__ s_a,
   }
 }
 
+// ---------------------------------------------------------------- LDS-staged kernel
+//
+// The copies are written as inline assembly on purpose. The compiler's own
+// global->LDS builtin makes its wait-count pass drain every copy in flight
+// before each LDS read that it cannot prove disjoint from them, which turns
+// the S-stage ring into a fully serialized one. Here the compiler does not see
+// the LDS writes, and the kernel orders them itself:
+//   * a copy into stage buffer b is issued only after a workgroup barrier that
+//     every wave reaches after its LDS reads of b completed (lgkmcnt(0));
+//   * a wave reads stage i only after waiting until at most (S-2) stages of
+//     its own copies are in flight (vmcnt, in issue order) and a barrier, so
+//     every wave's copies of stage i have landed.
+// The copy instruction takes its LDS base from m0, which it sets itself; no
+// other code in these kernels uses m0.
+typedef const __attribute__((address_space(3))) uint8_t* lds_cptr;
+// wave-uniform LDS byte address of a pointer into a __shared__ object
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_cptr)p)));
+}
+// 16 bytes per lane: lds + 16 lane <- g (per-lane address)
+__device__ __forceinline__ void lds_copy16(const void* g, const void* lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr(lds))
+               : "memory");
+}
+// 4 bytes per lane: lds + 4 lane <- g (per-lane address)
+__device__ __forceinline__ void lds_copy4(const void* g, const void* lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_addr(lds))
+               : "memory");
+}
+// workgroup barrier that the compiler may not move memory accesses across
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+// wait until this wave's LDS reads are done and at most N of its vector
+// memory loads (here: copies) are in flight
+template <int N>
+__device__ __forceinline__ void wait_copies() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+}
+
+template <int FW, int FT, int WW, int WT, int S, bool I32OUT>
+__global__ void __launch_bounds__(64 * WW * WT)
+gemm6_lds_kernel(const uint8_t* __restrict__ at, const float* __restrict__ s_a,
+                 const uint8_t* __restrict__ wt, const float* __restrict__ s_w,
+                 void* __restrict__ y, int T, int K, int N) {
+  constexpr int NW = WW * WT;
+  constexpr int TW = WW * FW * 32, TT = WT * FT * 32;
+  constexpr int NRB = WW * FW + WT * FT;      // 32-row blocks of the workgroup (W, then A)
+  constexpr int STAGE = NRB * 2 * kTileBytes;  // two k-tiles of each row block
+  constexpr int NI = STAGE / 1024;             // 1 KiB copies per stage
+  constexpr int LPW = (NI + NW - 1) / NW;      // copies per wave; the last round may repeat one
+  constexpr int SPW = FW * 32 + 8;             // bf16 pitch of a wave's staged rows
+  static_assert(S == 3 || S == 4, "stages");
+  static_assert(TW <= 256 && TT <= 256, "blocks stay inside the 256-row padding");
+  static_assert(NW * 32 * SPW * 2 <= STAGE, "epilogue staging fits one stage buffer");
+  static_assert((S - 2) * LPW < 64, "vmcnt range");
+  // one LDS object per stage, so that each is addressed with constants
+  __shared__ __attribute__((aligned(16))) uint8_t L0[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t L1[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t L2[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t L3[S > 3 ? STAGE : 16];
+  __shared__ __attribute__((aligned(16))) float sc[I32OUT ? 4 : TW + TT];  // s_w block | s_a block
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ww = wave % WW, wq = wave / WW;
+  const int nwt = (N + TW - 1) / TW, ntt = (T + TT - 1) / TT, nb = nwt * ntt;
+  int b = blockIdx.x;
+  if ((nb & 7) == 0) b = (b & 7) * (nb >> 3) + (b >> 3);
+  const int n0 = (b / ntt) * TW, t0 = (b % ntt) * TT;
+  const int KT = K >> 6, KS = KT >> 1;  // k-tiles, stages
+
+  // Copy i of a stage moves bytes [1024 i, 1024 i + 1024) of the stage: row
+  // block i / 3, third i % 3 of its two consecutive k-tiles (3072 contiguous
+  // bytes in the tile layout). The stage buffer keeps that order.
+  const uint8_t* src[LPW];
+  int dst[LPW];
+#pragma unroll
+  for (int m = 0; m < LPW; ++m) {
+    int i = wave + NW * m;
+    if (i >= NI) i -= NW;
+    const int rb = i / 3;
+    const uint8_t* row = rb < WW * FW
+        ? wt + static_cast<int64_t>((n0 >> 5) + rb) * KT * kTileBytes
+        : at + static_cast<int64_t>((t0 >> 5) + rb - WW * FW) * KT * kTileBytes;
+    src[m] = row + (i % 3) * 1024 + lane * 16;
+    dst[m] = i * 1024;
+  }
+  auto fetch = [&](uint8_t* L, int st) {
+#pragma unroll
+    for (int m = 0; m < LPW; ++m)
+      lds_copy16(src[m] + static_cast<int64_t>(st) * (2 * kTileBytes), L + dst[m]);
+  };
+  // the block's scales go first, so the first stage wait covers them
+  if constexpr (!I32OUT) {
+    static_assert((TW + TT) % 64 == 0, "scale copies");
+    for (int m = wave; m < (TW + TT) / 64; m += NW) {
+      const int e = m * 64 + lane;
+      const float* p = e < TW ? s_w + min(n0 + e, N - 1) : s_a + min(t0 + e - TW, T - 1);
+      lds_copy4(p, sc + m * 64);
+    }
+  }
+
+  v16f acc[FW][FT];
+#pragma unroll
+  for (int i = 0; i < FW; ++i)
+#pragma unroll
+    for (int j = 0; j < FT; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  auto compute = [&](const uint8_t* L) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      v8i ow[FW], oa[FT];
+#pragma unroll
+      for (int i = 0; i < FW; ++i) {
+        const uint8_t* q = L + (ww * FW + i) * (2 * kTileBytes) + h * kTileBytes;
+        ow[i] = opnd(*reinterpret_cast<const uint4*>(q + lane * 16),
+                     *reinterpret_cast<const uint2*>(q + kPlane1 + lane * 8));
+      }
+#pragma unroll
+      for (int j = 0; j < FT; ++j) {
+        const uint8_t* q = L + (WW * FW + wq * FT + j) * (2 * kTileBytes) + h * kTileBytes;
+        oa[j] = opnd(*reinterpret_cast<const uint4*>(q + lane * 16),
+                     *reinterpret_cast<const uint2*>(q + kPlane1 + lane * 8));
+      }
+#pragma unroll
+      for (int i = 0; i < FW; ++i)
+#pragma unroll
+        for (int j = 0; j < FT; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ow[i], oa[j], acc[i][j], 2,
+                                                                      2, 0, 127, 0, 127);
+    }
+  };
+  // stage i lives in buffer i % S; step i refills the buffer read in step i - 1
+  auto step = [&](int i, const uint8_t* cur, uint8_t* nxt) {
+    wait_copies<(S - 2) * LPW>();
+    block_barrier();
+    fetch(nxt, i + S - 1 < KS ? i + S - 1 : KS - 1);  // clamped copies are harmless repeats
+    compute(cur);
+  };
+  fetch(L0, 0);
+  fetch(L1, 1 < KS ? 1 : KS - 1);
+  if constexpr (S > 3) fetch(L2, 2 < KS ? 2 : KS - 1);
+  int i = 0;
+  for (; i + S <= KS; i += S) {
+    if constexpr (S == 3) {
+      step(i, L0, L2);
+      step(i + 1, L1, L0);
+      step(i + 2, L2, L1);
+    } else {
+      step(i, L0, L3);
+      step(i + 1, L1, L0);
+      step(i + 2, L2, L1);
+      step(i + 3, L3, L2);
+    }
+  }
+  const int rem = KS - i;  // uniform
+  if (rem > 0) step(i, L0, S == 3 ? L2 : L3);
+  if (rem > 1) step(i + 1, L1, L0);
+  if constexpr (S > 3)
+    if (rem > 2) step(i + 2, L2, L1);
+  // all copies (the repeats included) have landed and every wave is done with
+  // the stage buffers before L0 is reused for the epilogue
+  __builtin_amdgcn_s_waitcnt(0);
+  block_barrier();
+  // results of the last MFMAs are read by plain VALU code below
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_sleep(1);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // accumulator element (i, j, v): weight row wn0 + 32 i + 8 (v / 4) + 4 (lane / 32) + v % 4,
+  // token wt0 + 32 j + lane % 32
+  const int wn0 = n0 + ww * FW * 32, wt0 = t0 + wq * FT * 32;
+  if constexpr (I32OUT) {
+    int32_t* yo = static_cast<int32_t*>(y);
+#pragma unroll
+    for (int j = 0; j < FT; ++j) {
+      const int t = wt0 + 32 * j + (lane & 31);
+      if (t >= T) continue;
+#pragma unroll
+      for (int ii = 0; ii < FW; ++ii)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = wn0 + 32 * ii + 8 * q + 4 * (lane >> 5);
+          int32_t* o = yo + static_cast<int64_t>(t) * N + n;
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            if (n + c < N) o[c] = static_cast<int32_t>(acc[ii][j][4 * q + c]);
+        }
+    }
+  } else {
+    // each wave stages 32 tokens x FW * 32 columns at a time in its own part of L0
+    uint16_t* st = reinterpret_cast<uint16_t*>(L0) + wave * 32 * SPW;
+    uint16_t* yo = static_cast<uint16_t*>(y);
+    const int tl = lane & 31;
+#pragma unroll
+    for (int j = 0; j < FT; ++j) {
+      const float sa = sc[TW + wq * FT * 32 + 32 * j + tl];
+#pragma unroll
+      for (int ii = 0; ii < FW; ++ii)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int nl = 32 * ii + 8 * q + 4 * (lane >> 5);
+          const float4 sw = *reinterpret_cast<const float4*>(&sc[ww * FW * 32 + nl]);
+          const float v0 = (acc[ii][j][4 * q + 0] * sa) * sw.x;
+          const float v1 = (acc[ii][j][4 * q + 1] * sa) * sw.y;
+          const float v2 = (acc[ii][j][4 * q + 2] * sa) * sw.z;
+          const float v3 = (acc[ii][j][4 * q + 3] * sa) * sw.w;
+          *reinterpret_cast<uint2*>(&st[tl * SPW + nl]) =
+              make_uint2(f32_to_bf16(v0) | (static_cast<uint32_t>(f32_to_bf16(v1)) << 16),
+                         f32_to_bf16(v2) | (static_cast<uint32_t>(f32_to_bf16(v3)) << 16));
+        }
+      // the wave reads back only what it wrote (LDS accesses of a wave are in order)
+      constexpr int CPR = FW * 4;  // 16-byte chunks per staged row
+#pragma unroll
+      for (int c = lane; c < 32 * CPR; c += 64) {
+        const int row = c / CPR, col = (c % CPR) * 8;
+        const int t = wt0 + 32 * j + row, n = wn0 + col;
+        if (t < T && n < N) {
+          uint16_t* o = yo + static_cast<int64_t>(t) * N + n;
+          if (n + 8 <= N && (N & 7) == 0) {
+            *reinterpret_cast<uint4*>(o) = *reinterpret_cast<const uint4*>(&st[row * SPW + col]);
+          } else {
+            const uint16_t* e = &st[row * SPW + col];
+            for (int k = 0; k < 8 && n + k < N; ++k) o[k] = e[k];
+          }
+        }
+      }
+    }
+  }
+}
+
 // INT4 rows [R][K/2] -> FP6 tiles of Rp rows (rows >= R get code 0); one
 // thread per 12-byte field group. A code of -8 (not representable) is stored
 // as 0 and raises *bad.
@@ -213,6 +460,18 @@ hipError_t launch_cfg(const uint8_t* a, const float* s_a, const uint8_t* w, cons
   return hipGetLastError();
 }
 
+template <int FW, int FT, int WW, int WT, int S, bool I32>
+hipError_t launch_lds(const uint8_t* a, const float* s_a, const uint8_t* w, const float* s_w,
+                      void* y, int64_t T, int64_t K, int64_t N, hipStream_t s) {
+  constexpr int64_t TW = WW * FW * 32, TT = WT * FT * 32;
+  const int64_t nb = ((N + TW - 1) / TW) * ((T + TT - 1) / TT);
+  if (nb > 0x7FFFFFFF || K < 128 || K % 128) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((gemm6_lds_kernel<FW, FT, WW, WT, S, I32>), dim3(static_cast<unsigned>(nb)),
+                     dim3(64 * WW * WT), 0, s, a, s_a, w, s_w, y, static_cast<int>(T),
+                     static_cast<int>(K), static_cast<int>(N));
+  return hipGetLastError();
+}
+
 }  // namespace g6
 
 int64_t tiles_rows(int64_t R) { return (R + 255) / 256 * 256; }
@@ -235,12 +494,18 @@ hipError_t launch_gemm_tiles(const uint8_t* a, const float* s_a, const uint8_t* 
                              const float* s_w, void* y, bool i32_out, int64_t T, int64_t K,
                              int64_t N, hipStream_t s) {
   if (T == 0 || N == 0) return hipSuccess;
-  const bool big = T >= 4096 && N >= 4096;
-  if (i32_out)
-    return big ? g6::launch_cfg<4, 4, 2, true>(a, s_a, w, s_w, y, T, K, N, s)
-               : g6::launch_cfg<4, 2, 4, true>(a, s_a, w, s_w, y, T, K, N, s);
-  return big ? g6::launch_cfg<4, 4, 2, false>(a, s_a, w, s_w, y, T, K, N, s)
-             : g6::launch_cfg<4, 2, 4, false>(a, s_a, w, s_w, y, T, K, N, s);
+  if (K % 128 == 0 && T >= 128) {
+    // 256 x 128 blocks of eight waves for large products, 128 x 128 blocks of
+    // four waves (two workgroups per CU) otherwise
+    const bool big = T >= 4096 && N >= 4096;
+    if (i32_out)
+      return big ? g6::launch_lds<2, 2, 4, 2, 3, true>(a, s_a, w, s_w, y, T, K, N, s)
+                 : g6::launch_lds<2, 2, 2, 2, 3, true>(a, s_a, w, s_w, y, T, K, N, s);
+    return big ? g6::launch_lds<2, 2, 4, 2, 3, false>(a, s_a, w, s_w, y, T, K, N, s)
+               : g6::launch_lds<2, 2, 2, 2, 3, false>(a, s_a, w, s_w, y, T, K, N, s);
+  }
+  if (i32_out) return g6::launch_cfg<4, 2, 4, true>(a, s_a, w, s_w, y, T, K, N, s);
+  return g6::launch_cfg<4, 2, 4, false>(a, s_a, w, s_w, y, T, K, N, s);
 }
 
 }  // namespace rw4

@@ -248,8 +248,11 @@ def test_tile_codes_rejects_minus8(rw):
         rw.w4a4_tile_codes(dev(packed))
 
 
+# T >= 128 with K % 128 == 0 takes the LDS-staged kernel (one stage of 128 k:
+# K = 128; stage-ring tails: K / 128 = 4, 5, 32), the rest the direct kernel
 @pytest.mark.parametrize("T,K,N", [(1, 64, 1), (64, 256, 256), (300, 512, 384), (129, 4096, 130),
                                    (17, 16384, 64), (8, 4096, 12288), (257, 192, 1000),
+                                   (256, 128, 256), (200, 640, 520),
                                    (4096, 4096, 4096), (4100, 1024, 4104)])
 def test_w4a4_gemm_tiles(rw, T, K, N):
     say(f"w4a4_gemm_tiles T={T} K={K} N={N}")
