@@ -218,6 +218,42 @@ rw4_status rotated_linear(const void* x, int64_t ldx, int64_t T, int64_t D,
 /* bytes of workspace rotated_linear needs for (T, D, r, flags); 0 on bad input */
 size_t rotated_linear_workspace_size(int64_t T, int64_t D, int64_t r, unsigned flags);
 
+/*
+ * respin_prepare_basis -- the part of the alignment that depends only on the
+ * layer's (Q, M) ["ReSpinQuant" paper notes, key design 3: x + Q (M - I) Q^T x],
+ * computed once and kept with the layer's weights, like the weight tiles:
+ *   bf16 hi/lo splits of Q in both orientations, (M - I) transposed (fp32),
+ *   and, when D is a power of two in [256, 4096] and r <= 64, the Hadamard
+ *   image H_D Q / sqrt(D) split the same way ["QuaRot 与 SpinQuant" §2.2: H
+ *   is orthogonal and symmetric, so H (x + Q z) = H x + (H Q) z].
+ *   Q, M, D, r  as respin_align (1 <= r <= min(D, 128), r % 4 == 0, D % 64 == 0)
+ *   basis       device memory of respin_basis_size(D, r) bytes, 256-byte
+ *               aligned, owned by the caller; its layout is internal.
+ * Asynchronous on `stream`; argument errors are reported before any launch.
+ */
+rw4_status respin_prepare_basis(const float* Q, const float* M, int64_t D, int64_t r,
+                                void* basis, size_t basis_bytes, void* stream);
+
+/* bytes of a prepared basis for (D, r); 0 when (D, r) is unsupported */
+size_t respin_basis_size(int64_t D, int64_t r);
+
+/*
+ * rotated_linear_prepared -- rotated_linear with the alignment's basis
+ * prepared by respin_prepare_basis(Q, M, D, r) instead of (Q, M): same
+ * arguments, same results bit for bit, same workspace contents after the
+ * call (tiles at 0, scales at rw4_align256(w4a4_tiles_size(T, D))), but no
+ * per-call basis preparation. basis may be NULL without RW4_ALIGN or r = 0.
+ * Workspace: rotated_linear_prepared_workspace_size(T, D, r, flags) bytes.
+ */
+rw4_status rotated_linear_prepared(const void* x, int64_t ldx, int64_t T, int64_t D,
+                                   const void* basis, int64_t r, unsigned flags,
+                                   const uint8_t* w, const float* s_w, int64_t N, void* y,
+                                   void* workspace, size_t ws_bytes, float* dbg_prequant,
+                                   void* stream);
+
+/* bytes of workspace rotated_linear_prepared needs; 0 on bad input */
+size_t rotated_linear_prepared_workspace_size(int64_t T, int64_t D, int64_t r, unsigned flags);
+
 /* n rounded up to a multiple of 256 (workspace offsets) */
 size_t rw4_align256(size_t n);
 
@@ -227,7 +263,7 @@ const char* rw4_status_string(rw4_status s);
 /* ABI version of this header (bumped on any signature change) */
 int rw4_abi_version(void);
 
-#define RW4_ABI_VERSION 3
+#define RW4_ABI_VERSION 4
 
 #ifdef __cplusplus
 }

@@ -16,6 +16,8 @@ __all__ = [
     "RW4_ALIGN", "RW4_FWHT", "RW4_SWIGLU", "Rw4Error", "lib", "library_path",
     "respin_align", "fwht", "quant_act_int4", "w4a4_gemm", "rotated_linear",
     "rotated_linear_workspace_size", "respin_align_workspace_size", "workspace_views",
+    "respin_basis_size", "respin_prepare_basis", "rotated_linear_prepared",
+    "rotated_linear_prepared_workspace_size",
     "w4a4_tiles_size", "w4a4_tile_codes", "w4a4_gemm_tiles", "prep_weight", "layer",
 ]
 
@@ -28,7 +30,9 @@ _lib = None
 
 EXPORTS = ("respin_align", "respin_align_workspace_size", "fwht", "quant_act_int4", "w4a4_gemm",
            "w4a4_tiles_size", "w4a4_tile_codes", "w4a4_gemm_tiles", "rotated_linear",
-           "rotated_linear_workspace_size", "rw4_align256", "rw4_status_string", "rw4_abi_version")
+           "rotated_linear_workspace_size", "respin_basis_size", "respin_prepare_basis",
+           "rotated_linear_prepared", "rotated_linear_prepared_workspace_size", "rw4_align256",
+           "rw4_status_string", "rw4_abi_version")
 
 
 class Rw4Error(RuntimeError):
@@ -63,13 +67,21 @@ def lib() -> ctypes.CDLL:
                                  vp, vp]
     L.rotated_linear_workspace_size.argtypes = [i64, i64, i64, u32]
     L.rotated_linear_workspace_size.restype = sz
+    L.respin_basis_size.argtypes = [i64, i64]
+    L.respin_basis_size.restype = sz
+    L.respin_prepare_basis.argtypes = [vp, vp, i64, i64, vp, sz, vp]
+    L.rotated_linear_prepared.argtypes = [vp, i64, i64, i64, vp, i64, u32, vp, vp, i64, vp, vp,
+                                          sz, vp, vp]
+    L.rotated_linear_prepared_workspace_size.argtypes = [i64, i64, i64, u32]
+    L.rotated_linear_prepared_workspace_size.restype = sz
     L.rw4_align256.argtypes = [sz]
     L.rw4_align256.restype = sz
     L.rw4_status_string.argtypes = [i32]
     L.rw4_status_string.restype = ctypes.c_char_p
     L.rw4_abi_version.restype = i32
     for f in ("respin_align", "fwht", "quant_act_int4", "w4a4_gemm", "w4a4_tile_codes",
-              "w4a4_gemm_tiles", "rotated_linear"):
+              "w4a4_gemm_tiles", "rotated_linear", "respin_prepare_basis",
+              "rotated_linear_prepared"):
         getattr(L, f).restype = i32
     _lib = L
     return L
@@ -271,6 +283,61 @@ def rotated_linear(x, w, s_w, flags: int, Q=None, M=None, out=None, workspace=No
                               _p(workspace), workspace.numel() * workspace.element_size(),
                               _p(dbg_prequant), _stream())
     _check("rotated_linear", st)
+    return out, workspace
+
+
+def respin_basis_size(D: int, r: int) -> int:
+    return int(lib().respin_basis_size(D, r))
+
+
+def respin_prepare_basis(Q, M, basis=None):
+    """The alignment's per-layer basis from Q fp32 [D][r] and M fp32 [r][r]
+    (flat uint8 device buffer, layout internal to the library)."""
+    torch = _torch()
+    _contig(Q)
+    _contig(M)
+    D, r = Q.shape
+    n = respin_basis_size(D, r)
+    if n == 0:
+        raise Rw4Error("respin_prepare_basis", -2, lib().rw4_status_string(-2).decode())
+    if basis is None:
+        basis = torch.empty((n,), dtype=torch.uint8, device=Q.device)
+    st = lib().respin_prepare_basis(_p(Q), _p(M), D, r, _p(basis),
+                                    basis.numel() * basis.element_size(), _stream())
+    _check("respin_prepare_basis", st)
+    return basis
+
+
+def rotated_linear_prepared_workspace_size(T: int, D: int, r: int, flags: int) -> int:
+    return int(lib().rotated_linear_prepared_workspace_size(T, D, r, flags))
+
+
+def rotated_linear_prepared(x, w, s_w, flags: int, basis=None, r: int = 0, out=None,
+                            workspace=None, dbg_prequant=None):
+    """``rotated_linear`` with a basis from ``respin_prepare_basis`` (r = its
+    rank) in place of (Q, M). Returns (y, workspace)."""
+    torch = _torch()
+    _rows(x)
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bf16")
+    T = x.shape[0]
+    D = x.shape[1] // 2 if flags & RW4_SWIGLU else x.shape[1]
+    N = s_w.shape[0]
+    if w.numel() * w.element_size() < w4a4_tiles_size(N, D):
+        raise ValueError("w: weight tile buffer too small for [N][D]")
+    r = r if flags & RW4_ALIGN else 0
+    if r and basis.numel() * basis.element_size() < respin_basis_size(D, r):
+        raise ValueError("basis: buffer too small for (D, r)")
+    need = rotated_linear_prepared_workspace_size(T, D, r, flags)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    st = lib().rotated_linear_prepared(_p(x), x.stride(0), T, D, _p(basis) if r else None, r,
+                                       flags, _p(w), _p(s_w), N, _p(out), _p(workspace),
+                                       workspace.numel() * workspace.element_size(),
+                                       _p(dbg_prequant), _stream())
+    _check("rotated_linear_prepared", st)
     return out, workspace
 
 

@@ -27,6 +27,85 @@ rw4_status check_align_args(const void* x, rw4_dtype x_dt, const void* out, rw4_
   return RW4_OK;
 }
 
+// P (the Hadamard image of the basis) is prepared when the fused prologue can run
+inline bool with_p(int64_t D, int64_t r) { return rw4::lfq_supported(D, r); }
+
+// per-call part of the rotated_linear workspace: activation tiles, scales,
+// and with alignment the projection's parts (plus fp32 aligned rows when the
+// prologue is not fused)
+size_t call_ws_bytes(int64_t T, int64_t D, int64_t r) {
+  size_t n = rw4_align256(rw4::tiles_bytes(T, D)) + rw4_align256(4u * static_cast<size_t>(T));
+  if (r > 0) {
+    n += rw4::align_zpart_bytes(T, D, r);
+    if (!rw4::lfq_supported(D, r))
+      n += rw4_align256(4u * static_cast<size_t>(T) * static_cast<size_t>(D));
+  }
+  return n;
+}
+
+// checks shared by rotated_linear and rotated_linear_prepared (Q, M and the
+// basis are checked by the callers)
+rw4_status check_linear(const void* x, int64_t ldx, int64_t T, int64_t D, int64_t r,
+                        unsigned flags, const uint8_t* w, const float* s_w, int64_t N, void* y,
+                        const float* dbg) {
+  if (T < 0 || N < 1) return RW4_ERR_INVALID_ARG;
+  if (flags & ~static_cast<unsigned>(RW4_ALIGN | RW4_FWHT | RW4_SWIGLU)) return RW4_ERR_INVALID_ARG;
+  if ((flags & RW4_ALIGN) && (flags & RW4_SWIGLU)) return RW4_ERR_INVALID_ARG;
+  if (!pow2(D) || D < 64 || D > 32768) return RW4_ERR_UNSUPPORTED;
+  if (T == 0) return RW4_OK;
+  if (!x || !w || !s_w || !y) return RW4_ERR_INVALID_ARG;
+  const int64_t width = (flags & RW4_SWIGLU) ? 2 * D : D;
+  if (ldx < width || (ldx % 8) != 0) return RW4_ERR_INVALID_ARG;
+  if (flags & RW4_ALIGN) {
+    if (r < 0) return RW4_ERR_INVALID_ARG;
+    if (r > D || r > 128 || (r % 4) != 0) return RW4_ERR_UNSUPPORTED;
+    if (ldx != D) return RW4_ERR_UNSUPPORTED;
+    if (r > 0 && !rw4::align_mfma_supported(D, r)) return RW4_ERR_UNSUPPORTED;
+  }
+  if (T > (int64_t(1) << 31) - 256 || N > (int64_t(1) << 31) - 256) return RW4_ERR_UNSUPPORTED;
+  if (!al16(x) || !al16(w) || !al16(s_w) || !al16(y)) return RW4_ERR_MISALIGNED;
+  if (dbg && !al16(dbg)) return RW4_ERR_MISALIGNED;
+  return RW4_OK;
+}
+
+// the unit after validation; basis prepared for (D, r) when r > 0
+rw4_status run_linear(const void* x, int64_t ldx, int64_t T, int64_t D, const void* basis,
+                      int64_t r, unsigned flags, const uint8_t* w, const float* s_w, int64_t N,
+                      void* y, void* workspace, float* dbg, hipStream_t s) {
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint8_t* codes = ws;
+  float* s_a = reinterpret_cast<float*>(ws + rw4_align256(rw4::tiles_bytes(T, D)));
+  const void* src = x;
+  int in = (flags & RW4_SWIGLU) ? rw4::IN_SWIGLU : rw4::IN_BF16;
+  int64_t ld = ldx;
+  if (r > 0) {
+    float* Zpart = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(s_a) +
+                                            rw4_align256(4u * static_cast<size_t>(T)));
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    const bool fused = rw4::lfq_supported(D, r);
+    if (rw4::launch_yproj(xb, T, D, r, basis, with_p(D, r), Zpart, s) != hipSuccess)
+      return RW4_ERR_HIP;
+    if (fused) {
+      // lift + transform + quantization on chip
+      if (rw4::launch_lift_fwht_quant(xb, T, D, r, basis, Zpart, (flags & RW4_FWHT) != 0, codes,
+                                      s_a, dbg, s) != hipSuccess)
+        return RW4_ERR_HIP;
+      return hip_status(rw4::launch_gemm_tiles(codes, s_a, w, s_w, y, false, T, D, N, s));
+    }
+    float* tmp = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(Zpart) +
+                                          rw4::align_zpart_bytes(T, D, r));
+    if (rw4::launch_lift(xb, tmp, 1, nullptr, T, D, r, basis, with_p(D, r), Zpart, s) != hipSuccess)
+      return RW4_ERR_HIP;
+    src = tmp;
+    in = rw4::IN_F32;
+    ld = D;
+  }
+  hipError_t e = rw4::launch_row(src, in, ld, T, D, (flags & RW4_FWHT) != 0, nullptr, codes, true,
+                                 s_a, dbg, s);
+  if (e != hipSuccess) return RW4_ERR_HIP;
+  return hip_status(rw4::launch_gemm_tiles(codes, s_a, w, s_w, y, false, T, D, N, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -148,72 +227,71 @@ rw4_status w4a4_gemm_tiles(const uint8_t* a, const float* s_a, const uint8_t* w,
       rw4::launch_gemm_tiles(a, s_a, w, s_w, y, y_dt == RW4_I32, T, K, N, strm(stream)));
 }
 
-size_t rotated_linear_workspace_size(int64_t T, int64_t D, int64_t r, unsigned flags) {
+size_t respin_basis_size(int64_t D, int64_t r) {
+  if (D < 1 || r < 1 || r > 128 || (r % 4) != 0 || r > D) return 0;
+  if (!rw4::align_mfma_supported(D, r)) return 0;
+  return rw4::align_basis_bytes(D, r, with_p(D, r));
+}
+
+rw4_status respin_prepare_basis(const float* Q, const float* M, int64_t D, int64_t r, void* basis,
+                                size_t basis_bytes, void* stream) {
+  if (!Q || !M || D < 1 || r < 1) return RW4_ERR_INVALID_ARG;
+  const size_t need = respin_basis_size(D, r);
+  if (need == 0) return RW4_ERR_UNSUPPORTED;
+  if (!al16(Q) || (reinterpret_cast<uintptr_t>(M) & 3u)) return RW4_ERR_MISALIGNED;
+  if (!basis || (reinterpret_cast<uintptr_t>(basis) & 255u) || basis_bytes < need)
+    return RW4_ERR_WORKSPACE;
+  return hip_status(rw4::launch_basis_prep(Q, M, D, r, with_p(D, r), basis, strm(stream)));
+}
+
+size_t rotated_linear_prepared_workspace_size(int64_t T, int64_t D, int64_t r, unsigned flags) {
   if (T < 0 || !pow2(D) || D < 64 || D > 32768 || r < 0) return 0;
-  size_t n = rw4_align256(rw4::tiles_bytes(T, D)) + rw4_align256(4u * static_cast<size_t>(T));
-  if ((flags & RW4_ALIGN) && r > 0) {
-    if (!rw4::align_mfma_supported(D, r)) return 0;
-    n += rw4_align256(4u * static_cast<size_t>(T) * static_cast<size_t>(D));
-    n += rw4::align_mfma_workspace(T, D, r);
-  }
-  return n;
+  if ((flags & RW4_ALIGN) && r > 0 && respin_basis_size(D, r) == 0) return 0;
+  return call_ws_bytes(T, D, (flags & RW4_ALIGN) ? r : 0);
+}
+
+rw4_status rotated_linear_prepared(const void* x, int64_t ldx, int64_t T, int64_t D,
+                                   const void* basis, int64_t r, unsigned flags, const uint8_t* w,
+                                   const float* s_w, int64_t N, void* y, void* workspace,
+                                   size_t ws_bytes, float* dbg_prequant, void* stream) {
+  rw4_status st = check_linear(x, ldx, T, D, r, flags, w, s_w, N, y, dbg_prequant);
+  if (st != RW4_OK || T == 0) return st;
+  const int64_t re = (flags & RW4_ALIGN) ? r : 0;
+  if (re > 0 && (!basis || (reinterpret_cast<uintptr_t>(basis) & 255u))) return RW4_ERR_INVALID_ARG;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return RW4_ERR_WORKSPACE;
+  if (ws_bytes < call_ws_bytes(T, D, re)) return RW4_ERR_WORKSPACE;
+  return run_linear(x, ldx, T, D, basis, re, flags, w, s_w, N, y, workspace, dbg_prequant,
+                    strm(stream));
+}
+
+size_t rotated_linear_workspace_size(int64_t T, int64_t D, int64_t r, unsigned flags) {
+  const size_t n = rotated_linear_prepared_workspace_size(T, D, r, flags);
+  if (n == 0 || !(flags & RW4_ALIGN) || r == 0) return n;
+  return n + rw4_align256(respin_basis_size(D, r));
 }
 
 rw4_status rotated_linear(const void* x, int64_t ldx, int64_t T, int64_t D, const float* Q,
                           const float* M, int64_t r, unsigned flags, const uint8_t* w,
                           const float* s_w, int64_t N, void* y, void* workspace, size_t ws_bytes,
                           float* dbg_prequant, void* stream) {
-  if (T < 0 || N < 1) return RW4_ERR_INVALID_ARG;
-  if (flags & ~static_cast<unsigned>(RW4_ALIGN | RW4_FWHT | RW4_SWIGLU)) return RW4_ERR_INVALID_ARG;
-  if ((flags & RW4_ALIGN) && (flags & RW4_SWIGLU)) return RW4_ERR_INVALID_ARG;
-  if (!pow2(D) || D < 64 || D > 32768) return RW4_ERR_UNSUPPORTED;
-  if (T == 0) return RW4_OK;
-  if (!x || !w || !s_w || !y) return RW4_ERR_INVALID_ARG;
-  const int64_t width = (flags & RW4_SWIGLU) ? 2 * D : D;
-  if (ldx < width || (ldx % 8) != 0) return RW4_ERR_INVALID_ARG;
+  rw4_status st = check_linear(x, ldx, T, D, r, flags, w, s_w, N, y, dbg_prequant);
+  if (st != RW4_OK || T == 0) return st;
+  const int64_t re = (flags & RW4_ALIGN) ? r : 0;
   if (flags & RW4_ALIGN) {
-    rw4_status st = check_align_args(x, RW4_BF16, x, RW4_F32, Q, M, T, D, r);
+    st = check_align_args(x, RW4_BF16, x, RW4_F32, Q, M, T, D, r);
     if (st != RW4_OK) return st;
-    if (ldx != D) return RW4_ERR_UNSUPPORTED;
-    if (r > 0 && !rw4::align_mfma_supported(D, r)) return RW4_ERR_UNSUPPORTED;
   }
-  if (T > (int64_t(1) << 31) - 256 || N > (int64_t(1) << 31) - 256) return RW4_ERR_UNSUPPORTED;
-  if (!al16(x) || !al16(w) || !al16(s_w) || !al16(y)) return RW4_ERR_MISALIGNED;
-  if (dbg_prequant && !al16(dbg_prequant)) return RW4_ERR_MISALIGNED;
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return RW4_ERR_WORKSPACE;
-  if (ws_bytes < rotated_linear_workspace_size(T, D, (flags & RW4_ALIGN) ? r : 0, flags))
-    return RW4_ERR_WORKSPACE;
-
+  if (ws_bytes < rotated_linear_workspace_size(T, D, re, flags)) return RW4_ERR_WORKSPACE;
   hipStream_t s = strm(stream);
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  uint8_t* codes = ws;
-  float* s_a = reinterpret_cast<float*>(ws + rw4_align256(rw4::tiles_bytes(T, D)));
-  const void* src = x;
-  int in = (flags & RW4_SWIGLU) ? rw4::IN_SWIGLU : rw4::IN_BF16;
-  int64_t ld = ldx;
-  if ((flags & RW4_ALIGN) && r > 0) {
-    uint8_t* tmpb = reinterpret_cast<uint8_t*>(s_a) + rw4_align256(4u * static_cast<size_t>(T));
-    float* tmp = reinterpret_cast<float*>(tmpb);
-    void* aws = tmpb + rw4_align256(4u * static_cast<size_t>(T) * static_cast<size_t>(D));
-    const uint16_t* xb = static_cast<const uint16_t*>(x);
-    if (rw4::lfq_supported(D, r)) {
-      // projection, then lift + transform + quantization on chip
-      if (rw4::launch_align_prep_proj(xb, Q, M, T, D, r, aws, s) != hipSuccess) return RW4_ERR_HIP;
-      if (rw4::launch_lift_fwht_quant(xb, T, D, r, aws, (flags & RW4_FWHT) != 0, codes, s_a,
-                                      dbg_prequant, s) != hipSuccess)
-        return RW4_ERR_HIP;
-      return hip_status(rw4::launch_gemm_tiles(codes, s_a, w, s_w, y, false, T, D, N, s));
-    }
-    hipError_t e = rw4::launch_align_mfma(xb, tmp, 1, Q, M, nullptr, T, D, r, aws, s);
-    if (e != hipSuccess) return RW4_ERR_HIP;
-    src = tmp;
-    in = rw4::IN_F32;
-    ld = D;
+  void* basis = nullptr;
+  if (re > 0) {
+    // the basis goes after the per-call part of the workspace
+    basis = static_cast<uint8_t*>(workspace) + call_ws_bytes(T, D, re);
+    if (rw4::launch_basis_prep(Q, M, D, re, with_p(D, re), basis, s) != hipSuccess)
+      return RW4_ERR_HIP;
   }
-  hipError_t e = rw4::launch_row(src, in, ld, T, D, (flags & RW4_FWHT) != 0, nullptr, codes, true,
-                                 s_a, dbg_prequant, s);
-  if (e != hipSuccess) return RW4_ERR_HIP;
-  return hip_status(rw4::launch_gemm_tiles(codes, s_a, w, s_w, y, false, T, D, N, s));
+  return run_linear(x, ldx, T, D, basis, re, flags, w, s_w, N, y, workspace, dbg_prequant, s);
 }
 
 }  // extern "C"

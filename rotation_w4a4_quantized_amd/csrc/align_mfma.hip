@@ -1,20 +1,23 @@
 // Low-rank residual alignment on bf16 matrix cores ("ReSpinQuant" paper notes,
 // key design 3: y = Q^T x, z = (M - I) y, out = x + Q z).
 //
-// The activations are bf16, so x is exact as an MFMA operand. Q is split once
-// per call into two bf16 terms, Q = Qh + Ql + O(2^-17 |Q|), and z likewise:
-//   y   = x.Qh + x.Ql                      (two bf16 products, fp32 accumulate)
+// The activations are bf16, so x is exact as an MFMA operand. The basis is
+// split into two bf16 terms, A = Ah + Al + O(2^-17 |A|), and z likewise:
+//   z   = x.Q'h + x.Q'l                    (Q' = Q (M - I)^T; two bf16 products,
+//                                           fp32 accumulate: z = (M - I) Q^T x)
 //   out = x + Qh.zh + Ql.zh + Qh.zl        (the dropped Ql.zl is ~2^-17 relative)
 // which keeps the fp32 alignment well inside a 1e-5 normwise error while
-// running on v_mfma_f32_16x16x32_bf16 instead of fp32 FMAs. With M = I, z is
-// exactly zero and the output equals the input.
+// running on v_mfma_f32_16x16x32_bf16 instead of fp32 FMAs. With M = I, Q' and
+// z are exactly zero and the output equals the input.
 //
-// Three launches:
-//   prep : Qh/Ql in both orientations ([r][D] for the projection, [D][r] for
-//          the lift), zero-padded in r; (M - I) transposed, fp32.
-//   yproj: per (64 tokens, 512-column D part): partial y of the part on the
-//          matrix cores, reduced over the eight waves in LDS, then the partial
-//          z = (M - I) y_part (z is linear in y) -> Zpart[part][t][i].
+// The basis (everything that depends on Q and M only) is prepared once and
+// can be kept with the layer's weights; then two launches per call:
+//   prep : Q'h/Q'l as [r][D] rows for the projection, Qh/Ql as [D][r] rows for
+//          the lift, zero-padded in r; and, for the fused prologue, the
+//          Hadamard image P = H Q / sqrt(D) split the same way.
+//   yproj: per (64 tokens, 512-column D part): the part's share of z on the
+//          matrix cores, reduced over the eight waves in LDS ->
+//          Zpart[part][t][i] (z is the sum of the parts).
 //   lift : per (64 tokens, D part): z = sum of the parts in a fixed order
 //          (deterministic), its bf16 split in LDS, then out = x + Q z. The
 //          MFMA's row order is permuted so a lane's accumulator covers the same
@@ -33,19 +36,37 @@ namespace {
 constexpr int TB = 16;          // tokens per workgroup (MFMA rows)
 constexpr int NW = 4;           // waves per workgroup
 
-// One workgroup per 64 (d) x 32 (j) tile of Q: coalesced fp32 reads, the
-// bf16 split, [D][RK] rows written directly and [RP][D] rows through an LDS
-// transpose. Columns j >= r are zero padding.
+// One workgroup per 64 (d) x 32 (j) tile: the lift operand Q (bf16 hi/lo,
+// [D][RK] rows written directly) and the projection operand Q' = Q (M - I)^T
+// ([RP][D] rows of the same split, through an LDS transpose). With Q' the
+// projection yields z = (M - I) Q^T x directly: Q'^T x = (M - I) Q^T x. The
+// entries of M - I are exact in fp32 (M's diagonal lies well inside [0.5, 2]
+// for the sub-rotations of the pages, so M_ii - 1 is exact by Sterbenz), and
+// Q' is summed in fp32. Columns j >= r are zero padding.
+constexpr int kPrepRmax = 128;
+
 __global__ void __launch_bounds__(256)
 basis_prep_kernel(const float* __restrict__ Q, const float* __restrict__ M, int D, int r, int RP,
                   int RK, uint16_t* __restrict__ QtH, uint16_t* __restrict__ QtL,
-                  uint16_t* __restrict__ QH, uint16_t* __restrict__ QL, float* __restrict__ Mm) {
+                  uint16_t* __restrict__ QH, uint16_t* __restrict__ QL) {
   __shared__ uint16_t th[32][64 + 2];
   __shared__ uint16_t tlo[32][64 + 2];
+  __shared__ float qrow[64][kPrepRmax + 1];     // Q rows d0 .. d0 + 63
+  __shared__ float mi[32][kPrepRmax + 1];       // (M - I) rows j0 .. j0 + 31
   const int tid = threadIdx.x;
   const int d0 = blockIdx.x * 64;
   const int j0 = blockIdx.y * 32;
-  // 64 x 32 tile: thread -> (row dd = tid / 4, 8 columns jj = 8 * (tid % 4) + 0..7)
+  for (int c = tid; c < 64 * r; c += 256) {
+    const int dd = c / r, k = c % r;
+    qrow[dd][k] = d0 + dd < D ? Q[static_cast<int64_t>(d0 + dd) * r + k] : 0.0f;
+  }
+  for (int c = tid; c < 32 * r; c += 256) {
+    const int i = c / r, k = c % r;
+    const int row = j0 + i;
+    mi[i][k] = row < r ? (row == k ? M[row * r + k] - 1.0f : M[row * r + k]) : 0.0f;
+  }
+  __syncthreads();
+  // 64 x 32 tile: thread -> (row dd = tid / 4, 8 columns jb + 0..7)
   const int dd = tid >> 2;
   const int jb = (tid & 3) * 8;
   const int d = d0 + dd;
@@ -53,11 +74,9 @@ basis_prep_kernel(const float* __restrict__ Q, const float* __restrict__ M, int 
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const int j = j0 + jb + e;
-    const float q = (d < D && j < r) ? Q[static_cast<int64_t>(d) * r + j] : 0.0f;
+    const float q = j < r ? qrow[dd][j] : 0.0f;
     h[e] = f32_to_bf16(q);
     l[e] = f32_to_bf16(q - bf16_to_f32(h[e]));
-    th[jb + e][dd] = h[e];
-    tlo[jb + e][dd] = l[e];
   }
   if (d < D && j0 + jb < RK) {
     uint4 vh, vl;
@@ -67,6 +86,15 @@ basis_prep_kernel(const float* __restrict__ Q, const float* __restrict__ M, int 
     vl.z = l[4] | (uint32_t(l[5]) << 16); vl.w = l[6] | (uint32_t(l[7]) << 16);
     *reinterpret_cast<uint4*>(QH + static_cast<int64_t>(d) * RK + j0 + jb) = vh;
     *reinterpret_cast<uint4*>(QL + static_cast<int64_t>(d) * RK + j0 + jb) = vl;
+  }
+  // Q'[d][j] = sum_k Q[d][k] (M - I)[j][k] (zero for j >= r), split the same way
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float acc = 0.0f;
+    for (int k = 0; k < r; ++k) acc = fmaf(qrow[dd][k], mi[jb + e][k], acc);
+    const uint16_t hh = f32_to_bf16(acc);
+    th[jb + e][dd] = hh;
+    tlo[jb + e][dd] = f32_to_bf16(acc - bf16_to_f32(hh));
   }
   __syncthreads();
   // transposed rows: thread -> (row j = tid / 8, 8 consecutive d)
@@ -82,12 +110,38 @@ basis_prep_kernel(const float* __restrict__ Q, const float* __restrict__ M, int 
     *reinterpret_cast<uint4*>(QtH + static_cast<int64_t>(j) * D + d0 + db) = vh;
     *reinterpret_cast<uint4*>(QtL + static_cast<int64_t>(j) * D + d0 + db) = vl;
   }
-  // (M - I) stored transposed: Mm[j * r + i] = M[i][j] - [i == j]
-  if (blockIdx.x == 0 && blockIdx.y == 0) {
-    for (int i = tid; i < r * r; i += 256) {
-      const int a = i / r, b = i % r;
-      Mm[b * r + a] = a == b ? M[i] - 1.0f : M[i];
+}
+
+// Hadamard image of the basis for the fused prologue: P = H_D Q / sqrt(D),
+// bf16 hi/lo split like Q, [D][RK] (columns j >= r are zero). One workgroup
+// per column; the column is transformed in LDS with the butterfly order of
+// the FWHT (h = 1, 2, ..., D/2) in fp32. Since H_D / sqrt(D) is symmetric and
+// orthogonal, H (x + Q z) / sqrt(D) = H x / sqrt(D) + P z.
+constexpr int kBasisFwhtMax = 4096;
+
+__global__ void __launch_bounds__(1024)
+basis_fwht_kernel(const float* __restrict__ Q, int D, int r, int RK, float norm,
+                  uint16_t* __restrict__ PH, uint16_t* __restrict__ PL) {
+  __shared__ float col[kBasisFwhtMax];
+  const int tid = threadIdx.x;
+  const int j = blockIdx.x;
+  for (int d = tid; d < D; d += 1024) col[d] = j < r ? Q[static_cast<int64_t>(d) * r + j] : 0.0f;
+  __syncthreads();
+  for (int lh = 0; (1 << lh) < D; ++lh) {
+    const int h = 1 << lh;
+    for (int i = tid; i < D / 2; i += 1024) {
+      const int lo = ((i >> lh) << (lh + 1)) + (i & (h - 1));
+      const float a = col[lo], b = col[lo + h];
+      col[lo] = a + b;
+      col[lo + h] = a - b;
     }
+    __syncthreads();
+  }
+  for (int d = tid; d < D; d += 1024) {
+    const float v = col[d] * norm;
+    const uint16_t hi = f32_to_bf16(v);
+    PH[static_cast<int64_t>(d) * RK + j] = hi;
+    PL[static_cast<int64_t>(d) * RK + j] = f32_to_bf16(v - bf16_to_f32(hi));
   }
 }
 
@@ -112,12 +166,10 @@ template <int RP>
 __global__ void __launch_bounds__(YNW * 64)
 yproj_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int r,
              const uint16_t* __restrict__ QtH, const uint16_t* __restrict__ QtL,
-             const float* __restrict__ MmT, float* __restrict__ Zpart) {
+             float* __restrict__ Zpart) {
   constexpr int RK = (RP + 31) / 32 * 32;
-  constexpr bool MLDS = RK <= 64;                      // (M - I)^T staged in LDS when small
   constexpr int NT = YNW * 64;
   __shared__ float red[4][YTPW][RP + 1];
-  __shared__ float mt[MLDS ? RK * RK : 1];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -194,8 +246,6 @@ yproj_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int r,
 #pragma unroll
         for (int v = 0; v < 4; ++v) red[wave - 4][16 * b + 4 * g + v][16 * nb + tl] = acc[b][nb][v];
   }
-  if constexpr (MLDS)
-    for (int o = tid; o < r * r; o += NT) mt[o] = MmT[o];
   __syncthreads();
   if (wave < 4) {
 #pragma unroll
@@ -209,21 +259,14 @@ yproj_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int r,
         }
   }
   __syncthreads();
-  // partial y of this D part for the workgroup's tokens, into red[0]
-  for (int o = tid; o < YTPW * RP; o += NT) {
-    const int t = o / RP;
-    const int j = o % RP;
-    red[0][t][j] = (red[0][t][j] + red[1][t][j]) + (red[2][t][j] + red[3][t][j]);
-  }
-  __syncthreads();
-  // partial z = (M - I) (partial y): z is linear in y, so the lift only sums
-  // the parts. (M - I) is stored transposed: consecutive i read consecutive words.
+  // partial z of this D part for the workgroup's tokens (the operand is
+  // Q (M - I)^T, so the sums are z's parts; the consumers add the parts);
+  // columns past RP (padding up to RK) are zero
   for (int o = tid; o < YTPW * RK; o += NT) {
     const int t = o / RK;
     const int i = o % RK;
     float z = 0.0f;
-    if (i < r)
-      for (int j = 0; j < r; ++j) z = fmaf(MLDS ? mt[j * r + i] : MmT[j * r + i], red[0][t][j], z);
+    if (i < RP) z = (red[0][t][i] + red[1][t][i]) + (red[2][t][i] + red[3][t][i]);
     if (t0 + t < T) Zpart[(static_cast<int64_t>(part) * T + t0 + t) * RK + i] = z;
   }
 }
@@ -386,9 +429,9 @@ inline size_t a256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 
 template <int RP>
 hipError_t run_yproj(const uint16_t* x, int64_t T, int D, int P, int S, int r, const uint16_t* QtH,
-                     const uint16_t* QtL, const float* MmT, float* Zpart, hipStream_t s) {
+                     const uint16_t* QtL, float* Zpart, hipStream_t s) {
   hipLaunchKernelGGL(yproj_kernel<RP>, dim3(static_cast<unsigned>((T + YTPW - 1) / YTPW), S), dim3(YNW * 64),
-                     0, s, x, T, D, P, r, QtH, QtL, MmT, Zpart);
+                     0, s, x, T, D, P, r, QtH, QtL, Zpart);
   return hipGetLastError();
 }
 
@@ -412,62 +455,94 @@ hipError_t run_lift(const uint16_t* x, int64_t T, int D, int P, int S, int r, co
 
 bool align_mfma_supported(int64_t D, int64_t r) { return r > 0 && r <= 128 && D % 64 == 0; }
 
-size_t align_mfma_workspace(int64_t T, int64_t D, int64_t r) {
-  const int RP = rp_of(r), RK = rk_of(r);
-  const int64_t S = (D + kPart - 1) / kPart;
-  return 2 * a256(static_cast<size_t>(RP) * D * 2) + 2 * a256(static_cast<size_t>(D) * RK * 2) +
-         a256(static_cast<size_t>(r) * r * 4) + a256(static_cast<size_t>(S) * T * RK * 4);
+int align_parts_count(int64_t D) { return static_cast<int>((D + kPart - 1) / kPart); }
+
+size_t align_zpart_bytes(int64_t T, int64_t D, int64_t r) {
+  return a256(static_cast<size_t>(align_parts_count(D)) * static_cast<size_t>(T) *
+              static_cast<size_t>(rk_of(r)) * 4);
 }
 
-AlignParts align_parts(void* ws, int64_t T, int64_t D, int64_t r) {
-  const int RP = rp_of(r), RK = rk_of(r);
-  AlignParts a;
-  a.RP = RP;
-  a.RK = RK;
-  a.S = static_cast<int>((D + kPart - 1) / kPart);
-  uint8_t* p = static_cast<uint8_t*>(ws);
-  a.QtH = reinterpret_cast<uint16_t*>(p); p += a256(static_cast<size_t>(RP) * D * 2);
-  a.QtL = reinterpret_cast<uint16_t*>(p); p += a256(static_cast<size_t>(RP) * D * 2);
-  a.QH = reinterpret_cast<uint16_t*>(p);  p += a256(static_cast<size_t>(D) * RK * 2);
-  a.QL = reinterpret_cast<uint16_t*>(p);  p += a256(static_cast<size_t>(D) * RK * 2);
-  a.Mm = reinterpret_cast<float*>(p);     p += a256(static_cast<size_t>(r) * r * 4);
-  a.Zpart = reinterpret_cast<float*>(p);
-  (void)T;
+size_t align_basis_bytes(int64_t D, int64_t r, bool with_p) {
+  const size_t RP = rp_of(r), RK = rk_of(r), Dz = static_cast<size_t>(D);
+  size_t n = 2 * a256(RP * Dz * 2) + 2 * a256(Dz * RK * 2);
+  if (with_p) n += 2 * a256(Dz * RK * 2);
+  return n;
+}
+
+AlignBasis align_basis(const void* basis, int64_t D, int64_t r, bool with_p) {
+  const size_t RP = rp_of(r), RK = rk_of(r), Dz = static_cast<size_t>(D);
+  AlignBasis a;
+  a.RP = static_cast<int>(RP);
+  a.RK = static_cast<int>(RK);
+  uint8_t* p = static_cast<uint8_t*>(const_cast<void*>(basis));
+  a.QtH = reinterpret_cast<uint16_t*>(p); p += a256(RP * Dz * 2);
+  a.QtL = reinterpret_cast<uint16_t*>(p); p += a256(RP * Dz * 2);
+  a.QH = reinterpret_cast<uint16_t*>(p);  p += a256(Dz * RK * 2);
+  a.QL = reinterpret_cast<uint16_t*>(p);  p += a256(Dz * RK * 2);
+  a.PH = with_p ? reinterpret_cast<uint16_t*>(p) : nullptr;
+  if (with_p) p += a256(Dz * RK * 2);
+  a.PL = with_p ? reinterpret_cast<uint16_t*>(p) : nullptr;
   return a;
 }
 
-hipError_t launch_align_prep_proj(const uint16_t* x, const float* Q, const float* M, int64_t T,
-                                  int64_t D, int64_t r, void* ws, hipStream_t s) {
-  if (T == 0) return hipSuccess;
-  const AlignParts a = align_parts(ws, T, D, r);
+hipError_t launch_basis_prep(const float* Q, const float* M, int64_t D, int64_t r, bool with_p,
+                             void* basis, hipStream_t s) {
+  const AlignBasis a = align_basis(basis, D, r, with_p);
   const dim3 pgrid(static_cast<unsigned>((D + 63) / 64), static_cast<unsigned>(a.RK / 32));
   hipLaunchKernelGGL(basis_prep_kernel, pgrid, dim3(256), 0, s, Q, M, static_cast<int>(D),
-                     static_cast<int>(r), a.RP, a.RK, a.QtH, a.QtL, a.QH, a.QL, a.Mm);
+                     static_cast<int>(r), a.RP, a.RK, a.QtH, a.QtL, a.QH, a.QL);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !with_p) return e;
+  if ((D & (D - 1)) != 0 || D > kBasisFwhtMax) return hipErrorInvalidValue;
+  const float norm = static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(D)));
+  hipLaunchKernelGGL(basis_fwht_kernel, dim3(static_cast<unsigned>(a.RK)), dim3(1024), 0, s, Q,
+                     static_cast<int>(D), static_cast<int>(r), a.RK, norm, a.PH, a.PL);
+  return hipGetLastError();
+}
+
+hipError_t launch_yproj(const uint16_t* x, int64_t T, int64_t D, int64_t r, const void* basis,
+                        bool with_p, float* Zpart, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const AlignBasis a = align_basis(basis, D, r, with_p);
   const int Di = static_cast<int>(D);
   const int ri = static_cast<int>(r);
+  const int S = align_parts_count(D);
   switch (a.RP) {
-#define RW4_Y(V) case V: return run_yproj<V>(x, T, Di, kPart, a.S, ri, a.QtH, a.QtL, a.Mm, a.Zpart, s);
+#define RW4_Y(V) case V: return run_yproj<V>(x, T, Di, kPart, S, ri, a.QtH, a.QtL, Zpart, s);
     RW4_Y(16) RW4_Y(32) RW4_Y(48) RW4_Y(64) RW4_Y(80) RW4_Y(96) RW4_Y(112) RW4_Y(128)
 #undef RW4_Y
     default: return hipErrorInvalidValue;
   }
 }
 
+size_t align_mfma_workspace(int64_t T, int64_t D, int64_t r) {
+  return align_basis_bytes(D, r, false) + align_zpart_bytes(T, D, r);
+}
+
 hipError_t launch_align_mfma(const uint16_t* x, void* out, int out_f32, const float* Q,
                              const float* M, const void* addend, int64_t T, int64_t D, int64_t r,
                              void* ws, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  hipError_t e = launch_align_prep_proj(x, Q, M, T, D, r, ws, s);
+  hipError_t e = launch_basis_prep(Q, M, D, r, false, ws, s);
   if (e != hipSuccess) return e;
-  const AlignParts a = align_parts(ws, T, D, r);
+  float* Zpart = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align_basis_bytes(D, r, false));
+  e = launch_yproj(x, T, D, r, ws, false, Zpart, s);
+  if (e != hipSuccess) return e;
+  return launch_lift(x, out, out_f32, addend, T, D, r, ws, false, Zpart, s);
+}
+
+hipError_t launch_lift(const uint16_t* x, void* out, int out_f32, const void* addend, int64_t T,
+                       int64_t D, int64_t r, const void* basis, bool with_p, const float* Zpart,
+                       hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const AlignBasis a = align_basis(basis, D, r, with_p);
   const int Di = static_cast<int>(D);
   const int ri = static_cast<int>(r);
+  const int S = align_parts_count(D);
   const bool of32 = out_f32 != 0;
   switch (a.RP) {
 #define RW4_L(V, K) \
-  case V: return run_lift<V, K>(x, T, Di, kPart, a.S, ri, a.Zpart, a.QH, a.QL, addend, out, of32, s);
+  case V: return run_lift<V, K>(x, T, Di, kPart, S, ri, Zpart, a.QH, a.QL, addend, out, of32, s);
     RW4_L(16, 32) RW4_L(32, 32) RW4_L(48, 64) RW4_L(64, 64) RW4_L(80, 96) RW4_L(96, 96)
     RW4_L(112, 128) RW4_L(128, 128)
 #undef RW4_L

@@ -141,6 +141,21 @@ struct RowQuant {
     }
     return static_cast<float>(quant4(v, s));
   }
+  // codes of v[0..NV) from the reciprocal, with one check for all of them:
+  // true when every value is at least 2^-18 from a half-integer (then each
+  // q[e] equals code(v[e])); false when the caller must use code()
+  template <int NV>
+  __device__ __forceinline__ bool fast_codes(const float (&v)[NV], float (&q)[NV]) const {
+    float mx = 0.0f;
+#pragma unroll
+    for (int e = 0; e < NV; ++e) {
+      const float t = v[e] * y;
+      const float r = rintf(t);
+      q[e] = r + 0.0f;
+      mx = fmaxf(mx, fabsf(t - r));
+    }
+    return fast && 0.5f - mx >= 3.814697265625e-06f;
+  }
 };
 
 // Packed E2M3 fields from integer-valued floats in [-7, 7] (no -0) with the

@@ -32,24 +32,37 @@ hipError_t launch_align_mfma(const uint16_t* x, void* out, int out_f32, const fl
                              const float* M, const void* addend, int64_t T, int64_t D, int64_t r,
                              void* ws, hipStream_t s);
 
-// Pieces of the matrix-core alignment workspace: the prepared basis (bf16
-// hi/lo Q in both orientations, (M - I) transposed) and the per-part z sums.
-struct AlignParts {
+// The prepared basis of the matrix-core alignment (depends on Q and M only),
+// bf16 hi/lo splits of: the projection operand (Q (M - I)^T)^T [RP][D], the
+// lift operand Q [D][RK], and optionally the Hadamard image P = H Q / sqrt(D)
+// [D][RK] for the fused prologue (D a power of two <= 4096).
+struct AlignBasis {
   uint16_t* QtH; uint16_t* QtL; uint16_t* QH; uint16_t* QL;
-  float* Mm; float* Zpart;
-  int RP, RK, S;   // r padded to 16 and to 32; number of D parts of Zpart
+  uint16_t* PH; uint16_t* PL;   // null without P
+  int RP, RK;                   // r padded to 16 and to 32
 };
-AlignParts align_parts(void* ws, int64_t T, int64_t D, int64_t r);
-// basis preparation and the projection z = sum over parts of (M - I) Q_part^T x_part
-hipError_t launch_align_prep_proj(const uint16_t* x, const float* Q, const float* M, int64_t T,
-                                  int64_t D, int64_t r, void* ws, hipStream_t s);
+size_t align_basis_bytes(int64_t D, int64_t r, bool with_p);
+AlignBasis align_basis(const void* basis, int64_t D, int64_t r, bool with_p);
+hipError_t launch_basis_prep(const float* Q, const float* M, int64_t D, int64_t r, bool with_p,
+                             void* basis, hipStream_t s);
+// per-call projection: Zpart[part][t][i] = ((M - I) Q_part^T x_part)[i] for
+// the align_parts_count(D) D parts (z is their sum)
+int align_parts_count(int64_t D);
+size_t align_zpart_bytes(int64_t T, int64_t D, int64_t r);
+hipError_t launch_yproj(const uint16_t* x, int64_t T, int64_t D, int64_t r, const void* basis,
+                        bool with_p, float* Zpart, hipStream_t s);
+// unfused lift out = x + Q z (+ addend), fp32 or bf16 out
+hipError_t launch_lift(const uint16_t* x, void* out, int out_f32, const void* addend, int64_t T,
+                       int64_t D, int64_t r, const void* basis, bool with_p, const float* Zpart,
+                       hipStream_t s);
 
 // Fused lift + [Walsh-Hadamard] + INT4 quantization into FP6 tiles, after
-// launch_align_prep_proj: per token, v = x + Q z, [v = H v], codes of v.
+// launch_yproj: per token, u = [H x / sqrt(D)] + P z (P = H Q / sqrt(D) with
+// the transform, Q without), codes of u. Needs a basis prepared with P.
 bool lfq_supported(int64_t D, int64_t r);
-hipError_t launch_lift_fwht_quant(const uint16_t* x, int64_t T, int64_t D, int64_t r, void* ws,
-                                  bool do_fwht, uint8_t* tiles, float* s_a, float* dbg,
-                                  hipStream_t s);
+hipError_t launch_lift_fwht_quant(const uint16_t* x, int64_t T, int64_t D, int64_t r,
+                                  const void* basis, const float* Zpart, bool do_fwht,
+                                  uint8_t* tiles, float* s_a, float* dbg, hipStream_t s);
 
 // W4A4 GEMM, bf16 (dequantized) or raw int32 output.
 hipError_t launch_gemm(const uint8_t* a, const float* s_a, const uint8_t* w, const float* s_w,

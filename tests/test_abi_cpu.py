@@ -22,7 +22,7 @@ def _declared():
 def test_library_built_and_loads():
     assert os.path.exists(rw.library_path), "build the HIP library first"
     L = rw.lib()
-    assert L.rw4_abi_version() == 3
+    assert L.rw4_abi_version() == 4
 
 
 def test_exports_every_declared_symbol():
@@ -55,13 +55,36 @@ def test_workspace_size():
     assert L.rotated_linear_workspace_size(T, D, 32, 2) == base
     aws = L.respin_align_workspace_size(T, D, 32)
     assert aws > 0
-    assert L.rotated_linear_workspace_size(T, D, 32, 3) == base + 4 * T * D + aws
+    # projection parts: D / 512 parts x T tokens x r padded to 32, fp32
+    zpart = L.rw4_align256((D // 512) * T * 32 * 4)
+    assert L.rotated_linear_prepared_workspace_size(T, D, 32, 3) == base + zpart
+    assert L.rotated_linear_prepared_workspace_size(T, D, 32, 2) == base
+    assert L.rotated_linear_workspace_size(T, D, 32, 3) == (
+        base + zpart + L.rw4_align256(L.respin_basis_size(D, 32)))
+    # D = 8192 is past the fused prologue: aligned rows go through an fp32 buffer
+    T8, D8 = 64, 8192
+    base8 = L.rw4_align256(L.w4a4_tiles_size(T8, D8)) + L.rw4_align256(4 * T8)
+    assert L.rotated_linear_prepared_workspace_size(T8, D8, 64, 3) == (
+        base8 + L.rw4_align256(16 * T8 * 64 * 4) + 4 * T8 * D8)
     assert L.rotated_linear_workspace_size(T, D, 0, 3) == base
     assert L.rotated_linear_workspace_size(-1, D, 0, 0) == 0
     assert L.rotated_linear_workspace_size(4, 7, 0, 0) == 0
     assert L.rotated_linear_workspace_size(4, 32, 0, 0) == 0   # tiles need D >= 64
     # matrix-core alignment needs D % 64 == 0
     assert L.respin_align_workspace_size(4, 1000, 12) == 0
+
+
+def test_basis_size():
+    L = rw.lib()
+    # bf16 hi/lo of the projection operand [r padded to 16][D] and of Q [D][r
+    # padded to 32], plus the Hadamard image of Q (hi/lo, [D][r padded to 32])
+    # for D a power of two in [256, 4096] with r <= 64
+    assert L.respin_basis_size(4096, 32) == 6 * (4096 * 32 * 2)
+    assert L.respin_basis_size(8192, 64) == 4 * (8192 * 64 * 2)
+    assert L.respin_basis_size(256, 8) == 2 * (256 * 16 * 2) + 4 * (256 * 32 * 2)
+    assert L.respin_basis_size(4096, 0) == 0 and L.respin_basis_size(4096, 6) == 0
+    assert L.respin_basis_size(4096, 132) == 0 and L.respin_basis_size(1000, 8) == 0
+    assert L.respin_basis_size(64, 68) == 0
 
 
 # fake, 256-byte aligned addresses: validation must reject before dereferencing
@@ -162,6 +185,40 @@ def test_gemm_tiles_validation(args, expect):
 def _rl(x=A, ldx=64, T=4, D=64, Q=B, M=C, r=8, flags=3, w=Dp, sw=A, N=16, y=B, ws=C,
         wsb=1 << 20, dbg=NUL):
     return rw.lib().rotated_linear(x, ldx, T, D, Q, M, r, flags, w, sw, N, y, ws, wsb, dbg, NUL)
+
+
+def _prep(Q=A, M=B, D=256, r=8, basis=C, nb=1 << 20):
+    return rw.lib().respin_prepare_basis(Q, M, D, r, basis, nb, NUL)
+
+
+def test_prepare_basis_validation():
+    assert _prep(Q=NUL) == INV and _prep(M=NUL) == INV and _prep(r=0) == INV
+    assert _prep(r=6) == UNS and _prep(D=1000) == UNS and _prep(r=132) == UNS
+    assert _prep(Q=ODD) == MIS
+    assert _prep(M=ctypes.c_void_p(0x20002)) == MIS
+    assert _prep(basis=NUL) == WSE and _prep(nb=100) == WSE
+    assert _prep(basis=ctypes.c_void_p(0x30010)) == WSE
+
+
+def _rlp(x=A, ldx=64, T=4, D=64, basis=B, r=8, flags=3, w=Dp, sw=A, N=16, y=B, ws=C,
+         wsb=1 << 20, dbg=NUL):
+    return rw.lib().rotated_linear_prepared(x, ldx, T, D, basis, r, flags, w, sw, N, y, ws, wsb,
+                                            dbg, NUL)
+
+
+def test_rotated_linear_prepared_validation():
+    assert _rlp(flags=8) == INV
+    assert _rlp(flags=1 | 4) == INV
+    assert _rlp(D=48) == UNS
+    assert _rlp(r=6) == UNS
+    assert _rlp(ldx=128) == UNS
+    assert _rlp(basis=NUL) == INV                  # align with r > 0 needs a basis
+    assert _rlp(basis=ctypes.c_void_p(0x20010)) == INV
+    assert _rlp(ws=ctypes.c_void_p(0x30010)) == WSE
+    assert _rlp(wsb=100) == WSE
+    assert _rlp(x=ODD) == MIS
+    assert _rlp(T=0) == 0
+    assert _rlp(T=0, x=NUL, w=NUL, sw=NUL, y=NUL, basis=NUL) == 0
 
 
 def test_rotated_linear_validation():

@@ -383,6 +383,35 @@ def test_rotated_linear_flags(rw, T, D, N, flags):
     _check_unit(rw, xb, Q, M, flags, codes_w, s_w, qw, sw_h)
 
 
+# the prepared basis gives the same results bit for bit; the fused prologue's
+# geometry changes with D (lane bits of a row), r (32 or 64 padded), and the
+# transform flag (without it the lift operand is Q itself); D = 8192 runs the
+# unfused path on the same basis layout
+@pytest.mark.parametrize("T,D,N,r,flags", [(45, 512, 128, 16, 3), (61, 1024, 64, 48, 3),
+                                           (200, 2048, 96, 64, 3), (9, 4096, 64, 64, 1),
+                                           (70, 256, 64, 8, 1), (3, 8192, 64, 64, 3)])
+def test_rotated_linear_prepared(rw, T, D, N, r, flags):
+    say(f"rotated_linear_prepared T={T} D={D} N={N} r={r} flags={flags}")
+    t = torch()
+    xb = W.gen_x(T + D + r, T, D, 4, 30.0)
+    Q, M = W.gen_basis(T + r, D, r)
+    Wf = W.gen_weight(N + r, N, D, 0.02)
+    codes_w, s_w, qw, sw_h = _prep(rw, Wf, bool(flags & 2))
+    y_ref = _check_unit(rw, xb, Q, M, flags, codes_w, s_w, qw, sw_h)
+    d1 = t.empty((T, D), dtype=t.float32, device="cuda")
+    _, ws1 = rw.rotated_linear(dev(xb), codes_w, s_w, flags, dev(Q), dev(M), dbg_prequant=d1)
+    basis = rw.respin_prepare_basis(dev(Q), dev(M))
+    d2 = t.empty((T, D), dtype=t.float32, device="cuda")
+    y2, ws2 = rw.rotated_linear_prepared(dev(xb), codes_w, s_w, flags, basis, r, dbg_prequant=d2)
+    _sync()
+    np.testing.assert_array_equal(host(y2), y_ref)
+    np.testing.assert_array_equal(host(d2), host(d1))
+    (t1, s1), (t2, s2) = rw.workspace_views(ws1, T, D), rw.workspace_views(ws2, T, D)
+    np.testing.assert_array_equal(host(s2), host(s1))
+    # rows past T of the padded tiles are not written by either call
+    np.testing.assert_array_equal(F.untile(host(t2), T, D), F.untile(host(t1), T, D))
+
+
 def test_rotated_linear_strided_input(rw):
     """Row-strided bf16 input (the V third of a QKV output)."""
     T, D, N = 24, 256, 64
