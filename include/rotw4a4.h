@@ -62,8 +62,10 @@ typedef enum rw4_status {
 
 typedef enum rw4_dtype { RW4_BF16 = 0, RW4_F32 = 1, RW4_I32 = 2 } rw4_dtype;
 
-/* flags of rotated_linear */
-enum { RW4_ALIGN = 1, RW4_FWHT = 2, RW4_SWIGLU = 4 };
+/* flags of rotated_linear; RW4_ABITS(b) selects b-bit activation codes
+   (b = 2, 3 or 4; 0 in that field means 4) */
+enum { RW4_ALIGN = 1, RW4_FWHT = 2, RW4_SWIGLU = 4, RW4_ABITS_SHIFT = 8 };
+#define RW4_ABITS(b) ((unsigned)(b) << RW4_ABITS_SHIFT)
 
 /*
  * respin_align -- online low-rank residual alignment [RSQ key design 3].
@@ -118,6 +120,18 @@ rw4_status fwht(const void* x, rw4_dtype x_dt, float* y, int64_t T, int64_t D, v
  */
 rw4_status quant_act_int4(const void* x, rw4_dtype x_dt, uint8_t* codes, float* scales,
                           int64_t T, int64_t D, void* stream);
+
+/*
+ * quant_act_sym -- quant_act_int4 for b-bit codes ["ReSpinQuant" paper notes,
+ * 实验 (W3A3 and W4A4 settings); IQ2 FlatQuant Preliminaries (the signed
+ * b-bit grid)]:
+ *   scales[t] = fl32(max_i |x[t][i]| / (2^(b-1) - 1))
+ *   q         = clamp(rint(fl32(x[t][i] / scales[t])), -2^(b-1), 2^(b-1) - 1)
+ * Codes are stored as INT4 nibbles like quant_act_int4 (b = 4 is that call).
+ *   bits  2, 3 or 4 (otherwise RW4_ERR_INVALID_ARG)
+ */
+rw4_status quant_act_sym(const void* x, rw4_dtype x_dt, uint8_t* codes, float* scales,
+                         int64_t T, int64_t D, int bits, void* stream);
 
 /*
  * w4a4_gemm -- INT4 x INT4 GEMM with int32 accumulation and dequantization
@@ -190,6 +204,8 @@ rw4_status w4a4_gemm_tiles(const uint8_t* a, const float* s_a, const uint8_t* w,
  *          RW4_SWIGLU: the input row is a gate|up pair of width 2D; the
  *            quantized vector is SiLU(gate) * up in fp32 (SiLU(g) = g/(1+e^-g)).
  *          RW4_FWHT: Hadamard transform of size D before quantization.
+ *          RW4_ABITS(b): b-bit activation codes as quant_act_sym (W3A3 with
+ *            3-bit weight codes; the GEMM takes any codes in [-7, 7]).
  *          flags = 0: quantize x as is. ALIGN and SWIGLU are exclusive.
  *   x        bf16, T rows of D (or 2D with SWIGLU) values, row stride ldx
  *            elements (ldx >= width, ldx % 8 == 0)
@@ -263,7 +279,7 @@ const char* rw4_status_string(rw4_status s);
 /* ABI version of this header (bumped on any signature change) */
 int rw4_abi_version(void);
 
-#define RW4_ABI_VERSION 4
+#define RW4_ABI_VERSION 5
 
 #ifdef __cplusplus
 }

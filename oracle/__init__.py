@@ -289,12 +289,13 @@ def prequant(x: np.ndarray, flags: int, Q=None, M=None) -> np.ndarray:
 
 
 def rotated_linear(x_bits: np.ndarray, flags: int, wq: np.ndarray, s_w: np.ndarray,
-                   Q=None, M=None):
-    """Whole unit on bf16 input bits: pre-quant values -> fp32 -> per-token INT4
-    -> integer GEMM -> dequantized bf16.  Returns a dict of every stage."""
+                   Q=None, M=None, bits: int = 4):
+    """Whole unit on bf16 input bits: pre-quant values -> fp32 -> per-token
+    ``bits``-bit codes (4: INT4; 3: the W3A3 setting [RSQ 实验]) -> integer GEMM
+    -> dequantized bf16.  Returns a dict of every stage."""
     v = prequant(bf16_to_f64(x_bits), flags, Q, M)
     v32 = v.astype(np.float32)
-    qa, s_a = quant_int4(v32)
+    qa, s_a = quant_sym(v32, bits)
     acc = gemm_int(qa, wq)
     y = epilogue(acc, s_a, s_w)
     return {"prequant": v, "prequant32": v32, "codes": qa, "s_a": s_a, "acc": acc, "y": y}

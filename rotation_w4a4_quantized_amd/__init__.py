@@ -19,16 +19,23 @@ __all__ = [
     "respin_basis_size", "respin_prepare_basis", "rotated_linear_prepared",
     "rotated_linear_prepared_workspace_size",
     "w4a4_tiles_size", "w4a4_tile_codes", "w4a4_gemm_tiles", "prep_weight", "layer",
+    "quant_act_sym", "RW4_ABITS",
 ]
 
 RW4_ALIGN, RW4_FWHT, RW4_SWIGLU = 1, 2, 4
+
+
+def RW4_ABITS(bits: int) -> int:
+    """rotated_linear flag field for b-bit activation codes (b = 2, 3, 4)."""
+    return bits << 8
 _BF16, _F32, _I32 = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "librotw4a4.so")
 _lib = None
 
-EXPORTS = ("respin_align", "respin_align_workspace_size", "fwht", "quant_act_int4", "w4a4_gemm",
+EXPORTS = ("respin_align", "respin_align_workspace_size", "fwht", "quant_act_int4",
+           "quant_act_sym", "w4a4_gemm",
            "w4a4_tiles_size", "w4a4_tile_codes", "w4a4_gemm_tiles", "rotated_linear",
            "rotated_linear_workspace_size", "respin_basis_size", "respin_prepare_basis",
            "rotated_linear_prepared", "rotated_linear_prepared_workspace_size", "rw4_align256",
@@ -58,6 +65,7 @@ def lib() -> ctypes.CDLL:
     L.respin_align_workspace_size.restype = sz
     L.fwht.argtypes = [vp, i32, vp, i64, i64, vp]
     L.quant_act_int4.argtypes = [vp, i32, vp, vp, i64, i64, vp]
+    L.quant_act_sym.argtypes = [vp, i32, vp, vp, i64, i64, i32, vp]
     L.w4a4_gemm.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, vp]
     L.w4a4_tiles_size.argtypes = [i64, i64]
     L.w4a4_tiles_size.restype = sz
@@ -79,7 +87,8 @@ def lib() -> ctypes.CDLL:
     L.rw4_status_string.argtypes = [i32]
     L.rw4_status_string.restype = ctypes.c_char_p
     L.rw4_abi_version.restype = i32
-    for f in ("respin_align", "fwht", "quant_act_int4", "w4a4_gemm", "w4a4_tile_codes",
+    for f in ("respin_align", "fwht", "quant_act_int4", "quant_act_sym", "w4a4_gemm",
+              "w4a4_tile_codes",
               "w4a4_gemm_tiles", "rotated_linear", "respin_prepare_basis",
               "rotated_linear_prepared"):
         getattr(L, f).restype = i32
@@ -188,6 +197,21 @@ def quant_act_int4(x, codes=None, scales=None) -> Tuple:
         scales = torch.empty((T,), dtype=torch.float32, device=x.device)
     st = lib().quant_act_int4(_p(x), _fdt(x), _p(codes), _p(scales), T, D, _stream())
     _check("quant_act_int4", st)
+    return codes, scales
+
+
+def quant_act_sym(x, bits: int, codes=None, scales=None) -> Tuple:
+    """Per-row absmax b-bit codes (b = 2, 3, 4) stored as INT4 nibbles:
+    (codes uint8 [T][D/2], scales fp32 [T])."""
+    torch = _torch()
+    _contig(x)
+    T, D = x.shape
+    if codes is None:
+        codes = torch.empty((T, D // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((T,), dtype=torch.float32, device=x.device)
+    st = lib().quant_act_sym(_p(x), _fdt(x), _p(codes), _p(scales), T, D, bits, _stream())
+    _check("quant_act_sym", st)
     return codes, scales
 
 
@@ -350,13 +374,13 @@ def workspace_views(workspace, T: int, D: int):
     return tiles, scales
 
 
-def prep_weight(W, rotate: bool):
+def prep_weight(W, rotate: bool, bits: int = 4):
     """Offline weight preparation on the GPU: optional row-wise Hadamard along K
-    (fwht), per-output-channel INT4 (quant_act_int4), then FP6 tiles.
+    (fwht), per-output-channel b-bit codes (quant_act_sym), then FP6 tiles.
     W fp32 [N][K]. Returns (tiles, s_w, codes [N][K/2], rotated W)."""
     _contig(W)
     src = fwht(W) if rotate else W
-    codes, s_w = quant_act_int4(src)
+    codes, s_w = quant_act_sym(src, bits)
     tiles = w4a4_tile_codes(codes)
     return tiles, s_w, codes, src
 

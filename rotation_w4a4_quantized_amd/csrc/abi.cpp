@@ -27,6 +27,13 @@ rw4_status check_align_args(const void* x, rw4_dtype x_dt, const void* out, rw4_
   return RW4_OK;
 }
 
+// activation code width from the flags (0 means the default 4)
+inline int abits(unsigned flags) {
+  const int b = static_cast<int>((flags >> RW4_ABITS_SHIFT) & 0xFu);
+  return b == 0 ? 4 : b;
+}
+constexpr unsigned kFlagMask = RW4_ALIGN | RW4_FWHT | RW4_SWIGLU | (0xFu << RW4_ABITS_SHIFT);
+
 // P (the Hadamard image of the basis) is prepared when the fused prologue can run
 inline bool with_p(int64_t D, int64_t r) { return rw4::lfq_supported(D, r); }
 
@@ -49,8 +56,9 @@ rw4_status check_linear(const void* x, int64_t ldx, int64_t T, int64_t D, int64_
                         unsigned flags, const uint8_t* w, const float* s_w, int64_t N, void* y,
                         const float* dbg) {
   if (T < 0 || N < 1) return RW4_ERR_INVALID_ARG;
-  if (flags & ~static_cast<unsigned>(RW4_ALIGN | RW4_FWHT | RW4_SWIGLU)) return RW4_ERR_INVALID_ARG;
+  if (flags & ~kFlagMask) return RW4_ERR_INVALID_ARG;
   if ((flags & RW4_ALIGN) && (flags & RW4_SWIGLU)) return RW4_ERR_INVALID_ARG;
+  if (abits(flags) < 2 || abits(flags) > 4) return RW4_ERR_INVALID_ARG;
   if (!pow2(D) || D < 64 || D > 32768) return RW4_ERR_UNSUPPORTED;
   if (T == 0) return RW4_OK;
   if (!x || !w || !s_w || !y) return RW4_ERR_INVALID_ARG;
@@ -88,7 +96,7 @@ rw4_status run_linear(const void* x, int64_t ldx, int64_t T, int64_t D, const vo
     if (fused) {
       // lift + transform + quantization on chip
       if (rw4::launch_lift_fwht_quant(xb, T, D, r, basis, Zpart, (flags & RW4_FWHT) != 0, codes,
-                                      s_a, dbg, s) != hipSuccess)
+                                      s_a, dbg, s, abits(flags)) != hipSuccess)
         return RW4_ERR_HIP;
       return hip_status(rw4::launch_gemm_tiles(codes, s_a, w, s_w, y, false, T, D, N, s));
     }
@@ -101,7 +109,7 @@ rw4_status run_linear(const void* x, int64_t ldx, int64_t T, int64_t D, const vo
     ld = D;
   }
   hipError_t e = rw4::launch_row(src, in, ld, T, D, (flags & RW4_FWHT) != 0, nullptr, codes, true,
-                                 s_a, dbg, s);
+                                 s_a, dbg, s, abits(flags));
   if (e != hipSuccess) return RW4_ERR_HIP;
   return hip_status(rw4::launch_gemm_tiles(codes, s_a, w, s_w, y, false, T, D, N, s));
 }
@@ -164,19 +172,23 @@ rw4_status fwht(const void* x, rw4_dtype x_dt, float* y, int64_t T, int64_t D, v
                                     y, nullptr, false, nullptr, nullptr, strm(stream)));
 }
 
-rw4_status quant_act_int4(const void* x, rw4_dtype x_dt, uint8_t* codes, float* scales, int64_t T,
-                          int64_t D, void* stream) {
-  if (T < 0 || !fdt(x_dt)) return RW4_ERR_INVALID_ARG;
+rw4_status quant_act_sym(const void* x, rw4_dtype x_dt, uint8_t* codes, float* scales, int64_t T,
+                         int64_t D, int bits, void* stream) {
+  if (T < 0 || !fdt(x_dt) || bits < 2 || bits > 4) return RW4_ERR_INVALID_ARG;
   if (D < 2 || (D % 2) != 0 || D > (int64_t(1) << 20)) return RW4_ERR_UNSUPPORTED;
   if (T == 0) return RW4_OK;
   if (!x || !codes || !scales) return RW4_ERR_INVALID_ARG;
   if (!al16(x) || !al16(codes) || !al16(scales)) return RW4_ERR_MISALIGNED;
-  if (T == 0) return RW4_OK;
   const int in = x_dt == RW4_F32 ? rw4::IN_F32 : rw4::IN_BF16;
   if (pow2(D) && D <= 32768)
     return hip_status(rw4::launch_row(x, in, D, T, D, false, nullptr, codes, false, scales,
-                                      nullptr, strm(stream)));
-  return hip_status(rw4::launch_quant_generic(x, in, D, T, D, codes, scales, strm(stream)));
+                                      nullptr, strm(stream), bits));
+  return hip_status(rw4::launch_quant_generic(x, in, D, T, D, codes, scales, strm(stream), bits));
+}
+
+rw4_status quant_act_int4(const void* x, rw4_dtype x_dt, uint8_t* codes, float* scales, int64_t T,
+                          int64_t D, void* stream) {
+  return quant_act_sym(x, x_dt, codes, scales, T, D, 4, stream);
 }
 
 rw4_status w4a4_gemm(const uint8_t* a, const float* s_a, const uint8_t* w, const float* s_w,

@@ -119,9 +119,9 @@ __device__ __forceinline__ void store_fields16(uint8_t* tiles, int64_t t, int64_
 }
 
 // Per-row quantizer with the step's reciprocal. For a row with step s
-// (s = fl32(absmax / 7), normal) and y = fl32(1 / s) (correctly rounded),
-// t = fl32(v * y) differs from v / s by at most 2^-23 |v / s| <= 8.4e-7 and
-// fl32(v / s) from v / s by at most 4.2e-7. So when t is at least 2^-18 away
+// (s = fl32(absmax / qmax), normal; qmax <= 7) and y = fl32(1 / s) (correctly
+// rounded), t = fl32(v * y) differs from v / s by at most
+// 2^-23 |v / s| <= 8.4e-7 and fl32(v / s) from v / s by at most 4.2e-7. So when t is at least 2^-18 away
 // from every half-integer, fl32(v / s) lies strictly between the same two
 // half-integers as t and rint(fl32(v / s)) == rint(t); otherwise the exact
 // quotient decides. Codes equal quant4(v, s) for every v.
@@ -134,7 +134,7 @@ struct RowQuant {
   __device__ __forceinline__ float code(float v) const {
     if (!(s > 0.0f)) return 0.0f;
     if (fast) {
-      const float t = v * y;               // |t| <= 7.0000009, so |rint(t)| <= 7
+      const float t = v * y;               // |t| <= qmax + 8.4e-7, so |rint(t)| <= qmax
       const float q = rintf(t);
       if (0.5f - fabsf(t - q) >= 3.814697265625e-06f)  // 2^-18
         return q + 0.0f;

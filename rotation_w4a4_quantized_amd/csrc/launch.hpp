@@ -9,16 +9,16 @@ namespace rw4 {
 enum InMode { IN_BF16 = 0, IN_F32 = 1, IN_SWIGLU = 2 };
 
 // Per-row transform: [SiLU gate] -> [Walsh-Hadamard] -> output.
-// Output either fp32 values (yf) or INT4 codes + scales (+ optional fp32 dump).
-// Codes go to packed INT4 rows, or (tiled, D >= 64) to FP6 operand tiles.
-// D must be a power of two in [2, 32768].
+// Output either fp32 values (yf) or b-bit codes (b = bits, 2..4) + scales
+// (+ optional fp32 dump). Codes go to packed INT4 rows, or (tiled, D >= 64)
+// to FP6 operand tiles. D must be a power of two in [2, 32768].
 hipError_t launch_row(const void* x, int in_mode, int64_t ldx, int64_t T, int64_t D, bool do_fwht,
                       float* yf, uint8_t* codes, bool tiled, float* scales, float* dbg,
-                      hipStream_t s);
+                      hipStream_t s, int bits = 4);
 
-// Per-row INT4 quantization for any even D (no transform).
+// Per-row b-bit quantization for any even D (no transform).
 hipError_t launch_quant_generic(const void* x, int in_mode, int64_t ldx, int64_t T, int64_t D,
-                                uint8_t* codes, float* scales, hipStream_t s);
+                                uint8_t* codes, float* scales, hipStream_t s, int bits = 4);
 
 // Low-rank residual alignment out = x + Q (M - I) Q^T x (+ addend).
 hipError_t launch_align(const void* x, int x_f32, void* out, int out_f32, const float* Q,
@@ -62,7 +62,8 @@ hipError_t launch_lift(const uint16_t* x, void* out, int out_f32, const void* ad
 bool lfq_supported(int64_t D, int64_t r);
 hipError_t launch_lift_fwht_quant(const uint16_t* x, int64_t T, int64_t D, int64_t r,
                                   const void* basis, const float* Zpart, bool do_fwht,
-                                  uint8_t* tiles, float* s_a, float* dbg, hipStream_t s);
+                                  uint8_t* tiles, float* s_a, float* dbg, hipStream_t s,
+                                  int bits = 4);
 
 // W4A4 GEMM, bf16 (dequantized) or raw int32 output.
 hipError_t launch_gemm(const uint8_t* a, const float* s_a, const uint8_t* w, const float* s_w,

@@ -5,7 +5,8 @@
 // §2.2; "Infra Quant II", QuaRot Method):
 //   v = x + Q z          (z = (M - I) Q^T x, summed from the projection's parts)
 //   u = H_D v / sqrt(D)  (optional)
-//   step = fl32(max |u| / 7), code = clamp(rint(fl32(u / step)), -8, 7)
+//   step = fl32(max |u| / qmax), code = rint(fl32(u / step)) (qmax = 2^(b-1) - 1
+//   for b-bit codes, 7 for INT4; |code| <= qmax by construction)
 // H_D / sqrt(D) is symmetric and orthogonal, so H v / sqrt(D) =
 // H x / sqrt(D) + P z with P = H Q / sqrt(D), prepared once with the basis
 // (without the transform P is Q itself). The two terms are computed at the
@@ -83,7 +84,7 @@ __global__ void __launch_bounds__(kThreads)
 lfq_kernel(const uint16_t* __restrict__ x, int64_t T, const float* __restrict__ Zpart, int S,
            const uint16_t* __restrict__ PH, const uint16_t* __restrict__ PL,
            uint8_t* __restrict__ tiles, float* __restrict__ s_a, float* __restrict__ dbg,
-           float norm) {
+           float norm, float qmax) {
   constexpr int D = 1 << N;
   constexpr int NCH = D / 32;                   // 32-value chunks per row
   constexpr int NS = NCH > 64 ? NCH / 64 : 1;   // chunks per lane
@@ -289,7 +290,7 @@ lfq_kernel(const uint16_t* __restrict__ x, int64_t T, const float* __restrict__ 
   m = act ? m : 0.0f;
   m = wave_max(m);
   if (t < T && act) {
-    const float st = m / 7.0f;
+    const float st = m / qmax;
     if (lane == 0) s_a[t] = st;
     const RowQuant rq(st);
 #pragma unroll
@@ -315,13 +316,13 @@ lfq_kernel(const uint16_t* __restrict__ x, int64_t T, const float* __restrict__ 
 template <int N, int RK>
 hipError_t launch_n(const uint16_t* x, int64_t T, const float* Zpart, int S, const uint16_t* PH,
                     const uint16_t* PL, bool fw, uint8_t* tiles, float* s_a, float* dbg,
-                    hipStream_t s) {
+                    float qmax, hipStream_t s) {
   const float norm = static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(1 << N)));
   const dim3 grid(static_cast<unsigned>((T + kTok - 1) / kTok));
 #define RW4_LFQ(F, G)                                                                           \
   if (fw == F && (dbg != nullptr) == G) {                                                       \
     hipLaunchKernelGGL((lfq_kernel<N, RK, F, G>), grid, dim3(kThreads), 0, s, x, T, Zpart, S,   \
-                       PH, PL, tiles, s_a, dbg, norm);                                          \
+                       PH, PL, tiles, s_a, dbg, norm, qmax);                                    \
     return hipGetLastError();                                                                   \
   }
   RW4_LFQ(true, false) RW4_LFQ(true, true) RW4_LFQ(false, false) RW4_LFQ(false, true)
@@ -332,13 +333,13 @@ hipError_t launch_n(const uint16_t* x, int64_t T, const float* Zpart, int S, con
 template <int RK>
 hipError_t launch_rk(int n, const uint16_t* x, int64_t T, const float* Zpart, int S,
                      const uint16_t* PH, const uint16_t* PL, bool fw, uint8_t* tiles, float* s_a,
-                     float* dbg, hipStream_t s) {
+                     float* dbg, float qmax, hipStream_t s) {
   switch (n) {
-    case 8: return launch_n<8, RK>(x, T, Zpart, S, PH, PL, fw, tiles, s_a, dbg, s);
-    case 9: return launch_n<9, RK>(x, T, Zpart, S, PH, PL, fw, tiles, s_a, dbg, s);
-    case 10: return launch_n<10, RK>(x, T, Zpart, S, PH, PL, fw, tiles, s_a, dbg, s);
-    case 11: return launch_n<11, RK>(x, T, Zpart, S, PH, PL, fw, tiles, s_a, dbg, s);
-    case 12: return launch_n<12, RK>(x, T, Zpart, S, PH, PL, fw, tiles, s_a, dbg, s);
+    case 8: return launch_n<8, RK>(x, T, Zpart, S, PH, PL, fw, tiles, s_a, dbg, qmax, s);
+    case 9: return launch_n<9, RK>(x, T, Zpart, S, PH, PL, fw, tiles, s_a, dbg, qmax, s);
+    case 10: return launch_n<10, RK>(x, T, Zpart, S, PH, PL, fw, tiles, s_a, dbg, qmax, s);
+    case 11: return launch_n<11, RK>(x, T, Zpart, S, PH, PL, fw, tiles, s_a, dbg, qmax, s);
+    case 12: return launch_n<12, RK>(x, T, Zpart, S, PH, PL, fw, tiles, s_a, dbg, qmax, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -354,9 +355,11 @@ bool lfq_supported(int64_t D, int64_t r) {
 
 hipError_t launch_lift_fwht_quant(const uint16_t* x, int64_t T, int64_t D, int64_t r,
                                   const void* basis, const float* Zpart, bool do_fwht,
-                                  uint8_t* tiles, float* s_a, float* dbg, hipStream_t s) {
+                                  uint8_t* tiles, float* s_a, float* dbg, hipStream_t s,
+                                  int bits) {
   if (T == 0) return hipSuccess;
-  if (!lfq_supported(D, r)) return hipErrorInvalidValue;
+  if (!lfq_supported(D, r) || bits < 2 || bits > 4) return hipErrorInvalidValue;
+  const float qmax = static_cast<float>((1 << (bits - 1)) - 1);
   const AlignBasis a = align_basis(basis, D, r, true);
   // without the transform the lift operand is Q itself
   const uint16_t* PH = do_fwht ? a.PH : a.QH;
@@ -364,8 +367,8 @@ hipError_t launch_lift_fwht_quant(const uint16_t* x, int64_t T, int64_t D, int64
   const int S = align_parts_count(D);
   int n = 0;
   while ((int64_t(1) << n) < D) ++n;
-  if (a.RK == 32) return launch_rk<32>(n, x, T, Zpart, S, PH, PL, do_fwht, tiles, s_a, dbg, s);
-  if (a.RK == 64) return launch_rk<64>(n, x, T, Zpart, S, PH, PL, do_fwht, tiles, s_a, dbg, s);
+  if (a.RK == 32) return launch_rk<32>(n, x, T, Zpart, S, PH, PL, do_fwht, tiles, s_a, dbg, qmax, s);
+  if (a.RK == 64) return launch_rk<64>(n, x, T, Zpart, S, PH, PL, do_fwht, tiles, s_a, dbg, qmax, s);
   return hipErrorInvalidValue;
 }
 

@@ -11,9 +11,12 @@
 // in registers and writes them back. The 1/sqrt(D) scale is one multiply after
 // the last stage.
 //
-// Quantization ("Infra Quant II", QuaRot Method; SpinQuant MOTIVATION):
-// per row, step = fl32(absmax / 7), code = clamp(rint(fl32(v / step)), -8, 7),
-// packed two per byte (element 2j in the low nibble).
+// Quantization ("Infra Quant II", QuaRot Method; SpinQuant MOTIVATION): for
+// b-bit codes (b = 4, or 3 and 2 for the lower settings of the ReSpinQuant
+// notes' experiments), per row step = fl32(absmax / (2^(b-1) - 1)) and
+// code = clamp(rint(fl32(v / step)), -2^(b-1), 2^(b-1) - 1); symmetric absmax
+// keeps every code in [-(2^(b-1) - 1), 2^(b-1) - 1]. Codes are stored as INT4
+// nibbles (element 2j in the low nibble) or FP6 tile fields, whatever b.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -229,7 +232,7 @@ template <int N, int E, int IN, bool FW, bool QOUT, bool TILED>
 __global__ void __launch_bounds__(1024)
 row_kernel(const void* __restrict__ x, int64_t ldx, int64_t T, float* __restrict__ yf,
            uint8_t* __restrict__ codes, float* __restrict__ scales, float* __restrict__ dbg,
-           float norm) {
+           float norm, float qmax) {
   constexpr int D = 1 << N;
   constexpr int EPT = 1 << E;
   constexpr int P = D >> E;                         // threads per row
@@ -287,7 +290,7 @@ row_kernel(const void* __restrict__ x, int64_t ldx, int64_t T, float* __restrict
       for (int i = 1; i < WPR; ++i) m = fmaxf(m, red[rl * WPR + i]);
     }
     if (!active) return;
-    const float s = m / 7.0f;
+    const float s = m / qmax;
     if (t == 0) scales[row] = s;
     if constexpr (TILED)
       store_tiled<EPT>(codes, row, static_cast<int64_t>(t) * EPT, D, v, s);
@@ -299,7 +302,7 @@ row_kernel(const void* __restrict__ x, int64_t ldx, int64_t T, float* __restrict
 
 template <int N, int IN, bool FW, bool QOUT, bool TILED>
 hipError_t launch_row_n(const void* x, int64_t ldx, int64_t T, float* yf, uint8_t* codes,
-                        float* scales, float* dbg, hipStream_t s) {
+                        float* scales, float* dbg, float qmax, hipStream_t s) {
   constexpr int E = N >= 15 ? 5 : (N < 4 ? N : 4);
   constexpr int P = (1 << N) >> E;
   constexpr int ROWS = P >= kRowThreads ? 1 : kRowThreads / P;
@@ -308,16 +311,16 @@ hipError_t launch_row_n(const void* x, int64_t ldx, int64_t T, float* yf, uint8_
   if constexpr (TILED && (1 << E) < 16) return hipErrorInvalidValue;
   hipLaunchKernelGGL((row_kernel<N, E, IN, FW, QOUT, TILED && (1 << E) >= 16>),
                      dim3(static_cast<unsigned>(blocks)),
-                     dim3(P * ROWS), 0, s, x, ldx, T, yf, codes, scales, dbg, norm);
+                     dim3(P * ROWS), 0, s, x, ldx, T, yf, codes, scales, dbg, norm, qmax);
   return hipGetLastError();
 }
 
 template <int IN, bool FW, bool QOUT, bool TILED>
 hipError_t dispatch_n(int n, const void* x, int64_t ldx, int64_t T, float* yf, uint8_t* codes,
-                      float* scales, float* dbg, hipStream_t s) {
+                      float* scales, float* dbg, float qmax, hipStream_t s) {
   switch (n) {
 #define RW4_CASE(k) \
-  case k: return launch_row_n<k, IN, FW, QOUT, TILED>(x, ldx, T, yf, codes, scales, dbg, s);
+  case k: return launch_row_n<k, IN, FW, QOUT, TILED>(x, ldx, T, yf, codes, scales, dbg, qmax, s);
     RW4_CASE(1) RW4_CASE(2) RW4_CASE(3) RW4_CASE(4) RW4_CASE(5) RW4_CASE(6) RW4_CASE(7)
     RW4_CASE(8) RW4_CASE(9) RW4_CASE(10) RW4_CASE(11) RW4_CASE(12) RW4_CASE(13) RW4_CASE(14)
     RW4_CASE(15)
@@ -330,7 +333,7 @@ hipError_t dispatch_n(int n, const void* x, int64_t ldx, int64_t T, float* yf, u
 template <int IN>
 __global__ void __launch_bounds__(256)
 quant_generic_kernel(const void* __restrict__ x, int64_t ldx, int64_t D,
-                     uint8_t* __restrict__ codes, float* __restrict__ scales) {
+                     uint8_t* __restrict__ codes, float* __restrict__ scales, float qmax) {
   __shared__ float red[4];
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x;
@@ -344,7 +347,7 @@ quant_generic_kernel(const void* __restrict__ x, int64_t ldx, int64_t D,
   if ((tid & 63) == 0) red[tid >> 6] = m;
   __syncthreads();
   m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float s = m / 7.0f;
+  const float s = m / qmax;
   if (tid == 0) scales[row] = s;
   for (int64_t j = tid; j < D / 2; j += 256) {
     const int q0 = s > 0.0f ? quant4(val(2 * j), s) : 0;
@@ -357,15 +360,17 @@ quant_generic_kernel(const void* __restrict__ x, int64_t ldx, int64_t D,
 
 hipError_t launch_row(const void* x, int in_mode, int64_t ldx, int64_t T, int64_t D, bool do_fwht,
                       float* yf, uint8_t* codes, bool tiled, float* scales, float* dbg,
-                      hipStream_t s) {
+                      hipStream_t s, int bits) {
   if (T == 0) return hipSuccess;
+  if (bits < 2 || bits > 4) return hipErrorInvalidValue;
+  const float qmax = static_cast<float>((1 << (bits - 1)) - 1);
   int n = 0;
   while ((int64_t(1) << n) < D) ++n;
   const bool q = codes != nullptr;
   if (tiled && (!q || D < 64)) return hipErrorInvalidValue;
 #define RW4_SEL(INM, FW, Q, TL) \
   if (in_mode == INM && do_fwht == FW && q == Q && tiled == TL) \
-    return dispatch_n<INM, FW, Q, TL>(n, x, ldx, T, yf, codes, scales, dbg, s);
+    return dispatch_n<INM, FW, Q, TL>(n, x, ldx, T, yf, codes, scales, dbg, qmax, s);
   RW4_SEL(IN_BF16, true, true, false) RW4_SEL(IN_BF16, true, false, false)
   RW4_SEL(IN_F32, true, true, false) RW4_SEL(IN_F32, true, false, false)
   RW4_SEL(IN_SWIGLU, true, true, false) RW4_SEL(IN_SWIGLU, false, true, false)
@@ -378,14 +383,16 @@ hipError_t launch_row(const void* x, int in_mode, int64_t ldx, int64_t T, int64_
 }
 
 hipError_t launch_quant_generic(const void* x, int in_mode, int64_t ldx, int64_t T, int64_t D,
-                                uint8_t* codes, float* scales, hipStream_t s) {
+                                uint8_t* codes, float* scales, hipStream_t s, int bits) {
   if (T == 0) return hipSuccess;
+  if (bits < 2 || bits > 4) return hipErrorInvalidValue;
+  const float qmax = static_cast<float>((1 << (bits - 1)) - 1);
   if (in_mode == IN_F32)
     hipLaunchKernelGGL(quant_generic_kernel<IN_F32>, dim3(static_cast<unsigned>(T)), dim3(256), 0,
-                       s, x, ldx, D, codes, scales);
+                       s, x, ldx, D, codes, scales, qmax);
   else
     hipLaunchKernelGGL(quant_generic_kernel<IN_BF16>, dim3(static_cast<unsigned>(T)), dim3(256), 0,
-                       s, x, ldx, D, codes, scales);
+                       s, x, ldx, D, codes, scales, qmax);
   return hipGetLastError();
 }
 

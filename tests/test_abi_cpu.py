@@ -22,7 +22,7 @@ def _declared():
 def test_library_built_and_loads():
     assert os.path.exists(rw.library_path), "build the HIP library first"
     L = rw.lib()
-    assert L.rw4_abi_version() == 4
+    assert L.rw4_abi_version() == 5
 
 
 def test_exports_every_declared_symbol():
@@ -221,8 +221,22 @@ def test_rotated_linear_prepared_validation():
     assert _rlp(T=0, x=NUL, w=NUL, sw=NUL, y=NUL, basis=NUL) == 0
 
 
+def test_quant_sym_validation():
+    L = rw.lib()
+    for bits in (0, 1, 5, 8):
+        assert L.quant_act_sym(A, 0, B, C, 4, 64, bits, NUL) == INV
+    assert L.quant_act_sym(A, 0, B, C, 4, 63, 3, NUL) == UNS
+    assert L.quant_act_sym(A, 0, B, NUL, 4, 64, 3, NUL) == INV
+    assert L.quant_act_sym(ODD, 0, B, C, 4, 64, 3, NUL) == MIS
+    assert L.quant_act_sym(NUL, 0, NUL, NUL, 0, 64, 2, NUL) == 0
+
+
 def test_rotated_linear_validation():
     assert _rl(flags=8) == INV                     # unknown flag
+    assert _rl(flags=3 | (1 << 8)) == INV          # 1-bit codes
+    assert _rl(flags=3 | (5 << 8)) == INV          # 5-bit codes
+    assert _rl(flags=3 | (1 << 12)) == INV         # unknown flag above the bit field
+    assert _rl(T=0, flags=3 | (3 << 8)) == 0       # 3-bit codes accepted
     assert _rl(flags=1 | 4) == INV                 # align + swiglu
     assert _rl(D=48) == UNS                        # not a power of two
     assert _rl(D=32, ldx=32, flags=0) == UNS       # below the 64-code tile width

@@ -61,6 +61,18 @@ def test_quant_act_int4(rw, T, D, dt):
     np.testing.assert_array_equal(host(codes), O.pack_int4(q))
 
 
+@pytest.mark.parametrize("T,D", [(3, 64), (300, 4096), (5, 1000), (17, 16384)])
+@pytest.mark.parametrize("bits", [2, 3])
+def test_quant_act_sym(rw, T, D, bits):
+    say(f"quant_act_sym T={T} D={D} bits={bits}")
+    x = _quant_input(T, D, seed=T * 5 + D + bits)
+    codes, scales = rw.quant_act_sym(dev(x), bits)
+    _sync()
+    q, s = O.quant_sym(x, bits)
+    np.testing.assert_array_equal(host(scales), s)
+    np.testing.assert_array_equal(host(codes), O.pack_int4(q))
+
+
 def test_quant_near_half_integers(rw):
     """Values whose quotient by the step sits within a few ulps of k + 1/2, the
     case where the fp32 quotient's rounding decides the code (R6)."""
@@ -294,12 +306,12 @@ def test_w4a4_gemm_tiles_extremes(rw):
 
 
 # ---------------------------------------------------------------- weight prep and the unit
-def _prep(rw, Wf, rotate):
-    tiles, s_w, codes, src = rw.prep_weight(dev(Wf), rotate)
+def _prep(rw, Wf, rotate, bits=4):
+    tiles, s_w, codes, src = rw.prep_weight(dev(Wf), rotate, bits)
     src_h = host(src)
     if rotate:
         assert normwise(src_h, O.fwht(Wf)) <= FP32_TOL
-    q, s = O.quant_int4(src_h)
+    q, s = O.quant_sym(src_h, bits)
     np.testing.assert_array_equal(host(s_w), s)
     np.testing.assert_array_equal(host(codes), O.pack_int4(q))
     np.testing.assert_array_equal(host(tiles), F.tile(q))
@@ -325,7 +337,8 @@ def _check_unit(rw, xb, Q, M, flags, codes_w, s_w, qw, sw_h, rows=None):
     ref_pre = O.prequant(O.bf16_to_f64(xb[sel]), flags, Q, M)
     assert normwise(pre[sel], ref_pre) <= FP32_TOL
     # 2. codes and scales: bit-exact on the GPU's own fp32 values
-    q, s = O.quant_int4(pre[sel])
+    bits = (flags >> 8) & 0xF or 4
+    q, s = O.quant_sym(pre[sel], bits)
     np.testing.assert_array_equal(sa_g[sel], s)
     np.testing.assert_array_equal(codes_g[sel], q)
     # 3. GEMM + epilogue on those codes
@@ -333,7 +346,7 @@ def _check_unit(rw, xb, Q, M, flags, codes_w, s_w, qw, sw_h, rows=None):
     nbad, worst = bf16_rel(y[sel], ref_y)
     assert nbad == 0, worst
     # 4. end to end against the oracle's own chain: rare code flips only
-    q_own, _ = O.quant_int4(ref_pre.astype(np.float32))
+    q_own, _ = O.quant_sym(ref_pre.astype(np.float32), bits)
     flips = float((q_own != q).mean())
     say(f"   end-to-end code flips vs float64 chain: {flips:.2e}")
     assert flips < 1e-3
@@ -410,6 +423,21 @@ def test_rotated_linear_prepared(rw, T, D, N, r, flags):
     np.testing.assert_array_equal(host(s2), host(s1))
     # rows past T of the padded tiles are not written by either call
     np.testing.assert_array_equal(F.untile(host(t2), T, D), F.untile(host(t1), T, D))
+
+
+# lower code widths [RSQ 实验: W3A3]: 3-bit weights and activations through the
+# fused prologue (D = 4096), the tiny workload's shape, the unfused path
+# (D = 8192), and 2-bit activations on the transform-only path
+@pytest.mark.parametrize("T,D,N,r,flags,bits", [(64, 256, 256, 8, 3, 3), (300, 4096, 384, 32, 3, 3),
+                                                (40, 8192, 96, 64, 3, 3), (50, 1024, 64, 0, 2, 2)])
+def test_rotated_linear_low_bits(rw, T, D, N, r, flags, bits):
+    say(f"rotated_linear W{bits}A{bits} T={T} D={D} N={N} r={r} flags={flags}")
+    xb = W.gen_x(T + D + bits, T, D, 4, 30.0)
+    Q, M = W.gen_basis(T + r, D, r) if flags & 1 else (None, None)
+    Wf = W.gen_weight(N + bits, N, D, 0.02)
+    codes_w, s_w, qw, sw_h = _prep(rw, Wf, bool(flags & 2), bits)
+    assert np.abs(qw).max() == 2 ** (bits - 1) - 1
+    _check_unit(rw, xb, Q, M, flags | rw.RW4_ABITS(bits), codes_w, s_w, qw, sw_h)
 
 
 def test_rotated_linear_strided_input(rw):

@@ -179,23 +179,37 @@ def _nearest_grid_brute(qf: np.ndarray, lo: int, hi: int) -> np.ndarray:
     return out
 
 
-def test_quant_brute_force_and_bounds():
-    rng = np.random.default_rng(21)
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_quant_brute_force_and_bounds(bits):
+    rng = np.random.default_rng(21 + bits)
     v = (rng.standard_normal((6, 48)) * rng.uniform(0.01, 100, (6, 1))).astype(np.float32)
     v[2, 5] = 0.0
-    q, s = O.quant_int4(v)
+    q, s = O.quant_sym(v, bits) if bits != 4 else O.quant_int4(v)
+    qmax, qmin = 2 ** (bits - 1) - 1, -2 ** (bits - 1)
     # brute-force step and nearest grid point, in the same fp32 precision
     for t in range(6):
         a = np.float32(max(abs(float(e)) for e in v[t]))
-        st = np.float32(a / np.float32(7))
+        st = np.float32(a / np.float32(qmax))
         assert s[t] == st
         qf = np.array([np.float32(e / st) for e in v[t]], np.float32)
-        np.testing.assert_array_equal(q[t], _nearest_grid_brute(qf, -8, 7))
-        # RTN bound |v - s q| <= s/2 (+ fp32 rounding of the quotient), max |q| = 7
+        np.testing.assert_array_equal(q[t], _nearest_grid_brute(qf, qmin, qmax))
+        # RTN bound |v - s q| <= s/2 (+ fp32 rounding of the quotient), max |q| = qmax
         err = np.abs(v[t].astype(np.float64) - float(st) * q[t])
         assert np.all(err <= float(st) * (0.5 + 8 * 2.0 ** -24))
-        assert np.abs(q[t]).max() == 7
-    assert q.min() >= -8 and q.max() <= 7
+        assert np.abs(q[t]).max() == qmax
+    assert q.min() >= qmin and q.max() <= qmax
+
+
+def test_quant_low_bit_closed_forms():
+    # the page's outlier vector on the 3-bit grid: step 20/3, codes [3, 0, 0, 0];
+    # after the rotation the flat [10, 10, 10, 10] maps to [3, 3, 3, 3]
+    q, s = O.quant_sym(np.array([[20.0, 0, 0, 0], [10.0, 10, 10, 10]], np.float32), 3)
+    assert s[0] == np.float32(20.0) / np.float32(3) and s[1] == np.float32(10.0) / np.float32(3)
+    np.testing.assert_array_equal(q, [[3, 0, 0, 0], [3, 3, 3, 3]])
+    # 2-bit grid: step = absmax, codes in {-1, 0, 1}; 0.5 ties to 0
+    q, s = O.quant_sym(np.array([[4.0, 1.9, 2.0, 2.1, -3.0, -2.0]], np.float32), 2)
+    assert s[0] == 4.0
+    np.testing.assert_array_equal(q[0], [1, 0, 0, 1, -1, 0])
 
 
 def test_quant_zero_row_and_bits():
