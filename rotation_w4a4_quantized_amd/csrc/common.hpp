@@ -60,6 +60,81 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
+// ----------------------------------------------------------------------------
+// Cross-lane butterflies of the register-resident Walsh-Hadamard transforms.
+// A butterfly on index bit b pairs values whose indices differ only in b; when
+// b is a lane bit the partner value sits in another lane of the wave.
+// butterfly with the lane whose index differs in one bit, partner read by a
+// DPP move: the lower lane gets a + b, the upper b' - a' = a - b
+template <int CTRL>
+__device__ __forceinline__ float dpp_bfly(float v, float sgn) {
+  const float p = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+  return fmaf(sgn, v, p);
+}
+// lane bit 2 inside a 16-lane row: banks 0 and 2 (bit clear) read lane + 4
+// (row_ror:12), banks 1 and 3 read lane - 4 (row_ror:4)
+__device__ __forceinline__ float bfly_x4(float v, float sgn) {
+  int p = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x12C, 0xF, 0x5, true);
+  p = __builtin_amdgcn_update_dpp(p, __float_as_int(v), 0x124, 0xF, 0xA, false);
+  return fmaf(sgn, v, __int_as_float(p));
+}
+// lane bit 4 (permlane16 swap) or 5 (permlane32 swap) for two values a, b at
+// once: the swap moves the partner half-row of a next to a's own half and b's
+// lower half next to b's upper half, the butterfly runs in-lane, and a second
+// swap restores the layout
+template <int BIT>
+__device__ __forceinline__ void bfly_swap(float& a, float& b) {
+  const unsigned ua = __float_as_uint(a), ub = __float_as_uint(b);
+  auto p = BIT == 4 ? __builtin_amdgcn_permlane16_swap(ua, ub, false, false)
+                    : __builtin_amdgcn_permlane32_swap(ua, ub, false, false);
+  const float A = __uint_as_float(p[0]), B = __uint_as_float(p[1]);
+  const unsigned us = __float_as_uint(A + B), ud = __float_as_uint(A - B);
+  auto q = BIT == 4 ? __builtin_amdgcn_permlane16_swap(us, ud, false, false)
+                    : __builtin_amdgcn_permlane32_swap(us, ud, false, false);
+  a = __uint_as_float(q[0]);
+  b = __uint_as_float(q[1]);
+}
+
+// all butterflies of the six lane bits of a wave, for NV values per lane
+// (sg1.. are +1 on lanes whose bit is clear, -1 where it is set); one lane bit
+// at a time over every value, so that independent moves issue back to back
+template <int NV, int LB>
+__device__ __forceinline__ void lane_butterflies(float (&v)[NV], int lane) {
+  static_assert(NV % 32 == 0 || LB <= 4, "swap butterflies pair values j and j + 16 of 32");
+  const float sg1 = (lane & 1) ? -1.0f : 1.0f;
+  const float sg2 = (lane & 2) ? -1.0f : 1.0f;
+  const float sg4 = (lane & 4) ? -1.0f : 1.0f;
+  const float sg8 = (lane & 8) ? -1.0f : 1.0f;
+  if constexpr (LB > 0) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) v[j] = dpp_bfly<0xB1>(v[j], sg1);  // quad_perm 1,0,3,2
+  }
+  if constexpr (LB > 1) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) v[j] = dpp_bfly<0x4E>(v[j], sg2);  // quad_perm 2,3,0,1
+  }
+  if constexpr (LB > 2) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) v[j] = bfly_x4(v[j], sg4);
+  }
+  if constexpr (LB > 3) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) v[j] = dpp_bfly<0x128>(v[j], sg8);  // row_ror:8
+  }
+  if constexpr (LB > 4) {
+#pragma unroll
+    for (int j0 = 0; j0 < NV; j0 += 32)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) bfly_swap<4>(v[j0 + j], v[j0 + j + 16]);
+  }
+  if constexpr (LB > 5) {
+#pragma unroll
+    for (int j0 = 0; j0 < NV; j0 += 32)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) bfly_swap<5>(v[j0 + j], v[j0 + j + 16]);
+  }
+}
+
 // symmetric absmax INT4 code of v with step s (s > 0): clamp(rint(v / s), -8, 7).
 // The quotient is the correctly rounded fp32 division, rounded half-to-even.
 __device__ __forceinline__ int quant4(float v, float s) {

@@ -48,37 +48,6 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// butterfly with the lane whose index differs in one bit, partner read by a
-// DPP move: the lower lane gets a + b, the upper b' - a' = a - b
-template <int CTRL>
-__device__ __forceinline__ float dpp_bfly(float v, float sgn) {
-  const float p = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
-  return fmaf(sgn, v, p);
-}
-// lane bit 2 inside a 16-lane row: banks 0 and 2 (bit clear) read lane + 4
-// (row_ror:12), banks 1 and 3 read lane - 4 (row_ror:4)
-__device__ __forceinline__ float bfly_x4(float v, float sgn) {
-  int p = __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x12C, 0xF, 0x5, true);
-  p = __builtin_amdgcn_update_dpp(p, __float_as_int(v), 0x124, 0xF, 0xA, false);
-  return fmaf(sgn, v, __int_as_float(p));
-}
-// lane bit 4 (permlane16 swap) or 5 (permlane32 swap) for two values a, b at
-// once: the swap moves the partner half-row of a next to a's own half and b's
-// lower half next to b's upper half, the butterfly runs in-lane, and a second
-// swap restores the layout
-template <int BIT>
-__device__ __forceinline__ void bfly_swap(float& a, float& b) {
-  const unsigned ua = __float_as_uint(a), ub = __float_as_uint(b);
-  auto p = BIT == 4 ? __builtin_amdgcn_permlane16_swap(ua, ub, false, false)
-                    : __builtin_amdgcn_permlane32_swap(ua, ub, false, false);
-  const float A = __uint_as_float(p[0]), B = __uint_as_float(p[1]);
-  const unsigned us = __float_as_uint(A + B), ud = __float_as_uint(A - B);
-  auto q = BIT == 4 ? __builtin_amdgcn_permlane16_swap(us, ud, false, false)
-                    : __builtin_amdgcn_permlane32_swap(us, ud, false, false);
-  a = __uint_as_float(q[0]);
-  b = __uint_as_float(q[1]);
-}
-
 template <int N, int RK, bool FW, bool DBG>
 __global__ void __launch_bounds__(kThreads)
 lfq_kernel(const uint16_t* __restrict__ x, int64_t T, const float* __restrict__ Zpart, int S,

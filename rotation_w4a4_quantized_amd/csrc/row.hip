@@ -300,6 +300,138 @@ row_kernel(const void* __restrict__ x, int64_t ldx, int64_t T, float* __restrict
   }
 }
 
+// ---------------------------------------------------------------- one wave per row
+// For D = 2^N with N in [11, 13] a row fits one wave's registers, and every
+// wave streams its own row: no LDS, no barriers, many rows' loads in flight
+// per CU. Two register layouts:
+//   * coalesced (fp32 or packed-code output): lane L holds the 4 consecutive
+//     values 256 c + 4 L + e (c < D / 256), so each load and store
+//     instruction of the wave covers one contiguous 1 KiB (fp32) piece;
+//   * tiled output: lane L holds 16 consecutive values 1024 k + 16 L + e, the
+//     unit of a tile field group.
+// Either way some index bits are register bits (butterflies in registers)
+// and six are lane bits (the cross-lane moves of common.hpp); the absmax is a
+// wave reduction.
+constexpr int kWaveRows = 4;                        // rows (waves) per workgroup
+
+template <int IN, int G>
+__device__ __forceinline__ void load_group(float (&q)[G], const void* x, int64_t off, int D) {
+  static_assert(G == 4 || G == 16, "groups of 4 or 16 values");
+  if constexpr (IN == IN_F32) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(x) + off);
+#pragma unroll
+    for (int i = 0; i < G / 4; ++i) {
+      const float4 a = p[i];
+      q[4 * i] = a.x; q[4 * i + 1] = a.y; q[4 * i + 2] = a.z; q[4 * i + 3] = a.w;
+    }
+  } else {
+    auto unpack = [](const uint16_t* p, float (&o)[G]) {
+#pragma unroll
+      for (int i = 0; i < G / 4; ++i) {
+        const uint2 a = reinterpret_cast<const uint2*>(p)[i];
+        o[4 * i] = bf16lo(a.x); o[4 * i + 1] = bf16hi(a.x);
+        o[4 * i + 2] = bf16lo(a.y); o[4 * i + 3] = bf16hi(a.y);
+      }
+    };
+    const uint16_t* p = static_cast<const uint16_t*>(x) + off;
+    unpack(p, q);
+    if constexpr (IN == IN_SWIGLU) {
+      // gate = first D values of the row, up = next D values; fp32 SiLU(g) * u
+      float u[G];
+      unpack(p + D, u);
+#pragma unroll
+      for (int i = 0; i < G; ++i) q[i] = q[i] / (1.0f + expf(-q[i])) * u[i];
+    }
+  }
+}
+
+template <int N, int IN, bool FW, bool QOUT, bool TILED>
+__global__ void __launch_bounds__(64 * kWaveRows)
+rowwave_kernel(const void* __restrict__ x, int64_t ldx, int64_t T, float* __restrict__ yf,
+               uint8_t* __restrict__ codes, float* __restrict__ scales, float* __restrict__ dbg,
+               float norm, float qmax) {
+  constexpr int D = 1 << N;
+  constexpr int G = TILED ? 16 : 4;                 // consecutive values per group
+  constexpr int NG = D / (64 * G);                  // groups per lane
+  constexpr int NV = D / 64;
+  static_assert(N >= 11 && N <= 13, "D in [2048, 8192]");
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  int64_t blk = blockIdx.x;
+  if (TILED && (gridDim.x & 7) == 0) blk = (blk & 7) * (gridDim.x >> 3) + (blk >> 3);
+  const int64_t row = blk * kWaveRows + wave;
+  const bool active = row < T;
+  const int64_t rowoff = (active ? row : T - 1) * ldx;  // rows past T re-read the last row
+  auto col = [&](int c) { return static_cast<int64_t>(64 * G) * c + G * lane; };
+
+  float v[NV];
+#pragma unroll
+  for (int c = 0; c < NG; ++c) {
+    float q[G];
+    load_group<IN, G>(q, x, rowoff + col(c), D);
+#pragma unroll
+    for (int e = 0; e < G; ++e) v[G * c + e] = active ? q[e] : 0.0f;
+  }
+  if constexpr (FW) {
+    // register bits: butterflies on v[j], v[j + h]
+#pragma unroll
+    for (int h = 1; h < NV; h <<= 1)
+#pragma unroll
+      for (int j = 0; j < NV; ++j)
+        if ((j & h) == 0) {
+          const float a = v[j], b = v[j + h];
+          v[j] = a + b;
+          v[j + h] = a - b;
+        }
+    lane_butterflies<NV, 6>(v, lane);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) v[j] *= norm;
+  }
+  auto put_f32 = [&](float* base) {
+#pragma unroll
+    for (int c = 0; c < NG; ++c) {
+      float q[G];
+#pragma unroll
+      for (int e = 0; e < G; ++e) q[e] = v[G * c + e];
+      store_f32<G>(base + row * D + col(c), q);
+    }
+  };
+  if constexpr (!QOUT) {
+    if (active) put_f32(yf);
+  } else {
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) m = fmaxf(m, fabsf(v[j]));
+    m = wave_max(m);
+    if (!active) return;
+    const float st = m / qmax;
+    if (lane == 0) scales[row] = st;
+    const RowQuant rq(st);
+    // codes per group of G values from the reciprocal, checked once per group
+    // (RowQuant::fast_codes); a group with a value too close to a half-integer
+    // takes the exact quotient
+#pragma unroll
+    for (int c = 0; c < NG; ++c) {
+      float u[G], f[G];
+#pragma unroll
+      for (int e = 0; e < G; ++e) u[e] = v[G * c + e];
+      if (!rq.fast_codes(u, f)) {
+#pragma unroll
+        for (int e = 0; e < G; ++e) f[e] = rq.code(u[e]);
+      }
+      if constexpr (TILED) {
+        store_fields16(codes, row, col(c), D, pack_fp6_16(f));
+      } else {
+        uint32_t w = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w |= nib(static_cast<int>(f[e])) << (4 * e);
+        *reinterpret_cast<uint16_t*>(codes + row * (D / 2) + col(c) / 2) = static_cast<uint16_t>(w);
+      }
+    }
+    if (dbg) put_f32(dbg);
+  }
+}
+
 template <int N, int IN, bool FW, bool QOUT, bool TILED>
 hipError_t launch_row_n(const void* x, int64_t ldx, int64_t T, float* yf, uint8_t* codes,
                         float* scales, float* dbg, float qmax, hipStream_t s) {
@@ -307,6 +439,12 @@ hipError_t launch_row_n(const void* x, int64_t ldx, int64_t T, float* yf, uint8_
   constexpr int P = (1 << N) >> E;
   constexpr int ROWS = P >= kRowThreads ? 1 : kRowThreads / P;
   const float norm = static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(1 << N)));
+  if constexpr (N >= 11 && N <= 13) {
+    const int64_t wblocks = (T + kWaveRows - 1) / kWaveRows;
+    hipLaunchKernelGGL((rowwave_kernel<N, IN, FW, QOUT, TILED>), dim3(static_cast<unsigned>(wblocks)),
+                       dim3(64 * kWaveRows), 0, s, x, ldx, T, yf, codes, scales, dbg, norm, qmax);
+    return hipGetLastError();
+  }
   const int64_t blocks = (T + ROWS - 1) / ROWS;
   if constexpr (TILED && (1 << E) < 16) return hipErrorInvalidValue;
   hipLaunchKernelGGL((row_kernel<N, E, IN, FW, QOUT, TILED && (1 << E) >= 16>),

@@ -385,7 +385,8 @@ def test_rotated_linear_config4_sampled(rw):
 
 @pytest.mark.parametrize("T,D,N,flags", [(77, 512, 200, 0), (77, 512, 200, 2), (50, 256, 64, 4 | 2),
                                          (33, 1024, 96, 4), (130, 2048, 260, 1),
-                                         (1, 4096, 4096, 3)])
+                                         (1, 4096, 4096, 3), (21, 4096, 64, 4 | 2),
+                                         (6, 8192, 64, 4 | 2), (9, 2048, 64, 2)])
 def test_rotated_linear_flags(rw, T, D, N, flags):
     say(f"rotated_linear T={T} D={D} N={N} flags={flags}")
     width = 2 * D if flags & 4 else D
