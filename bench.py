@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 PEAK_I8_TOPS = 5000.0          # MI355X dense int8 MFMA, TOP/s
 PEAK_FP6_TFLOPS = 10100.0      # MI355X dense FP6/FP4 MFMA, TFLOP/s (the GEMM's operand type)
 PEAK_HBM_GBS = 8000.0
+PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 vector, TFLOP/s
 METRIC = "rotated W4A4 linear tokens/s; GEMM int8-MFMA TOPS and align/quant GB/s vs peak"
 GEMM_SRC = os.path.join(ROOT, "rotation_w4a4_quantized_amd", "csrc", "gemm6.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w4a4_gemm_D4096_T2048_traffic.json")
@@ -199,7 +200,11 @@ def main():
                                                     out=s0["y"], workspace=uws))
     basis_ms = timed(lambda: rw.respin_prepare_basis(Qg, Mg, basis=s0["basis"]))
     aws = torch.empty((rw.respin_align_workspace_size(T, D, r),), dtype=torch.uint8, device=dev)
-    align_ms = timed(lambda: rw.respin_align(s0["x"], Qg, Mg, out=tmp, workspace=aws))
+    align_unprep_ms = timed(lambda: rw.respin_align(s0["x"], Qg, Mg, out=tmp, workspace=aws))
+    pws = torch.empty((rw.respin_align_prepared_workspace_size(T, D, r),), dtype=torch.uint8,
+                      device=dev)
+    align_ms = timed(lambda: rw.respin_align_prepared(s0["x"], s0["basis"], r, out=tmp,
+                                                      workspace=pws))
     fwht_ms = timed(lambda: rw.fwht(tmp, out=tmp))
     quant_ms = timed(lambda: rw.quant_act_int4(tmp, codes_t, sa_t))
 
@@ -209,6 +214,19 @@ def main():
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
+
+    # standalone stages against HBM: algorithmic bytes per call (x in, result
+    # out, plus the layer's basis for the alignment) over the measured time
+    stage_bytes = {"align": T * 6 * D + 4 * D * r + 4 * r * r, "fwht": T * 8 * D,
+                   "quant": T * (4 * D + D // 2 + 4)}
+    stage_ms = {"align": align_ms, "fwht": fwht_ms, "quant": quant_ms}
+    bw = {}
+    for k, nbytes in stage_bytes.items():
+        gbs = nbytes / (stage_ms[k] * 1e-3) / 1e9
+        bw[k] = {"bytes": nbytes, "GB/s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS}
+    align_flop = T * (4 * D * r + 2 * r * r)
+    bw["align"]["TFLOP/s"] = align_flop / (align_ms * 1e-3) / 1e12
+    bw["align"]["frac_fp32"] = bw["align"]["TFLOP/s"] / PEAK_FP32_TFLOPS
 
     traffic = traffic_bytes()
     out = {
@@ -236,7 +254,9 @@ def main():
         "stages_us": {"step_events": step_ms_ev * 1e3, "align": align_ms * 1e3,
                       "fwht": fwht_ms * 1e3, "quant": quant_ms * 1e3, "gemm": gemm_ms * 1e3,
                       "basis_prep": basis_ms * 1e3,
+                      "align_with_basis_prep": align_unprep_ms * 1e3,
                       "step_with_basis_prep": unprepared_ms * 1e3},
+        "stages_vs_hbm": bw,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)

@@ -254,6 +254,28 @@ rw4_status respin_prepare_basis(const float* Q, const float* M, int64_t D, int64
 size_t respin_basis_size(int64_t D, int64_t r);
 
 /*
+ * respin_align_prepared -- respin_align on its matrix-core path with the basis
+ * prepared by respin_prepare_basis(Q, M, D, r) instead of (Q, M): the per-call
+ * work is the projection z = (M - I) Q^T x and the lift x + Q z ["ReSpinQuant"
+ * paper notes, key design 3], with the same results bit for bit as respin_align
+ * given a workspace.
+ *   x      bf16 [T][D]
+ *   out    [T][D] of out_dt (RW4_BF16 or RW4_F32); must not alias x
+ *   basis  prepared for (D, r); 256-byte aligned
+ *   addend nullable, [T][D] of out_dt, added after the alignment
+ *   workspace, ws_bytes: respin_align_prepared_workspace_size(T, D, r) bytes
+ *          of device scratch, 256-byte aligned
+ * Constraints: those of respin_basis_size (1 <= r <= min(D, 128), r % 4 == 0,
+ * D % 64 == 0). Asynchronous on `stream`; argument errors come before any launch.
+ */
+rw4_status respin_align_prepared(const void* x, void* out, rw4_dtype out_dt, const void* basis,
+                                 const void* addend, int64_t T, int64_t D, int64_t r,
+                                 void* workspace, size_t ws_bytes, void* stream);
+
+/* bytes of workspace respin_align_prepared needs; 0 on bad input */
+size_t respin_align_prepared_workspace_size(int64_t T, int64_t D, int64_t r);
+
+/*
  * rotated_linear_prepared -- rotated_linear with the alignment's basis
  * prepared by respin_prepare_basis(Q, M, D, r) instead of (Q, M): same
  * arguments, same results bit for bit, same workspace contents after the
@@ -279,7 +301,7 @@ const char* rw4_status_string(rw4_status s);
 /* ABI version of this header (bumped on any signature change) */
 int rw4_abi_version(void);
 
-#define RW4_ABI_VERSION 5
+#define RW4_ABI_VERSION 6
 
 #ifdef __cplusplus
 }

@@ -17,6 +17,7 @@ __all__ = [
     "respin_align", "fwht", "quant_act_int4", "w4a4_gemm", "rotated_linear",
     "rotated_linear_workspace_size", "respin_align_workspace_size", "workspace_views",
     "respin_basis_size", "respin_prepare_basis", "rotated_linear_prepared",
+    "respin_align_prepared", "respin_align_prepared_workspace_size",
     "rotated_linear_prepared_workspace_size",
     "w4a4_tiles_size", "w4a4_tile_codes", "w4a4_gemm_tiles", "prep_weight", "layer",
     "quant_act_sym", "RW4_ABITS",
@@ -38,7 +39,8 @@ EXPORTS = ("respin_align", "respin_align_workspace_size", "fwht", "quant_act_int
            "quant_act_sym", "w4a4_gemm",
            "w4a4_tiles_size", "w4a4_tile_codes", "w4a4_gemm_tiles", "rotated_linear",
            "rotated_linear_workspace_size", "respin_basis_size", "respin_prepare_basis",
-           "rotated_linear_prepared", "rotated_linear_prepared_workspace_size", "rw4_align256",
+           "rotated_linear_prepared", "rotated_linear_prepared_workspace_size",
+           "respin_align_prepared", "respin_align_prepared_workspace_size", "rw4_align256",
            "rw4_status_string", "rw4_abi_version")
 
 
@@ -82,6 +84,9 @@ def lib() -> ctypes.CDLL:
                                           sz, vp, vp]
     L.rotated_linear_prepared_workspace_size.argtypes = [i64, i64, i64, u32]
     L.rotated_linear_prepared_workspace_size.restype = sz
+    L.respin_align_prepared.argtypes = [vp, vp, i32, vp, vp, i64, i64, i64, vp, sz, vp]
+    L.respin_align_prepared_workspace_size.argtypes = [i64, i64, i64]
+    L.respin_align_prepared_workspace_size.restype = sz
     L.rw4_align256.argtypes = [sz]
     L.rw4_align256.restype = sz
     L.rw4_status_string.argtypes = [i32]
@@ -90,7 +95,7 @@ def lib() -> ctypes.CDLL:
     for f in ("respin_align", "fwht", "quant_act_int4", "quant_act_sym", "w4a4_gemm",
               "w4a4_tile_codes",
               "w4a4_gemm_tiles", "rotated_linear", "respin_prepare_basis",
-              "rotated_linear_prepared"):
+              "rotated_linear_prepared", "respin_align_prepared"):
         getattr(L, f).restype = i32
     _lib = L
     return L
@@ -171,6 +176,37 @@ def respin_align(x, Q, M, out=None, addend=None, out_dtype=None, workspace=None,
                             _p(M) if r else None, _p(addend), T, D, r, _p(workspace), nbytes,
                             _stream())
     _check("respin_align", st)
+    return out
+
+
+def respin_align_prepared_workspace_size(T: int, D: int, r: int) -> int:
+    return int(lib().respin_align_prepared_workspace_size(T, D, r))
+
+
+def respin_align_prepared(x, basis, r: int, out=None, addend=None, out_dtype=None,
+                          workspace=None):
+    """``respin_align`` with a basis from ``respin_prepare_basis`` (rank r) in
+    place of (Q, M); x bf16 [T][D]. Returns out."""
+    torch = _torch()
+    _contig(x)
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bf16")
+    T, D = x.shape
+    if basis.numel() * basis.element_size() < respin_basis_size(D, r):
+        raise ValueError("basis: buffer too small for (D, r)")
+    if out is None:
+        out = torch.empty((T, D), dtype=out_dtype or torch.float32, device=x.device)
+    if addend is not None:
+        _contig(addend)
+        if addend.dtype != out.dtype or addend.shape != out.shape:
+            raise ValueError("addend must match out in dtype and shape")
+    need = respin_align_prepared_workspace_size(T, D, r)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=x.device)
+    st = lib().respin_align_prepared(_p(x), _p(out), _fdt(out), _p(basis), _p(addend), T, D, r,
+                                     _p(workspace), workspace.numel() * workspace.element_size(),
+                                     _stream())
+    _check("respin_align_prepared", st)
     return out
 
 

@@ -256,6 +256,32 @@ rw4_status respin_prepare_basis(const float* Q, const float* M, int64_t D, int64
   return hip_status(rw4::launch_basis_prep(Q, M, D, r, with_p(D, r), basis, strm(stream)));
 }
 
+size_t respin_align_prepared_workspace_size(int64_t T, int64_t D, int64_t r) {
+  if (T < 0 || respin_basis_size(D, r) == 0) return 0;
+  return rw4::align_zpart_bytes(T, D, r);
+}
+
+rw4_status respin_align_prepared(const void* x, void* out, rw4_dtype out_dt, const void* basis,
+                                 const void* addend, int64_t T, int64_t D, int64_t r,
+                                 void* workspace, size_t ws_bytes, void* stream) {
+  if (!x || !out || !basis || T < 0 || D < 1 || r < 1 || !fdt(out_dt)) return RW4_ERR_INVALID_ARG;
+  if (respin_basis_size(D, r) == 0) return RW4_ERR_UNSUPPORTED;
+  if (!al16(x) || !al16(out) || (addend && !al16(addend))) return RW4_ERR_MISALIGNED;
+  if (reinterpret_cast<uintptr_t>(basis) & 255u) return RW4_ERR_INVALID_ARG;
+  if (x == out) return RW4_ERR_INVALID_ARG;
+  if (T == 0) return RW4_OK;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) ||
+      ws_bytes < rw4::align_zpart_bytes(T, D, r))
+    return RW4_ERR_WORKSPACE;
+  hipStream_t s = strm(stream);
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  float* Zpart = static_cast<float*>(workspace);
+  if (rw4::launch_yproj(xb, T, D, r, basis, with_p(D, r), Zpart, s) != hipSuccess)
+    return RW4_ERR_HIP;
+  return hip_status(rw4::launch_lift(xb, out, out_dt == RW4_F32, addend, T, D, r, basis,
+                                     with_p(D, r), Zpart, s));
+}
+
 size_t rotated_linear_prepared_workspace_size(int64_t T, int64_t D, int64_t r, unsigned flags) {
   if (T < 0 || !pow2(D) || D < 64 || D > 32768 || r < 0) return 0;
   if ((flags & RW4_ALIGN) && r > 0 && respin_basis_size(D, r) == 0) return 0;

@@ -88,13 +88,17 @@ basis_prep_kernel(const float* __restrict__ Q, const float* __restrict__ M, int 
     *reinterpret_cast<uint4*>(QL + static_cast<int64_t>(d) * RK + j0 + jb) = vl;
   }
   // Q'[d][j] = sum_k Q[d][k] (M - I)[j][k] (zero for j >= r), split the same way
+  float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  for (int k = 0; k < r; ++k) {
+    const float q = qrow[dd][k];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = fmaf(q, mi[jb + e][k], acc[e]);
+  }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    float acc = 0.0f;
-    for (int k = 0; k < r; ++k) acc = fmaf(qrow[dd][k], mi[jb + e][k], acc);
-    const uint16_t hh = f32_to_bf16(acc);
+    const uint16_t hh = f32_to_bf16(acc[e]);
     th[jb + e][dd] = hh;
-    tlo[jb + e][dd] = f32_to_bf16(acc - bf16_to_f32(hh));
+    tlo[jb + e][dd] = f32_to_bf16(acc[e] - bf16_to_f32(hh));
   }
   __syncthreads();
   // transposed rows: thread -> (row j = tid / 8, 8 consecutive d)
@@ -535,6 +539,8 @@ hipError_t launch_lift(const uint16_t* x, void* out, int out_f32, const void* ad
                        int64_t D, int64_t r, const void* basis, bool with_p, const float* Zpart,
                        hipStream_t s) {
   if (T == 0) return hipSuccess;
+  if (lfq_supported(D, r))
+    return launch_align_rows(x, out, out_f32, addend, T, D, r, basis, with_p, Zpart, s);
   const AlignBasis a = align_basis(basis, D, r, with_p);
   const int Di = static_cast<int>(D);
   const int ri = static_cast<int>(r);

@@ -21,6 +21,8 @@ __device__ __forceinline__ v4f mfma(v8bf a, v8bf b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef float v16f __attribute__((ext_vector_type(16)));
+
 // Let the last matrix-core results land before anything else reads them: no
 // instruction may be scheduled across, and the wave sleeps ~64 cycles (longer
 // than the instruction's pipeline) in between.

@@ -36,7 +36,6 @@ namespace rw4 {
 namespace g6 {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v16f __attribute__((ext_vector_type(16)));
 
 // MFMA operand from a lane's two plane loads (elements 6, 7 are not read for FP6)
 __device__ __forceinline__ v8i opnd(const uint4& a, const uint2& b) {

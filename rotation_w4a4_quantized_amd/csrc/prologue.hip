@@ -39,6 +39,9 @@ constexpr int kTok = 8;              // tokens per workgroup
 constexpr int kThreads = 1024;       // 8 row waves + 8 lift waves
 constexpr int kChunkPitch = 144;     // bytes per 32-value chunk in the lift buffer (16-byte pad)
 
+// byte offset of 32-value chunk c in a token's lift buffer
+__device__ __forceinline__ int lift_off(int c) { return c * kChunkPitch; }
+
 // this wave's LDS writes have completed, then a workgroup barrier that the
 // compiler may not move memory accesses across
 __device__ __forceinline__ void lds_barrier() {
@@ -46,6 +49,93 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+}
+
+// The lift waves of a 16-wave workgroup of kTok tokens (waves 8..15, lw =
+// wave - 8): z of the tokens from the projection's parts (summed in a fixed
+// order, bf16 hi/lo split into zh/zl), then A z on bf16 matrix cores for
+// A = P (or Q), streamed from L2 in double-buffered groups of 16-row blocks;
+// put(token, d, v) receives A z at columns d .. d + 3. Runs the workgroup's
+// two barriers (z in LDS; results in LDS) at raised wave priority; the row
+// waves meet the first as soon as their row loads are issued.
+template <int D, int RK, typename Put>
+__device__ __forceinline__ void lift_waves(int lw, int lane, int64_t t0, int64_t T,
+                                           const float* __restrict__ Zpart, int S,
+                                           const uint16_t* __restrict__ AH,
+                                           const uint16_t* __restrict__ AL,
+                                           uint16_t (&zh)[16][RK + 8], uint16_t (&zl)[16][RK + 8],
+                                           Put put) {
+  constexpr int KK = RK / 32;
+  constexpr int NB = D / 128;                   // 16-column blocks per lift wave
+  constexpr int QB = NB < 8 / KK ? NB : 8 / KK; // blocks per load group
+  constexpr int NG = NB / QB;
+  static_assert(NB % QB == 0, "groups");
+  __builtin_amdgcn_s_setprio(3);
+  const int i16 = lane & 15;                    // A row (column d0 + i16); B, C column (token)
+  const int g = lane >> 4;
+  const int dw = lw * (D / 8);
+  v8bf qa[2][QB][KK], qb[2][QB][KK];
+  auto loadq = [&](int buf, int grp) {
+#pragma unroll
+    for (int b = 0; b < QB; ++b)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const int64_t qo = static_cast<int64_t>(dw + 16 * (grp * QB + b) + i16) * RK + 32 * kk + 8 * g;
+        qa[buf][b][kk] = ld8(AH + qo);
+        qb[buf][b][kk] = ld8(AL + qo);
+      }
+  };
+  loadq(0, 0);
+  // z of the workgroup's tokens into LDS (MFMA columns 8..15 get zero): the
+  // parts' loads are all issued before the first add, and the sum runs in
+  // part order from zero
+  constexpr int SP = (D + 511) / 512;           // D parts of the projection
+  for (int c = lw * 64 + lane; c < 16 * RK; c += 512) {
+    const int tt = c / RK;
+    const int i = c % RK;
+    const int64_t trow = min(t0 + (tt & 7), T - 1);
+    float zp[SP];
+#pragma unroll
+    for (int p = 0; p < SP; ++p) zp[p] = Zpart[(static_cast<int64_t>(p) * T + trow) * RK + i];
+    float z = 0.0f;
+#pragma unroll
+    for (int p = 0; p < SP; ++p) z += zp[p];
+    z = tt < kTok ? z : 0.0f;
+    const uint16_t h = f32_to_bf16(z);
+    zh[tt][i] = h;
+    zl[tt][i] = f32_to_bf16(z - bf16_to_f32(h));
+  }
+  lds_barrier();  // 1: z in LDS
+  v8bf bh[KK], bl[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    bh[kk] = *reinterpret_cast<const v8bf*>(&zh[i16][32 * kk + 8 * g]);
+    bl[kk] = *reinterpret_cast<const v8bf*>(&zl[i16][32 * kk + 8 * g]);
+  }
+#pragma unroll
+  for (int grp = 0; grp < NG; ++grp) {
+    const int buf = grp & 1;
+    if (grp + 1 < NG) loadq(buf ^ 1, grp + 1);  // compile-time condition (unrolled)
+    v4f acc[QB];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      acc[b] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        acc[b] = mfma(qa[buf][b][kk], bh[kk], acc[b]);
+        acc[b] = mfma(qb[buf][b][kk], bh[kk], acc[b]);
+        acc[b] = mfma(qa[buf][b][kk], bl[kk], acc[b]);
+      }
+    }
+    mfma_drain();
+    // C: lane holds token i16, columns d .. d + 3 of this block
+    if (i16 < kTok) {
+#pragma unroll
+      for (int b = 0; b < QB; ++b)
+        put(i16, dw + 16 * (grp * QB + b) + 4 * g, make_float4(acc[b][0], acc[b][1], acc[b][2], acc[b][3]));
+    }
+  }
+  lds_barrier();  // 2: A z in LDS
 }
 
 template <int N, int RK, bool FW, bool DBG>
@@ -60,12 +150,8 @@ lfq_kernel(const uint16_t* __restrict__ x, int64_t T, const float* __restrict__ 
   constexpr int NA = NCH < 64 ? NCH : 64;       // lanes holding chunks
   constexpr int LB = N - 5 - (NS == 2 ? 1 : 0); // lane bits of the index
   constexpr int LPITCH = NCH * kChunkPitch + 64;  // bytes per token in the lift buffer
-  constexpr int KK = RK / 32;
-  constexpr int NB = D / 128;                   // 16-column lift blocks per lift wave
-  constexpr int QB = NB < 8 / KK ? NB : 8 / KK; // blocks per load group
-  constexpr int NG = NB / QB;
   static_assert(N >= 8 && N <= 12, "D in [256, 4096]");
-  static_assert(NS <= 2 && NB % QB == 0, "geometry");
+  static_assert(NS <= 2, "geometry");
   __shared__ __attribute__((aligned(16))) uint8_t lift[kTok * LPITCH];
   __shared__ __attribute__((aligned(16))) uint16_t zh[16][RK + 8];
   __shared__ __attribute__((aligned(16))) uint16_t zl[16][RK + 8];
@@ -80,70 +166,11 @@ lfq_kernel(const uint16_t* __restrict__ x, int64_t T, const float* __restrict__ 
   const int64_t t0 = blk * kTok;
 
   if (wave >= 8) {
-    // ------------------------------------------------------------- lift waves
-    __builtin_amdgcn_s_setprio(3);
-    const int lw = wave - 8;
-    const int i16 = lane & 15;                  // A row (column d0 + i16); B, C column (token)
-    const int g = lane >> 4;
-    const int dw = lw * (D / 8);
-    v8bf qa[2][QB][KK], qb[2][QB][KK];
-    auto loadq = [&](int buf, int grp) {
-#pragma unroll
-      for (int b = 0; b < QB; ++b)
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const int64_t qo = static_cast<int64_t>(dw + 16 * (grp * QB + b) + i16) * RK + 32 * kk + 8 * g;
-          qa[buf][b][kk] = ld8(PH + qo);
-          qb[buf][b][kk] = ld8(PL + qo);
-        }
-    };
-    loadq(0, 0);
-    // z = sum over the parts (fixed order), bf16 split; MFMA columns 8..15 get zero
-    for (int c = lw * 64 + lane; c < 16 * RK; c += 512) {
-      const int tt = c / RK;
-      const int i = c % RK;
-      const int64_t trow = min(t0 + (tt & 7), T - 1);
-      float z = 0.0f;
-      for (int p = 0; p < S; ++p) z += Zpart[(static_cast<int64_t>(p) * T + trow) * RK + i];
-      z = tt < kTok ? z : 0.0f;
-      const uint16_t h = f32_to_bf16(z);
-      zh[tt][i] = h;
-      zl[tt][i] = f32_to_bf16(z - bf16_to_f32(h));
-    }
-    lds_barrier();  // 1: z in LDS
-    v8bf bh[KK], bl[KK];
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      bh[kk] = *reinterpret_cast<const v8bf*>(&zh[i16][32 * kk + 8 * g]);
-      bl[kk] = *reinterpret_cast<const v8bf*>(&zl[i16][32 * kk + 8 * g]);
-    }
-#pragma unroll
-    for (int grp = 0; grp < NG; ++grp) {
-      const int buf = grp & 1;
-      if (grp + 1 < NG) loadq(buf ^ 1, grp + 1);  // compile-time condition (unrolled)
-      v4f acc[QB];
-#pragma unroll
-      for (int b = 0; b < QB; ++b) {
-        acc[b] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          acc[b] = mfma(qa[buf][b][kk], bh[kk], acc[b]);
-          acc[b] = mfma(qb[buf][b][kk], bh[kk], acc[b]);
-          acc[b] = mfma(qa[buf][b][kk], bl[kk], acc[b]);
-        }
-      }
-      mfma_drain();
-      // C: lane holds token i16, columns d .. d + 3 of this block
-      if (i16 < kTok) {
-#pragma unroll
-        for (int b = 0; b < QB; ++b) {
-          const int d = dw + 16 * (grp * QB + b) + 4 * g;
-          *reinterpret_cast<float4*>(lift + i16 * LPITCH + (d >> 5) * kChunkPitch + (d & 31) * 4) =
-              make_float4(acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
-        }
-      }
-    }
-    lds_barrier();  // 2: P z in LDS
+    lift_waves<D, RK>(wave - 8, lane, t0, T, Zpart, S, PH, PL, zh, zl,
+                      [&](int tok, int d, float4 v) {
+                        *reinterpret_cast<float4*>(lift + tok * LPITCH + lift_off(d >> 5) +
+                                                   (d & 31) * 4) = v;
+                      });
     return;
   }
 
@@ -153,20 +180,28 @@ lfq_kernel(const uint16_t* __restrict__ x, int64_t T, const float* __restrict__ 
   const int64_t trow = t < T ? t : T - 1;   // rows past T repeat the last one; never stored
   const bool act = lane < NA;
   float u[NS][32];
+  float m = 0.0f;
+  uint4 raw[NS][4];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const int c = act ? 64 * s + lane : NCH - 1;  // unconditional load, clamped
     const uint4* p = reinterpret_cast<const uint4*>(x + trow * D + 32 * c);
 #pragma unroll
+    for (int q = 0; q < 4; ++q) raw[s][q] = p[q];
+  }
+  lds_barrier();  // 1 (the row is still in flight)
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+#pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const uint4 v = p[q];
+      uint4 v = raw[s][q];
+      asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
       u[s][8 * q + 0] = bf16lo(v.x); u[s][8 * q + 1] = bf16hi(v.x);
       u[s][8 * q + 2] = bf16lo(v.y); u[s][8 * q + 3] = bf16hi(v.y);
       u[s][8 * q + 4] = bf16lo(v.z); u[s][8 * q + 5] = bf16hi(v.z);
       u[s][8 * q + 6] = bf16lo(v.w); u[s][8 * q + 7] = bf16hi(v.w);
     }
   }
-  lds_barrier();  // 1
   if constexpr (FW) {
     // index i = 2048 s + 32 lane + j; every butterfly stage commutes with the others
 #pragma unroll
@@ -240,18 +275,17 @@ lfq_kernel(const uint16_t* __restrict__ x, int64_t T, const float* __restrict__ 
   for (int s = 0; s < NS; ++s)
 #pragma unroll
     for (int j = 0; j < 32; ++j) asm volatile("" : "+v"(u[s][j]));
-  lds_barrier();  // 2
+  lds_barrier();  // 2: lift in LDS
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const int c = act ? 64 * s + lane : NCH - 1;
-    const float4* p = reinterpret_cast<const float4*>(lift + tok * LPITCH + c * kChunkPitch);
+    const float4* p = reinterpret_cast<const float4*>(lift + tok * LPITCH + lift_off(c));
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const float4 v = p[q];
       u[s][4 * q + 0] += v.x; u[s][4 * q + 1] += v.y; u[s][4 * q + 2] += v.z; u[s][4 * q + 3] += v.w;
     }
   }
-  float m = 0.0f;
 #pragma unroll
   for (int s = 0; s < NS; ++s)
 #pragma unroll
@@ -280,6 +314,84 @@ lfq_kernel(const uint16_t* __restrict__ x, int64_t T, const float* __restrict__ 
       }
     }
   }
+}
+
+// ---------------------------------------------------------------- alignment alone
+// respin_align for bf16 x and D a power of two in [256, 4096]: the same lift
+// waves (A = Q), and row waves that hold x in the coalesced layout (lane L:
+// values 256 c + 4 L + e), add Q z (+ addend) and store fp32 or bf16 rows
+// with 1 KiB (fp32) or 512 B (bf16) per instruction.
+template <int N, int RK, bool OF32, bool ADD>
+__global__ void __launch_bounds__(kThreads)
+align_rows_kernel(const uint16_t* __restrict__ x, int64_t T, const float* __restrict__ Zpart,
+                  int S, const uint16_t* __restrict__ QH, const uint16_t* __restrict__ QL,
+                  const void* __restrict__ addend, void* __restrict__ out) {
+  constexpr int D = 1 << N;
+  constexpr int NSL = D / 256;                  // 4-value slots per lane
+  constexpr int PITCH = NSL * 64 + 4;           // float4s per token (4 pad: banks)
+  static_assert(N >= 8 && N <= 12, "D in [256, 4096]");
+  __shared__ float4 lift[kTok * PITCH];
+  __shared__ __attribute__((aligned(16))) uint16_t zh[16][RK + 8];
+  __shared__ __attribute__((aligned(16))) uint16_t zl[16][RK + 8];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTok;
+  if (wave >= 8) {
+    lift_waves<D, RK>(wave - 8, lane, t0, T, Zpart, S, QH, QL, zh, zl,
+                      [&](int tok, int d, float4 v) {
+                        lift[tok * PITCH + (d >> 8) * 64 + ((d & 255) >> 2)] = v;
+                      });
+    return;
+  }
+  const int tok = wave;
+  const int64_t t = t0 + tok;
+  const int64_t trow = t < T ? t : T - 1;      // rows past T repeat the last one; never stored
+  uint2 xv[NSL];
+#pragma unroll
+  for (int c = 0; c < NSL; ++c)
+    xv[c] = *reinterpret_cast<const uint2*>(x + trow * D + 256 * c + 4 * lane);
+  lds_barrier();  // 1
+  lds_barrier();  // 2: lift in LDS
+  if (t >= T) return;
+#pragma unroll
+  for (int c = 0; c < NSL; ++c) {
+    const int64_t off = t * D + 256 * c + 4 * lane;
+    const float4 l = lift[tok * PITCH + c * 64 + lane];
+    float o[4] = {bf16lo(xv[c].x) + l.x, bf16hi(xv[c].x) + l.y, bf16lo(xv[c].y) + l.z,
+                  bf16hi(xv[c].y) + l.w};
+    if constexpr (OF32) {
+      if constexpr (ADD) {
+        const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(addend) + off);
+        o[0] += a.x; o[1] += a.y; o[2] += a.z; o[3] += a.w;
+      }
+      *reinterpret_cast<float4*>(static_cast<float*>(out) + off) = make_float4(o[0], o[1], o[2], o[3]);
+    } else {
+      if constexpr (ADD) {
+        const uint2 a = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(addend) + off);
+        o[0] += bf16lo(a.x); o[1] += bf16hi(a.x); o[2] += bf16lo(a.y); o[3] += bf16hi(a.y);
+      }
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + off) =
+          make_uint2(f32_to_bf16(o[0]) | (static_cast<uint32_t>(f32_to_bf16(o[1])) << 16),
+                     f32_to_bf16(o[2]) | (static_cast<uint32_t>(f32_to_bf16(o[3])) << 16));
+    }
+  }
+}
+
+template <int N, int RK>
+hipError_t launch_align_rows_n(const uint16_t* x, int64_t T, const float* Zpart, int S,
+                               const uint16_t* QH, const uint16_t* QL, const void* addend,
+                               void* out, bool of32, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((T + kTok - 1) / kTok));
+#define RW4_AR(OF, AD)                                                                           \
+  if (of32 == OF && (addend != nullptr) == AD) {                                                 \
+    hipLaunchKernelGGL((align_rows_kernel<N, RK, OF, AD>), grid, dim3(kThreads), 0, s, x, T,     \
+                       Zpart, S, QH, QL, addend, out);                                           \
+    return hipGetLastError();                                                                    \
+  }
+  RW4_AR(true, false) RW4_AR(true, true) RW4_AR(false, false) RW4_AR(false, true)
+#undef RW4_AR
+  return hipErrorInvalidValue;
 }
 
 template <int N, int RK>
@@ -334,10 +446,30 @@ hipError_t launch_lift_fwht_quant(const uint16_t* x, int64_t T, int64_t D, int64
   const uint16_t* PH = do_fwht ? a.PH : a.QH;
   const uint16_t* PL = do_fwht ? a.PL : a.QL;
   const int S = align_parts_count(D);
+  if (S != (D + 511) / 512) return hipErrorInvalidValue;  // the lift waves' part count
   int n = 0;
   while ((int64_t(1) << n) < D) ++n;
   if (a.RK == 32) return launch_rk<32>(n, x, T, Zpart, S, PH, PL, do_fwht, tiles, s_a, dbg, qmax, s);
   if (a.RK == 64) return launch_rk<64>(n, x, T, Zpart, S, PH, PL, do_fwht, tiles, s_a, dbg, qmax, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_align_rows(const uint16_t* x, void* out, int out_f32, const void* addend,
+                             int64_t T, int64_t D, int64_t r, const void* basis, bool with_p,
+                             const float* Zpart, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (!lfq_supported(D, r)) return hipErrorInvalidValue;
+  const AlignBasis a = align_basis(basis, D, r, with_p);
+  const int S = align_parts_count(D);
+  if (S != (D + 511) / 512) return hipErrorInvalidValue;  // the lift waves' part count
+  int n = 0;
+  while ((int64_t(1) << n) < D) ++n;
+  const bool of32 = out_f32 != 0;
+#define RW4_ARN(NN, K) \
+  if (n == NN && a.RK == K) return launch_align_rows_n<NN, K>(x, T, Zpart, S, a.QH, a.QL, addend, out, of32, s);
+  RW4_ARN(8, 32) RW4_ARN(9, 32) RW4_ARN(10, 32) RW4_ARN(11, 32) RW4_ARN(12, 32)
+  RW4_ARN(8, 64) RW4_ARN(9, 64) RW4_ARN(10, 64) RW4_ARN(11, 64) RW4_ARN(12, 64)
+#undef RW4_ARN
   return hipErrorInvalidValue;
 }
 

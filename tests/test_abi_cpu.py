@@ -22,7 +22,7 @@ def _declared():
 def test_library_built_and_loads():
     assert os.path.exists(rw.library_path), "build the HIP library first"
     L = rw.lib()
-    assert L.rw4_abi_version() == 5
+    assert L.rw4_abi_version() == 6
 
 
 def test_exports_every_declared_symbol():
@@ -219,6 +219,28 @@ def test_rotated_linear_prepared_validation():
     assert _rlp(x=ODD) == MIS
     assert _rlp(T=0) == 0
     assert _rlp(T=0, x=NUL, w=NUL, sw=NUL, y=NUL, basis=NUL) == 0
+
+
+def _rap(x=A, out=B, odt=1, basis=C, add=NUL, T=4, D=256, r=8, ws=Dp, wsb=1 << 20):
+    return rw.lib().respin_align_prepared(x, out, odt, basis, add, T, D, r, ws, wsb, NUL)
+
+
+def test_respin_align_prepared_validation():
+    L = rw.lib()
+    # the per-call workspace is the projection's parts alone
+    assert L.respin_align_prepared_workspace_size(2048, 4096, 32) == \
+        L.rw4_align256((4096 // 512) * 2048 * 32 * 4)
+    assert L.respin_align_prepared_workspace_size(4, 1000, 8) == 0
+    assert L.respin_align_prepared_workspace_size(-1, 256, 8) == 0
+    assert _rap(x=NUL) == INV and _rap(out=NUL) == INV and _rap(basis=NUL) == INV
+    assert _rap(odt=2) == INV and _rap(T=-1) == INV and _rap(r=0) == INV
+    assert _rap(r=6) == UNS and _rap(D=1000) == UNS and _rap(r=132) == UNS
+    assert _rap(x=ODD) == MIS and _rap(add=ODD) == MIS
+    assert _rap(basis=ctypes.c_void_p(0x30010)) == INV
+    assert _rap(out=A) == INV                      # out aliases x
+    assert _rap(ws=NUL) == WSE and _rap(wsb=100) == WSE
+    assert _rap(ws=ctypes.c_void_p(0x40010)) == WSE
+    assert _rap(T=0, ws=NUL) == 0
 
 
 def test_quant_sym_validation():

@@ -179,6 +179,35 @@ def test_respin_align_identity_cases(rw):
     np.testing.assert_allclose(np.linalg.norm(out, axis=1), np.linalg.norm(x, axis=1), rtol=1e-5)
 
 
+@pytest.mark.parametrize("T,D,r", [(37, 4096, 32), (2048, 4096, 32), (9, 256, 8), (70, 1024, 64),
+                                   (13, 2048, 40), (5, 4096, 128), (11, 8192, 64), (6, 576, 16)])
+@pytest.mark.parametrize("odt", ["f32", "bf16"])
+@pytest.mark.parametrize("add", [False, True])
+def test_respin_align_prepared(rw, T, D, r, odt, add):
+    """respin_align_prepared equals respin_align (given a workspace) bit for bit,
+    and the oracle's alignment within the fp32 (bf16) tolerance."""
+    say(f"respin_align_prepared T={T} D={D} r={r} out={odt} addend={add}")
+    tt = torch()
+    Q, M = W.gen_basis(D * 3 + r, D, r)
+    xb = W.gen_x(D + T, T, D, 8, 80.0)
+    x = W.bf16_bits_to_f32(xb)
+    out_dtype = tt.float32 if odt == "f32" else tt.bfloat16
+    addend = None
+    if add:
+        a32 = W.bf16_bits_to_f32(W.gen_x(D + T + 1, T, D, 0, 1.0))
+        addend = dev(a32) if odt == "f32" else dev(W.f32_to_bf16_bits(a32))
+    basis = rw.respin_prepare_basis(dev(Q), dev(M))
+    out = host(rw.respin_align_prepared(dev(xb), basis, r, addend=addend, out_dtype=out_dtype))
+    ref = host(rw.respin_align(dev(xb), dev(Q), dev(M), addend=addend, out_dtype=out_dtype))
+    np.testing.assert_array_equal(out, ref)
+    want = O.align(x, Q, M)
+    if add:
+        want = want + (host(addend) if odt == "f32" else O.bf16_to_f64(host(addend)))
+    got = out if odt == "f32" else O.bf16_to_f64(out)
+    tol = FP32_TOL if odt == "f32" else BF16_TOL
+    assert normwise(got, want) <= tol
+
+
 @pytest.mark.parametrize("T,D,r", [(33, 4096, 32), (8, 4096, 32), (70, 256, 8)])
 @pytest.mark.parametrize("direct", [False, True])
 def test_respin_align_bf16_residual(rw, T, D, r, direct):
