@@ -39,6 +39,7 @@ __all__ = [
     "bf16_to_f64", "f64_to_bf16", "align", "align_dense", "t_hat", "fwht", "hadamard",
     "quant_sym", "quant_int4", "pack_int4", "unpack_int4", "gemm_int", "gemm_int_loop",
     "epilogue", "silu_gate", "prep_weight", "prequant", "rotated_linear", "residual", "layer",
+    "quadratic_character", "jacobsthal", "paley_hadamard", "hadamard_kron", "head_hadamard",
     "FLAG_ALIGN", "FLAG_FWHT", "FLAG_SWIGLU",
 ]
 
@@ -145,6 +146,97 @@ def fwht(v: np.ndarray) -> np.ndarray:
         b[..., 1, :] = lo - hi
         h *= 2
     return a / np.sqrt(D)
+
+
+# ----------------------------------------------------------------------------
+# Structured Hadamard transforms  [IQ2 QuaRot Background, QuaRot Method]
+# ----------------------------------------------------------------------------
+def _is_prime(q: int) -> bool:
+    return q >= 2 and all(q % d for d in range(2, int(q ** 0.5) + 1))
+
+
+def quadratic_character(q: int) -> np.ndarray:
+    """chi over the integers mod a prime q: chi(0) = 0, chi(a) = +1 if a is a
+    nonzero square mod q, else -1 (the Legendre symbol)."""
+    if not _is_prime(q) or q == 2:
+        raise ValueError("odd prime q required")
+    chi = -np.ones(q, dtype=np.int64)
+    chi[0] = 0
+    for y in range(1, q):
+        chi[(y * y) % q] = 1
+    return chi
+
+
+def jacobsthal(q: int) -> np.ndarray:
+    """Jacobsthal matrix of a prime q: J[a][b] = chi(a - b mod q)."""
+    chi = quadratic_character(q)
+    a = np.arange(q)
+    return chi[(a[:, None] - a[None, :]) % q]
+
+
+def paley_hadamard(m: int) -> np.ndarray:
+    """A +-1 Hadamard matrix of order m by Paley's construction (the pages need
+    one of non-power-of-two order m [IQ2 QuaRot Background] and print none).
+
+    * Paley I, q = m - 1 prime with q = 3 (mod 4): the Jacobsthal matrix J is
+      skew, S = [[0, 1^T], [-1, J]] (index 0 first, then 0..q-1 of the
+      integers mod q), H = I + S.
+    * Paley II, q = m/2 - 1 prime with q = 1 (mod 4): J is symmetric,
+      C = [[0, 1^T], [1, J]], H = C (x) [[1, 1], [1, -1]] + I (x) [[1, -1], [-1, -1]].
+    """
+    if m >= 4 and _is_prime(m - 1) and (m - 1) % 4 == 3:
+        q = m - 1
+        S = np.zeros((m, m), dtype=np.int64)
+        S[0, 1:] = 1
+        S[1:, 0] = -1
+        S[1:, 1:] = jacobsthal(q)
+        return np.eye(m, dtype=np.int64) + S
+    if m % 2 == 0 and m >= 4 and _is_prime(m // 2 - 1) and (m // 2 - 1) % 4 == 1:
+        q = m // 2 - 1
+        C = np.zeros((q + 1, q + 1), dtype=np.int64)
+        C[0, 1:] = 1
+        C[1:, 0] = 1
+        C[1:, 1:] = jacobsthal(q)
+        A = np.array([[1, 1], [1, -1]], dtype=np.int64)
+        B = np.array([[1, -1], [-1, -1]], dtype=np.int64)
+        return np.kron(C, A) + np.kron(np.eye(q + 1, dtype=np.int64), B)
+    raise ValueError(f"no Paley construction of order {m} over a prime field")
+
+
+def hadamard_kron(v: np.ndarray, m: int, signs=None) -> np.ndarray:
+    """(H_{2^n} (x) H_m) diag(s) v / sqrt(D) for every row, D = 2^n m
+    [IQ2 QuaRot Background: H_d = H_{2^n} (x) H_m for d = 2^n m, and the
+    randomized H diag(s) with s in {+1, -1}^d]. m = 1 is the plain WHT; H_m
+    for m > 1 is paley_hadamard(m). Index f = i m + j (i < 2^n, j < m), so
+    the row as a 2^n x m matrix V becomes H_{2^n} V H_m^T."""
+    a = np.array(v, dtype=np.float64, copy=True)
+    D = a.shape[-1]
+    if D % m:
+        raise ValueError("D must be a multiple of m")
+    A = D // m
+    if signs is not None:
+        a = a * np.asarray(signs, dtype=np.float64)
+    V = a.reshape(a.shape[:-1] + (A, m))
+    if m > 1:
+        V = V @ paley_hadamard(m).T.astype(np.float64)
+    # H_{2^n} along i: the normalized transform of the columns, times sqrt(A)
+    V = np.swapaxes(fwht(np.swapaxes(V, -1, -2)), -1, -2) * np.sqrt(A)
+    return V.reshape(a.shape) / np.sqrt(D)
+
+
+def head_hadamard(v: np.ndarray, n_h: int) -> np.ndarray:
+    """(H_{n_h} (x) I_{d_h}) v / sqrt(n_h) for every row, d_h = D / n_h: the
+    online transform across attention heads before the output projection
+    [IQ2 QuaRot Method, value projection: Z <- Z (H_{n_h} (x) I), by reshaping
+    and a Walsh-Hadamard transform; H_{n_h} is symmetric, so the row form
+    equals the column form]."""
+    a = np.array(v, dtype=np.float64, copy=True)
+    D = a.shape[-1]
+    if D % n_h:
+        raise ValueError("D must be a multiple of n_h")
+    V = a.reshape(a.shape[:-1] + (n_h, D // n_h))
+    V = np.swapaxes(fwht(np.swapaxes(V, -1, -2)), -1, -2)
+    return V.reshape(a.shape)
 
 
 # ----------------------------------------------------------------------------

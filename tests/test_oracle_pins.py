@@ -30,6 +30,94 @@ def test_hadamard_worked_example():
     assert np.linalg.norm(out) == pytest.approx(np.linalg.norm(g["x"]), rel=0, abs=1e-12)
 
 
+# ---------------------------------------------------------------- structured Hadamard
+def test_quadratic_character_textbook_residues():
+    # nonzero squares mod 11 are {1, 3, 4, 5, 9}; mod 13 {1, 3, 4, 9, 10, 12};
+    # mod 19 {1, 4, 5, 6, 7, 9, 11, 16, 17}
+    for q, res in ((11, {1, 3, 4, 5, 9}), (13, {1, 3, 4, 9, 10, 12}),
+                   (19, {1, 4, 5, 6, 7, 9, 11, 16, 17})):
+        chi = O.quadratic_character(q)
+        assert chi[0] == 0
+        assert {a for a in range(1, q) if chi[a] == 1} == res
+        # Euler's criterion: chi(a) = a^((q-1)/2) mod q
+        for a in range(1, q):
+            e = pow(a, (q - 1) // 2, q)
+            assert chi[a] == (1 if e == 1 else -1)
+
+
+@pytest.mark.parametrize("m", [12, 20, 28, 36, 44, 60, 108])
+def test_paley_hadamard_is_hadamard(m):
+    H = O.paley_hadamard(m)
+    assert H.shape == (m, m) and set(np.unique(H)) == {-1, 1}
+    np.testing.assert_array_equal(H @ H.T, m * np.eye(m, dtype=np.int64))
+    np.testing.assert_array_equal(H.T @ H, m * np.eye(m, dtype=np.int64))
+
+
+def test_paley_structure():
+    # Paley I (q = 11): H - I is skew-symmetric (a skew Hadamard matrix)
+    H = O.paley_hadamard(12)
+    S = H - np.eye(12, dtype=np.int64)
+    np.testing.assert_array_equal(S, -S.T)
+    # Paley II (q = 13): the 2x2 blocks are +-[[1, 1], [1, -1]] off the diagonal
+    # and [[1, -1], [-1, -1]] on it; H is symmetric
+    H = O.paley_hadamard(28)
+    np.testing.assert_array_equal(H, H.T)
+    for b in range(14):
+        np.testing.assert_array_equal(H[2 * b:2 * b + 2, 2 * b:2 * b + 2], [[1, -1], [-1, -1]])
+    # Jacobsthal properties: J J^T = q I - ones, rows sum to zero
+    for q in (11, 13, 19):
+        J = O.jacobsthal(q)
+        np.testing.assert_array_equal(J @ J.T, q * np.eye(q, dtype=np.int64) - 1)
+        np.testing.assert_array_equal(J.sum(axis=1), 0)
+    with pytest.raises(ValueError):
+        O.paley_hadamard(52)          # q = 51 and q = 25 are not primes
+
+
+@pytest.mark.parametrize("n,m", [(3, 12), (2, 20), (4, 28), (0, 12)])
+def test_hadamard_kron_against_numpy_kron(n, m):
+    rng = np.random.default_rng(n * 100 + m)
+    A = 1 << n
+    D = A * m
+    x = rng.standard_normal((3, D))
+    s = rng.choice([-1.0, 1.0], D)
+    HA = scipy.linalg.hadamard(A).astype(np.float64)                 # library routine
+    Hd = np.kron(HA, O.paley_hadamard(m).astype(np.float64)) / np.sqrt(D)
+    np.testing.assert_allclose(O.hadamard_kron(x, m, s), (x * s) @ Hd.T, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(O.hadamard_kron(x, m), x @ Hd.T, rtol=0, atol=1e-12)
+    # orthogonal: H_d^T undoes it (norm kept)
+    y = O.hadamard_kron(x, m, s)
+    np.testing.assert_allclose((y @ Hd) * s, x, rtol=0, atol=1e-12)
+
+
+def test_hadamard_kron_power_of_two_is_the_wht():
+    x = np.random.default_rng(5).standard_normal((4, 512))
+    np.testing.assert_allclose(O.hadamard_kron(x, 1), O.fwht(x), rtol=0, atol=1e-13)
+    ones = np.ones(512)
+    np.testing.assert_allclose(O.hadamard_kron(x, 1, ones), O.fwht(x), rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("n_h,D", [(32, 4096), (8, 256), (1, 64), (64, 64), (4, 24)])
+def test_head_hadamard_cases(n_h, D):
+    x = np.random.default_rng(n_h + D).standard_normal((3, D))
+    d_h = D // n_h
+    ref = x @ np.kron(scipy.linalg.hadamard(n_h), np.eye(d_h)).T / np.sqrt(n_h)
+    np.testing.assert_allclose(O.head_hadamard(x, n_h), ref, rtol=0, atol=1e-12)
+    if n_h == 1:
+        np.testing.assert_array_equal(O.head_hadamard(x, 1), x)
+    if d_h == 1:
+        np.testing.assert_allclose(O.head_hadamard(x, n_h), O.fwht(x), rtol=0, atol=1e-13)
+
+
+def test_head_hadamard_completes_the_full_transform():
+    # with n_h and d_h powers of two, (H_{n_h} (x) I)(I (x) H_{d_h}) = H_D: the
+    # per-head transform folded into the value/output weights plus the online
+    # transform across heads give the whole Walsh-Hadamard transform
+    n_h, d_h = 32, 128
+    x = np.random.default_rng(9).standard_normal((5, n_h * d_h))
+    within = O.fwht(x.reshape(5, n_h, d_h)).reshape(5, -1)
+    np.testing.assert_allclose(O.head_hadamard(within, n_h), O.fwht(x), rtol=0, atol=1e-12)
+
+
 @pytest.mark.parametrize("D", [2, 4, 8, 64, 256, 1024])
 def test_fwht_matches_scipy_sylvester(D):
     Hs = scipy.linalg.hadamard(D).astype(np.float64) / np.sqrt(D)   # library routine
