@@ -63,9 +63,15 @@ typedef enum rw4_status {
 typedef enum rw4_dtype { RW4_BF16 = 0, RW4_F32 = 1, RW4_I32 = 2 } rw4_dtype;
 
 /* flags of rotated_linear; RW4_ABITS(b) selects b-bit activation codes
-   (b = 2, 3 or 4; 0 in that field means 4) */
-enum { RW4_ALIGN = 1, RW4_FWHT = 2, RW4_SWIGLU = 4, RW4_ABITS_SHIFT = 8 };
+   (b = 2, 3 or 4; 0 in that field means 4). With RW4_FWHT, RW4_KRON(m)
+   (m = 12, 20, 28) makes the transform H_{2^n} (x) H_m over D = 2^n m (see
+   hadamard_transform). RW4_HEADS(k) selects the transform across heads,
+   H_{n_h} (x) I with n_h = 2^k (see head_hadamard), instead of RW4_FWHT. */
+enum { RW4_ALIGN = 1, RW4_FWHT = 2, RW4_SWIGLU = 4, RW4_ABITS_SHIFT = 8, RW4_KRON_SHIFT = 16,
+       RW4_HEADS_SHIFT = 24 };
 #define RW4_ABITS(b) ((unsigned)(b) << RW4_ABITS_SHIFT)
+#define RW4_KRON(m) ((unsigned)(m) << RW4_KRON_SHIFT)
+#define RW4_HEADS(k) ((unsigned)(k) << RW4_HEADS_SHIFT)
 
 /*
  * respin_align -- online low-rank residual alignment [RSQ key design 3].
@@ -206,6 +212,10 @@ rw4_status w4a4_gemm_tiles(const uint8_t* a, const float* s_a, const uint8_t* w,
  *          RW4_FWHT: Hadamard transform of size D before quantization.
  *          RW4_ABITS(b): b-bit activation codes as quant_act_sym (W3A3 with
  *            3-bit weight codes; the GEMM takes any codes in [-7, 7]).
+ *          RW4_KRON(m) with RW4_FWHT: the transform is H_{2^n} (x) H_m of
+ *            hadamard_transform (D = 2^n m, m = 12, 20, 28, D <= 16384).
+ *          RW4_HEADS(k): the transform across 2^k heads of head_hadamard
+ *            instead (no FWHT, ALIGN or SWIGLU; D <= 16384).
  *          flags = 0: quantize x as is. ALIGN and SWIGLU are exclusive.
  *   x        bf16, T rows of D (or 2D with SWIGLU) values, row stride ldx
  *            elements (ldx >= width, ldx % 8 == 0)
@@ -223,7 +233,9 @@ rw4_status w4a4_gemm_tiles(const uint8_t* a, const float* s_a, const uint8_t* w,
  *            internal.
  *   dbg_prequant nullable fp32 [T][D]: if given, receives the fp32 values that
  *            were quantized (for stage-wise checking).
- * Constraints: D a power of two, 64 <= D <= 32768; 1 <= N, T < 2^31 - 256.
+ * Constraints: D a power of two, 64 <= D <= 32768, or with RW4_KRON(m)
+ * D = 2^n m, or with RW4_HEADS(k) any D; for both of these D % 64 == 0 and
+ * D <= 16384. 1 <= N, T < 2^31 - 256.
  */
 rw4_status rotated_linear(const void* x, int64_t ldx, int64_t T, int64_t D,
                           const float* Q, const float* M, int64_t r, unsigned flags,
@@ -233,6 +245,37 @@ rw4_status rotated_linear(const void* x, int64_t ldx, int64_t T, int64_t D,
 
 /* bytes of workspace rotated_linear needs for (T, D, r, flags); 0 on bad input */
 size_t rotated_linear_workspace_size(int64_t T, int64_t D, int64_t r, unsigned flags);
+
+/*
+ * hadamard_transform -- y = H~ x / sqrt(D) for every row, H~ = (H_{2^n} (x) H_m)
+ * diag(s) ["Infra Quant II", QuaRot Background: H_d = H_{2^n} (x) H_m for
+ * d = 2^n m, and the randomized H diag(s) with s in {+1, -1}^d]. H_{2^n} is
+ * the Sylvester (natural-order) matrix. H_m (m = 12, 20, 28; the pages print
+ * none) is Paley's construction: type I (q = m - 1) for 12 and 20, type II
+ * (q = m/2 - 1) for 28, rows and columns ordered as the point at infinity,
+ * then the integers 0..q-1 mod q. m = 1 is the plain transform. Element f of
+ * a row is index (i, j) = (f / m, f % m) of the Kronecker product.
+ *   x      [T][ldx] of x_dt (RW4_BF16 or RW4_F32), D values per row
+ *   y      fp32 [T][D]; may be x itself (fp32, ldx == D)
+ *   signs  nullable, fp32 [D] of +1 / -1 (values not checked)
+ * Constraints: m in {1, 12, 20, 28}; D = 2^n m with n >= 0, D % 4 == 0,
+ * D <= 16384; ldx >= D, ldx % 4 == 0. Arithmetic is fp32.
+ */
+rw4_status hadamard_transform(const void* x, rw4_dtype x_dt, int64_t ldx, float* y, int64_t T,
+                              int64_t D, int64_t m, const float* signs, void* stream);
+
+/*
+ * head_hadamard -- y = (H_{n_h} (x) I_{d_h}) x / sqrt(n_h) for every row: the
+ * online transform across attention heads before the output projection
+ * ["Infra Quant II", QuaRot Method, value projection: Z <- Z (H_{n_h} (x) I)
+ * by reshaping and a Walsh-Hadamard transform; H_{n_h} is symmetric, so this
+ * is the same as the row form]. Element h d_h + c belongs to head h.
+ *   x [T][ldx] of x_dt; y fp32 [T][n_h d_h] (may be x: fp32, ldx == D)
+ * Constraints: n_h a power of two; D = n_h d_h, D % 4 == 0, D <= 16384;
+ * ldx >= D, ldx % 4 == 0.
+ */
+rw4_status head_hadamard(const void* x, rw4_dtype x_dt, int64_t ldx, float* y, int64_t T,
+                         int64_t n_h, int64_t d_h, void* stream);
 
 /*
  * respin_prepare_basis -- the part of the alignment that depends only on the
@@ -301,7 +344,7 @@ const char* rw4_status_string(rw4_status s);
 /* ABI version of this header (bumped on any signature change) */
 int rw4_abi_version(void);
 
-#define RW4_ABI_VERSION 6
+#define RW4_ABI_VERSION 7
 
 #ifdef __cplusplus
 }

@@ -40,12 +40,14 @@ __all__ = [
     "quant_sym", "quant_int4", "pack_int4", "unpack_int4", "gemm_int", "gemm_int_loop",
     "epilogue", "silu_gate", "prep_weight", "prequant", "rotated_linear", "residual", "layer",
     "quadratic_character", "jacobsthal", "paley_hadamard", "hadamard_kron", "head_hadamard",
-    "FLAG_ALIGN", "FLAG_FWHT", "FLAG_SWIGLU",
+    "FLAG_ALIGN", "FLAG_FWHT", "FLAG_SWIGLU", "FLAG_KRON_SHIFT", "FLAG_HEADS_SHIFT",
 ]
 
 FLAG_ALIGN = 1
 FLAG_FWHT = 2
 FLAG_SWIGLU = 4
+FLAG_KRON_SHIFT = 16     # with FLAG_FWHT: H_{2^n} (x) H_m, m in bits 16..23
+FLAG_HEADS_SHIFT = 24    # H_{n_h} (x) I across heads, log2(n_h) in bits 24..28
 
 
 # ----------------------------------------------------------------------------
@@ -354,12 +356,17 @@ def silu_gate(gu: np.ndarray) -> np.ndarray:
 # ----------------------------------------------------------------------------
 # chains
 # ----------------------------------------------------------------------------
-def prep_weight(W: np.ndarray, rotate: bool, bits: int = 4):
+def prep_weight(W: np.ndarray, rotate: bool, bits: int = 4, m: int = 1, signs=None):
     """Offline weight preparation: optional Hadamard rotation of every row along K
-    (the online Hadamard's inverse folded into the weight, [IQ2 QuaRot Method]),
-    then per-output-channel symmetric quantization (rows of W [N][K]).
+    (the online Hadamard's inverse folded into the weight, [IQ2 QuaRot Method]:
+    with x' = H x online, W' = W H^T, i.e. every row w becomes H w; H may be the
+    Kronecker H_{2^n} (x) H_m and randomized by signs), then per-output-channel
+    symmetric quantization (rows of W [N][K]).
     Returns (codes int8 [N][K], s_w float32 [N], the fp32 values that were quantized)."""
-    Wr = fwht(W).astype(np.float32) if rotate else np.asarray(W, np.float32)
+    if rotate:
+        Wr = (fwht(W) if m == 1 and signs is None else hadamard_kron(W, m, signs)).astype(np.float32)
+    else:
+        Wr = np.asarray(W, np.float32)
     q, s = quant_sym(Wr, bits)
     return q, s, Wr
 
@@ -368,15 +375,21 @@ def prequant(x: np.ndarray, flags: int, Q=None, M=None) -> np.ndarray:
     """float64 values that reach the activation quantizer.
 
     ``x`` is float64 [T][D] (or [T][2D] gate|up with FLAG_SWIGLU).  Order:
-    align -> gate -> Hadamard, as selected by ``flags``.
+    align -> gate -> Hadamard, as selected by ``flags``; the Hadamard is H_D
+    (power-of-two D), H_{2^n} (x) H_m (m in the FLAG_KRON_SHIFT field), or
+    the transform across heads (log2 n_h in the FLAG_HEADS_SHIFT field).
     """
     v = np.asarray(x, np.float64)
+    m = (flags >> FLAG_KRON_SHIFT) & 0xFF
+    lg = (flags >> FLAG_HEADS_SHIFT) & 0x1F
     if flags & FLAG_ALIGN:
         v = align(v, Q, M)
     if flags & FLAG_SWIGLU:
         v = silu_gate(v)
     if flags & FLAG_FWHT:
-        v = fwht(v)
+        v = hadamard_kron(v, m) if m else fwht(v)
+    if lg:
+        v = head_hadamard(v, 1 << lg)
     return v
 
 

@@ -20,7 +20,7 @@ __all__ = [
     "respin_align_prepared", "respin_align_prepared_workspace_size",
     "rotated_linear_prepared_workspace_size",
     "w4a4_tiles_size", "w4a4_tile_codes", "w4a4_gemm_tiles", "prep_weight", "layer",
-    "quant_act_sym", "RW4_ABITS",
+    "quant_act_sym", "RW4_ABITS", "RW4_KRON", "RW4_HEADS", "hadamard_transform", "head_hadamard",
 ]
 
 RW4_ALIGN, RW4_FWHT, RW4_SWIGLU = 1, 2, 4
@@ -29,6 +29,18 @@ RW4_ALIGN, RW4_FWHT, RW4_SWIGLU = 1, 2, 4
 def RW4_ABITS(bits: int) -> int:
     """rotated_linear flag field for b-bit activation codes (b = 2, 3, 4)."""
     return bits << 8
+
+
+def RW4_KRON(m: int) -> int:
+    """rotated_linear flag field (with RW4_FWHT): H_{2^n} (x) H_m, m = 12, 20, 28."""
+    return m << 16
+
+
+def RW4_HEADS(n_h: int) -> int:
+    """rotated_linear flag field: the transform across n_h heads (a power of two)."""
+    if n_h < 2 or n_h & (n_h - 1):
+        raise ValueError("n_h must be a power of two >= 2")
+    return (n_h.bit_length() - 1) << 24
 _BF16, _F32, _I32 = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -40,7 +52,8 @@ EXPORTS = ("respin_align", "respin_align_workspace_size", "fwht", "quant_act_int
            "w4a4_tiles_size", "w4a4_tile_codes", "w4a4_gemm_tiles", "rotated_linear",
            "rotated_linear_workspace_size", "respin_basis_size", "respin_prepare_basis",
            "rotated_linear_prepared", "rotated_linear_prepared_workspace_size",
-           "respin_align_prepared", "respin_align_prepared_workspace_size", "rw4_align256",
+           "respin_align_prepared", "respin_align_prepared_workspace_size",
+           "hadamard_transform", "head_hadamard", "rw4_align256",
            "rw4_status_string", "rw4_abi_version")
 
 
@@ -87,6 +100,8 @@ def lib() -> ctypes.CDLL:
     L.respin_align_prepared.argtypes = [vp, vp, i32, vp, vp, i64, i64, i64, vp, sz, vp]
     L.respin_align_prepared_workspace_size.argtypes = [i64, i64, i64]
     L.respin_align_prepared_workspace_size.restype = sz
+    L.hadamard_transform.argtypes = [vp, i32, i64, vp, i64, i64, i64, vp, vp]
+    L.head_hadamard.argtypes = [vp, i32, i64, vp, i64, i64, i64, vp]
     L.rw4_align256.argtypes = [sz]
     L.rw4_align256.restype = sz
     L.rw4_status_string.argtypes = [i32]
@@ -95,7 +110,8 @@ def lib() -> ctypes.CDLL:
     for f in ("respin_align", "fwht", "quant_act_int4", "quant_act_sym", "w4a4_gemm",
               "w4a4_tile_codes",
               "w4a4_gemm_tiles", "rotated_linear", "respin_prepare_basis",
-              "rotated_linear_prepared", "respin_align_prepared"):
+              "rotated_linear_prepared", "respin_align_prepared", "hadamard_transform",
+              "head_hadamard"):
         getattr(L, f).restype = i32
     _lib = L
     return L
@@ -219,6 +235,39 @@ def fwht(x, out=None):
         out = torch.empty((T, D), dtype=torch.float32, device=x.device)
     st = lib().fwht(_p(x), _fdt(x), _p(out), T, D, _stream())
     _check("fwht", st)
+    return out
+
+
+def hadamard_transform(x, m: int = 1, signs=None, out=None, D: int = None):
+    """(H_{2^n} (x) H_m) diag(signs) x / sqrt(D) for every row -> fp32 [T][D]
+    (H_m by Paley's construction, m = 12, 20, 28; m = 1 the plain transform).
+    x may be row-strided; D defaults to its width; out may be x (fp32)."""
+    torch = _torch()
+    _rows(x)
+    T = x.shape[0]
+    D = x.shape[1] if D is None else D
+    if out is None:
+        out = torch.empty((T, D), dtype=torch.float32, device=x.device)
+    if signs is not None and (signs.dtype != torch.float32 or signs.numel() != D
+                              or not signs.is_cuda or not signs.is_contiguous()):
+        raise ValueError("signs: contiguous fp32 [D] on the device")
+    st = lib().hadamard_transform(_p(x), _fdt(x), x.stride(0), _p(out), T, D, m, _p(signs),
+                                  _stream())
+    _check("hadamard_transform", st)
+    return out
+
+
+def head_hadamard(x, n_h: int, out=None):
+    """(H_{n_h} (x) I_{d_h}) x / sqrt(n_h) for every row -> fp32 [T][D]."""
+    torch = _torch()
+    _rows(x)
+    T, D = x.shape
+    if D % n_h:
+        raise ValueError("D must be a multiple of n_h")
+    if out is None:
+        out = torch.empty((T, D), dtype=torch.float32, device=x.device)
+    st = lib().head_hadamard(_p(x), _fdt(x), x.stride(0), _p(out), T, n_h, D // n_h, _stream())
+    _check("head_hadamard", st)
     return out
 
 
@@ -410,12 +459,16 @@ def workspace_views(workspace, T: int, D: int):
     return tiles, scales
 
 
-def prep_weight(W, rotate: bool, bits: int = 4):
+def prep_weight(W, rotate: bool, bits: int = 4, m: int = 1, signs=None):
     """Offline weight preparation on the GPU: optional row-wise Hadamard along K
-    (fwht), per-output-channel b-bit codes (quant_act_sym), then FP6 tiles.
+    (fwht; H_{2^n} (x) H_m and random signs with hadamard_transform), per-output-
+    channel b-bit codes (quant_act_sym), then FP6 tiles.
     W fp32 [N][K]. Returns (tiles, s_w, codes [N][K/2], rotated W)."""
     _contig(W)
-    src = fwht(W) if rotate else W
+    if rotate:
+        src = fwht(W) if m == 1 and signs is None else hadamard_transform(W, m, signs)
+    else:
+        src = W
     codes, s_w = quant_act_sym(src, bits)
     tiles = w4a4_tile_codes(codes)
     return tiles, s_w, codes, src

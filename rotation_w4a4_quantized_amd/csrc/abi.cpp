@@ -32,7 +32,32 @@ inline int abits(unsigned flags) {
   const int b = static_cast<int>((flags >> RW4_ABITS_SHIFT) & 0xFu);
   return b == 0 ? 4 : b;
 }
-constexpr unsigned kFlagMask = RW4_ALIGN | RW4_FWHT | RW4_SWIGLU | (0xFu << RW4_ABITS_SHIFT);
+constexpr unsigned kFlagMask = RW4_ALIGN | RW4_FWHT | RW4_SWIGLU | (0xFu << RW4_ABITS_SHIFT) |
+                               (0xFFu << RW4_KRON_SHIFT) | (0x1Fu << RW4_HEADS_SHIFT);
+inline int kron_m(unsigned flags) { return static_cast<int>((flags >> RW4_KRON_SHIFT) & 0xFFu); }
+inline int heads_lg(unsigned flags) { return static_cast<int>((flags >> RW4_HEADS_SHIFT) & 0x1Fu); }
+
+// D and the transform flags of the unit: a power-of-two D for the plain
+// transform, or D = 2^n m / D = n_h d_h for the structured ones (kernel
+// limits: D % 64 == 0 for the tiles, D <= kKronMaxD)
+rw4_status check_transform(int64_t D, unsigned flags) {
+  const int m = kron_m(flags), lg = heads_lg(flags);
+  if (m && lg) return RW4_ERR_INVALID_ARG;
+  if (m) {
+    if (!(flags & RW4_FWHT)) return RW4_ERR_INVALID_ARG;
+    if (!rw4::kron_order_supported(m)) return RW4_ERR_UNSUPPORTED;
+    if (D % m != 0 || !pow2(D / m) || D % 64 != 0 || D > rw4::kKronMaxD) return RW4_ERR_UNSUPPORTED;
+    return RW4_OK;
+  }
+  if (lg) {
+    if (flags & (RW4_FWHT | RW4_ALIGN | RW4_SWIGLU)) return RW4_ERR_INVALID_ARG;
+    if (lg > 14 || D % (int64_t(1) << lg) != 0 || D % 64 != 0 || D > rw4::kKronMaxD)
+      return RW4_ERR_UNSUPPORTED;
+    return RW4_OK;
+  }
+  if (!pow2(D) || D < 64 || D > 32768) return RW4_ERR_UNSUPPORTED;
+  return RW4_OK;
+}
 
 // P (the Hadamard image of the basis) is prepared when the fused prologue can run
 inline bool with_p(int64_t D, int64_t r) { return rw4::lfq_supported(D, r); }
@@ -59,7 +84,8 @@ rw4_status check_linear(const void* x, int64_t ldx, int64_t T, int64_t D, int64_
   if (flags & ~kFlagMask) return RW4_ERR_INVALID_ARG;
   if ((flags & RW4_ALIGN) && (flags & RW4_SWIGLU)) return RW4_ERR_INVALID_ARG;
   if (abits(flags) < 2 || abits(flags) > 4) return RW4_ERR_INVALID_ARG;
-  if (!pow2(D) || D < 64 || D > 32768) return RW4_ERR_UNSUPPORTED;
+  const rw4_status ts = check_transform(D, flags);
+  if (ts != RW4_OK) return ts;
   if (T == 0) return RW4_OK;
   if (!x || !w || !s_w || !y) return RW4_ERR_INVALID_ARG;
   const int64_t width = (flags & RW4_SWIGLU) ? 2 * D : D;
@@ -108,8 +134,19 @@ rw4_status run_linear(const void* x, int64_t ldx, int64_t T, int64_t D, const vo
     in = rw4::IN_F32;
     ld = D;
   }
-  hipError_t e = rw4::launch_row(src, in, ld, T, D, (flags & RW4_FWHT) != 0, nullptr, codes, true,
-                                 s_a, dbg, s, abits(flags));
+  hipError_t e;
+  if (kron_m(flags) || heads_lg(flags)) {
+    const int m = kron_m(flags);
+    const int64_t A = m ? D / m : (int64_t(1) << heads_lg(flags));
+    const int64_t B = D / A;
+    const double c = m ? static_cast<double>(D) : static_cast<double>(A);
+    e = rw4::launch_kron(src, in, ld, T, A, B, m, nullptr,
+                         static_cast<float>(1.0 / __builtin_sqrt(c)), nullptr, codes, true, s_a,
+                         dbg, abits(flags), s);
+  } else {
+    e = rw4::launch_row(src, in, ld, T, D, (flags & RW4_FWHT) != 0, nullptr, codes, true, s_a, dbg,
+                        s, abits(flags));
+  }
   if (e != hipSuccess) return RW4_ERR_HIP;
   return hip_status(rw4::launch_gemm_tiles(codes, s_a, w, s_w, y, false, T, D, N, s));
 }
@@ -170,6 +207,38 @@ rw4_status fwht(const void* x, rw4_dtype x_dt, float* y, int64_t T, int64_t D, v
   if (T == 0) return RW4_OK;
   return hip_status(rw4::launch_row(x, x_dt == RW4_F32 ? rw4::IN_F32 : rw4::IN_BF16, D, T, D, true,
                                     y, nullptr, false, nullptr, nullptr, strm(stream)));
+}
+
+rw4_status hadamard_transform(const void* x, rw4_dtype x_dt, int64_t ldx, float* y, int64_t T,
+                              int64_t D, int64_t m, const float* signs, void* stream) {
+  if (T < 0 || !fdt(x_dt)) return RW4_ERR_INVALID_ARG;
+  if (m != 1 && !rw4::kron_order_supported(m)) return RW4_ERR_UNSUPPORTED;
+  if (D < 4 || D % m != 0 || !pow2(D / m) || D % 4 != 0 || D > rw4::kKronMaxD)
+    return RW4_ERR_UNSUPPORTED;
+  if (T == 0) return RW4_OK;
+  if (!x || !y || ldx < D || ldx % 4 != 0) return RW4_ERR_INVALID_ARG;
+  if (!al16(x) || !al16(y) || (signs && !al16(signs))) return RW4_ERR_MISALIGNED;
+  if (x == static_cast<const void*>(y) && (x_dt != RW4_F32 || ldx != D)) return RW4_ERR_INVALID_ARG;
+  const int64_t A = D / m;
+  return hip_status(rw4::launch_kron(x, x_dt == RW4_F32 ? rw4::IN_F32 : rw4::IN_BF16, ldx, T, A,
+                                     m, m == 1 ? 0 : static_cast<int>(m), signs,
+                                     static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(D))),
+                                     y, nullptr, false, nullptr, nullptr, 4, strm(stream)));
+}
+
+rw4_status head_hadamard(const void* x, rw4_dtype x_dt, int64_t ldx, float* y, int64_t T,
+                         int64_t n_h, int64_t d_h, void* stream) {
+  if (T < 0 || !fdt(x_dt) || n_h < 1 || d_h < 1) return RW4_ERR_INVALID_ARG;
+  if (!pow2(n_h) || n_h * d_h > rw4::kKronMaxD || (n_h * d_h) % 4 != 0) return RW4_ERR_UNSUPPORTED;
+  const int64_t D = n_h * d_h;
+  if (T == 0) return RW4_OK;
+  if (!x || !y || ldx < D || ldx % 4 != 0) return RW4_ERR_INVALID_ARG;
+  if (!al16(x) || !al16(y)) return RW4_ERR_MISALIGNED;
+  if (x == static_cast<const void*>(y) && (x_dt != RW4_F32 || ldx != D)) return RW4_ERR_INVALID_ARG;
+  return hip_status(rw4::launch_kron(x, x_dt == RW4_F32 ? rw4::IN_F32 : rw4::IN_BF16, ldx, T, n_h,
+                                     d_h, 0, nullptr,
+                                     static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(n_h))),
+                                     y, nullptr, false, nullptr, nullptr, 4, strm(stream)));
 }
 
 rw4_status quant_act_sym(const void* x, rw4_dtype x_dt, uint8_t* codes, float* scales, int64_t T,
@@ -283,7 +352,7 @@ rw4_status respin_align_prepared(const void* x, void* out, rw4_dtype out_dt, con
 }
 
 size_t rotated_linear_prepared_workspace_size(int64_t T, int64_t D, int64_t r, unsigned flags) {
-  if (T < 0 || !pow2(D) || D < 64 || D > 32768 || r < 0) return 0;
+  if (T < 0 || r < 0 || (flags & ~kFlagMask) || check_transform(D, flags) != RW4_OK) return 0;
   if ((flags & RW4_ALIGN) && r > 0 && respin_basis_size(D, r) == 0) return 0;
   return call_ws_bytes(T, D, (flags & RW4_ALIGN) ? r : 0);
 }

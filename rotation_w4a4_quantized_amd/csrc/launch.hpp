@@ -16,6 +16,17 @@ hipError_t launch_row(const void* x, int in_mode, int64_t ldx, int64_t T, int64_
                       float* yf, uint8_t* codes, bool tiled, float* scales, float* dbg,
                       hipStream_t s, int bits = 4);
 
+// Structured Hadamard transform of rows, y = (H_A (x) K_B) diag(s) x * norm
+// with A a power of two, K_B = Paley H_m (m = B in {12, 20, 28}) or the
+// identity (m = 0); D = A B <= kKronMaxD, D % 4 == 0. Output fp32 rows (y),
+// or b-bit codes + scales (+ fp32 dump) as packed INT4 rows or FP6 tiles
+// (then D % 32 == 0, tiles D % 64 == 0). signs nullable ([D] of +-1).
+constexpr int kKronMaxD = 16384;
+bool kron_order_supported(int64_t m);
+hipError_t launch_kron(const void* x, int in_mode, int64_t ldx, int64_t T, int64_t A, int64_t B,
+                       int m, const float* signs, float norm, float* y, uint8_t* codes,
+                       bool tiled, float* scales, float* dbg, int bits, hipStream_t s);
+
 // Per-row b-bit quantization for any even D (no transform).
 hipError_t launch_quant_generic(const void* x, int in_mode, int64_t ldx, int64_t T, int64_t D,
                                 uint8_t* codes, float* scales, hipStream_t s, int bits = 4);

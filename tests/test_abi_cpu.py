@@ -22,7 +22,7 @@ def _declared():
 def test_library_built_and_loads():
     assert os.path.exists(rw.library_path), "build the HIP library first"
     L = rw.lib()
-    assert L.rw4_abi_version() == 6
+    assert L.rw4_abi_version() == 7
 
 
 def test_exports_every_declared_symbol():
@@ -241,6 +241,41 @@ def test_respin_align_prepared_validation():
     assert _rap(ws=NUL) == WSE and _rap(wsb=100) == WSE
     assert _rap(ws=ctypes.c_void_p(0x40010)) == WSE
     assert _rap(T=0, ws=NUL) == 0
+
+
+def test_structured_transform_validation():
+    L = rw.lib()
+    ht = lambda x=A, dt=0, ldx=192, y=B, T=4, D=192, m=12, sg=NUL: L.hadamard_transform(
+        x, dt, ldx, y, T, D, m, sg, NUL)
+    assert ht(m=16) == UNS and ht(m=52) == UNS and ht(D=200) == UNS   # order, D not 2^n m
+    assert ht(D=12 * 2048) == UNS                 # beyond 16384
+    assert ht(dt=2) == INV and ht(T=-1) == INV
+    assert ht(ldx=100) == INV and ht(ldx=194) == INV
+    assert ht(x=NUL) == INV and ht(y=NUL) == INV
+    assert ht(x=ODD) == MIS and ht(sg=ODD) == MIS
+    assert ht(y=A) == INV                         # in place needs fp32 input
+    assert ht(y=A, dt=1, ldx=256) == INV          # ... and ldx == D
+    assert ht(T=0, x=NUL, y=NUL) == 0
+    hh = lambda x=A, dt=0, ldx=4096, y=B, T=4, nh=32, dh=128: L.head_hadamard(
+        x, dt, ldx, y, T, nh, dh, NUL)
+    assert hh(nh=24) == UNS and hh(nh=256, dh=128) == UNS and hh(nh=1, dh=6) == UNS
+    assert hh(nh=0) == INV and hh(dh=0) == INV and hh(ldx=4000) == INV
+    assert hh(x=ODD) == MIS and hh(y=A) == INV
+    assert hh(T=0, x=NUL, y=NUL) == 0
+    # rotated_linear flag fields
+    K28, H5 = 28 << 16, 5 << 24
+    assert L.rotated_linear_prepared_workspace_size(64, 28 * 512, 0, 2 | K28) > 0
+    assert L.rotated_linear_prepared_workspace_size(64, 28 * 512, 0, K28) == 0   # needs FWHT
+    assert L.rotated_linear_prepared_workspace_size(64, 28 * 1024, 0, 2 | K28) == 0  # > 16384
+    assert L.rotated_linear_prepared_workspace_size(64, 12 * 4, 0, 2 | (12 << 16)) == 0  # D % 64
+    assert L.rotated_linear_prepared_workspace_size(64, 4096, 0, H5) > 0
+    assert L.rotated_linear_prepared_workspace_size(64, 4096, 0, H5 | 2) == 0
+    assert L.rotated_linear_prepared_workspace_size(64, 4096, 0, H5 | K28 | 2) == 0
+    assert _rl(D=28 * 16, ldx=28 * 16, flags=K28, r=0) == INV
+    assert _rl(D=28 * 16, ldx=28 * 16, flags=2 | (16 << 16), r=0) == UNS
+    assert _rl(D=4096, ldx=4096, flags=H5 | 1, r=0) == INV
+    assert _rl(D=4096, ldx=4096, flags=(15 << 24), r=0) == UNS
+    assert _rl(D=4096, ldx=4096, flags=(1 << 29), r=0) == INV   # unknown bit
 
 
 def test_quant_sym_validation():

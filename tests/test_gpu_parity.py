@@ -132,6 +132,63 @@ def test_fwht_in_place_and_involution(rw):
     assert normwise(host(g), x) <= 2 * FP32_TOL
 
 
+# ---------------------------------------------------------------- structured Hadamard
+@pytest.mark.parametrize("T,n,m", [(37, 4, 12), (9, 5, 20), (5, 9, 28), (20, 12, 1), (3, 14, 1),
+                                   (2, 1, 12), (4, 0, 28), (6, 8, 20)])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("randomized", [False, True])
+def test_hadamard_transform(rw, T, n, m, dt, randomized):
+    """(H_{2^n} (x) H_m) diag(s) x / sqrt(D) against the oracle (Paley H_m)."""
+    D = (1 << n) * m
+    say(f"hadamard_transform T={T} D={D} m={m} {dt} signs={randomized}")
+    rng = np.random.default_rng(D + T + m)
+    x32 = W.bf16_bits_to_f32(W.gen_x(D + T, T, D, min(4, D // 2), 40.0))
+    s = rng.choice([-1.0, 1.0], D).astype(np.float32) if randomized else None
+    xg = dev(W.f32_to_bf16_bits(x32)) if dt == "bf16" else dev(x32)
+    out = host(rw.hadamard_transform(xg, m, dev(s) if s is not None else None))
+    assert normwise(out, O.hadamard_kron(x32, m, s)) <= FP32_TOL
+
+
+def test_hadamard_transform_in_place_strided_and_inverse(rw):
+    T, m, n = 11, 28, 6
+    D = (1 << n) * m
+    x32 = W.bf16_bits_to_f32(W.gen_x(3, T, D, 4, 40.0))
+    g = dev(x32)
+    rw.hadamard_transform(g, m, out=g)                     # in place
+    y = host(g)
+    assert normwise(y, O.hadamard_kron(x32, m)) <= FP32_TOL
+    # the transpose undoes it (orthogonal): H_D^T y = x
+    Hd = np.kron(O.hadamard(1 << n) * np.sqrt(1 << n), O.paley_hadamard(m)) / np.sqrt(D)
+    assert normwise(y.astype(np.float64) @ Hd, x32) <= 2 * FP32_TOL
+    # row-strided input: the middle third of wider rows
+    big = W.gen_x(4, T, 3 * D, 4, 40.0)
+    gb = dev(big)[:, D:2 * D]
+    out = host(rw.hadamard_transform(gb, m))
+    assert normwise(out, O.hadamard_kron(W.bf16_bits_to_f32(big[:, D:2 * D]), m)) <= FP32_TOL
+
+
+@pytest.mark.parametrize("T,n_h,d_h", [(33, 32, 128), (7, 8, 32), (5, 64, 64), (4, 4, 6),
+                                       (3, 128, 128), (9, 2, 48)])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_head_hadamard(rw, T, n_h, d_h, dt):
+    D = n_h * d_h
+    say(f"head_hadamard T={T} n_h={n_h} d_h={d_h} {dt}")
+    x32 = W.bf16_bits_to_f32(W.gen_x(D + 7, T, D, min(4, D // 2), 40.0))
+    xg = dev(W.f32_to_bf16_bits(x32)) if dt == "bf16" else dev(x32)
+    out = host(rw.head_hadamard(xg, n_h))
+    assert normwise(out, O.head_hadamard(x32, n_h)) <= FP32_TOL
+
+
+def test_head_hadamard_completes_the_transform(rw):
+    """The page's identity on the GPU: the transform within heads (fwht of
+    each head's d_h values) followed by the one across heads is H_D."""
+    T, n_h, d_h = 12, 32, 128
+    x32 = W.bf16_bits_to_f32(W.gen_x(8, T, n_h * d_h, 4, 40.0))
+    within = rw.fwht(dev(x32.reshape(T * n_h, d_h))).reshape(T, n_h * d_h)
+    out = host(rw.head_hadamard(within, n_h))
+    assert normwise(out, O.fwht(x32)) <= 2 * FP32_TOL
+
+
 # ---------------------------------------------------------------- alignment
 @pytest.mark.parametrize("T,D,r", [(64, 256, 8), (37, 4096, 32), (19, 8192, 64), (9, 4096, 128),
                                    (13, 1000, 12), (1, 64, 4)])
@@ -335,11 +392,12 @@ def test_w4a4_gemm_tiles_extremes(rw):
 
 
 # ---------------------------------------------------------------- weight prep and the unit
-def _prep(rw, Wf, rotate, bits=4):
-    tiles, s_w, codes, src = rw.prep_weight(dev(Wf), rotate, bits)
+def _prep(rw, Wf, rotate, bits=4, m=1, signs=None):
+    tiles, s_w, codes, src = rw.prep_weight(dev(Wf), rotate, bits, m,
+                                            dev(signs) if signs is not None else None)
     src_h = host(src)
     if rotate:
-        assert normwise(src_h, O.fwht(Wf)) <= FP32_TOL
+        assert normwise(src_h, O.hadamard_kron(Wf, m, signs)) <= FP32_TOL
     q, s = O.quant_sym(src_h, bits)
     np.testing.assert_array_equal(host(s_w), s)
     np.testing.assert_array_equal(host(codes), O.pack_int4(q))
@@ -468,6 +526,35 @@ def test_rotated_linear_low_bits(rw, T, D, N, r, flags, bits):
     codes_w, s_w, qw, sw_h = _prep(rw, Wf, bool(flags & 2), bits)
     assert np.abs(qw).max() == 2 ** (bits - 1) - 1
     _check_unit(rw, xb, Q, M, flags | rw.RW4_ABITS(bits), codes_w, s_w, qw, sw_h)
+
+
+# structured transforms inside the unit: H_{2^n} (x) H_m (the FFN width
+# 14336 = 512 x 28 of the pages' 8B model, gated), after the alignment on the
+# unfused path, and the transform across heads before the output projection
+@pytest.mark.parametrize("T,D,N,r,flags,m,bits", [
+    (50, 14336, 64, 0, 4 | 2, 28, 4), (37, 28 * 512, 96, 0, 2, 28, 4),
+    (21, 640, 64, 16, 1 | 2, 20, 4), (130, 768, 128, 0, 2, 12, 3),
+    (33, 4096, 128, 0, 0, 0, 4), (9, 2048, 64, 0, 0, 0, 3)])
+def test_rotated_linear_structured(rw, T, D, N, r, flags, m, bits):
+    fl = flags | rw.RW4_ABITS(bits)
+    if m:
+        fl |= rw.RW4_KRON(m)
+    else:
+        fl |= rw.RW4_HEADS(32 if D == 4096 else 16)
+    say(f"rotated_linear structured T={T} D={D} N={N} r={r} flags={fl:#x}")
+    width = 2 * D if flags & 4 else D
+    xb = W.gen_x(T + D + m, T, width, 4, 30.0)
+    Q, M = W.gen_basis(T + r, D, r) if flags & 1 else (None, None)
+    Wf = W.gen_weight(N + m, N, D, 0.02)
+    rotate = m > 0
+    signs = np.random.default_rng(D).choice([-1.0, 1.0], D).astype(np.float32) if m == 12 else None
+    if signs is not None:
+        # a randomized rotation of the weights exercises the signs; the unit's
+        # own online transform is the plain one, so the weights it sees are
+        # only used for the GEMM stage check
+        _prep(rw, Wf, True, bits, m, signs)
+    codes_w, s_w, qw, sw_h = _prep(rw, Wf, rotate, bits, m if m else 1)
+    _check_unit(rw, xb, Q, M, fl, codes_w, s_w, qw, sw_h)
 
 
 def test_rotated_linear_strided_input(rw):

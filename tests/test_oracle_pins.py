@@ -118,6 +118,24 @@ def test_head_hadamard_completes_the_full_transform():
     np.testing.assert_allclose(O.head_hadamard(within, n_h), O.fwht(x), rtol=0, atol=1e-12)
 
 
+def test_prequant_structured_transforms():
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((3, 28 * 16))
+    fl = O.FLAG_FWHT | (28 << O.FLAG_KRON_SHIFT)
+    Hd = np.kron(scipy.linalg.hadamard(16), O.paley_hadamard(28)) / np.sqrt(28 * 16)
+    np.testing.assert_allclose(O.prequant(x, fl), x @ Hd.T, rtol=0, atol=1e-12)
+    y = rng.standard_normal((3, 256))
+    fl = 3 << O.FLAG_HEADS_SHIFT
+    Hh = np.kron(scipy.linalg.hadamard(8), np.eye(32)) / np.sqrt(8)
+    np.testing.assert_allclose(O.prequant(y, fl), y @ Hh.T, rtol=0, atol=1e-12)
+    # weight preparation folds the same transform into the rows: W' x' = W x
+    W = rng.standard_normal((5, 28 * 16))
+    s = rng.choice([-1.0, 1.0], 28 * 16)
+    _, _, Wr = O.prep_weight(W, True, 4, 28, s)
+    xs = O.hadamard_kron(x, 28, s)
+    np.testing.assert_allclose(xs @ Wr.astype(np.float64).T, x @ W.T, rtol=0, atol=1e-5)
+
+
 @pytest.mark.parametrize("D", [2, 4, 8, 64, 256, 1024])
 def test_fwht_matches_scipy_sylvester(D):
     Hs = scipy.linalg.hadamard(D).astype(np.float64) / np.sqrt(D)   # library routine
