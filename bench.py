@@ -90,6 +90,43 @@ def cpu_baseline(wl, inp, seconds):
                       f"{t_total:.1f} s"}
 
 
+def structured_rows(rw, torch, dev, timed, with_oracle):
+    """The structured transforms on their workload shapes: H_{2^n} (x) H_m with
+    random signs at the gated FFN width of the pages' 8B model (T = 4096
+    tokens of the prefill layer, D = 14336 = 512 x 28), and the transform
+    across 32 heads at the prefill linear (T = 2048, D = 4096, d_h = 128);
+    bf16 in, fp32 out. Algorithmic bytes: T D (2 + 4), plus 4 D of signs."""
+    import workloads as W
+    out = {}
+    g = torch.Generator().manual_seed(7)
+    cases = [("hadamard_kron_m28_signs", 4096, 14336, 28), ("head_hadamard_nh32", 2048, 4096, 0)]
+    for name, T, D, m in cases:
+        x = torch.randn((T, D), generator=g).to(torch.bfloat16).to(dev)
+        y = torch.empty((T, D), dtype=torch.float32, device=dev)
+        if m:
+            s = (torch.randint(0, 2, (D,), generator=g).float() * 2 - 1).to(dev)
+            fn = lambda: rw.hadamard_transform(x, m, s, out=y)
+            nbytes = T * D * 6 + 4 * D
+        else:
+            fn = lambda: rw.head_hadamard(x, 32, out=y)
+            nbytes = T * D * 6
+        ms = timed(fn)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        rec = {"T": T, "D": D, "us": ms * 1e3, "bytes": nbytes, "GB/s": gbs,
+               "frac_hbm": gbs / PEAK_HBM_GBS, "rows_per_s": T / (ms * 1e-3)}
+        if with_oracle:
+            import oracle as O
+            xs = W.bf16_bits_to_f32(W.f32_to_bf16_bits(np.random.default_rng(1).standard_normal((256, D)).astype(np.float32)))
+            t0 = time.perf_counter()
+            if m:
+                O.hadamard_kron(xs, m, np.ones(D))
+            else:
+                O.head_hadamard(xs, 32)
+            rec["oracle_rows_per_s"] = 256 / (time.perf_counter() - t0)
+        out[name] = rec
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -208,6 +245,8 @@ def main():
     fwht_ms = timed(lambda: rw.fwht(tmp, out=tmp))
     quant_ms = timed(lambda: rw.quant_act_int4(tmp, codes_t, sa_t))
 
+    rows = structured_rows(rw, torch, dev, timed, not args.no_cpu_baseline)
+
     if args.copy_calibration:
         src = torch.empty((256 << 20,), dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -257,6 +296,7 @@ def main():
                       "align_with_basis_prep": align_unprep_ms * 1e3,
                       "step_with_basis_prep": unprepared_ms * 1e3},
         "stages_vs_hbm": bw,
+        "structured_transforms": rows,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)

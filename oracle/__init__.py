@@ -36,7 +36,8 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "bf16_to_f64", "f64_to_bf16", "align", "align_dense", "t_hat", "fwht", "hadamard",
+    "bf16_to_f64", "f64_to_bf16", "align", "align_dense", "t_hat", "construct_basis", "fwht",
+    "hadamard",
     "quant_sym", "quant_int4", "pack_int4", "unpack_int4", "gemm_int", "gemm_int_loop",
     "epilogue", "silu_gate", "prep_weight", "prequant", "rotated_linear", "residual", "layer",
     "quadratic_character", "jacobsthal", "paley_hadamard", "hadamard_kron", "head_hadamard",
@@ -102,6 +103,26 @@ def t_hat(Q: np.ndarray, M: np.ndarray) -> np.ndarray:
     M = np.asarray(M, np.float64)
     D, r = Q.shape
     return np.eye(D) + Q @ (M - np.eye(r)) @ Q.T
+
+
+def construct_basis(T: np.ndarray, r: int):
+    """Offline (Q, R_sub) of a residual transition T = R_out R_in^T, the steps of
+    [RSQ 关键设计 2] in order:
+      1. Delta T = T - I;
+      2. its SVD; Q = the top-r left singular vectors ([D][r]);
+      3. T_sub = Q^T T Q (r x r);
+      4. polar decomposition of T_sub = U_sub S V_sub^T: R_sub = U_sub V_sub^T.
+    T_hat = I + Q (R_sub - I) Q^T (t_hat) is then orthogonal. Q is unique up
+    to a rotation inside degenerate singular subspaces (the planes of T come
+    in pairs of equal singular values); T_hat depends only on span(Q).
+    Returns (Q, R_sub, singular values of Delta T), float64."""
+    T = np.asarray(T, np.float64)
+    D = T.shape[0]
+    U, S, _ = np.linalg.svd(T - np.eye(D))
+    Q = U[:, :r]
+    Tsub = Q.T @ T @ Q
+    Us, _, Vts = np.linalg.svd(Tsub)
+    return Q, Us @ Vts, S
 
 
 def align_dense(x: np.ndarray, Q: np.ndarray, M: np.ndarray) -> np.ndarray:

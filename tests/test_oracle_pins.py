@@ -194,6 +194,78 @@ def test_t_hat_is_special_orthogonal():
     assert np.linalg.det(Td) == pytest.approx(1.0, abs=1e-12)
 
 
+# ---------------------------------------------------------------- offline construction
+def _rand_orth(rng, D):
+    Qm, R = np.linalg.qr(rng.standard_normal((D, D)))
+    Qm = Qm * np.sign(np.diag(R))
+    if np.linalg.det(Qm) < 0:
+        Qm[:, 0] = -Qm[:, 0]
+    return Qm
+
+
+def test_construct_recovers_an_exact_rank_r_transition():
+    # T = I + Q0 (M0 - I) Q0^T: Delta T has rank r, its top-r left singular
+    # vectors span col(Q0), T_sub = O^T M0 O is orthogonal already, so T_hat = T
+    Q0, M0 = W.gen_basis(31, 96, 12, skew_std=0.3)
+    Q0, M0 = Q0.astype(np.float64), M0.astype(np.float64)
+    Q0, _ = np.linalg.qr(Q0)
+    U, _, Vt = np.linalg.svd(M0)
+    M0 = U @ Vt                                           # exactly orthogonal in fp64
+    T = np.eye(96) + Q0 @ (M0 - np.eye(12)) @ Q0.T
+    Q, R, S = O.construct_basis(T, 12)
+    np.testing.assert_allclose(O.t_hat(Q, R), T, rtol=0, atol=1e-12)
+    assert S[12] < 1e-12 and S[11] > 1e-3
+    # the projector onto span(Q) is that of Q0
+    np.testing.assert_allclose(Q @ Q.T, Q0 @ Q0.T, rtol=0, atol=1e-12)
+
+
+def test_construct_full_rank_returns_the_transition():
+    T = _rand_orth(np.random.default_rng(3), 24)
+    Q, R, _ = O.construct_basis(T, 24)
+    np.testing.assert_allclose(O.t_hat(Q, R), T, rtol=0, atol=1e-12)
+
+
+def test_construct_polar_step():
+    T = W.gen_hadamard_transition(5, 64, 6).astype(np.float64)
+    Q, R, _ = O.construct_basis(T, 12)
+    Tsub = Q.T @ T @ Q
+    Rp, Pp = scipy.linalg.polar(Tsub)                         # library routine
+    np.testing.assert_allclose(R, Rp, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(R.T @ R, np.eye(12), rtol=0, atol=1e-12)
+    # nearest orthogonal matrix in the Frobenius norm
+    rng = np.random.default_rng(8)
+    best = np.linalg.norm(Tsub - R)
+    for _ in range(200):
+        assert best <= np.linalg.norm(Tsub - _rand_orth(rng, 12)) + 1e-12
+
+
+def test_construct_tiny_closed_form():
+    # T = rot(0.9) (+) rot(0.2) on planes (e0, e1) and (e2, e3); with r = 2 the
+    # larger plane is kept: T_hat = rot(0.9) (+) I
+    def rot(a):
+        return np.array([[np.cos(a), -np.sin(a)], [np.sin(a), np.cos(a)]])
+    T = scipy.linalg.block_diag(rot(0.9), rot(0.2))
+    Q, R, S = O.construct_basis(T, 2)
+    np.testing.assert_allclose(S, [2 * np.sin(0.45)] * 2 + [2 * np.sin(0.1)] * 2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(O.t_hat(Q, R), scipy.linalg.block_diag(rot(0.9), np.eye(2)),
+                               rtol=0, atol=1e-12)
+
+
+def test_construct_eckart_young_and_special_orthogonal():
+    T = W.gen_hadamard_transition(9, 256, 16).astype(np.float64)
+    r = 32
+    Q, R, S = O.construct_basis(T, r)
+    np.testing.assert_allclose(Q.T @ Q, np.eye(r), rtol=0, atol=1e-12)
+    dT = T - np.eye(256)
+    # the residual of Delta T off span(Q) has 2-norm sigma_{r+1}
+    assert np.linalg.norm(dT - Q @ (Q.T @ dT), 2) == pytest.approx(S[r], rel=1e-9)
+    Th = O.t_hat(Q, R)
+    np.testing.assert_allclose(Th @ Th.T, np.eye(256), rtol=0, atol=1e-12)
+    assert np.linalg.det(Th) == pytest.approx(1.0, abs=1e-9)
+    # the pages' claim: the approximation keeps most of Delta T
+    assert np.linalg.norm(Th - T) < 0.05 * np.linalg.norm(dT)
+
+
 def test_align_identity_cases():
     x = W.bf16_bits_to_f32(W.gen_x(3, 7, 64, 2, 50.0)).astype(np.float64)
     Q, _ = _basis(64, 8)

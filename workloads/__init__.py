@@ -146,6 +146,37 @@ def gen_basis(key: int, D: int, r: int, stream: str = "basis",
     return Qm.astype(np.float32), M.astype(np.float32)
 
 
+def gen_lowrank_transition(key: int, D: int, r: int, skew_std: float = 0.3) -> np.ndarray:
+    """fp32 [D][D]: I + Q0 (M0 - I) Q0^T for a seeded (Q0, M0) of rank r, i.e. a
+    transition whose deviation from the identity has rank r exactly."""
+    Q0, M0 = gen_basis(key, D, r, stream="transition", skew_std=skew_std)
+    Q0 = Q0.astype(np.float64)
+    M0 = M0.astype(np.float64)
+    return (np.eye(D) + Q0 @ (M0 - np.eye(r)) @ Q0.T).astype(np.float32)
+
+
+def gen_hadamard_transition(key: int, D: int, n_big: int, big=(0.3, 1.0),
+                            small: float = 0.01) -> np.ndarray:
+    """fp32 [D][D] synthetic residual transition near the identity, of the kind
+    the pages describe (rotations that stay close to a shared Hadamard start):
+    T = Hn G Hn^T with Hn the normalized Sylvester matrix and G block-diagonal
+    plane rotations on the coordinate pairs (2k, 2k+1): n_big seeded pairs
+    turn by angles in ``big``, all others by angles below ``small``. D must
+    be a power of two."""
+    import scipy.linalg
+    g = rng(key, "transition.angles")
+    theta = g.uniform(0.0, small, D // 2)
+    pick = g.permutation(D // 2)[:n_big]
+    theta[pick] = g.uniform(big[0], big[1], n_big)
+    Hn = scipy.linalg.hadamard(D).astype(np.float64) / np.sqrt(D)
+    c, s = np.cos(theta), np.sin(theta)
+    # Y = G Hn^T: rotate row pairs of Hn^T (= Hn)
+    Y = Hn.copy()
+    Y[0::2], Y[1::2] = c[:, None] * Hn[0::2] - s[:, None] * Hn[1::2], \
+        s[:, None] * Hn[0::2] + c[:, None] * Hn[1::2]
+    return (Hn @ Y).astype(np.float32)
+
+
 def gen_weight(key: int, N: int, K: int, std: float, stream: str = "w") -> np.ndarray:
     """fp32 weights [N][K], entries N(0, std^2)."""
     g = rng(key, stream)
