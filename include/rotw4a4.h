@@ -278,6 +278,34 @@ rw4_status head_hadamard(const void* x, rw4_dtype x_dt, int64_t ldx, float* y, i
                          int64_t n_h, int64_t d_h, void* stream);
 
 /*
+ * respin_construct -- the offline step upstream of the alignment: (Q, R_sub)
+ * of a residual transition T = R_out R_in^T ["ReSpinQuant" paper notes, key
+ * design 2]: Delta T = T - I; Q = its top-r left singular vectors; T_sub =
+ * Q^T T Q; R_sub = U_sub V_sub^T, the orthogonal polar factor of T_sub. Then
+ * T_hat = I + Q (R_sub - I) Q^T, and (Q, R_sub) are the (Q, M) of
+ * respin_align / respin_prepare_basis.
+ * The singular subspace comes from a randomized range finder with `iters`
+ * steps of subspace iteration (oversampling 16, fixed pseudo-random start),
+ * in fp64; its accuracy depends on the gap between the r-th and the
+ * (r + 17)-th singular values of Delta T: each iteration shrinks the error by
+ * about their squared ratio (4 steps are ample when the ratio is below 0.3).
+ * Q is defined up to a rotation inside degenerate singular subspaces; T_hat
+ * depends only on span(Q).
+ *   T          fp32 [D][D], row-major (row i is the image coefficients of
+ *              output i: y = T x)
+ *   Q          fp32 [D][r] out; R_sub fp32 [r][r] out
+ *   workspace  device memory of respin_construct_workspace_size(D, r) bytes,
+ *              256-byte aligned
+ * Constraints: D % 64 == 0, 64 <= D <= 16384; r % 4 == 0, 4 <= r <= min(64, D);
+ * 0 <= iters <= 32. Asynchronous on `stream`; argument errors come before any launch.
+ */
+rw4_status respin_construct(const float* T, int64_t D, int64_t r, int iters, float* Q,
+                            float* R_sub, void* workspace, size_t ws_bytes, void* stream);
+
+/* bytes of workspace respin_construct needs; 0 when (D, r) is unsupported */
+size_t respin_construct_workspace_size(int64_t D, int64_t r);
+
+/*
  * respin_prepare_basis -- the part of the alignment that depends only on the
  * layer's (Q, M) ["ReSpinQuant" paper notes, key design 3: x + Q (M - I) Q^T x],
  * computed once and kept with the layer's weights, like the weight tiles:
@@ -344,7 +372,7 @@ const char* rw4_status_string(rw4_status s);
 /* ABI version of this header (bumped on any signature change) */
 int rw4_abi_version(void);
 
-#define RW4_ABI_VERSION 7
+#define RW4_ABI_VERSION 8
 
 #ifdef __cplusplus
 }

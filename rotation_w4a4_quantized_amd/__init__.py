@@ -21,6 +21,7 @@ __all__ = [
     "rotated_linear_prepared_workspace_size",
     "w4a4_tiles_size", "w4a4_tile_codes", "w4a4_gemm_tiles", "prep_weight", "layer",
     "quant_act_sym", "RW4_ABITS", "RW4_KRON", "RW4_HEADS", "hadamard_transform", "head_hadamard",
+    "respin_construct", "respin_construct_workspace_size",
 ]
 
 RW4_ALIGN, RW4_FWHT, RW4_SWIGLU = 1, 2, 4
@@ -53,7 +54,8 @@ EXPORTS = ("respin_align", "respin_align_workspace_size", "fwht", "quant_act_int
            "rotated_linear_workspace_size", "respin_basis_size", "respin_prepare_basis",
            "rotated_linear_prepared", "rotated_linear_prepared_workspace_size",
            "respin_align_prepared", "respin_align_prepared_workspace_size",
-           "hadamard_transform", "head_hadamard", "rw4_align256",
+           "hadamard_transform", "head_hadamard", "respin_construct",
+           "respin_construct_workspace_size", "rw4_align256",
            "rw4_status_string", "rw4_abi_version")
 
 
@@ -101,6 +103,9 @@ def lib() -> ctypes.CDLL:
     L.respin_align_prepared_workspace_size.argtypes = [i64, i64, i64]
     L.respin_align_prepared_workspace_size.restype = sz
     L.hadamard_transform.argtypes = [vp, i32, i64, vp, i64, i64, i64, vp, vp]
+    L.respin_construct.argtypes = [vp, i64, i64, i32, vp, vp, vp, sz, vp]
+    L.respin_construct_workspace_size.argtypes = [i64, i64]
+    L.respin_construct_workspace_size.restype = sz
     L.head_hadamard.argtypes = [vp, i32, i64, vp, i64, i64, i64, vp]
     L.rw4_align256.argtypes = [sz]
     L.rw4_align256.restype = sz
@@ -111,7 +116,7 @@ def lib() -> ctypes.CDLL:
               "w4a4_tile_codes",
               "w4a4_gemm_tiles", "rotated_linear", "respin_prepare_basis",
               "rotated_linear_prepared", "respin_align_prepared", "hadamard_transform",
-              "head_hadamard"):
+              "head_hadamard", "respin_construct"):
         getattr(L, f).restype = i32
     _lib = L
     return L
@@ -393,6 +398,31 @@ def rotated_linear(x, w, s_w, flags: int, Q=None, M=None, out=None, workspace=No
                               _p(dbg_prequant), _stream())
     _check("rotated_linear", st)
     return out, workspace
+
+
+def respin_construct_workspace_size(D: int, r: int) -> int:
+    return int(lib().respin_construct_workspace_size(D, r))
+
+
+def respin_construct(T, r: int, iters: int = 4, workspace=None):
+    """(Q fp32 [D][r], R_sub fp32 [r][r]) of a residual transition T fp32 [D][D]:
+    the top-r left singular vectors of T - I and the polar factor of Q^T T Q."""
+    torch = _torch()
+    _contig(T)
+    if T.dtype != torch.float32 or T.shape[0] != T.shape[1]:
+        raise TypeError("T must be a square fp32 matrix")
+    D = T.shape[0]
+    need = respin_construct_workspace_size(D, r)
+    if need == 0:
+        raise Rw4Error("respin_construct", -2, lib().rw4_status_string(-2).decode())
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=T.device)
+    Q = torch.empty((D, r), dtype=torch.float32, device=T.device)
+    R = torch.empty((r, r), dtype=torch.float32, device=T.device)
+    st = lib().respin_construct(_p(T), D, r, iters, _p(Q), _p(R), _p(workspace),
+                                workspace.numel() * workspace.element_size(), _stream())
+    _check("respin_construct", st)
+    return Q, R
 
 
 def respin_basis_size(D: int, r: int) -> int:

@@ -308,6 +308,22 @@ rw4_status w4a4_gemm_tiles(const uint8_t* a, const float* s_a, const uint8_t* w,
       rw4::launch_gemm_tiles(a, s_a, w, s_w, y, y_dt == RW4_I32, T, K, N, strm(stream)));
 }
 
+size_t respin_construct_workspace_size(int64_t D, int64_t r) {
+  if (!rw4::construct_supported(D, r)) return 0;
+  return rw4::construct_workspace(D, r);
+}
+
+rw4_status respin_construct(const float* T, int64_t D, int64_t r, int iters, float* Q,
+                            float* R_sub, void* workspace, size_t ws_bytes, void* stream) {
+  if (!T || !Q || !R_sub || iters < 0 || iters > 32) return RW4_ERR_INVALID_ARG;
+  if (!rw4::construct_supported(D, r)) return RW4_ERR_UNSUPPORTED;
+  if (!al16(T) || !al16(Q) || !al16(R_sub)) return RW4_ERR_MISALIGNED;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) ||
+      ws_bytes < rw4::construct_workspace(D, r))
+    return RW4_ERR_WORKSPACE;
+  return hip_status(rw4::launch_construct(T, D, r, iters, Q, R_sub, workspace, strm(stream)));
+}
+
 size_t respin_basis_size(int64_t D, int64_t r) {
   if (D < 1 || r < 1 || r > 128 || (r % 4) != 0 || r > D) return 0;
   if (!rw4::align_mfma_supported(D, r)) return 0;

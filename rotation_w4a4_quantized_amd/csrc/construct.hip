@@ -1,0 +1,344 @@
+// Offline construction of the alignment's (Q, R_sub) from a residual
+// transition T = R_out R_in^T (ReSpinQuant paper notes, key design 2):
+//   Delta T = T - I; Q = its top-r left singular vectors; T_sub = Q^T T Q;
+//   R_sub = U_sub V_sub^T, the orthogonal polar factor of T_sub.
+//
+// The top-r singular subspace comes from a randomized range finder with
+// subspace iteration (Halko, Martinsson and Tropp, "Finding structure with
+// randomness", 2011), in fp64 throughout:
+//   Z = Delta T Omega (Omega: D x p Rademacher signs from a counter hash,
+//       p = r + 16);
+//   q times: Z <- orth(Z); Y = Delta T^T Z; Y <- orth(Y); Z = Delta T Y;
+//   Z <- orth(Z); C = (Delta T^T Z)^T (Delta T^T Z) = Z^T Delta T Delta T^T Z;
+//   C = W L W^T (eigenvalues descending): Q = Z W[:, :r] (Rayleigh-Ritz).
+// orth() is SVQB (Stathopoulos and Wu, 2002): G = Y^T Y = V L V^T,
+// Y <- Y V L^-1/2, with columns of eigenvalue below 1e-22 of the largest set
+// to zero, so a rank-deficient block (Delta T of rank < p) stays exact.
+// The polar factor is T_sub (T_sub^T T_sub)^-1/2 from the same eigensolver:
+// a cyclic Jacobi method in one workgroup, the pairs of each step chosen by
+// the round-robin ordering so that all n/2 rotations of a step run at once.
+// Products with T read it from HBM as fp32 and accumulate in fp64; only Q
+// and R_sub are rounded to fp32 at the end.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace rw4 {
+namespace {
+
+constexpr int kCPad = 16;      // oversampling of the range finder
+constexpr int kCMaxN = 80;     // largest eigenproblem (r <= 64)
+constexpr int kCRows = 16;     // output rows per workgroup of the T products
+constexpr int kCChunk = 64;    // k-chunk of the T products
+
+// Rademacher sign of entry (d, k) of Omega: bit 0 of a 32-bit mix of the index
+__device__ __forceinline__ double omega_sign(uint32_t d, uint32_t k) {
+  uint32_t h = d * 0x9E3779B1u ^ (k + 0x7F4A7C15u) * 0x85EBCA77u;
+  h ^= h >> 16; h *= 0x7FEB352Du; h ^= h >> 15; h *= 0x846CA68Bu; h ^= h >> 16;
+  return (h & 1u) ? -1.0 : 1.0;
+}
+
+__global__ void omega_kernel(double* __restrict__ Y, int D, int p) {
+  const int64_t n = static_cast<int64_t>(D) * p;
+  for (int64_t e = blockIdx.x * 256 + threadIdx.x; e < n; e += static_cast<int64_t>(gridDim.x) * 256)
+    Y[e] = omega_sign(static_cast<uint32_t>(e / p), static_cast<uint32_t>(e % p));
+}
+
+// Y[i][c] = sum_j op(T)[i][j] X[j][c] - sub X[i][c] for c < nc; X, Y fp64 [D][nc];
+// op(T) = T (TR false) or T^T (TR true). One workgroup per 16 output rows.
+template <bool TR>
+__global__ void __launch_bounds__(256)
+tmul_kernel(const float* __restrict__ T, int D, const double* __restrict__ X, int nc, double sub,
+            double* __restrict__ Y) {
+  __shared__ float Tt[kCRows][kCChunk + 1];
+  __shared__ double Xt[kCChunk][kCMaxN];
+  const int tid = threadIdx.x;
+  const int lr = tid >> 4;                 // output row in the block
+  const int cg = tid & 15;                 // column group: c = cg + 16 k
+  const int i0 = blockIdx.x * kCRows;
+  double acc[kCMaxN / 16];
+#pragma unroll
+  for (int k = 0; k < kCMaxN / 16; ++k) acc[k] = 0.0;
+  for (int j0 = 0; j0 < D; j0 += kCChunk) {
+    // T block: rows i0.., columns j0.. of op(T)
+    for (int e = tid; e < kCRows * kCChunk; e += 256) {
+      int r, c;
+      if constexpr (TR) {
+        c = e / kCRows; r = e % kCRows;           // T[j0 + c][i0 + r]: 16 consecutive floats
+        Tt[r][c] = T[static_cast<int64_t>(j0 + c) * D + i0 + r];
+      } else {
+        r = e / kCChunk; c = e % kCChunk;
+        Tt[r][c] = T[static_cast<int64_t>(i0 + r) * D + j0 + c];
+      }
+    }
+    for (int e = tid; e < kCChunk * nc; e += 256)
+      Xt[e / nc][e % nc] = X[static_cast<int64_t>(j0 + e / nc) * nc + e % nc];
+    __syncthreads();
+#pragma unroll 4
+    for (int jj = 0; jj < kCChunk; ++jj) {
+      const double t = static_cast<double>(Tt[lr][jj]);
+#pragma unroll
+      for (int k = 0; k < kCMaxN / 16; ++k) {
+        const int c = cg + 16 * k;
+        if (c < nc) acc[k] = fma(t, Xt[jj][c], acc[k]);
+      }
+    }
+    __syncthreads();
+  }
+  const int i = i0 + lr;
+#pragma unroll
+  for (int k = 0; k < kCMaxN / 16; ++k) {
+    const int c = cg + 16 * k;
+    if (c < nc) {
+      const int64_t o = static_cast<int64_t>(i) * nc + c;
+      Y[o] = acc[k] - sub * X[o];
+    }
+  }
+}
+
+// G[i][j] = sum_d A[d][i] B[d][j] (A [D][na], B [D][nb]); workgroup (i, 16 columns)
+__global__ void __launch_bounds__(256)
+gram_kernel(const double* __restrict__ A, int na, const double* __restrict__ B, int nb, int D,
+            double* __restrict__ G) {
+  __shared__ double part[4][16];
+  const int i = blockIdx.x;
+  const int j0 = blockIdx.y * 16;
+  const int tid = threadIdx.x;
+  double acc[16];
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj) acc[jj] = 0.0;
+  for (int d = tid; d < D; d += 256) {
+    const double a = A[static_cast<int64_t>(d) * na + i];
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj)
+      if (j0 + jj < nb) acc[jj] = fma(a, B[static_cast<int64_t>(d) * nb + j0 + jj], acc[jj]);
+  }
+  // fixed-order reduction: butterflies inside the wave, then the four waves
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj)
+    for (int o = 32; o > 0; o >>= 1) acc[jj] += __shfl_xor(acc[jj], o);
+  if ((tid & 63) == 0)
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) part[tid >> 6][jj] = acc[jj];
+  __syncthreads();
+  if (tid < 16 && j0 + tid < nb)
+    G[static_cast<int64_t>(i) * nb + j0 + tid] = (part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid]);
+}
+
+// Y[d][c] = sum_k X[d][k] M[k][c] (X [D][nx], M [nx][nm], Y [D][nm]); Y may not alias X
+__global__ void __launch_bounds__(256)
+rmul_kernel(const double* __restrict__ X, int nx, const double* __restrict__ Mm, int nm, int D,
+            double* __restrict__ Y) {
+  __shared__ double Ms[kCMaxN * kCMaxN];
+  for (int e = threadIdx.x; e < nx * nm; e += 256) Ms[e] = Mm[e];
+  __syncthreads();
+  const int64_t n = static_cast<int64_t>(D) * nm;
+  for (int64_t e = blockIdx.x * 256 + threadIdx.x; e < n; e += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t d = e / nm;
+    const int c = static_cast<int>(e % nm);
+    double acc = 0.0;
+    for (int k = 0; k < nx; ++k) acc = fma(X[d * nx + k], Ms[k * nm + c], acc);
+    Y[e] = acc;
+  }
+}
+
+// symmetric eigenproblem A = V diag(A') V^T in LDS, n even (<= kCMaxN), 256 threads
+__device__ void jacobi_eig(double (*A)[kCMaxN], double (*V)[kCMaxN], int n, double* cs_c,
+                          double* cs_s, double* red) {
+  const int tid = threadIdx.x;
+  for (int e = tid; e < n * n; e += 256) V[e / n][e % n] = (e / n == e % n) ? 1.0 : 0.0;
+  // scale of the matrix: its Frobenius norm squared
+  double fro = 0.0;
+  for (int e = tid; e < n * n; e += 256) fro += A[e / n][e % n] * A[e / n][e % n];
+  for (int o = 32; o > 0; o >>= 1) fro += __shfl_xor(fro, o);
+  if ((tid & 63) == 0) red[tid >> 6] = fro;
+  __syncthreads();
+  fro = (red[0] + red[1]) + (red[2] + red[3]);
+  __syncthreads();
+  const int h = n / 2;
+  for (int sweep = 0; sweep < 40; ++sweep) {
+    double off = 0.0;
+    for (int e = tid; e < n * n; e += 256)
+      if (e / n != e % n) off += A[e / n][e % n] * A[e / n][e % n];
+    for (int o = 32; o > 0; o >>= 1) off += __shfl_xor(off, o);
+    if ((tid & 63) == 0) red[tid >> 6] = off;
+    __syncthreads();
+    off = (red[0] + red[1]) + (red[2] + red[3]);
+    __syncthreads();
+    if (!(off > 1e-30 * fro)) break;            // uniform across the workgroup
+    for (int rr = 0; rr < n - 1; ++rr) {
+      // round-robin pairs: position 0 stays, positions 1..n-1 rotate by rr
+      auto player = [&](int j) { return j == 0 ? 0 : 1 + (j - 1 + rr) % (n - 1); };
+      if (tid < h) {
+        int p = player(tid), q = player(n - 1 - tid);
+        if (p > q) { const int t = p; p = q; q = t; }
+        const double apq = A[p][q];
+        double c = 1.0, s = 0.0;
+        if (apq != 0.0) {
+          const double tau = (A[q][q] - A[p][p]) / (2.0 * apq);
+          const double t = (tau >= 0.0 ? 1.0 : -1.0) / (fabs(tau) + sqrt(1.0 + tau * tau));
+          c = 1.0 / sqrt(1.0 + t * t);
+          s = t * c;
+        }
+        cs_c[tid] = c;
+        cs_s[tid] = s;
+      }
+      __syncthreads();
+      // rows p, q <- J^T A
+      for (int e = tid; e < h * n; e += 256) {
+        const int k = e / n, col = e % n;
+        int p = player(k), q = player(n - 1 - k);
+        if (p > q) { const int t = p; p = q; q = t; }
+        const double c = cs_c[k], s = cs_s[k];
+        const double ap = A[p][col], aq = A[q][col];
+        A[p][col] = c * ap - s * aq;
+        A[q][col] = s * ap + c * aq;
+      }
+      __syncthreads();
+      // columns p, q <- A J, V J
+      for (int e = tid; e < h * n; e += 256) {
+        const int k = e / n, row = e % n;
+        int p = player(k), q = player(n - 1 - k);
+        if (p > q) { const int t = p; p = q; q = t; }
+        const double c = cs_c[k], s = cs_s[k];
+        const double ap = A[row][p], aq = A[row][q];
+        A[row][p] = c * ap - s * aq;
+        A[row][q] = s * ap + c * aq;
+        const double vp = V[row][p], vq = V[row][q];
+        V[row][p] = c * vp - s * vq;
+        V[row][q] = s * vp + c * vq;
+      }
+      __syncthreads();
+    }
+  }
+}
+
+enum SmallMode { SM_SVQB = 0, SM_RR = 1, SM_POLAR = 2 };
+
+// One workgroup. SVQB: G (n x n) -> out = V diag(l^-1/2 or 0) (n x n).
+// RR: C (n x n) -> out = the r eigenvectors of the largest eigenvalues, in
+// descending order (n x r). POLAR: T_sub (n x n = r x r) -> R fp32 (n x n).
+template <int MODE>
+__global__ void __launch_bounds__(256)
+small_kernel(const double* __restrict__ in, int n, int r, double* __restrict__ out,
+             float* __restrict__ out32) {
+  __shared__ double A[kCMaxN][kCMaxN];
+  __shared__ double V[kCMaxN][kCMaxN];
+  __shared__ double cs_c[kCMaxN / 2], cs_s[kCMaxN / 2], red[4], lam[kCMaxN];
+  __shared__ int perm[kCMaxN];
+  const int tid = threadIdx.x;
+  if constexpr (MODE == SM_POLAR) {
+    // A = T_sub^T T_sub
+    for (int e = tid; e < n * n; e += 256) {
+      const int i = e / n, j = e % n;
+      double acc = 0.0;
+      for (int k = 0; k < n; ++k) acc = fma(in[k * n + i], in[k * n + j], acc);
+      A[i][j] = acc;
+    }
+  } else {
+    for (int e = tid; e < n * n; e += 256) A[e / n][e % n] = in[e];
+  }
+  __syncthreads();
+  jacobi_eig(A, V, n, cs_c, cs_s, red);
+  if (tid < n) lam[tid] = A[tid][tid];
+  __syncthreads();
+  double lmax = 0.0;
+  for (int k = 0; k < n; ++k) lmax = fmax(lmax, lam[k]);
+  if constexpr (MODE == SM_SVQB) {
+    for (int e = tid; e < n * n; e += 256) {
+      const int i = e / n, j = e % n;
+      const double l = lam[j];
+      out[e] = l > 1e-22 * lmax ? V[i][j] / sqrt(l) : 0.0;
+    }
+  } else if constexpr (MODE == SM_RR) {
+    if (tid < n) {
+      int rank = 0;
+      for (int k = 0; k < n; ++k)
+        rank += (lam[k] > lam[tid]) || (lam[k] == lam[tid] && k < tid);
+      perm[rank] = tid;
+    }
+    __syncthreads();
+    for (int e = tid; e < n * r; e += 256) out[e] = V[e / r][perm[e % r]];
+  } else {
+    // R = T_sub V diag(l^-1/2) V^T (eigenvalues below 1e-22 of the largest dropped)
+    for (int e = tid; e < n * n; e += 256) {
+      const int i = e / n, j = e % n;
+      double acc = 0.0;
+      for (int k = 0; k < n; ++k) {
+        if (!(lam[k] > 1e-22 * lmax)) continue;
+        double tv = 0.0;                         // (T_sub V)[i][k]
+        for (int m = 0; m < n; ++m) tv = fma(in[i * n + m], V[m][k], tv);
+        acc = fma(tv / sqrt(lam[k]), V[j][k], acc);
+      }
+      out32[e] = static_cast<float>(acc);
+    }
+  }
+}
+
+__global__ void to_f32_kernel(const double* __restrict__ a, int64_t n, float* __restrict__ o) {
+  for (int64_t e = blockIdx.x * 256 + threadIdx.x; e < n; e += static_cast<int64_t>(gridDim.x) * 256)
+    o[e] = static_cast<float>(a[e]);
+}
+
+inline int64_t a256c(int64_t n) { return (n + 255) & ~static_cast<int64_t>(255); }
+
+}  // namespace
+
+int construct_oversampled(int64_t D, int64_t r) {
+  const int64_t p = r + kCPad;
+  return static_cast<int>(p < D ? p : D);
+}
+
+size_t construct_workspace(int64_t D, int64_t r) {
+  const int64_t p = construct_oversampled(D, r);
+  return static_cast<size_t>(2 * a256c(D * p * 8) + 2 * a256c(kCMaxN * kCMaxN * 8));
+}
+
+bool construct_supported(int64_t D, int64_t r) {
+  return r >= 4 && r <= 64 && r % 4 == 0 && D >= 64 && D % 64 == 0 && D <= 16384 && r <= D;
+}
+
+hipError_t launch_construct(const float* T, int64_t D64, int64_t r64, int iters, float* Qout,
+                            float* Rout, void* ws, hipStream_t s) {
+  if (!construct_supported(D64, r64) || iters < 0 || iters > 32) return hipErrorInvalidValue;
+  const int D = static_cast<int>(D64), r = static_cast<int>(r64);
+  const int p = construct_oversampled(D64, r64);
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  double* Y = reinterpret_cast<double*>(w);
+  double* Z = reinterpret_cast<double*>(w + a256c(int64_t(D) * p * 8));
+  double* G = reinterpret_cast<double*>(w + 2 * a256c(int64_t(D) * p * 8));
+  double* Mm = reinterpret_cast<double*>(w + 2 * a256c(int64_t(D) * p * 8) + a256c(kCMaxN * kCMaxN * 8));
+  const dim3 b256(256);
+  const unsigned rows = static_cast<unsigned>(D / kCRows);
+  const int64_t ewn = (int64_t(D) * p + 255) / 256;
+  const unsigned ew = static_cast<unsigned>(ewn < 4096 ? ewn : 4096);
+  auto tmul = [&](bool tr, const double* X, int nc, double sub, double* Yo) {
+    if (tr) hipLaunchKernelGGL((tmul_kernel<true>), dim3(rows), b256, 0, s, T, D, X, nc, sub, Yo);
+    else hipLaunchKernelGGL((tmul_kernel<false>), dim3(rows), b256, 0, s, T, D, X, nc, sub, Yo);
+  };
+  // X <- orth(X) through tmp
+  auto orth = [&](double* X, double* tmp) {
+    hipLaunchKernelGGL(gram_kernel, dim3(p, (p + 15) / 16), b256, 0, s, X, p, X, p, D, G);
+    hipLaunchKernelGGL((small_kernel<SM_SVQB>), dim3(1), b256, 0, s, G, p, p, Mm, nullptr);
+    hipLaunchKernelGGL(rmul_kernel, dim3(ew), b256, 0, s, X, p, Mm, p, D, tmp);
+  };
+  hipLaunchKernelGGL(omega_kernel, dim3(ew), b256, 0, s, Y, D, p);
+  tmul(false, Y, p, 1.0, Z);                        // Z = dT Omega
+  for (int it = 0; it < iters; ++it) {
+    orth(Z, Y);                                     // Y = orth(Z)
+    tmul(true, Y, p, 1.0, Z);                       // Z = dT^T Y
+    orth(Z, Y);                                     // Y = orth(Z)
+    tmul(false, Y, p, 1.0, Z);                      // Z = dT Y
+  }
+  orth(Z, Y);                                       // Y: orthonormal range basis
+  tmul(true, Y, p, 1.0, Z);                         // Z = dT^T Y
+  hipLaunchKernelGGL(gram_kernel, dim3(p, (p + 15) / 16), b256, 0, s, Z, p, Z, p, D, G);
+  hipLaunchKernelGGL((small_kernel<SM_RR>), dim3(1), b256, 0, s, G, p, r, Mm, nullptr);
+  hipLaunchKernelGGL(rmul_kernel, dim3(ew), b256, 0, s, Y, p, Mm, r, D, Z);  // Z: Q [D][r]
+  tmul(false, Z, r, 0.0, Y);                        // Y = T Q [D][r]
+  hipLaunchKernelGGL(gram_kernel, dim3(r, (r + 15) / 16), b256, 0, s, Z, r, Y, r, D, G);  // T_sub
+  hipLaunchKernelGGL((small_kernel<SM_POLAR>), dim3(1), b256, 0, s, G, r, r, nullptr, Rout);
+  hipLaunchKernelGGL(to_f32_kernel, dim3(ew), b256, 0, s, Z, int64_t(D) * r, Qout);
+  return hipGetLastError();
+}
+
+}  // namespace rw4

@@ -27,6 +27,13 @@ hipError_t launch_kron(const void* x, int in_mode, int64_t ldx, int64_t T, int64
                        int m, const float* signs, float norm, float* y, uint8_t* codes,
                        bool tiled, float* scales, float* dbg, int bits, hipStream_t s);
 
+// Offline (Q, R_sub) of a residual transition T (fp32 [D][D]) on the device,
+// fp64 inside; workspace of construct_workspace(D, r) bytes.
+bool construct_supported(int64_t D, int64_t r);
+size_t construct_workspace(int64_t D, int64_t r);
+hipError_t launch_construct(const float* T, int64_t D, int64_t r, int iters, float* Q, float* R,
+                            void* ws, hipStream_t s);
+
 // Per-row b-bit quantization for any even D (no transform).
 hipError_t launch_quant_generic(const void* x, int in_mode, int64_t ldx, int64_t T, int64_t D,
                                 uint8_t* codes, float* scales, hipStream_t s, int bits = 4);

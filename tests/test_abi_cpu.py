@@ -22,7 +22,7 @@ def _declared():
 def test_library_built_and_loads():
     assert os.path.exists(rw.library_path), "build the HIP library first"
     L = rw.lib()
-    assert L.rw4_abi_version() == 7
+    assert L.rw4_abi_version() == 8
 
 
 def test_exports_every_declared_symbol():
@@ -276,6 +276,22 @@ def test_structured_transform_validation():
     assert _rl(D=4096, ldx=4096, flags=H5 | 1, r=0) == INV
     assert _rl(D=4096, ldx=4096, flags=(15 << 24), r=0) == UNS
     assert _rl(D=4096, ldx=4096, flags=(1 << 29), r=0) == INV   # unknown bit
+
+
+def test_construct_validation():
+    L = rw.lib()
+    # Y and Z (D x p fp64, p = r + 16) plus two small fp64 matrices
+    p = 48
+    assert L.respin_construct_workspace_size(4096, 32) == 2 * 4096 * p * 8 + 2 * L.rw4_align256(80 * 80 * 8)
+    assert L.respin_construct_workspace_size(4096, 30) == 0 and L.respin_construct_workspace_size(4000, 32) == 0
+    assert L.respin_construct_workspace_size(4096, 68) == 0 and L.respin_construct_workspace_size(32768, 32) == 0
+    cs = lambda T=A, D=256, r=32, it=4, Q=B, R=C, ws=Dp, wsb=1 << 24: L.respin_construct(
+        T, D, r, it, Q, R, ws, wsb, NUL)
+    assert cs(T=NUL) == INV and cs(Q=NUL) == INV and cs(R=NUL) == INV
+    assert cs(it=-1) == INV and cs(it=33) == INV
+    assert cs(D=200) == UNS and cs(r=6) == UNS and cs(r=72) == UNS and cs(D=64, r=68) == UNS
+    assert cs(T=ODD) == MIS and cs(Q=ODD) == MIS
+    assert cs(ws=NUL) == WSE and cs(wsb=100) == WSE and cs(ws=ctypes.c_void_p(0x40010)) == WSE
 
 
 def test_quant_sym_validation():

@@ -189,6 +189,43 @@ def test_head_hadamard_completes_the_transform(rw):
     assert normwise(out, O.fwht(x32)) <= 2 * FP32_TOL
 
 
+# ---------------------------------------------------------------- offline construction
+@pytest.mark.parametrize("D,r,n_big,iters", [(256, 32, 16, 4), (1024, 64, 32, 4), (512, 16, 8, 2),
+                                             (64, 64, 16, 2)])
+def test_respin_construct_against_oracle(rw, D, r, n_big, iters):
+    """(Q, R_sub) of a perturbed-Hadamard transition: the GPU's T_hat and span(Q)
+    against the oracle's full SVD and polar factor."""
+    say(f"respin_construct D={D} r={r} iters={iters}")
+    T = W.gen_hadamard_transition(D + r, D, n_big)
+    Qg, Rg = rw.respin_construct(dev(T), r, iters)
+    Qg, Rg = host(Qg).astype(np.float64), host(Rg).astype(np.float64)
+    Qo, Ro, S = O.construct_basis(T, r)
+    X = np.random.default_rng(D).standard_normal((16, D))
+    err = np.linalg.norm(O.align(X, Qg, Rg) - O.align(X, Qo, Ro)) / np.linalg.norm(X)
+    assert err <= 1e-5, err
+    assert np.linalg.norm(Qg @ Qg.T - Qo @ Qo.T) / np.sqrt(r) <= 1e-5
+    np.testing.assert_allclose(Rg.T @ Rg, np.eye(r), rtol=0, atol=1e-5)
+    assert np.linalg.det(Rg) == pytest.approx(np.linalg.det(Ro), abs=1e-4)
+
+
+@pytest.mark.parametrize("D,r", [(4096, 32), (8192, 64)])
+def test_respin_construct_recovers_exact_rank(rw, D, r):
+    """At the workload sizes: an exact rank-r transition is recovered (T_hat = T),
+    checked on random vectors without a dense SVD; the basis then drives the
+    online alignment."""
+    say(f"respin_construct exact rank D={D} r={r}")
+    T = W.gen_lowrank_transition(D + 1, D, r)
+    Qg, Rg = rw.respin_construct(dev(T), r, 2)
+    X = np.random.default_rng(r).standard_normal((8, D))
+    Q64, R64 = host(Qg).astype(np.float64), host(Rg).astype(np.float64)
+    want = X @ T.astype(np.float64).T
+    assert np.linalg.norm(O.align(X, Q64, R64) - want) / np.linalg.norm(X) <= 1e-5
+    # the same through the device alignment (bf16 tokens)
+    xb = W.f32_to_bf16_bits(X.astype(np.float32))
+    out = host(rw.respin_align(dev(xb), Qg, Rg))
+    assert normwise(out, W.bf16_bits_to_f32(xb).astype(np.float64) @ T.astype(np.float64).T) <= 1e-5
+
+
 # ---------------------------------------------------------------- alignment
 @pytest.mark.parametrize("T,D,r", [(64, 256, 8), (37, 4096, 32), (19, 8192, 64), (9, 4096, 128),
                                    (13, 1000, 12), (1, 64, 4)])
