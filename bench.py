@@ -28,6 +28,7 @@ PEAK_I8_TOPS = 5000.0          # MI355X dense int8 MFMA, TOP/s
 PEAK_FP6_TFLOPS = 10100.0      # MI355X dense FP6/FP4 MFMA, TFLOP/s (the GEMM's operand type)
 PEAK_HBM_GBS = 8000.0
 PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 vector, TFLOP/s
+PEAK_FP64_TFLOPS = 78.6       # MI355X fp64 vector, TFLOP/s
 METRIC = "rotated W4A4 linear tokens/s; GEMM int8-MFMA TOPS and align/quant GB/s vs peak"
 GEMM_SRC = os.path.join(ROOT, "rotation_w4a4_quantized_amd", "csrc", "gemm6.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w4a4_gemm_D4096_T2048_traffic.json")
@@ -124,6 +125,26 @@ def structured_rows(rw, torch, dev, timed, with_oracle):
                 O.head_hadamard(xs, 32)
             rec["oracle_rows_per_s"] = 256 / (time.perf_counter() - t0)
         out[name] = rec
+    # offline construction of (Q, R_sub) at the prefill shape (D = 4096, r = 32,
+    # 4 subspace iterations): ten products with T (fp32 in, fp64 FMA), 2 D^2 p
+    # flops each (p = r + 16)
+    import workloads as W
+    D, r, iters = 4096, 32, 4
+    Tg = torch.from_numpy(W.gen_lowrank_transition(11, D, r)).to(dev)
+    ws = torch.empty((rw.respin_construct_workspace_size(D, r),), dtype=torch.uint8, device=dev)
+    ms = timed(lambda: rw.respin_construct(Tg, r, iters, workspace=ws), n=5)
+    p = r + 16
+    flops = (2 * iters + 2) * 2.0 * D * D * p + 2.0 * D * D * r
+    rec = {"D": D, "r": r, "iters": iters, "us": ms * 1e3, "flop": flops,
+           "TFLOP/s": flops / (ms * 1e-3) / 1e12,
+           "frac_fp64": flops / (ms * 1e-3) / 1e12 / PEAK_FP64_TFLOPS}
+    if with_oracle:
+        import oracle as O
+        Ts = W.gen_lowrank_transition(11, 1024, r)
+        t0 = time.perf_counter()
+        O.construct_basis(Ts, r)
+        rec["oracle_s_at_D1024"] = time.perf_counter() - t0
+    out["construct_D4096_r32"] = rec
     return out
 
 
@@ -220,9 +241,31 @@ def main():
     sa_t = torch.empty((T,), dtype=torch.float32, device=dev)
 
     def timed(fn, n=20):
+        """Average device time of one call: n calls captured once in a HIP graph
+        and replayed between two events, so that the host's per-call cost (the
+        Python binding) does not leave the device idle between short kernels;
+        eager back-to-back calls if capture is not possible."""
         for _ in range(3):
             fn()
+        torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        try:
+            g = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side), torch.cuda.graph(g, stream=side):
+                for _ in range(n):
+                    fn()
+            torch.cuda.current_stream().wait_stream(side)
+            g.replay()
+            torch.cuda.synchronize()
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / n
+        except Exception:
+            torch.cuda.synchronize()
         a.record()
         for _ in range(n):
             fn()

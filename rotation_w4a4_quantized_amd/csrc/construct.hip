@@ -58,29 +58,63 @@ tmul_kernel(const float* __restrict__ T, int D, const double* __restrict__ X, in
   double acc[kCMaxN / 16];
 #pragma unroll
   for (int k = 0; k < kCMaxN / 16; ++k) acc[k] = 0.0;
-  for (int j0 = 0; j0 < D; j0 += kCChunk) {
-    // T block: rows i0.., columns j0.. of op(T)
-    for (int e = tid; e < kCRows * kCChunk; e += 256) {
-      int r, c;
-      if constexpr (TR) {
-        c = e / kCRows; r = e % kCRows;           // T[j0 + c][i0 + r]: 16 consecutive floats
-        Tt[r][c] = T[static_cast<int64_t>(j0 + c) * D + i0 + r];
-      } else {
-        r = e / kCChunk; c = e % kCChunk;
-        Tt[r][c] = T[static_cast<int64_t>(i0 + r) * D + j0 + c];
-      }
+  // the next chunk is fetched into registers while the current one is used
+  constexpr int TPT = kCRows * kCChunk / 256;      // T values per thread
+  constexpr int XPT = kCChunk * kCMaxN / 256;      // X values per thread (at most)
+  float tr[TPT];
+  double xr[XPT];
+  // the chunk-relative row and column of this thread's X values (independent
+  // of the chunk: no division inside the loop)
+  int xrow[XPT], xcol[XPT];
+#pragma unroll
+  for (int m = 0; m < XPT; ++m) {
+    const int e = tid + 256 * m;
+    xrow[m] = e / nc;
+    xcol[m] = e % nc;
+  }
+  auto fetch = [&](int j0) {
+#pragma unroll
+    for (int m = 0; m < TPT; ++m) {
+      const int e = tid + 256 * m;
+      if constexpr (TR) tr[m] = T[static_cast<int64_t>(j0 + e / kCRows) * D + i0 + e % kCRows];
+      else tr[m] = T[static_cast<int64_t>(i0 + e / kCChunk) * D + j0 + e % kCChunk];
     }
-    for (int e = tid; e < kCChunk * nc; e += 256)
-      Xt[e / nc][e % nc] = X[static_cast<int64_t>(j0 + e / nc) * nc + e % nc];
+#pragma unroll
+    for (int m = 0; m < XPT; ++m) {
+      const int e = tid + 256 * m;
+      if (e < kCChunk * nc) xr[m] = X[static_cast<int64_t>(j0 + xrow[m]) * nc + xcol[m]];
+    }
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int m = 0; m < TPT; ++m) {
+      const int e = tid + 256 * m;
+      if constexpr (TR) Tt[e % kCRows][e / kCRows] = tr[m];
+      else Tt[e / kCChunk][e % kCChunk] = tr[m];
+    }
+#pragma unroll
+    for (int m = 0; m < XPT; ++m) {
+      const int e = tid + 256 * m;
+      if (e < kCChunk * nc) Xt[xrow[m]][xcol[m]] = xr[m];
+    }
+  };
+  // every workgroup starts at its own chunk: at any moment the workgroups
+  // read different parts of X (in lockstep they would all hit the same L2
+  // lines); the accumulation order is still fixed per row block
+  const int nch = D / kCChunk;
+  const int c0 = static_cast<int>(blockIdx.x % nch);
+  fetch(c0 * kCChunk);
+  for (int ci = 0; ci < nch; ++ci) {
+    stash();
     __syncthreads();
-#pragma unroll 4
+    if (ci + 1 < nch) fetch(((c0 + ci + 1) % nch) * kCChunk);
+    // branch-free: columns past nc accumulate whatever LDS holds there and
+    // are never stored
+#pragma unroll 8
     for (int jj = 0; jj < kCChunk; ++jj) {
       const double t = static_cast<double>(Tt[lr][jj]);
 #pragma unroll
-      for (int k = 0; k < kCMaxN / 16; ++k) {
-        const int c = cg + 16 * k;
-        if (c < nc) acc[k] = fma(t, Xt[jj][c], acc[k]);
-      }
+      for (int k = 0; k < kCMaxN / 16; ++k) acc[k] = fma(t, Xt[jj][cg + 16 * k], acc[k]);
     }
     __syncthreads();
   }
@@ -141,36 +175,42 @@ rmul_kernel(const double* __restrict__ X, int nx, const double* __restrict__ Mm,
   }
 }
 
-// symmetric eigenproblem A = V diag(A') V^T in LDS, n even (<= kCMaxN), 256 threads
-__device__ void jacobi_eig(double (*A)[kCMaxN], double (*V)[kCMaxN], int n, double* cs_c,
-                          double* cs_s, double* red) {
+__device__ __forceinline__ double block_sum(double v, double* red) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  v = (red[0] + red[1]) + (red[2] + red[3]);
+  __syncthreads();
+  return v;
+}
+
+// symmetric eigenproblem A = V diag(A') V^T in LDS, n even (<= kCMaxN), 256
+// threads. Each round's n/2 disjoint pairs come from the round-robin
+// ordering (position 0 fixed, positions 1..n-1 rotated by the round).
+__device__ void jacobi_eig(double (*A)[kCMaxN + 1], double (*V)[kCMaxN + 1], int n, double* cs_c,
+                          double* cs_s, int* pp, int* qq, double* red) {
   const int tid = threadIdx.x;
-  for (int e = tid; e < n * n; e += 256) V[e / n][e % n] = (e / n == e % n) ? 1.0 : 0.0;
-  // scale of the matrix: its Frobenius norm squared
+  for (int i = tid; i < n * kCMaxN; i += 256) {
+    const int row = i / kCMaxN, col = i % kCMaxN;
+    if (col < n) V[row][col] = row == col ? 1.0 : 0.0;
+  }
   double fro = 0.0;
-  for (int e = tid; e < n * n; e += 256) fro += A[e / n][e % n] * A[e / n][e % n];
-  for (int o = 32; o > 0; o >>= 1) fro += __shfl_xor(fro, o);
-  if ((tid & 63) == 0) red[tid >> 6] = fro;
-  __syncthreads();
-  fro = (red[0] + red[1]) + (red[2] + red[3]);
-  __syncthreads();
+  for (int row = 0; row < n; ++row)
+    for (int col = tid; col < n; col += 256) fro += A[row][col] * A[row][col];
+  fro = block_sum(fro, red);
   const int h = n / 2;
   for (int sweep = 0; sweep < 40; ++sweep) {
     double off = 0.0;
-    for (int e = tid; e < n * n; e += 256)
-      if (e / n != e % n) off += A[e / n][e % n] * A[e / n][e % n];
-    for (int o = 32; o > 0; o >>= 1) off += __shfl_xor(off, o);
-    if ((tid & 63) == 0) red[tid >> 6] = off;
-    __syncthreads();
-    off = (red[0] + red[1]) + (red[2] + red[3]);
-    __syncthreads();
-    if (!(off > 1e-30 * fro)) break;            // uniform across the workgroup
+    for (int row = 0; row < n; ++row)
+      for (int col = tid; col < n; col += 256)
+        if (col != row) off += A[row][col] * A[row][col];
+    off = block_sum(off, red);                      // identical in every thread
+    if (!(off > 1e-30 * fro)) break;
     for (int rr = 0; rr < n - 1; ++rr) {
-      // round-robin pairs: position 0 stays, positions 1..n-1 rotate by rr
-      auto player = [&](int j) { return j == 0 ? 0 : 1 + (j - 1 + rr) % (n - 1); };
       if (tid < h) {
-        int p = player(tid), q = player(n - 1 - tid);
-        if (p > q) { const int t = p; p = q; q = t; }
+        const int a = tid == 0 ? 0 : 1 + (tid - 1 + rr) % (n - 1);
+        const int b = 1 + (n - 2 - tid + rr) % (n - 1);
+        const int p = a < b ? a : b, q = a < b ? b : a;
         const double apq = A[p][q];
         double c = 1.0, s = 0.0;
         if (apq != 0.0) {
@@ -179,33 +219,35 @@ __device__ void jacobi_eig(double (*A)[kCMaxN], double (*V)[kCMaxN], int n, doub
           c = 1.0 / sqrt(1.0 + t * t);
           s = t * c;
         }
+        pp[tid] = p;
+        qq[tid] = q;
         cs_c[tid] = c;
         cs_s[tid] = s;
       }
       __syncthreads();
-      // rows p, q <- J^T A
-      for (int e = tid; e < h * n; e += 256) {
-        const int k = e / n, col = e % n;
-        int p = player(k), q = player(n - 1 - k);
-        if (p > q) { const int t = p; p = q; q = t; }
+      // rows p, q <- J^T A: thread -> (pair k, column col), pairs k = tid / 32 + 8 m
+      for (int k = tid >> 5; k < h; k += 8) {
+        const int p = pp[k], q = qq[k];
         const double c = cs_c[k], s = cs_s[k];
-        const double ap = A[p][col], aq = A[q][col];
-        A[p][col] = c * ap - s * aq;
-        A[q][col] = s * ap + c * aq;
+        for (int col = tid & 31; col < n; col += 32) {
+          const double ap = A[p][col], aq = A[q][col];
+          A[p][col] = c * ap - s * aq;
+          A[q][col] = s * ap + c * aq;
+        }
       }
       __syncthreads();
       // columns p, q <- A J, V J
-      for (int e = tid; e < h * n; e += 256) {
-        const int k = e / n, row = e % n;
-        int p = player(k), q = player(n - 1 - k);
-        if (p > q) { const int t = p; p = q; q = t; }
+      for (int k = tid >> 5; k < h; k += 8) {
+        const int p = pp[k], q = qq[k];
         const double c = cs_c[k], s = cs_s[k];
-        const double ap = A[row][p], aq = A[row][q];
-        A[row][p] = c * ap - s * aq;
-        A[row][q] = s * ap + c * aq;
-        const double vp = V[row][p], vq = V[row][q];
-        V[row][p] = c * vp - s * vq;
-        V[row][q] = s * vp + c * vq;
+        for (int row = tid & 31; row < n; row += 32) {
+          const double ap = A[row][p], aq = A[row][q];
+          A[row][p] = c * ap - s * aq;
+          A[row][q] = s * ap + c * aq;
+          const double vp = V[row][p], vq = V[row][q];
+          V[row][p] = c * vp - s * vq;
+          V[row][q] = s * vp + c * vq;
+        }
       }
       __syncthreads();
     }
@@ -221,24 +263,24 @@ template <int MODE>
 __global__ void __launch_bounds__(256)
 small_kernel(const double* __restrict__ in, int n, int r, double* __restrict__ out,
              float* __restrict__ out32) {
-  __shared__ double A[kCMaxN][kCMaxN];
-  __shared__ double V[kCMaxN][kCMaxN];
-  __shared__ double cs_c[kCMaxN / 2], cs_s[kCMaxN / 2], red[4], lam[kCMaxN];
-  __shared__ int perm[kCMaxN];
+  // rows padded by one double: column walks spread over the banks
+  __shared__ double A[kCMaxN][kCMaxN + 1];
+  __shared__ double V[kCMaxN][kCMaxN + 1];
+  __shared__ double cs_c[kCMaxN / 2], cs_s[kCMaxN / 2], lam[kCMaxN], red[4];
+  __shared__ int pp[kCMaxN / 2], qq[kCMaxN / 2], perm[kCMaxN];
   const int tid = threadIdx.x;
-  if constexpr (MODE == SM_POLAR) {
-    // A = T_sub^T T_sub
-    for (int e = tid; e < n * n; e += 256) {
-      const int i = e / n, j = e % n;
-      double acc = 0.0;
+  for (int e = tid; e < n * n; e += 256) {
+    const int i = e / n, j = e % n;
+    if constexpr (MODE == SM_POLAR) {
+      double acc = 0.0;                            // A = T_sub^T T_sub
       for (int k = 0; k < n; ++k) acc = fma(in[k * n + i], in[k * n + j], acc);
       A[i][j] = acc;
+    } else {
+      A[i][j] = in[e];
     }
-  } else {
-    for (int e = tid; e < n * n; e += 256) A[e / n][e % n] = in[e];
   }
   __syncthreads();
-  jacobi_eig(A, V, n, cs_c, cs_s, red);
+  jacobi_eig(A, V, n, cs_c, cs_s, pp, qq, red);
   if (tid < n) lam[tid] = A[tid][tid];
   __syncthreads();
   double lmax = 0.0;
@@ -259,16 +301,20 @@ small_kernel(const double* __restrict__ in, int n, int r, double* __restrict__ o
     __syncthreads();
     for (int e = tid; e < n * r; e += 256) out[e] = V[e / r][perm[e % r]];
   } else {
-    // R = T_sub V diag(l^-1/2) V^T (eigenvalues below 1e-22 of the largest dropped)
+    // R = (T_sub V) diag(l^-1/2) V^T, eigenvalues below 1e-22 of the largest
+    // dropped; T_sub V (scaled) reuses A
+    __syncthreads();
+    for (int e = tid; e < n * n; e += 256) {
+      const int i = e / n, k = e % n;
+      double tv = 0.0;
+      for (int m = 0; m < n; ++m) tv = fma(in[i * n + m], V[m][k], tv);
+      A[i][k] = lam[k] > 1e-22 * lmax ? tv / sqrt(lam[k]) : 0.0;
+    }
+    __syncthreads();
     for (int e = tid; e < n * n; e += 256) {
       const int i = e / n, j = e % n;
       double acc = 0.0;
-      for (int k = 0; k < n; ++k) {
-        if (!(lam[k] > 1e-22 * lmax)) continue;
-        double tv = 0.0;                         // (T_sub V)[i][k]
-        for (int m = 0; m < n; ++m) tv = fma(in[i * n + m], V[m][k], tv);
-        acc = fma(tv / sqrt(lam[k]), V[j][k], acc);
-      }
+      for (int k = 0; k < n; ++k) acc = fma(A[i][k], V[j][k], acc);
       out32[e] = static_cast<float>(acc);
     }
   }
