@@ -125,6 +125,36 @@ def structured_rows(rw, torch, dev, timed, with_oracle):
                 O.head_hadamard(xs, 32)
             rec["oracle_rows_per_s"] = 256 / (time.perf_counter() - t0)
         out[name] = rec
+    # decode (T = 8 tokens) through the GEMM of the decode layer's linears:
+    # weight-streaming, so against HBM; eight weight sets rotated so that
+    # they do not stay in the 256 MB last-level cache
+    dec = {}
+    for name, K, N in (("qkv", 4096, 12288), ("o", 4096, 4096), ("gate_up", 4096, 32768),
+                       ("down", 16384, 4096)):
+        wbytes = N * K * 3 // 4
+        nset = min(24, max(2, -(-(320 << 20) // wbytes)))   # >= 320 MiB of weights in rotation
+        Tdec = 8
+        codes_w = [torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, generator=g).to(dev) & 0x77
+                   for _ in range(nset)]
+        wt = [rw.w4a4_tile_codes(c) for c in codes_w]
+        del codes_w
+        at = rw.w4a4_tile_codes(torch.randint(0, 256, (Tdec, K // 2), dtype=torch.uint8, generator=g).to(dev) & 0x77)
+        sa = torch.rand(Tdec, device=dev)
+        sw = torch.rand(N, device=dev)
+        yd = torch.empty((Tdec, N), dtype=torch.bfloat16, device=dev)
+        cnt = [0]
+
+        def call():
+            i = cnt[0] % nset
+            cnt[0] += 1
+            rw.w4a4_gemm_tiles(at, sa, wt[i], sw, Tdec, K, N, out=yd)
+        ms = timed(call, n=2 * nset)
+        gbs = wbytes / (ms * 1e-3) / 1e9
+        dec[name] = {"K": K, "N": N, "us": ms * 1e3, "weight_bytes": wbytes, "GB/s": gbs,
+                     "frac_hbm": gbs / PEAK_HBM_GBS}
+        del wt
+    out["decode_gemm_T8"] = dec
+
     # offline construction of (Q, R_sub) at the prefill shape (D = 4096, r = 32,
     # 4 subspace iterations): ten products with T (fp32 in, fp64 FMA), 2 D^2 p
     # flops each (p = r + 16)

@@ -12,7 +12,7 @@
 // and equals the INT32 accumulator. No VALU widening of nibbles is needed, and
 // the FP6 rate is twice the int8 rate on this chip.
 //
-// Two kernels:
+// Three kernels:
 //
 // * gemm6_lds_kernel (K % 128 == 0, T >= 128): a workgroup of WW x WT waves
 //   computes a (WW FW 32) x (WT FT 32) output block; each wave owns FW x FT
@@ -25,6 +25,8 @@
 // * gemm6_kernel (any K % 64 == 0, and small T): one wave per workgroup,
 //   BW x BT fragments, tiles read straight into registers, PD k-tiles in
 //   flight.
+// * gemm6_decode_kernel (T <= 32): 32 weight rows per workgroup of 16 waves
+//   that split K, for the weight-streaming decode products.
 //
 // In both, workgroups are renumbered so that each XCD works on a contiguous
 // band of weight tiles, and the bf16 epilogue is staged in LDS so that rows
@@ -448,6 +450,75 @@ tile_kernel(const uint8_t* __restrict__ codes, int64_t R, int64_t Rp, int64_t K,
   if (neg8 && bad) atomicOr(bad, 1);
 }
 
+// Decode products (T <= 32: one token tile). A workgroup of 16 waves owns 32
+// weight rows; wave w takes the k-tiles w, w + 16, ... of the whole K, with
+// all of its loads in flight at once (PDD tiles per round), so that the
+// weight stream has enough bytes in flight per CU; the 16 partial 32 x 32
+// accumulators are then summed through LDS in wave order (deterministic) and
+// the epilogue writes the T valid token columns. A one-wave-per-block kernel
+// leaves N / 128 waves for the whole chip at T = 8.
+constexpr int kDecWaves = 16;
+constexpr int kDecPD = 4;   // k-tiles a wave has in flight
+
+template <bool I32OUT>
+__global__ void __launch_bounds__(64 * kDecWaves)
+gemm6_decode_kernel(const uint8_t* __restrict__ at, const float* __restrict__ s_a,
+                    const uint8_t* __restrict__ wt, const float* __restrict__ s_w,
+                    void* __restrict__ y, int T, int K, int N) {
+  __shared__ float red[kDecWaves][16][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nb = (N + 31) / 32;
+  int b = blockIdx.x;
+  if ((nb & 7) == 0) b = (b & 7) * (nb >> 3) + (b >> 3);
+  const int n0 = b * 32;
+  const int KT = K >> 6;
+  const uint8_t* wrow = wt + static_cast<int64_t>(n0 >> 5) * KT * kTileBytes;
+  const uint8_t* arow = at;                      // token tile 0
+  v16f acc;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+  // rounds of kDecPD k-tiles: every load of a round is issued before its MFMAs
+  for (int k0 = wave; k0 < KT; k0 += kDecWaves * kDecPD) {
+    uint4 w0[kDecPD], a0[kDecPD];
+    uint2 w1[kDecPD], a1[kDecPD];
+#pragma unroll
+    for (int u = 0; u < kDecPD; ++u) {
+      const int kt = k0 + u * kDecWaves;
+      const int kc = kt < KT ? kt : k0;          // past the end: a harmless repeat, not used
+      const uint8_t* pw = wrow + static_cast<int64_t>(kc) * kTileBytes;
+      const uint8_t* pa = arow + static_cast<int64_t>(kc) * kTileBytes;
+      w0[u] = *reinterpret_cast<const uint4*>(pw + lane * 16);
+      w1[u] = *reinterpret_cast<const uint2*>(pw + kPlane1 + lane * 8);
+      a0[u] = *reinterpret_cast<const uint4*>(pa + lane * 16);
+      a1[u] = *reinterpret_cast<const uint2*>(pa + kPlane1 + lane * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < kDecPD; ++u)
+      if (k0 + u * kDecWaves < KT)
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(opnd(w0[u], w1[u]), opnd(a0[u], a1[u]),
+                                                              acc, 2, 2, 0, 127, 0, 127);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_sleep(1);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) red[wave][v][lane] = acc[v];
+  __syncthreads();
+  // thread (v, l): weight row 8 (v / 4) + 4 (l / 32) + v % 4, token l % 32
+  const int v = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int t = l & 31;
+  const int n = n0 + 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
+  if (t >= T || n >= N) return;
+  float sum = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kDecWaves; ++w) sum += red[w][v][l];
+  if constexpr (I32OUT) {
+    static_cast<int32_t*>(y)[static_cast<int64_t>(t) * N + n] = static_cast<int32_t>(sum);
+  } else {
+    static_cast<uint16_t*>(y)[static_cast<int64_t>(t) * N + n] = f32_to_bf16((sum * s_a[t]) * s_w[n]);
+  }
+}
+
 template <int BW, int BT, int PD, bool I32>
 hipError_t launch_cfg(const uint8_t* a, const float* s_a, const uint8_t* w, const float* s_w,
                       void* y, int64_t T, int64_t K, int64_t N, hipStream_t s) {
@@ -505,6 +576,18 @@ hipError_t launch_gemm_tiles(const uint8_t* a, const float* s_a, const uint8_t* 
                  : g6::launch_lds<2, 2, 2, 2, 3, true>(a, s_a, w, s_w, y, T, K, N, s);
     return big ? g6::launch_lds<2, 2, 4, 2, 3, false>(a, s_a, w, s_w, y, T, K, N, s)
                : g6::launch_lds<2, 2, 2, 2, 3, false>(a, s_a, w, s_w, y, T, K, N, s);
+  }
+  // decode products whose one-wave grid (N / 128 waves) would not cover the
+  // chip: the split-K decode kernel
+  if (T <= 32 && N < 16384) {
+    const unsigned nb = static_cast<unsigned>((N + 31) / 32);
+    if (i32_out)
+      hipLaunchKernelGGL((g6::gemm6_decode_kernel<true>), dim3(nb), dim3(64 * g6::kDecWaves), 0, s,
+                         a, s_a, w, s_w, y, static_cast<int>(T), static_cast<int>(K), static_cast<int>(N));
+    else
+      hipLaunchKernelGGL((g6::gemm6_decode_kernel<false>), dim3(nb), dim3(64 * g6::kDecWaves), 0, s,
+                         a, s_a, w, s_w, y, static_cast<int>(T), static_cast<int>(K), static_cast<int>(N));
+    return hipGetLastError();
   }
   if (i32_out) return g6::launch_cfg<4, 2, 4, true>(a, s_a, w, s_w, y, T, K, N, s);
   return g6::launch_cfg<4, 2, 4, false>(a, s_a, w, s_w, y, T, K, N, s);

@@ -388,7 +388,11 @@ def test_tile_codes_rejects_minus8(rw):
 @pytest.mark.parametrize("T,K,N", [(1, 64, 1), (64, 256, 256), (300, 512, 384), (129, 4096, 130),
                                    (17, 16384, 64), (8, 4096, 12288), (257, 192, 1000),
                                    (256, 128, 256), (200, 640, 520),
-                                   (4096, 4096, 4096), (4100, 1024, 4104)])
+                                   (4096, 4096, 4096), (4100, 1024, 4104),
+                                   # decode products (split-K workgroups): a full token
+                                   # tile, ragged N, K with fewer k-tiles than waves
+                                   (32, 4096, 4096), (5, 192, 100), (31, 1088, 4000),
+                                   (8, 16384, 4096), (2, 64, 16383)])
 def test_w4a4_gemm_tiles(rw, T, K, N):
     say(f"w4a4_gemm_tiles T={T} K={K} N={N}")
     a, qa = _codes7(T + K, T, K)
