@@ -204,7 +204,6 @@ rw4_status fwht(const void* x, rw4_dtype x_dt, float* y, int64_t T, int64_t D, v
   if (!x || !y) return RW4_ERR_INVALID_ARG;
   if (!al16(x) || !al16(y)) return RW4_ERR_MISALIGNED;
   if (x == static_cast<const void*>(y) && x_dt != RW4_F32) return RW4_ERR_INVALID_ARG;
-  if (T == 0) return RW4_OK;
   return hip_status(rw4::launch_row(x, x_dt == RW4_F32 ? rw4::IN_F32 : rw4::IN_BF16, D, T, D, true,
                                     y, nullptr, false, nullptr, nullptr, strm(stream)));
 }
@@ -349,12 +348,13 @@ size_t respin_align_prepared_workspace_size(int64_t T, int64_t D, int64_t r) {
 rw4_status respin_align_prepared(const void* x, void* out, rw4_dtype out_dt, const void* basis,
                                  const void* addend, int64_t T, int64_t D, int64_t r,
                                  void* workspace, size_t ws_bytes, void* stream) {
-  if (!x || !out || !basis || T < 0 || D < 1 || r < 1 || !fdt(out_dt)) return RW4_ERR_INVALID_ARG;
+  if (T < 0 || D < 1 || r < 1 || !fdt(out_dt)) return RW4_ERR_INVALID_ARG;
   if (respin_basis_size(D, r) == 0) return RW4_ERR_UNSUPPORTED;
+  if (T == 0) return RW4_OK;
+  if (!x || !out || !basis) return RW4_ERR_INVALID_ARG;
   if (!al16(x) || !al16(out) || (addend && !al16(addend))) return RW4_ERR_MISALIGNED;
   if (reinterpret_cast<uintptr_t>(basis) & 255u) return RW4_ERR_INVALID_ARG;
   if (x == out) return RW4_ERR_INVALID_ARG;
-  if (T == 0) return RW4_OK;
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) ||
       ws_bytes < rw4::align_zpart_bytes(T, D, r))
     return RW4_ERR_WORKSPACE;

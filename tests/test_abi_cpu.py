@@ -241,6 +241,7 @@ def test_respin_align_prepared_validation():
     assert _rap(ws=NUL) == WSE and _rap(wsb=100) == WSE
     assert _rap(ws=ctypes.c_void_p(0x40010)) == WSE
     assert _rap(T=0, ws=NUL) == 0
+    assert _rap(T=0, x=NUL, out=NUL, basis=NUL, ws=NUL) == 0   # empty call: no pointer read
 
 
 def test_structured_transform_validation():

@@ -612,6 +612,103 @@ def test_rotated_linear_strided_input(rw):
     assert nbad == 0, worst
 
 
+def _special_rows(T, D, seed):
+    """bf16 bits [T][D]: degenerate rows first, then ordinary activations."""
+    rng = np.random.default_rng(seed)
+    x = W.bf16_bits_to_f32(W.gen_x(seed, T, D, 4, 30.0))
+    x[0] = 0.0                                                    # all zero
+    x[1] = 0.0
+    x[1, D // 3] = -3.0                                           # one entry
+    x[2] = W.bf16_bits_to_f32((rng.integers(1, 0x80, D) | (rng.integers(0, 2, D) << 15))
+                              .astype(np.uint16))                 # bf16 subnormals only
+    x[3] = rng.standard_normal(D).astype(np.float32) * np.float32(1e30)   # large
+    x[4] = 1.0                                                    # constant: one Walsh row
+    x[5] = np.where(np.arange(D) % 2 == 0, 1.0, -1.0)             # alternating: another
+    return W.f32_to_bf16_bits(x)
+
+
+# degenerate token rows through the fused prologue (D = 4096, r = 32), the
+# unfused path (D = 8192) and the quantizer alone; 3-bit codes on one case
+@pytest.mark.parametrize("T,D,r,flags,bits,prepared", [
+    (40, 4096, 32, 3, 4, True), (40, 4096, 32, 3, 4, False), (40, 4096, 32, 3, 3, True),
+    (12, 8192, 64, 3, 4, True), (12, 4096, 0, 2, 4, False), (12, 4096, 0, 0, 4, False)])
+def test_rotated_linear_special_rows(rw, T, D, r, flags, bits, prepared):
+    say(f"rotated_linear special rows T={T} D={D} r={r} flags={flags} bits={bits} "
+        f"prepared={prepared}")
+    t = torch()
+    N = 64
+    xb = _special_rows(T, D, seed=D + r + flags)
+    Q, M = W.gen_basis(D + r, D, r) if r else (None, None)
+    Wf = W.gen_weight(N + D, N, D, 0.02)
+    codes_w, s_w, qw, sw_h = _prep(rw, Wf, bool(flags & 2), bits)
+    fl = flags | rw.RW4_ABITS(bits)
+    dbg = t.empty((T, D), dtype=t.float32, device="cuda")
+    if prepared:
+        basis = rw.respin_prepare_basis(dev(Q), dev(M)) if r else None
+        y, ws = rw.rotated_linear_prepared(dev(xb), codes_w, s_w, fl, basis, r, dbg_prequant=dbg)
+    else:
+        y, ws = rw.rotated_linear(dev(xb), codes_w, s_w, fl, dev(Q) if r else None,
+                                  dev(M) if r else None, dbg_prequant=dbg)
+    _sync()
+    pre, y = host(dbg), host(y)
+    tiles_g, sa_g = (host(v) for v in rw.workspace_views(ws, T, D))
+    ref_pre = O.prequant(O.bf16_to_f64(xb), fl, Q, M)
+    assert np.isfinite(pre).all()
+    # the zero row stays exactly zero, with zero codes and a zero scale
+    assert not pre[0].any() and sa_g[0] == 0.0 and not y[0].any()
+    # every row with normal-range values on its own
+    for i in [1, 3, 4, 5] + list(range(6, T)):
+        assert normwise(pre[i:i + 1], ref_pre[i:i + 1]) <= FP32_TOL, i
+    # The subnormal row: the alignment's correction multiplies the r
+    # projections z = Q^T x as bf16 (hi, lo) pairs, and for |z_j| near 1e-39
+    # the low half underflows bf16's subnormal spacing 2^-133, so each z_j is
+    # off by at most 2^-134. Q is orthonormal and the Hadamard orthogonal,
+    # hence ||err||_inf <= ||err||_2 <= ||M - I||_2 sqrt(r) 2^-134, plus fp32's
+    # own subnormal rounding (2^-150 per step, log2 D steps of the transform).
+    floor = np.log2(D) * 2.0 ** -149
+    if r:
+        floor += np.linalg.norm(M.astype(np.float64) - np.eye(r), 2) * np.sqrt(r) * 2.0 ** -133
+    err2 = np.abs(pre[2] - ref_pre[2]).max()
+    say(f"   subnormal row: max error {err2:.3e}, bound {FP32_TOL * np.abs(ref_pre[2]).max() + floor:.3e}")
+    assert err2 <= FP32_TOL * np.abs(ref_pre[2]).max() + floor
+    q, s = O.quant_sym(pre, bits)
+    np.testing.assert_array_equal(sa_g, s)
+    np.testing.assert_array_equal(F.untile(tiles_g, T, D), q)
+    nbad, worst = bf16_rel(y, O.epilogue(O.gemm_int(q, qw), s, sw_h))
+    assert nbad == 0, worst
+
+
+def test_empty_batches(rw):
+    """T = 0 through every entry point that takes token rows: no error, no write."""
+    say("empty batches")
+    t = torch()
+    D, N, r = 4096, 64, 32
+    x0 = t.empty((0, D), dtype=t.bfloat16, device="cuda")
+    xf = t.empty((0, D), dtype=t.float32, device="cuda")
+    Q, M = (dev(v) for v in W.gen_basis(5, D, r))
+    basis = rw.respin_prepare_basis(Q, M)
+    codes_w, s_w, _, _ = _prep(rw, W.gen_weight(6, N, D, 0.02), True)
+    for direct in (False, True):
+        assert rw.respin_align(x0, Q, M, direct=direct).shape == (0, D)
+    assert rw.respin_align_prepared(x0, basis, r).shape == (0, D)
+    assert rw.fwht(xf).shape == (0, D)
+    assert rw.hadamard_transform(t.empty((0, 28 * 64), dtype=t.float32, device="cuda"),
+                                 28).shape == (0, 28 * 64)
+    assert rw.head_hadamard(x0, 32).shape == (0, D)
+    c, s = rw.quant_act_sym(xf, 3)
+    assert c.shape == (0, D // 2) and s.shape == (0,)
+    a = t.empty((0, D // 2), dtype=t.uint8, device="cuda")
+    w_codes = t.zeros((N, D // 2), dtype=t.uint8, device="cuda")
+    assert rw.w4a4_gemm(a, t.empty((0,), device="cuda"), w_codes, s_w).shape == (0, N)
+    guard = t.full((4, N), 7.0, dtype=t.bfloat16, device="cuda")
+    for fl in (3, 0, 2 | rw.RW4_ABITS(3), rw.RW4_HEADS(32)):
+        y, _ = rw.rotated_linear(x0, codes_w, s_w, fl, Q, M, out=guard[:0])
+        y2, _ = rw.rotated_linear_prepared(x0, codes_w, s_w, fl, basis, r, out=guard[:0])
+        assert y.shape == (0, N) and y2.shape == (0, N)
+    _sync()
+    assert bool((guard == 7.0).all())
+
+
 # ---------------------------------------------------------------- decoder layer
 def _layer_check(rw, cid, sample=None):
     wl = W.CONFIGS[cid]
