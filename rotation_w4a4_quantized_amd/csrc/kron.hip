@@ -8,13 +8,16 @@
 // heads, H_{n_h} (x) I_{d_h}; c = sqrt(n_h)). s is an optional +-1 vector (the
 // randomized H diag(s)), applied as the row is loaded.
 //
-// One workgroup per row, the row staged in LDS (fp32, D <= 16384):
-//   1. load (bf16, fp32, or the SiLU-gated front of a gate|up row), times s,
-//      and for K_B = H_m the m-point product of every group of m consecutive
-//      values, in registers (the +-1 table is a compile-time constant, so the
-//      product is straight-line adds and subtracts);
+// One workgroup of 512 threads per row, the row staged in LDS (fp32,
+// D <= 16384):
+//   1. load (bf16, fp32, or the SiLU-gated front of a gate|up row), coalesced,
+//      with every load of the thread's share issued before the first use,
+//      times s, into LDS; then for K_B = H_m the m-point product of every
+//      group of m consecutive values, read back into registers (the +-1 table
+//      is a compile-time constant, so the product is straight-line adds and
+//      subtracts);
 //   2. H_A along i (stride B) in LDS passes of radix 8 (the last one 2, 4 or
-//      8), one barrier per pass;
+//      8), one barrier per pass, on 4-column groups when B % 4 == 0;
 //   3. u = c^-1 x (the transform's scale), then fp32 rows, or the row's absmax
 //      step and its codes (packed INT4 rows or FP6 operand tiles), from
 //      32-value chunks of LDS.
@@ -24,7 +27,7 @@
 namespace rw4 {
 namespace {
 
-constexpr int kKronThreads = 256;
+constexpr int kKronThreads = 512;
 
 constexpr bool kron_prime(int q) {
   if (q < 2) return false;
@@ -97,43 +100,93 @@ __device__ __forceinline__ void paley_apply(const float (&v)[M], float (&o)[M]) 
   }
 }
 
-// four consecutive input values at element offset off of a row (16-byte
-// aligned for fp32, 8-byte for bf16); gate|up rows give SiLU(g) * u in fp32
+// Raw bits of four consecutive input values at element offset off of a row
+// (16-byte aligned for fp32, 8-byte for bf16; gate|up rows also hold the up
+// half). Every load of a row is issued before the first value is used, so a
+// thread waits for memory once per row.
 template <int IN>
-__device__ __forceinline__ void load4(float (&q)[4], const void* x, int64_t off, int D) {
+struct Raw4 {
+  uint4 a;  // fp32: four values; bf16: .x, .y; gate|up: gate in .x, .y, up in .z, .w
+};
+
+template <int IN>
+__device__ __forceinline__ void fetch4(Raw4<IN>& r, const void* x, int64_t off, int D) {
   if constexpr (IN == IN_F32) {
-    const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(x) + off);
-    q[0] = a.x; q[1] = a.y; q[2] = a.z; q[3] = a.w;
+    r.a = *reinterpret_cast<const uint4*>(static_cast<const float*>(x) + off);
   } else {
     const uint16_t* p = static_cast<const uint16_t*>(x) + off;
-    const uint2 a = *reinterpret_cast<const uint2*>(p);
-    q[0] = bf16lo(a.x); q[1] = bf16hi(a.x); q[2] = bf16lo(a.y); q[3] = bf16hi(a.y);
+    const uint2 g = *reinterpret_cast<const uint2*>(p);
+    r.a.x = g.x; r.a.y = g.y;
     if constexpr (IN == IN_SWIGLU) {
-      const uint2 b = *reinterpret_cast<const uint2*>(p + D);
-      const float u[4] = {bf16lo(b.x), bf16hi(b.x), bf16lo(b.y), bf16hi(b.y)};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) q[e] = q[e] / (1.0f + expf(-q[e])) * u[e];
+      const uint2 u = *reinterpret_cast<const uint2*>(p + D);
+      r.a.z = u.x; r.a.w = u.y;
     }
   }
 }
 
-// natural-order R-point transform of the values buf[base + r st], r < R
-template <int R>
-__device__ __forceinline__ void radix_pass(float* buf, int base, int st) {
-  float v[R];
+// the four fp32 values (SiLU(g) * u for gate|up rows), times the signs if any
+template <int IN>
+__device__ __forceinline__ void unpack4(float (&q)[4], const Raw4<IN>& r, bool use_signs,
+                                        const float4& sg) {
+  if constexpr (IN == IN_F32) {
+    q[0] = __uint_as_float(r.a.x); q[1] = __uint_as_float(r.a.y);
+    q[2] = __uint_as_float(r.a.z); q[3] = __uint_as_float(r.a.w);
+  } else {
+    q[0] = bf16lo(r.a.x); q[1] = bf16hi(r.a.x); q[2] = bf16lo(r.a.y); q[3] = bf16hi(r.a.y);
+    if constexpr (IN == IN_SWIGLU) {
+      const float u[4] = {bf16lo(r.a.z), bf16hi(r.a.z), bf16lo(r.a.w), bf16hi(r.a.w)};
 #pragma unroll
-  for (int r = 0; r < R; ++r) v[r] = buf[base + r * st];
+      for (int e = 0; e < 4; ++e) q[e] = q[e] / (1.0f + expf(-q[e])) * u[e];
+    }
+  }
+  if (use_signs) {
+    q[0] *= sg.x; q[1] *= sg.y; q[2] *= sg.z; q[3] *= sg.w;
+  }
+}
+
+// natural-order R-point transform of the values (float) or 4-value columns
+// (float4) at buf[base + r st], r < R
+template <int R, typename V>
+__device__ __forceinline__ void radix_pass(float* buf, int base, int st) {
+  V v[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) v[r] = *reinterpret_cast<const V*>(buf + base + r * st);
 #pragma unroll
   for (int h = 1; h < R; h <<= 1)
 #pragma unroll
     for (int r = 0; r < R; ++r)
       if ((r & h) == 0) {
-        const float a = v[r], b = v[r + h];
+        const V a = v[r], b = v[r + h];
         v[r] = a + b;
         v[r + h] = a - b;
       }
 #pragma unroll
-  for (int r = 0; r < R; ++r) buf[base + r * st] = v[r];
+  for (int r = 0; r < R; ++r) *reinterpret_cast<V*>(buf + base + r * st) = v[r];
+}
+
+// H_A along i (stride B) over the row in LDS: passes over three bits of i at
+// a time, one barrier each. With V = float4 a work item is four adjacent
+// columns j (B % 4 == 0), a quarter of the LDS instructions.
+template <typename V>
+__device__ __forceinline__ void h_a_passes(float* buf, int A, int B, int logA, int tid) {
+  constexpr int L = sizeof(V) / sizeof(float);
+  const int BL = B / L;
+  const int D = A * B;
+  for (int b0 = 0; b0 < logA; b0 += 3) {
+    const int rb = min(3, logA - b0);
+    const int items = (D >> rb) / L;
+    const int st = B << b0;
+    const int lomask = (1 << b0) - 1;
+    for (int w = tid; w < items; w += kKronThreads) {
+      const int jl = w % BL;
+      const int t = w / BL;
+      const int base = (((t >> b0) << (b0 + rb)) + (t & lomask)) * B + L * jl;
+      if (rb == 3) radix_pass<8, V>(buf, base, st);
+      else if (rb == 2) radix_pass<4, V>(buf, base, st);
+      else radix_pass<2, V>(buf, base, st);
+    }
+    __syncthreads();
+  }
 }
 
 enum KronOut { KRON_F32 = 0, KRON_PACKED = 1, KRON_TILES = 2 };
@@ -149,32 +202,42 @@ kron_row_kernel(const void* __restrict__ x, int64_t ldx, int A, int B, int logA,
   const int D = A * B;
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
-  const int64_t roff = row * ldx;
 
-  // 1. load, signs, inner factor
-  if constexpr (M == 0) {
-    for (int f = 4 * tid; f < D; f += 4 * kKronThreads) {
+  // 1. the row (all of the thread's loads issued before the first use; 4-value
+  // chunks f = 4 (tid + k kKronThreads), coalesced), times s, into LDS
+  constexpr int NC = kKronMaxD / (4 * kKronThreads);
+  Raw4<IN> raw[NC];
+  float4 sg[NC];
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    const int f = 4 * (tid + k * kKronThreads);
+    if (f < D) {
+      fetch4<IN>(raw[k], x, row * ldx + f, D);
+      sg[k] = signs ? *reinterpret_cast<const float4*>(signs + f) : make_float4(1.f, 1.f, 1.f, 1.f);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    const int f = 4 * (tid + k * kKronThreads);
+    if (f < D) {
       float q[4];
-      load4<IN>(q, x, roff + f, D);
-      if (signs) {
-        const float4 sg = *reinterpret_cast<const float4*>(signs + f);
-        q[0] *= sg.x; q[1] *= sg.y; q[2] *= sg.z; q[3] *= sg.w;
-      }
+      unpack4<IN>(q, raw[k], signs != nullptr, sg[k]);
       *reinterpret_cast<float4*>(buf + f) = make_float4(q[0], q[1], q[2], q[3]);
     }
-  } else {
+  }
+  __syncthreads();
+
+  // the inner factor H_m on every group of m consecutive values, in place
+  // (a group's float4 reads are m / 4 apart: no bank conflicts for m = 12,
+  // 20, 28)
+  if constexpr (M != 0) {
     static_assert(M % 4 == 0, "m is a multiple of 4");
     for (int i = tid; i < A; i += kKronThreads) {
       float v[M];
 #pragma unroll
       for (int c = 0; c < M / 4; ++c) {
-        float q[4];
-        load4<IN>(q, x, roff + static_cast<int64_t>(i) * M + 4 * c, D);
-        if (signs) {
-          const float4 sg = *reinterpret_cast<const float4*>(signs + i * M + 4 * c);
-          q[0] *= sg.x; q[1] *= sg.y; q[2] *= sg.z; q[3] *= sg.w;
-        }
-        v[4 * c] = q[0]; v[4 * c + 1] = q[1]; v[4 * c + 2] = q[2]; v[4 * c + 3] = q[3];
+        const float4 q = *reinterpret_cast<const float4*>(buf + i * M + 4 * c);
+        v[4 * c] = q.x; v[4 * c + 1] = q.y; v[4 * c + 2] = q.z; v[4 * c + 3] = q.w;
       }
       float o[M];
       paley_apply<M>(v, o);
@@ -183,25 +246,12 @@ kron_row_kernel(const void* __restrict__ x, int64_t ldx, int A, int B, int logA,
         *reinterpret_cast<float4*>(buf + i * M + 4 * c) =
             make_float4(o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]);
     }
-  }
-  __syncthreads();
-
-  // 2. H_A along i: passes over three bits of i at a time
-  for (int b0 = 0; b0 < logA; b0 += 3) {
-    const int rb = min(3, logA - b0);
-    const int items = D >> rb;
-    const int st = B << b0;
-    const int lomask = (1 << b0) - 1;
-    for (int w = tid; w < items; w += kKronThreads) {
-      const int j = w % B;
-      const int t = w / B;
-      const int base = (((t >> b0) << (b0 + rb)) + (t & lomask)) * B + j;
-      if (rb == 3) radix_pass<8>(buf, base, st);
-      else if (rb == 2) radix_pass<4>(buf, base, st);
-      else radix_pass<2>(buf, base, st);
-    }
     __syncthreads();
   }
+
+  // 2. H_A along i
+  if (B % 4 == 0) h_a_passes<float4>(buf, A, B, logA, tid);
+  else h_a_passes<float>(buf, A, B, logA, tid);
 
   // 3. output: u = norm * buf
   if constexpr (OUT == KRON_F32) {
@@ -216,7 +266,9 @@ kron_row_kernel(const void* __restrict__ x, int64_t ldx, int A, int B, int logA,
     m = wave_max(m);
     if ((tid & 63) == 0) red[tid >> 6] = m;
     __syncthreads();
-    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    m = red[0];
+#pragma unroll
+    for (int k = 1; k < kKronThreads / 64; ++k) m = fmaxf(m, red[k]);
     const float stp = m / qmax;
     if (tid == 0) scales[row] = stp;
     const RowQuant rq(stp);
@@ -255,22 +307,29 @@ kron_row_kernel(const void* __restrict__ x, int64_t ldx, int A, int B, int logA,
   }
 }
 
+template <int IN, int M, int OUT>
+hipError_t launch_kron_out(const void* x, int64_t ldx, int64_t T, int A, int B, int logA,
+                           const float* signs, float norm, float* y, uint8_t* codes,
+                           float* scales, float* dbg, float qmax, hipStream_t s) {
+  const size_t lds = static_cast<size_t>(A) * B * sizeof(float);
+  hipLaunchKernelGGL((kron_row_kernel<IN, M, OUT>), dim3(static_cast<unsigned>(T)),
+                     dim3(kKronThreads), lds, s, x, ldx, A, B, logA, signs, norm, y, codes,
+                     scales, dbg, qmax);
+  return hipGetLastError();
+}
+
 template <int IN, int M>
 hipError_t launch_kron_m(const void* x, int64_t ldx, int64_t T, int A, int B, int logA,
                          const float* signs, float norm, float* y, uint8_t* codes, bool tiled,
                          float* scales, float* dbg, float qmax, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(T)), block(kKronThreads);
-  const size_t lds = static_cast<size_t>(A) * B * sizeof(float);
   if (y)
-    hipLaunchKernelGGL((kron_row_kernel<IN, M, KRON_F32>), grid, block, lds, s, x, ldx, A, B, logA,
-                       signs, norm, y, codes, scales, dbg, qmax);
-  else if (tiled)
-    hipLaunchKernelGGL((kron_row_kernel<IN, M, KRON_TILES>), grid, block, lds, s, x, ldx, A, B,
-                       logA, signs, norm, y, codes, scales, dbg, qmax);
-  else
-    hipLaunchKernelGGL((kron_row_kernel<IN, M, KRON_PACKED>), grid, block, lds, s, x, ldx, A, B,
-                       logA, signs, norm, y, codes, scales, dbg, qmax);
-  return hipGetLastError();
+    return launch_kron_out<IN, M, KRON_F32>(x, ldx, T, A, B, logA, signs, norm, y, codes, scales,
+                                            dbg, qmax, s);
+  if (tiled)
+    return launch_kron_out<IN, M, KRON_TILES>(x, ldx, T, A, B, logA, signs, norm, y, codes,
+                                              scales, dbg, qmax, s);
+  return launch_kron_out<IN, M, KRON_PACKED>(x, ldx, T, A, B, logA, signs, norm, y, codes, scales,
+                                             dbg, qmax, s);
 }
 
 template <int IN>
