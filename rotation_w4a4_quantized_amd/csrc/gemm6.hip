@@ -451,14 +451,16 @@ tile_kernel(const uint8_t* __restrict__ codes, int64_t R, int64_t Rp, int64_t K,
 }
 
 // Decode products (T <= 32: one token tile). A workgroup of 16 waves owns 32
-// weight rows; wave w takes the k-tiles w, w + 16, ... of the whole K, with
-// all of its loads in flight at once (PDD tiles per round), so that the
-// weight stream has enough bytes in flight per CU; the 16 partial 32 x 32
-// accumulators are then summed through LDS in wave order (deterministic) and
-// the epilogue writes the T valid token columns. A one-wave-per-block kernel
-// leaves N / 128 waves for the whole chip at T = 8.
+// weight rows; wave w takes the k-tiles w, w + 16, ... of the whole K, and
+// the 16 partial 32 x 32 accumulators are then summed through LDS in wave
+// order (deterministic) before the epilogue writes the T valid token columns.
+// Lanes whose token row is past T load nothing and hold zeros: those rows
+// only reach output columns that are never written, and at T = 8 this drops
+// three quarters of the activation loads, which at K = 4096 are as many as the
+// weight loads. One k-tile in flight per wave streams the weights as fast as
+// four did: the chip-wide stream, not the per-wave depth, is the limit.
 constexpr int kDecWaves = 16;
-constexpr int kDecPD = 4;   // k-tiles a wave has in flight
+constexpr int kDecPD = 1;   // k-tiles a wave has in flight
 
 template <bool I32OUT>
 __global__ void __launch_bounds__(64 * kDecWaves)
@@ -489,8 +491,13 @@ gemm6_decode_kernel(const uint8_t* __restrict__ at, const float* __restrict__ s_
       const uint8_t* pa = arow + static_cast<int64_t>(kc) * kTileBytes;
       w0[u] = *reinterpret_cast<const uint4*>(pw + lane * 16);
       w1[u] = *reinterpret_cast<const uint2*>(pw + kPlane1 + lane * 8);
-      a0[u] = *reinterpret_cast<const uint4*>(pa + lane * 16);
-      a1[u] = *reinterpret_cast<const uint2*>(pa + kPlane1 + lane * 8);
+      if ((lane & 31) < T) {
+        a0[u] = *reinterpret_cast<const uint4*>(pa + lane * 16);
+        a1[u] = *reinterpret_cast<const uint2*>(pa + kPlane1 + lane * 8);
+      } else {
+        a0[u] = make_uint4(0, 0, 0, 0);
+        a1[u] = make_uint2(0, 0);
+      }
     }
 #pragma unroll
     for (int u = 0; u < kDecPD; ++u)
@@ -577,9 +584,8 @@ hipError_t launch_gemm_tiles(const uint8_t* a, const float* s_a, const uint8_t* 
     return big ? g6::launch_lds<2, 2, 4, 2, 3, false>(a, s_a, w, s_w, y, T, K, N, s)
                : g6::launch_lds<2, 2, 2, 2, 3, false>(a, s_a, w, s_w, y, T, K, N, s);
   }
-  // decode products whose one-wave grid (N / 128 waves) would not cover the
-  // chip: the split-K decode kernel
-  if (T <= 32 && N < 16384) {
+  // decode products (one token tile): the split-K decode kernel
+  if (T <= 32) {
     const unsigned nb = static_cast<unsigned>((N + 31) / 32);
     if (i32_out)
       hipLaunchKernelGGL((g6::gemm6_decode_kernel<true>), dim3(nb), dim3(64 * g6::kDecWaves), 0, s,

@@ -392,7 +392,7 @@ def test_tile_codes_rejects_minus8(rw):
                                    # decode products (split-K workgroups): a full token
                                    # tile, ragged N, K with fewer k-tiles than waves
                                    (32, 4096, 4096), (5, 192, 100), (31, 1088, 4000),
-                                   (8, 16384, 4096), (2, 64, 16383)])
+                                   (8, 16384, 4096), (2, 64, 16383), (8, 1024, 32768)])
 def test_w4a4_gemm_tiles(rw, T, K, N):
     say(f"w4a4_gemm_tiles T={T} K={K} N={N}")
     a, qa = _codes7(T + K, T, K)
@@ -419,6 +419,19 @@ def test_w4a4_gemm_tiles(rw, T, K, N):
     if ref is not None:
         nbad, worst = bf16_rel(y, O.epilogue(ref, s_a, s_w))
         assert nbad == 0, worst
+
+
+def test_w4a4_gemm_tiles_ignores_rows_past_T(rw):
+    """Activation tiles hold 32-row blocks; rows past T (unwritten workspace in
+    the unit) must not reach the T valid rows, on the decode path as elsewhere."""
+    K, N = 1024, 300
+    a, qa = _codes7(77, 32, K)
+    w, qw = _codes7(78, N, K)
+    at = rw.w4a4_tile_codes(dev(a))          # all 32 rows nonzero
+    for T in (1, 8, 31):
+        acc = host(rw.w4a4_gemm_tiles(at, None, rw.w4a4_tile_codes(dev(w)), None, T, K, N,
+                                      out_dtype=torch().int32))
+        np.testing.assert_array_equal(acc, O.gemm_int(qa[:T], qw))
 
 
 def test_w4a4_gemm_tiles_extremes(rw):
