@@ -12,7 +12,7 @@
 // and equals the INT32 accumulator. No VALU widening of nibbles is needed, and
 // the FP6 rate is twice the int8 rate on this chip.
 //
-// Three kernels:
+// Four kernels:
 //
 // * gemm6_lds_kernel (K % 128 == 0, T >= 128): a workgroup of WW x WT waves
 //   computes a (WW FW 32) x (WT FT 32) output block; each wave owns FW x FT
@@ -25,8 +25,9 @@
 // * gemm6_kernel (any K % 64 == 0, and small T): one wave per workgroup,
 //   BW x BT fragments, tiles read straight into registers, PD k-tiles in
 //   flight.
-// * gemm6_decode_kernel (T <= 32): 32 weight rows per workgroup of 16 waves
-//   that split K, for the weight-streaming decode products.
+// * gemm6_decode16_kernel (T <= 16, N <= 16384) and gemm6_decode_kernel
+//   (T <= 32): 16 or 32 weight rows per workgroup whose waves split K, for the
+//   weight-streaming decode products.
 //
 // In both, workgroups are renumbered so that each XCD works on a contiguous
 // band of weight tiles, and the bf16 epilogue is staged in LDS so that rows
@@ -526,6 +527,84 @@ gemm6_decode_kernel(const uint8_t* __restrict__ at, const float* __restrict__ s_
   }
 }
 
+// Decode products with at most 16 tokens on 16 x 16 x 128 MFMAs: 16 weight
+// rows per workgroup, twice the workgroups of the 32-row kernel, which leaves
+// half of the CUs idle at N = 4096. The operands come straight from the
+// 32-row tiles: operand lane l holds row l % 16 and K values 32 (l / 16) ..
+// + 31 of a 128-wide step, which is lane slot 32 ((l / 16) % 2) + row of
+// k-tile 2 kp + l / 32 (the 32 x 32 x 64 layout's K halves). NWV waves split
+// the k-pairs; the partial 16 x 16 sums are added through LDS in wave order.
+template <int NWV, bool I32OUT>
+__global__ void __launch_bounds__(64 * NWV)
+gemm6_decode16_kernel(const uint8_t* __restrict__ at, const float* __restrict__ s_a,
+                      const uint8_t* __restrict__ wt, const float* __restrict__ s_w,
+                      void* __restrict__ y, int T, int K, int N) {
+  __shared__ float red[NWV][4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nb = (N + 15) / 16;
+  int b = blockIdx.x;
+  if ((nb & 7) == 0) b = (b & 7) * (nb >> 3) + (b >> 3);
+  const int n0 = b * 16;
+  const int KT = K >> 6, KP = (KT + 1) >> 1;  // k-tiles, 128-wide steps (the last may be half)
+  const uint8_t* wrow = wt + static_cast<int64_t>(n0 >> 5) * KT * kTileBytes;
+  const int c = lane >> 4;
+  const int tsub = c >> 1;
+  const int wslot = (c & 1) * 32 + (n0 & 16) + (lane & 15);
+  const int aslot = (c & 1) * 32 + (lane & 15);
+  const bool aload = (lane & 15) < T;  // token rows past T hold zeros
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  for (int kp = wave; kp < KP; kp += NWV) {
+    const int kt = 2 * kp + tsub;
+    uint4 w0 = make_uint4(0, 0, 0, 0), a0 = make_uint4(0, 0, 0, 0);
+    uint2 w1 = make_uint2(0, 0), a1 = make_uint2(0, 0);
+    if (kt < KT) {
+      const uint8_t* pw = wrow + static_cast<int64_t>(kt) * kTileBytes;
+      w0 = *reinterpret_cast<const uint4*>(pw + wslot * 16);
+      w1 = *reinterpret_cast<const uint2*>(pw + kPlane1 + wslot * 8);
+      if (aload) {
+        const uint8_t* pa = at + static_cast<int64_t>(kt) * kTileBytes;
+        a0 = *reinterpret_cast<const uint4*>(pa + aslot * 16);
+        a1 = *reinterpret_cast<const uint2*>(pa + kPlane1 + aslot * 8);
+      }
+    }
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(opnd(w0, w1), opnd(a0, a1), acc, 2, 2,
+                                                           0, 127, 0, 127);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_sleep(1);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) red[wave][i][lane] = acc[i];
+  __syncthreads();
+  if (threadIdx.x >= 256) return;
+  // thread (i, l): weight row 4 (l / 16) + i, token l % 16
+  const int i = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int t = l & 15;
+  const int n = n0 + 4 * (l >> 4) + i;
+  if (t >= T || n >= N) return;
+  float sum = 0.0f;
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) sum += red[w][i][l];
+  if constexpr (I32OUT) {
+    static_cast<int32_t*>(y)[static_cast<int64_t>(t) * N + n] = static_cast<int32_t>(sum);
+  } else {
+    static_cast<uint16_t*>(y)[static_cast<int64_t>(t) * N + n] = f32_to_bf16((sum * s_a[t]) * s_w[n]);
+  }
+}
+
+template <int NWV>
+hipError_t launch_decode16(const uint8_t* a, const float* s_a, const uint8_t* w, const float* s_w,
+                           void* y, bool i32_out, int64_t T, int64_t K, int64_t N, hipStream_t s) {
+  const unsigned nb = static_cast<unsigned>((N + 15) / 16);
+  if (i32_out)
+    hipLaunchKernelGGL((gemm6_decode16_kernel<NWV, true>), dim3(nb), dim3(64 * NWV), 0, s, a, s_a,
+                       w, s_w, y, static_cast<int>(T), static_cast<int>(K), static_cast<int>(N));
+  else
+    hipLaunchKernelGGL((gemm6_decode16_kernel<NWV, false>), dim3(nb), dim3(64 * NWV), 0, s, a, s_a,
+                       w, s_w, y, static_cast<int>(T), static_cast<int>(K), static_cast<int>(N));
+  return hipGetLastError();
+}
+
 template <int BW, int BT, int PD, bool I32>
 hipError_t launch_cfg(const uint8_t* a, const float* s_a, const uint8_t* w, const float* s_w,
                       void* y, int64_t T, int64_t K, int64_t N, hipStream_t s) {
@@ -584,7 +663,15 @@ hipError_t launch_gemm_tiles(const uint8_t* a, const float* s_a, const uint8_t* 
     return big ? g6::launch_lds<2, 2, 4, 2, 3, false>(a, s_a, w, s_w, y, T, K, N, s)
                : g6::launch_lds<2, 2, 2, 2, 3, false>(a, s_a, w, s_w, y, T, K, N, s);
   }
-  // decode products (one token tile): the split-K decode kernel
+  // decode products: up to 16 tokens and N <= 16384 on 16-row workgroups,
+  // with fewer waves per workgroup as their number grows (measured at T = 8:
+  // 16 waves for N = 4096, 4 for N = 12288); otherwise 32-row workgroups
+  if (T <= 16 && N <= 16384) {
+    const int64_t nb = (N + 15) / 16;
+    if (nb <= 256) return g6::launch_decode16<16>(a, s_a, w, s_w, y, i32_out, T, K, N, s);
+    if (nb <= 512) return g6::launch_decode16<8>(a, s_a, w, s_w, y, i32_out, T, K, N, s);
+    return g6::launch_decode16<4>(a, s_a, w, s_w, y, i32_out, T, K, N, s);
+  }
   if (T <= 32) {
     const unsigned nb = static_cast<unsigned>((N + 31) / 32);
     if (i32_out)

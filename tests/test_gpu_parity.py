@@ -390,9 +390,14 @@ def test_tile_codes_rejects_minus8(rw):
                                    (256, 128, 256), (200, 640, 520),
                                    (4096, 4096, 4096), (4100, 1024, 4104),
                                    # decode products (split-K workgroups): a full token
-                                   # tile, ragged N, K with fewer k-tiles than waves
+                                   # tile, ragged N, K with fewer k-tiles than waves, an
+                                   # odd k-tile count; 16-row workgroups of 16, 8 and 4
+                                   # waves (N up to 4096, 8192, 16384), 32-row ones past
+                                   # 16 tokens or N = 16384
                                    (32, 4096, 4096), (5, 192, 100), (31, 1088, 4000),
-                                   (8, 16384, 4096), (2, 64, 16383), (8, 1024, 32768)])
+                                   (8, 16384, 4096), (2, 64, 16383), (8, 1024, 32768),
+                                   (8, 1024, 8192), (16, 1088, 12288), (17, 256, 4096),
+                                   (1, 64, 16400)])
 def test_w4a4_gemm_tiles(rw, T, K, N):
     say(f"w4a4_gemm_tiles T={T} K={K} N={N}")
     a, qa = _codes7(T + K, T, K)
