@@ -178,6 +178,81 @@ def structured_rows(rw, torch, dev, timed, with_oracle):
     return out
 
 
+def config_rows(rw, torch, dev, timed):
+    """The other configurations of the path, each timed whole: the 70B-shaped
+    linear (T = 8192, D = 8192, r = 64, 8192 -> 28672, align|fwht, basis
+    prepared), and the decode (T = 8) and prefill (T = 4096) layers of
+    D = 4096 (QKV 4096 -> 12288, O 4096 -> 4096, the two alignments with their
+    residual adds on bases prepared once, gate+up 4096 -> 32768, down
+    16384 -> 4096 behind the SwiGLU gate and the FWHT). Operands are drawn on the device (their values do not
+    change the time); the layers' weights are rotated over two sets (402 MB of
+    FP6 tiles), so that they do not stay in the 256 MB last-level cache."""
+    import workloads as W
+    gd = torch.Generator(device=dev).manual_seed(11)
+    out = {}
+
+    def weight(N, K, rotate):
+        Wf = torch.randn((N, K), generator=gd, device=dev).mul_(0.02)
+        tl, s, _, _ = rw.prep_weight(Wf, rotate)
+        del Wf
+        return tl, s
+
+    def basis_pair(key, D, r):
+        Q, M = W.gen_basis(key, D, r)
+        return torch.from_numpy(Q).to(dev), torch.from_numpy(M).to(dev)
+
+    # 70B-shaped linear
+    T, D, r, N = 8192, 8192, 64, 28672
+    Q, M = basis_pair(5, D, r)
+    basis = rw.respin_prepare_basis(Q, M)
+    x = torch.randn((T, D), generator=gd, device=dev).to(torch.bfloat16)
+    tl, sw = weight(N, D, True)
+    flags = rw.RW4_ALIGN | rw.RW4_FWHT
+    ws = torch.empty((rw.rotated_linear_prepared_workspace_size(T, D, r, flags),),
+                     dtype=torch.uint8, device=dev)
+    y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+    ms = timed(lambda: rw.rotated_linear_prepared(x, tl, sw, flags, basis, r, out=y, workspace=ws),
+               n=5)
+    a_t, s_a = rw.workspace_views(ws, T, D)
+    gms = timed(lambda: rw.w4a4_gemm_tiles(a_t, s_a, tl, sw, T, D, N, out=y), n=5)
+    ops = 2.0 * T * D * N
+    out["linear_70b_T8192"] = {"T": T, "D": D, "r": r, "N": N, "us": ms * 1e3,
+                               "tokens_per_s": T / (ms * 1e-3), "gemm_us": gms * 1e3,
+                               "gemm_frac_fp6": ops / (gms * 1e-3) / 1e12 / PEAK_FP6_TFLOPS,
+                               "gemm_frac_int8": ops / (gms * 1e-3) / 1e12 / PEAK_I8_TOPS,
+                               "prologue_us": (ms - gms) * 1e3}
+    del x, tl, sw, ws, y, basis, a_t, s_a
+
+    # decoder layers
+    D = 4096
+    shapes = {"qkv": (3 * D, D, False), "o": (D, D, False), "gate_up": (8 * D, D, False),
+              "down": (D, 4 * D, True)}
+    sets = [{k: weight(N, K, rot) for k, (N, K, rot) in shapes.items()} for _ in range(2)]
+    wbytes = sum(N * K // 2 for N, K, _ in shapes.values())          # INT4 codes
+    lops = sum(2.0 * N * K for N, K, _ in shapes.values())            # per token
+    aligns = tuple((rw.respin_prepare_basis(*basis_pair(k, D, 32)), 32) for k in (21, 22))
+    for name, T in (("layer_decode_T8", 8), ("layer_prefill_T4096", 4096)):
+        x0 = torch.randn((T, D), generator=gd, device=dev).to(torch.bfloat16)
+        cnt = [0]
+
+        def call():
+            i = cnt[0] % len(sets)
+            cnt[0] += 1
+            rw.layer(x0, aligns, sets[i], D)
+        ms = timed(call, n=4 if T > 8 else 20)
+        rec = {"T": T, "D": D, "us": ms * 1e3, "tokens_per_s": T / (ms * 1e-3),
+               "gemm_ops": lops * T, "TOPS": lops * T / (ms * 1e-3) / 1e12}
+        if T <= 32:
+            rec["weight_bytes_int4"] = wbytes
+            rec["GB/s_int4_weights"] = wbytes / (ms * 1e-3) / 1e9
+            rec["frac_hbm"] = rec["GB/s_int4_weights"] / PEAK_HBM_GBS
+        else:
+            rec["frac_int8"] = rec["TOPS"] / PEAK_I8_TOPS
+        out[name] = rec
+    del sets
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -319,6 +394,7 @@ def main():
     quant_ms = timed(lambda: rw.quant_act_int4(tmp, codes_t, sa_t))
 
     rows = structured_rows(rw, torch, dev, timed, not args.no_cpu_baseline)
+    configs = config_rows(rw, torch, dev, timed)
 
     if args.copy_calibration:
         src = torch.empty((256 << 20,), dtype=torch.uint8, device=dev)
@@ -370,6 +446,7 @@ def main():
                       "step_with_basis_prep": unprepared_ms * 1e3},
         "stages_vs_hbm": bw,
         "structured_transforms": rows,
+        "configs": configs,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)

@@ -314,6 +314,19 @@ row_kernel(const void* __restrict__ x, int64_t ldx, int64_t T, float* __restrict
 // wave reduction.
 constexpr int kWaveRows = 4;                        // rows (waves) per workgroup
 
+// One wave per row (rowwave_kernel) or a workgroup per row (row_kernel) for
+// rows of 2048..8192 values. Measured on MI355X (graph-replayed calls): the
+// workgroup kernel is as fast or faster for FP6-tile outputs at every T
+// (D = 8192, T = 4096 unit prologue: 49 against 89 us), for packed codes at
+// D = 8192, and below 1024 rows for everything (T = 8: 3.4 against 7.8 us);
+// one wave per row keeps the fp32 transform of many rows (T = 2048, D = 4096:
+// 13.5 against 18.1 us) and packed codes at D <= 4096 (6.0 against 7.4 us).
+template <int N, bool QOUT, bool TILED>
+inline bool row_per_wave(int64_t T) {
+  if (TILED || T < 1024) return false;
+  return !QOUT || N <= 12;
+}
+
 template <int IN, int G>
 __device__ __forceinline__ void load_group(float (&q)[G], const void* x, int64_t off, int D) {
   static_assert(G == 4 || G == 16, "groups of 4 or 16 values");
@@ -440,10 +453,13 @@ hipError_t launch_row_n(const void* x, int64_t ldx, int64_t T, float* yf, uint8_
   constexpr int ROWS = P >= kRowThreads ? 1 : kRowThreads / P;
   const float norm = static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(1 << N)));
   if constexpr (N >= 11 && N <= 13) {
-    const int64_t wblocks = (T + kWaveRows - 1) / kWaveRows;
-    hipLaunchKernelGGL((rowwave_kernel<N, IN, FW, QOUT, TILED>), dim3(static_cast<unsigned>(wblocks)),
-                       dim3(64 * kWaveRows), 0, s, x, ldx, T, yf, codes, scales, dbg, norm, qmax);
-    return hipGetLastError();
+    if (row_per_wave<N, QOUT, TILED>(T)) {
+      const int64_t wblocks = (T + kWaveRows - 1) / kWaveRows;
+      hipLaunchKernelGGL((rowwave_kernel<N, IN, FW, QOUT, TILED>),
+                         dim3(static_cast<unsigned>(wblocks)), dim3(64 * kWaveRows), 0, s, x, ldx,
+                         T, yf, codes, scales, dbg, norm, qmax);
+      return hipGetLastError();
+    }
   }
   const int64_t blocks = (T + ROWS - 1) / ROWS;
   if constexpr (TILED && (1 << E) < 16) return hipErrorInvalidValue;

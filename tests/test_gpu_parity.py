@@ -739,8 +739,8 @@ def _layer_check(rw, cid, sample=None):
         weights[lin.name] = (tl, s)
         qws[lin.name] = O.unpack_int4(host(c))
         sws[lin.name] = host(s)
-    basis = [(dev(Q), dev(M)) for Q, M in inp["basis"]]
-    st = rw.layer(dev(inp["x"]), basis, weights, D)
+    aligns = [(rw.respin_prepare_basis(dev(Q), dev(M)), Q.shape[1]) for Q, M in inp["basis"]]
+    st = rw.layer(dev(inp["x"]), aligns, weights, D)
     _sync()
     g = {k: host(v) for k, v in st.items()}
     rows = np.arange(wl.T) if sample is None else sample
