@@ -117,8 +117,16 @@ rw4_status run_linear(const void* x, int64_t ldx, int64_t T, int64_t D, const vo
                                             rw4_align256(4u * static_cast<size_t>(T)));
     const uint16_t* xb = static_cast<const uint16_t*>(x);
     const bool fused = rw4::lfq_supported(D, r);
-    if (rw4::launch_yproj(xb, T, D, r, basis, with_p(D, r), Zpart, s) != hipSuccess)
+    float* tmp = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(Zpart) +
+                                          rw4::align_zpart_bytes(T, D, r));
+    if (!fused && rw4::align_small(T, D)) {
+      // a short batch past the fused prologue: the alignment spread over D
+      if (rw4::launch_align_small(xb, tmp, 1, nullptr, T, D, r, basis, with_p(D, r), Zpart, s) !=
+          hipSuccess)
+        return RW4_ERR_HIP;
+    } else if (rw4::launch_yproj(xb, T, D, r, basis, with_p(D, r), Zpart, s) != hipSuccess) {
       return RW4_ERR_HIP;
+    }
     if (fused) {
       // lift + transform + quantization on chip
       if (rw4::launch_lift_fwht_quant(xb, T, D, r, basis, Zpart, (flags & RW4_FWHT) != 0, codes,
@@ -126,9 +134,8 @@ rw4_status run_linear(const void* x, int64_t ldx, int64_t T, int64_t D, const vo
         return RW4_ERR_HIP;
       return hip_status(rw4::launch_gemm_tiles(codes, s_a, w, s_w, y, false, T, D, N, s));
     }
-    float* tmp = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(Zpart) +
-                                          rw4::align_zpart_bytes(T, D, r));
-    if (rw4::launch_lift(xb, tmp, 1, nullptr, T, D, r, basis, with_p(D, r), Zpart, s) != hipSuccess)
+    if (!rw4::align_small(T, D) &&
+        rw4::launch_lift(xb, tmp, 1, nullptr, T, D, r, basis, with_p(D, r), Zpart, s) != hipSuccess)
       return RW4_ERR_HIP;
     src = tmp;
     in = rw4::IN_F32;
@@ -361,6 +368,9 @@ rw4_status respin_align_prepared(const void* x, void* out, rw4_dtype out_dt, con
   hipStream_t s = strm(stream);
   const uint16_t* xb = static_cast<const uint16_t*>(x);
   float* Zpart = static_cast<float*>(workspace);
+  if (rw4::align_small(T, D))
+    return hip_status(rw4::launch_align_small(xb, out, out_dt == RW4_F32, addend, T, D, r, basis,
+                                              with_p(D, r), Zpart, s));
   if (rw4::launch_yproj(xb, T, D, r, basis, with_p(D, r), Zpart, s) != hipSuccess)
     return RW4_ERR_HIP;
   return hip_status(rw4::launch_lift(xb, out, out_dt == RW4_F32, addend, T, D, r, basis,

@@ -27,6 +27,8 @@
 // inside branches whose values are used after the join read stale registers
 // with this toolchain, and a short drain separates the last MFMA from the
 // first non-MFMA read of its result.
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -427,6 +429,156 @@ lift_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int S, int 
   }
 }
 
+// Short batches (T <= kSmallT tokens, decode): the two steps on the vector
+// ALUs, spread over D instead of over tokens, since a few tokens leave the
+// token-blocked kernels a handful of workgroups that each pull the whole basis
+// through one CU. Every global load of a thread is issued before its first
+// use (compile-time bounded, predicated loops), so a thread waits for memory
+// once per phase rather than once per iteration.
+//   proj: one workgroup per 256-column chunk c: Zs[c][t][i] = sum over the
+//         chunk of Q'[i][d] x[t][d], Q' = Q'h + Q'l (exact in fp32), fp32 FMA
+//         in column order; x and 32-row blocks of Q' are staged in LDS.
+//   lift: one workgroup per 64 columns: z = sum of the chunks in chunk order
+//         (deterministic), then out[t][d] = x[t][d] + sum_i Q[d][i] z[t][i]
+//         (+ addend), Q = Qh + Ql.
+constexpr int kSmallT = 16;
+constexpr int kSmallChunk = 256;
+constexpr int kSmallLift = 64;
+constexpr int kSmallMaxD = 16384;
+
+__global__ void __launch_bounds__(256)
+asmall_proj_kernel(const uint16_t* __restrict__ x, int T, int D, int RP, int RK,
+                   const uint16_t* __restrict__ QtH, const uint16_t* __restrict__ QtL,
+                   float* __restrict__ Zs) {
+  __shared__ __attribute__((aligned(16))) float xs[kSmallT][kSmallChunk + 4];
+  __shared__ __attribute__((aligned(16))) float qs[32][kSmallChunk + 4];
+  const int tid = threadIdx.x;
+  const int c = blockIdx.x;
+  const int d0 = c * kSmallChunk;
+  const int nd = min(kSmallChunk, D - d0);           // a multiple of 64
+  const bool col = tid < nd;
+  const int dc = d0 + (col ? tid : nd - 1);
+  // thread tid stages column d0 + tid of every token; the loads are
+  // unconditional (clamped token and column, masked values), so that they
+  // are all in flight before the first use
+  uint16_t xr[kSmallT];
+#pragma unroll
+  for (int t = 0; t < kSmallT; ++t) xr[t] = x[static_cast<int64_t>(min(t, T - 1)) * D + dc];
+  float xv[kSmallT];
+#pragma unroll
+  for (int t = 0; t < kSmallT; ++t) xv[t] = col && t < T ? bf16_to_f32(xr[t]) : 0.0f;
+#pragma unroll
+  for (int t = 0; t < kSmallT; ++t) xs[t][tid] = xv[t];
+  for (int i0 = 0; i0 < RK; i0 += 32) {
+    // rows i0 .. i0 + 31 of Q' for this chunk, one column per thread
+    uint16_t hr[32], lr[32];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const int64_t o = static_cast<int64_t>(min(i0 + k, RP - 1)) * D + dc;
+      hr[k] = QtH[o];
+      lr[k] = QtL[o];
+    }
+    float qv[32];
+#pragma unroll
+    for (int k = 0; k < 32; ++k)
+      qv[k] = col && i0 + k < RP ? bf16_to_f32(hr[k]) + bf16_to_f32(lr[k]) : 0.0f;
+    __syncthreads();                                 // previous block's readers are done
+#pragma unroll
+    for (int k = 0; k < 32; ++k) qs[k][tid] = qv[k];
+    __syncthreads();
+    for (int o = tid; o < T * 32; o += 256) {
+      const int t = o >> 5, k = o & 31;
+      float acc = 0.0f;
+#pragma unroll 4
+      for (int d = 0; d < kSmallChunk; d += 4) {
+        const float4 q4 = *reinterpret_cast<const float4*>(&qs[k][d]);
+        const float4 x4 = *reinterpret_cast<const float4*>(&xs[t][d]);
+        acc = fmaf(q4.x, x4.x, acc);
+        acc = fmaf(q4.y, x4.y, acc);
+        acc = fmaf(q4.z, x4.z, acc);
+        acc = fmaf(q4.w, x4.w, acc);
+      }
+      Zs[(static_cast<int64_t>(c) * T + t) * RK + i0 + k] = acc;
+    }
+  }
+}
+
+template <bool OF32, bool ADD>
+__global__ void __launch_bounds__(256)
+asmall_lift_kernel(const uint16_t* __restrict__ x, int T, int D, int RK, int C,
+                   const float* __restrict__ Zs, const uint16_t* __restrict__ QH,
+                   const uint16_t* __restrict__ QL, const void* __restrict__ addend,
+                   void* __restrict__ out) {
+  __shared__ float zs[kSmallT][kPrepRmax + 1];
+  const int tid = threadIdx.x;
+  // z: every partial of a thread's entries loaded at once, summed in chunk order
+  for (int o = tid; o < T * RK; o += 256) {
+    const int t = o / RK, i = o % RK;
+    float z = 0.0f;
+    for (int c0 = 0; c0 < C; c0 += 16) {
+      float zp[16];
+#pragma unroll
+      for (int c = 0; c < 16; ++c)
+        zp[c] = Zs[(static_cast<int64_t>(min(c0 + c, C - 1)) * T + t) * RK + i];
+#pragma unroll
+      for (int c = 0; c < 16; ++c) z += c0 + c < C ? zp[c] : 0.0f;
+    }
+    zs[t][i] = z;
+  }
+  __syncthreads();
+  const int d = blockIdx.x * kSmallLift + (tid & (kSmallLift - 1));
+  if (d >= D) return;
+  // the thread's row of Q in blocks of 32 values (RK is a multiple of 32)
+  const uint4* qh = reinterpret_cast<const uint4*>(QH + static_cast<int64_t>(d) * RK);
+  const uint4* ql = reinterpret_cast<const uint4*>(QL + static_cast<int64_t>(d) * RK);
+  constexpr int TPT = (kSmallT + 256 / kSmallLift - 1) / (256 / kSmallLift);  // tokens per thread
+  const int tt0 = tid / kSmallLift;
+  float corr[TPT];
+#pragma unroll
+  for (int u = 0; u < TPT; ++u) corr[u] = 0.0f;
+  for (int i0 = 0; i0 < RK; i0 += 32) {
+    uint4 hv[4], lv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      hv[j] = qh[i0 / 8 + j];
+      lv[j] = ql[i0 / 8 + j];
+    }
+    float q[32];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t hw[4] = {hv[j].x, hv[j].y, hv[j].z, hv[j].w};
+      const uint32_t lw[4] = {lv[j].x, lv[j].y, lv[j].z, lv[j].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        q[8 * j + 2 * e] = bf16lo(hw[e]) + bf16lo(lw[e]);
+        q[8 * j + 2 * e + 1] = bf16hi(hw[e]) + bf16hi(lw[e]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const int t = min(tt0 + u * (256 / kSmallLift), kSmallT - 1);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) corr[u] = fmaf(q[i], zs[t][i0 + i], corr[u]);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < TPT; ++u) {
+    const int t = tt0 + u * (256 / kSmallLift);
+    if (t >= T) break;
+    const int64_t off = static_cast<int64_t>(t) * D + d;
+    const float xv = bf16_to_f32(x[off]);
+    float av = 0.0f;
+    if constexpr (ADD) {
+      if constexpr (OF32) av = static_cast<const float*>(addend)[off];
+      else av = bf16_to_f32(static_cast<const uint16_t*>(addend)[off]);
+    }
+    float acc = xv + corr[u];
+    if constexpr (ADD) acc += av;
+    if constexpr (OF32) static_cast<float*>(out)[off] = acc;
+    else static_cast<uint16_t*>(out)[off] = f32_to_bf16(acc);
+  }
+}
+
 inline int rp_of(int64_t r) { return static_cast<int>((r + 15) / 16 * 16); }
 inline int rk_of(int64_t r) { return static_cast<int>((r + 31) / 32 * 32); }
 inline size_t a256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
@@ -462,7 +614,10 @@ bool align_mfma_supported(int64_t D, int64_t r) { return r > 0 && r <= 128 && D 
 int align_parts_count(int64_t D) { return static_cast<int>((D + kPart - 1) / kPart); }
 
 size_t align_zpart_bytes(int64_t T, int64_t D, int64_t r) {
-  return a256(static_cast<size_t>(align_parts_count(D)) * static_cast<size_t>(T) *
+  const int64_t parts = align_small(T, D) ? std::max<int64_t>(align_parts_count(D),
+                                                         (D + kSmallChunk - 1) / kSmallChunk)
+                                     : align_parts_count(D);
+  return a256(static_cast<size_t>(parts) * static_cast<size_t>(T) *
               static_cast<size_t>(rk_of(r)) * 4);
 }
 
@@ -519,6 +674,31 @@ hipError_t launch_yproj(const uint16_t* x, int64_t T, int64_t D, int64_t r, cons
   }
 }
 
+bool align_small(int64_t T, int64_t D) { return T >= 1 && T <= kSmallT && D <= kSmallMaxD; }
+
+hipError_t launch_align_small(const uint16_t* x, void* out, int out_f32, const void* addend,
+                              int64_t T, int64_t D, int64_t r, const void* basis, bool with_p,
+                              float* Zs, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (!align_small(T, D) || D % 64 != 0 || D > kSmallMaxD || r < 1 || r > kPrepRmax)
+    return hipErrorInvalidValue;
+  const AlignBasis a = align_basis(basis, D, r, with_p);
+  const int Ti = static_cast<int>(T), Di = static_cast<int>(D);
+  const int C = static_cast<int>((D + kSmallChunk - 1) / kSmallChunk);
+  hipLaunchKernelGGL(asmall_proj_kernel, dim3(static_cast<unsigned>(C)), dim3(256), 0, s, x, Ti,
+                     Di, a.RP, a.RK, a.QtH, a.QtL, Zs);
+  const dim3 lg(static_cast<unsigned>((D + kSmallLift - 1) / kSmallLift));
+#define RW4_AS(OF, AD)                                                                            \
+  if ((out_f32 != 0) == OF && (addend != nullptr) == AD) {                                        \
+    hipLaunchKernelGGL((asmall_lift_kernel<OF, AD>), lg, dim3(256), 0, s, x, Ti, Di, a.RK, C, Zs, \
+                       a.QH, a.QL, addend, out);                                                  \
+    return hipGetLastError();                                                                     \
+  }
+  RW4_AS(true, false) RW4_AS(true, true) RW4_AS(false, false) RW4_AS(false, true)
+#undef RW4_AS
+  return hipErrorInvalidValue;
+}
+
 size_t align_mfma_workspace(int64_t T, int64_t D, int64_t r) {
   return align_basis_bytes(D, r, false) + align_zpart_bytes(T, D, r);
 }
@@ -530,6 +710,8 @@ hipError_t launch_align_mfma(const uint16_t* x, void* out, int out_f32, const fl
   hipError_t e = launch_basis_prep(Q, M, D, r, false, ws, s);
   if (e != hipSuccess) return e;
   float* Zpart = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align_basis_bytes(D, r, false));
+  if (align_small(T, D))
+    return launch_align_small(x, out, out_f32, addend, T, D, r, ws, false, Zpart, s);
   e = launch_yproj(x, T, D, r, ws, false, Zpart, s);
   if (e != hipSuccess) return e;
   return launch_lift(x, out, out_f32, addend, T, D, r, ws, false, Zpart, s);

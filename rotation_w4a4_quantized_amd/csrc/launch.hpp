@@ -69,6 +69,13 @@ int align_parts_count(int64_t D);
 size_t align_zpart_bytes(int64_t T, int64_t D, int64_t r);
 hipError_t launch_yproj(const uint16_t* x, int64_t T, int64_t D, int64_t r, const void* basis,
                         bool with_p, float* Zpart, hipStream_t s);
+// the whole alignment for short batches (align_small(T, D): 1 <= T <= 16
+// tokens, D <= 16384), spread over D: projection into Zs (align_zpart_bytes(T, D, r)
+// bytes) and lift, out = x + Q z (+ addend)
+bool align_small(int64_t T, int64_t D);
+hipError_t launch_align_small(const uint16_t* x, void* out, int out_f32, const void* addend,
+                              int64_t T, int64_t D, int64_t r, const void* basis, bool with_p,
+                              float* Zs, hipStream_t s);
 // unfused lift out = x + Q z (+ addend), fp32 or bf16 out
 hipError_t launch_lift(const uint16_t* x, void* out, int out_f32, const void* addend, int64_t T,
                        int64_t D, int64_t r, const void* basis, bool with_p, const float* Zpart,
