@@ -338,10 +338,20 @@ lift_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int S, int 
     const int tt = (4 * c) / RK;
     const int i = (4 * c) % RK;
     const int64_t trow = min(t0 + tt, T - 1);
+    // the parts in blocks of 8, each block's loads issued together
+    // (unconditional, clamped, masked) and added in part order
     float4 z = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    for (int p = 0; p < S; ++p) {
-      const float4 zp = *reinterpret_cast<const float4*>(Zpart + (static_cast<int64_t>(p) * T + trow) * RK + i);
-      z.x += zp.x; z.y += zp.y; z.z += zp.z; z.w += zp.w;
+    for (int p0 = 0; p0 < S; p0 += 8) {
+      float4 zp[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        zp[q] = *reinterpret_cast<const float4*>(
+            Zpart + (static_cast<int64_t>(min(p0 + q, S - 1)) * T + trow) * RK + i);
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (p0 + q < S) {
+          z.x += zp[q].x; z.y += zp[q].y; z.z += zp[q].z; z.w += zp[q].w;
+        }
     }
     const float zz[4] = {z.x, z.y, z.z, z.w};
 #pragma unroll
@@ -357,7 +367,9 @@ lift_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int S, int 
   // results are staged in LDS, then all threads write them as contiguous row
   // segments (the MFMA layout would scatter 16-byte pieces over 16 rows).
   const int ncols = dend - dbeg;
-#pragma unroll 1
+  // unrolled, so that xv[tb] stays in registers (a runtime index would move
+  // the array to scratch memory)
+#pragma unroll
   for (int tb = 0; tb < TBW; ++tb) {
     if (live) {
       v4f acc[4];
