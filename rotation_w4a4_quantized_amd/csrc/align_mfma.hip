@@ -733,8 +733,6 @@ hipError_t launch_lift(const uint16_t* x, void* out, int out_f32, const void* ad
                        int64_t D, int64_t r, const void* basis, bool with_p, const float* Zpart,
                        hipStream_t s) {
   if (T == 0) return hipSuccess;
-  if (lfq_supported(D, r))
-    return launch_align_rows(x, out, out_f32, addend, T, D, r, basis, with_p, Zpart, s);
   const AlignBasis a = align_basis(basis, D, r, with_p);
   const int Di = static_cast<int>(D);
   const int ri = static_cast<int>(r);

@@ -85,11 +85,6 @@ hipError_t launch_lift(const uint16_t* x, void* out, int out_f32, const void* ad
 // launch_yproj: per token, u = [H x / sqrt(D)] + P z (P = H Q / sqrt(D) with
 // the transform, Q without), codes of u. Needs a basis prepared with P.
 bool lfq_supported(int64_t D, int64_t r);
-// The same lift on its own (alignment of bf16 rows, D a power of two in
-// [256, 4096], r <= 64): out = x + Q z (+ addend), fp32 or bf16.
-hipError_t launch_align_rows(const uint16_t* x, void* out, int out_f32, const void* addend,
-                             int64_t T, int64_t D, int64_t r, const void* basis, bool with_p,
-                             const float* Zpart, hipStream_t s);
 hipError_t launch_lift_fwht_quant(const uint16_t* x, int64_t T, int64_t D, int64_t r,
                                   const void* basis, const float* Zpart, bool do_fwht,
                                   uint8_t* tiles, float* s_a, float* dbg, hipStream_t s,

@@ -316,84 +316,6 @@ lfq_kernel(const uint16_t* __restrict__ x, int64_t T, const float* __restrict__ 
   }
 }
 
-// ---------------------------------------------------------------- alignment alone
-// respin_align for bf16 x and D a power of two in [256, 4096]: the same lift
-// waves (A = Q), and row waves that hold x in the coalesced layout (lane L:
-// values 256 c + 4 L + e), add Q z (+ addend) and store fp32 or bf16 rows
-// with 1 KiB (fp32) or 512 B (bf16) per instruction.
-template <int N, int RK, bool OF32, bool ADD>
-__global__ void __launch_bounds__(kThreads)
-align_rows_kernel(const uint16_t* __restrict__ x, int64_t T, const float* __restrict__ Zpart,
-                  int S, const uint16_t* __restrict__ QH, const uint16_t* __restrict__ QL,
-                  const void* __restrict__ addend, void* __restrict__ out) {
-  constexpr int D = 1 << N;
-  constexpr int NSL = D / 256;                  // 4-value slots per lane
-  constexpr int PITCH = NSL * 64 + 4;           // float4s per token (4 pad: banks)
-  static_assert(N >= 8 && N <= 12, "D in [256, 4096]");
-  __shared__ float4 lift[kTok * PITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t zh[16][RK + 8];
-  __shared__ __attribute__((aligned(16))) uint16_t zl[16][RK + 8];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kTok;
-  if (wave >= 8) {
-    lift_waves<D, RK>(wave - 8, lane, t0, T, Zpart, S, QH, QL, zh, zl,
-                      [&](int tok, int d, float4 v) {
-                        lift[tok * PITCH + (d >> 8) * 64 + ((d & 255) >> 2)] = v;
-                      });
-    return;
-  }
-  const int tok = wave;
-  const int64_t t = t0 + tok;
-  const int64_t trow = t < T ? t : T - 1;      // rows past T repeat the last one; never stored
-  uint2 xv[NSL];
-#pragma unroll
-  for (int c = 0; c < NSL; ++c)
-    xv[c] = *reinterpret_cast<const uint2*>(x + trow * D + 256 * c + 4 * lane);
-  lds_barrier();  // 1
-  lds_barrier();  // 2: lift in LDS
-  if (t >= T) return;
-#pragma unroll
-  for (int c = 0; c < NSL; ++c) {
-    const int64_t off = t * D + 256 * c + 4 * lane;
-    const float4 l = lift[tok * PITCH + c * 64 + lane];
-    float o[4] = {bf16lo(xv[c].x) + l.x, bf16hi(xv[c].x) + l.y, bf16lo(xv[c].y) + l.z,
-                  bf16hi(xv[c].y) + l.w};
-    if constexpr (OF32) {
-      if constexpr (ADD) {
-        const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(addend) + off);
-        o[0] += a.x; o[1] += a.y; o[2] += a.z; o[3] += a.w;
-      }
-      *reinterpret_cast<float4*>(static_cast<float*>(out) + off) = make_float4(o[0], o[1], o[2], o[3]);
-    } else {
-      if constexpr (ADD) {
-        const uint2 a = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(addend) + off);
-        o[0] += bf16lo(a.x); o[1] += bf16hi(a.x); o[2] += bf16lo(a.y); o[3] += bf16hi(a.y);
-      }
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + off) =
-          make_uint2(f32_to_bf16(o[0]) | (static_cast<uint32_t>(f32_to_bf16(o[1])) << 16),
-                     f32_to_bf16(o[2]) | (static_cast<uint32_t>(f32_to_bf16(o[3])) << 16));
-    }
-  }
-}
-
-template <int N, int RK>
-hipError_t launch_align_rows_n(const uint16_t* x, int64_t T, const float* Zpart, int S,
-                               const uint16_t* QH, const uint16_t* QL, const void* addend,
-                               void* out, bool of32, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>((T + kTok - 1) / kTok));
-#define RW4_AR(OF, AD)                                                                           \
-  if (of32 == OF && (addend != nullptr) == AD) {                                                 \
-    hipLaunchKernelGGL((align_rows_kernel<N, RK, OF, AD>), grid, dim3(kThreads), 0, s, x, T,     \
-                       Zpart, S, QH, QL, addend, out);                                           \
-    return hipGetLastError();                                                                    \
-  }
-  RW4_AR(true, false) RW4_AR(true, true) RW4_AR(false, false) RW4_AR(false, true)
-#undef RW4_AR
-  return hipErrorInvalidValue;
-}
-
 template <int N, int RK>
 hipError_t launch_n(const uint16_t* x, int64_t T, const float* Zpart, int S, const uint16_t* PH,
                     const uint16_t* PL, bool fw, uint8_t* tiles, float* s_a, float* dbg,
@@ -451,25 +373,6 @@ hipError_t launch_lift_fwht_quant(const uint16_t* x, int64_t T, int64_t D, int64
   while ((int64_t(1) << n) < D) ++n;
   if (a.RK == 32) return launch_rk<32>(n, x, T, Zpart, S, PH, PL, do_fwht, tiles, s_a, dbg, qmax, s);
   if (a.RK == 64) return launch_rk<64>(n, x, T, Zpart, S, PH, PL, do_fwht, tiles, s_a, dbg, qmax, s);
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_align_rows(const uint16_t* x, void* out, int out_f32, const void* addend,
-                             int64_t T, int64_t D, int64_t r, const void* basis, bool with_p,
-                             const float* Zpart, hipStream_t s) {
-  if (T == 0) return hipSuccess;
-  if (!lfq_supported(D, r)) return hipErrorInvalidValue;
-  const AlignBasis a = align_basis(basis, D, r, with_p);
-  const int S = align_parts_count(D);
-  if (S != (D + 511) / 512) return hipErrorInvalidValue;  // the lift waves' part count
-  int n = 0;
-  while ((int64_t(1) << n) < D) ++n;
-  const bool of32 = out_f32 != 0;
-#define RW4_ARN(NN, K) \
-  if (n == NN && a.RK == K) return launch_align_rows_n<NN, K>(x, T, Zpart, S, a.QH, a.QL, addend, out, of32, s);
-  RW4_ARN(8, 32) RW4_ARN(9, 32) RW4_ARN(10, 32) RW4_ARN(11, 32) RW4_ARN(12, 32)
-  RW4_ARN(8, 64) RW4_ARN(9, 64) RW4_ARN(10, 64) RW4_ARN(11, 64) RW4_ARN(12, 64)
-#undef RW4_ARN
   return hipErrorInvalidValue;
 }
 
