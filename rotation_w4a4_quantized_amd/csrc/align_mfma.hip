@@ -282,7 +282,7 @@ yproj_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int r,
 constexpr int LNW = 8;
 
 template <int RP, int RK, bool OF32, bool ADD>
-__global__ void __launch_bounds__(LNW * 64)
+__global__ void __launch_bounds__(LNW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
 lift_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int S, int r,
             const float* __restrict__ Zpart, const uint16_t* __restrict__ QH,
             const uint16_t* __restrict__ QL, const void* __restrict__ addend,
@@ -302,7 +302,7 @@ lift_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int S, int 
   const int nds = (dend - dbeg) / 64;
   const int g = lane >> 4;
   const int tl = lane & 15;
-  constexpr int KQ = RK / 32 < 2 ? RK / 32 : 2;       // Q k-chunks loaded up front
+  constexpr int KQ = 1;                               // Q k-chunks loaded up front
   const bool live = wave < nds;                       // this wave's double step exists
   const int d0 = dbeg + 64 * (live ? wave : nds - 1);
   static_assert(TPW * RK % (4 * NT) == 0 || TPW * RK < 4 * NT, "z chunks");
