@@ -17,8 +17,9 @@
 // The polar factor is T_sub (T_sub^T T_sub)^-1/2 from the same eigensolver:
 // a cyclic Jacobi method in one workgroup, the pairs of each step chosen by
 // the round-robin ordering so that all n/2 rotations of a step run at once.
-// Products with T read it from HBM as fp32 and accumulate in fp64; only Q
-// and R_sub are rounded to fp32 at the end.
+// Products with T read it from HBM as fp32 and accumulate in fp64, as sums
+// over K parts (register-blocked workgroups of 128 rows, the parts added in
+// part order); only Q and R_sub are rounded to fp32 at the end.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -27,8 +28,6 @@ namespace {
 
 constexpr int kCPad = 16;      // oversampling of the range finder
 constexpr int kCMaxN = 80;     // largest eigenproblem (r <= 64)
-constexpr int kCRows = 16;     // output rows per workgroup of the T products
-constexpr int kCChunk = 64;    // k-chunk of the T products
 
 // Rademacher sign of entry (d, k) of Omega: bit 0 of a 32-bit mix of the index
 __device__ __forceinline__ double omega_sign(uint32_t d, uint32_t k) {
@@ -44,88 +43,119 @@ __global__ void omega_kernel(double* __restrict__ Y, int D, int p) {
 }
 
 // Y[i][c] = sum_j op(T)[i][j] X[j][c] - sub X[i][c] for c < nc; X, Y fp64 [D][nc];
-// op(T) = T (TR false) or T^T (TR true). One workgroup per 16 output rows.
-template <bool TR>
+// op(T) = T or T^T, T fp32 [D][D] (exact in fp64).
+// The same product as partial sums over K parts, register-blocked: a
+// workgroup of 256 threads owns 128 output rows x 16 NCPT columns of part q
+// (k in [q D / KS, (q + 1) D / KS)); thread (g, c) accumulates rows 8 g .. +7
+// and columns c + 16 j (j < NCPT) in fp64, so each k costs 8 + NCPT LDS reads
+// for 8 NCPT FMAs. Chunks of 32 k of op(T) (fp32) and X (fp64) are staged in
+// LDS (conflict-free: [k][row] with a 129-word pitch), the next chunk fetched
+// into registers meanwhile. Part sums go to P[q][i][c]; tsum_kernel adds the
+// parts in part order and subtracts sub X.
+constexpr int kTRows = 128;
+constexpr int kTChunk = 32;
+
+template <bool TR, int NCPT>
 __global__ void __launch_bounds__(256)
-tmul_kernel(const float* __restrict__ T, int D, const double* __restrict__ X, int nc, double sub,
-            double* __restrict__ Y) {
-  __shared__ float Tt[kCRows][kCChunk + 1];
-  __shared__ double Xt[kCChunk][kCMaxN];
+tpart_kernel(const float* __restrict__ T, int D, const double* __restrict__ X, int nc, int KL,
+             double* __restrict__ P) {
+  constexpr int NCB = 16 * NCPT;                       // columns of the block
+  constexpr int TPT = kTRows * kTChunk / 256;          // T values per thread and chunk
+  constexpr int XPT = (kTChunk * NCB + 255) / 256;     // X values per thread and chunk
+  __shared__ float Tt[kTChunk][kTRows + 1];
+  __shared__ double Xt[kTChunk][NCB];
   const int tid = threadIdx.x;
-  const int lr = tid >> 4;                 // output row in the block
-  const int cg = tid & 15;                 // column group: c = cg + 16 k
-  const int i0 = blockIdx.x * kCRows;
-  double acc[kCMaxN / 16];
+  const int g = tid >> 4, c = tid & 15;
+  const int i0 = blockIdx.x * kTRows;
+  const int q = blockIdx.y;
+  const int kbeg = q * KL;
+  double acc[8][NCPT];
 #pragma unroll
-  for (int k = 0; k < kCMaxN / 16; ++k) acc[k] = 0.0;
-  // the next chunk is fetched into registers while the current one is used
-  constexpr int TPT = kCRows * kCChunk / 256;      // T values per thread
-  constexpr int XPT = kCChunk * kCMaxN / 256;      // X values per thread (at most)
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int j = 0; j < NCPT; ++j) acc[a][j] = 0.0;
   float tr[TPT];
   double xr[XPT];
-  // the chunk-relative row and column of this thread's X values (independent
-  // of the chunk: no division inside the loop)
-  int xrow[XPT], xcol[XPT];
-#pragma unroll
-  for (int m = 0; m < XPT; ++m) {
-    const int e = tid + 256 * m;
-    xrow[m] = e / nc;
-    xcol[m] = e % nc;
-  }
-  auto fetch = [&](int j0) {
+  // loads are unconditional (clamped rows, masked columns), all in flight at once
+  auto fetch = [&](int k0) {
 #pragma unroll
     for (int m = 0; m < TPT; ++m) {
       const int e = tid + 256 * m;
-      if constexpr (TR) tr[m] = T[static_cast<int64_t>(j0 + e / kCRows) * D + i0 + e % kCRows];
-      else tr[m] = T[static_cast<int64_t>(i0 + e / kCChunk) * D + j0 + e % kCChunk];
+      if constexpr (TR) {
+        const int kk = e / kTRows, row = min(i0 + e % kTRows, D - 1);
+        tr[m] = T[static_cast<int64_t>(k0 + kk) * D + row];
+      } else {
+        const int row = min(i0 + e / kTChunk, D - 1), kk = e % kTChunk;
+        tr[m] = T[static_cast<int64_t>(row) * D + k0 + kk];
+      }
     }
 #pragma unroll
     for (int m = 0; m < XPT; ++m) {
-      const int e = tid + 256 * m;
-      if (e < kCChunk * nc) xr[m] = X[static_cast<int64_t>(j0 + xrow[m]) * nc + xcol[m]];
+      const int e = min(tid + 256 * m, kTChunk * NCB - 1);
+      const int kk = e / NCB, col = e % NCB;
+      xr[m] = X[static_cast<int64_t>(k0 + kk) * nc + min(col, nc - 1)];
     }
   };
   auto stash = [&]() {
 #pragma unroll
     for (int m = 0; m < TPT; ++m) {
       const int e = tid + 256 * m;
-      if constexpr (TR) Tt[e % kCRows][e / kCRows] = tr[m];
-      else Tt[e / kCChunk][e % kCChunk] = tr[m];
+      if constexpr (TR) Tt[e / kTRows][e % kTRows] = tr[m];
+      else Tt[e % kTChunk][e / kTChunk] = tr[m];
     }
 #pragma unroll
     for (int m = 0; m < XPT; ++m) {
       const int e = tid + 256 * m;
-      if (e < kCChunk * nc) Xt[xrow[m]][xcol[m]] = xr[m];
+      if (e < kTChunk * NCB) Xt[e / NCB][e % NCB] = e % NCB < nc ? xr[m] : 0.0;
     }
   };
-  // every workgroup starts at its own chunk: at any moment the workgroups
-  // read different parts of X (in lockstep they would all hit the same L2
-  // lines); the accumulation order is still fixed per row block
-  const int nch = D / kCChunk;
-  const int c0 = static_cast<int>(blockIdx.x % nch);
-  fetch(c0 * kCChunk);
+  const int nch = KL / kTChunk;
+  fetch(kbeg);
   for (int ci = 0; ci < nch; ++ci) {
     stash();
     __syncthreads();
-    if (ci + 1 < nch) fetch(((c0 + ci + 1) % nch) * kCChunk);
-    // branch-free: columns past nc accumulate whatever LDS holds there and
-    // are never stored
-#pragma unroll 8
-    for (int jj = 0; jj < kCChunk; ++jj) {
-      const double t = static_cast<double>(Tt[lr][jj]);
+    if (ci + 1 < nch) fetch(kbeg + (ci + 1) * kTChunk);
+#pragma unroll 4
+    for (int kk = 0; kk < kTChunk; ++kk) {
+      double x[NCPT];
 #pragma unroll
-      for (int k = 0; k < kCMaxN / 16; ++k) acc[k] = fma(t, Xt[jj][cg + 16 * k], acc[k]);
+      for (int j = 0; j < NCPT; ++j) x[j] = Xt[kk][c + 16 * j];
+#pragma unroll
+      for (int a = 0; a < 8; ++a) {
+        const double t = static_cast<double>(Tt[kk][8 * g + a]);
+#pragma unroll
+        for (int j = 0; j < NCPT; ++j) acc[a][j] = fma(t, x[j], acc[a][j]);
+      }
     }
     __syncthreads();
   }
-  const int i = i0 + lr;
 #pragma unroll
-  for (int k = 0; k < kCMaxN / 16; ++k) {
-    const int c = cg + 16 * k;
-    if (c < nc) {
-      const int64_t o = static_cast<int64_t>(i) * nc + c;
-      Y[o] = acc[k] - sub * X[o];
+  for (int a = 0; a < 8; ++a) {
+    const int i = i0 + 8 * g + a;
+    if (i >= D) continue;
+#pragma unroll
+    for (int j = 0; j < NCPT; ++j) {
+      const int col = c + 16 * j;
+      if (col < nc) P[(static_cast<int64_t>(q) * D + i) * nc + col] = acc[a][j];
     }
+  }
+}
+
+// Y[i][c] = sum over the KS parts (in part order) - sub X[i][c]
+__global__ void __launch_bounds__(256)
+tsum_kernel(const double* __restrict__ P, int KS, int64_t n, const double* __restrict__ X,
+            double sub, double* __restrict__ Y) {
+  for (int64_t e = blockIdx.x * 256 + threadIdx.x; e < n; e += static_cast<int64_t>(gridDim.x) * 256) {
+    double acc = 0.0;
+    for (int q0 = 0; q0 < KS; q0 += 8) {
+      double v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = P[static_cast<int64_t>(min(q0 + u, KS - 1)) * n + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (q0 + u < KS) acc += v[u];
+    }
+    Y[e] = acc - sub * X[e];
   }
 }
 
@@ -334,9 +364,19 @@ int construct_oversampled(int64_t D, int64_t r) {
   return static_cast<int>(p < D ? p : D);
 }
 
+// K parts of the products: about 256 workgroups of 128 rows, parts of at
+// least one 32-value chunk
+int construct_kparts(int64_t D) {
+  int64_t ks = (256 * kTRows) / D;
+  if (ks < 1) ks = 1;
+  while (ks > 1 && (D % (ks * kTChunk)) != 0) --ks;
+  return static_cast<int>(ks);
+}
+
 size_t construct_workspace(int64_t D, int64_t r) {
   const int64_t p = construct_oversampled(D, r);
-  return static_cast<size_t>(2 * a256c(D * p * 8) + 2 * a256c(kCMaxN * kCMaxN * 8));
+  return static_cast<size_t>(2 * a256c(D * p * 8) + 2 * a256c(kCMaxN * kCMaxN * 8) +
+                             a256c(static_cast<int64_t>(construct_kparts(D)) * D * p * 8));
 }
 
 bool construct_supported(int64_t D, int64_t r) {
@@ -354,12 +394,25 @@ hipError_t launch_construct(const float* T, int64_t D64, int64_t r64, int iters,
   double* G = reinterpret_cast<double*>(w + 2 * a256c(int64_t(D) * p * 8));
   double* Mm = reinterpret_cast<double*>(w + 2 * a256c(int64_t(D) * p * 8) + a256c(kCMaxN * kCMaxN * 8));
   const dim3 b256(256);
-  const unsigned rows = static_cast<unsigned>(D / kCRows);
   const int64_t ewn = (int64_t(D) * p + 255) / 256;
   const unsigned ew = static_cast<unsigned>(ewn < 4096 ? ewn : 4096);
+  double* Pp = reinterpret_cast<double*>(w + 2 * a256c(int64_t(D) * p * 8) +
+                                         2 * a256c(kCMaxN * kCMaxN * 8));
+  const int KS = construct_kparts(D);
+  const dim3 pgrid(static_cast<unsigned>((D + kTRows - 1) / kTRows), static_cast<unsigned>(KS));
   auto tmul = [&](bool tr, const double* X, int nc, double sub, double* Yo) {
-    if (tr) hipLaunchKernelGGL((tmul_kernel<true>), dim3(rows), b256, 0, s, T, D, X, nc, sub, Yo);
-    else hipLaunchKernelGGL((tmul_kernel<false>), dim3(rows), b256, 0, s, T, D, X, nc, sub, Yo);
+    const int KL = D / KS;
+#define RW4_TP(NC)                                                                           \
+    if ((nc + 15) / 16 == NC) {                                                              \
+      if (tr) hipLaunchKernelGGL((tpart_kernel<true, NC>), pgrid, b256, 0, s, T, D, X, nc, KL, Pp); \
+      else hipLaunchKernelGGL((tpart_kernel<false, NC>), pgrid, b256, 0, s, T, D, X, nc, KL, Pp); \
+    }
+    RW4_TP(1) RW4_TP(2) RW4_TP(3) RW4_TP(4) RW4_TP(5)
+#undef RW4_TP
+    const int64_t n = int64_t(D) * nc;
+    const int64_t sb = (n + 255) / 256;
+    hipLaunchKernelGGL(tsum_kernel, dim3(static_cast<unsigned>(sb < 4096 ? sb : 4096)), b256, 0, s, Pp,
+                       KS, n, X, sub, Yo);
   };
   // X <- orth(X) through tmp
   auto orth = [&](double* X, double* tmp) {

@@ -283,7 +283,10 @@ def test_construct_validation():
     L = rw.lib()
     # Y and Z (D x p fp64, p = r + 16) plus two small fp64 matrices
     p = 48
-    assert L.respin_construct_workspace_size(4096, 32) == 2 * 4096 * p * 8 + 2 * L.rw4_align256(80 * 80 * 8)
+    # two [D][p] fp64 blocks, two 80 x 80 fp64 matrices, and the K-part sums
+    # of the products (8 parts at D = 4096)
+    assert L.respin_construct_workspace_size(4096, 32) == (
+        2 * 4096 * p * 8 + 2 * L.rw4_align256(80 * 80 * 8) + 8 * 4096 * p * 8)
     assert L.respin_construct_workspace_size(4096, 30) == 0 and L.respin_construct_workspace_size(4000, 32) == 0
     assert L.respin_construct_workspace_size(4096, 68) == 0 and L.respin_construct_workspace_size(32768, 32) == 0
     cs = lambda T=A, D=256, r=32, it=4, Q=B, R=C, ws=Dp, wsb=1 << 24: L.respin_construct(
