@@ -225,15 +225,15 @@ __device__ void jacobi_eig(double (*A)[kCMaxN + 1], double (*V)[kCMaxN + 1], int
     if (col < n) V[row][col] = row == col ? 1.0 : 0.0;
   }
   double fro = 0.0;
-  for (int row = 0; row < n; ++row)
-    for (int col = tid; col < n; col += 256) fro += A[row][col] * A[row][col];
+  for (int e = tid; e < n * n; e += 256) fro += A[e / n][e % n] * A[e / n][e % n];
   fro = block_sum(fro, red);
   const int h = n / 2;
   for (int sweep = 0; sweep < 40; ++sweep) {
     double off = 0.0;
-    for (int row = 0; row < n; ++row)
-      for (int col = tid; col < n; col += 256)
-        if (col != row) off += A[row][col] * A[row][col];
+    for (int e = tid; e < n * n; e += 256) {
+      const int row = e / n, col = e % n;
+      if (col != row) off += A[row][col] * A[row][col];
+    }
     off = block_sum(off, red);                      // identical in every thread
     if (!(off > 1e-30 * fro)) break;
     for (int rr = 0; rr < n - 1; ++rr) {
@@ -255,29 +255,30 @@ __device__ void jacobi_eig(double (*A)[kCMaxN + 1], double (*V)[kCMaxN + 1], int
         cs_s[tid] = s;
       }
       __syncthreads();
-      // rows p, q <- J^T A: thread -> (pair k, column col), pairs k = tid / 32 + 8 m
-      for (int k = tid >> 5; k < h; k += 8) {
-        const int p = pp[k], q = qq[k];
-        const double c = cs_c[k], s = cs_s[k];
-        for (int col = tid & 31; col < n; col += 32) {
-          const double ap = A[p][col], aq = A[q][col];
-          A[p][col] = c * ap - s * aq;
-          A[q][col] = s * ap + c * aq;
-        }
+      // A <- J^T A J: the pairs cover every index once, so each entry lies in
+      // exactly one 2 x 2 block (rows of pair k, columns of pair l); a thread
+      // applies k's row rotation and then l's column rotation to a block, the
+      // same operations in the same order as a row pass followed by a column
+      // pass. V <- V J on the pairs' columns.
+      for (int e = tid; e < h * h; e += 256) {
+        const int k = e / h, l = e % h;
+        const int p = pp[k], q = qq[k], u = pp[l], v = qq[l];
+        const double ck = cs_c[k], sk = cs_s[k], cl = cs_c[l], sl = cs_s[l];
+        const double apu = A[p][u], apv = A[p][v], aqu = A[q][u], aqv = A[q][v];
+        const double bpu = ck * apu - sk * aqu, bqu = sk * apu + ck * aqu;
+        const double bpv = ck * apv - sk * aqv, bqv = sk * apv + ck * aqv;
+        A[p][u] = cl * bpu - sl * bpv;
+        A[p][v] = sl * bpu + cl * bpv;
+        A[q][u] = cl * bqu - sl * bqv;
+        A[q][v] = sl * bqu + cl * bqv;
       }
-      __syncthreads();
-      // columns p, q <- A J, V J
-      for (int k = tid >> 5; k < h; k += 8) {
-        const int p = pp[k], q = qq[k];
-        const double c = cs_c[k], s = cs_s[k];
-        for (int row = tid & 31; row < n; row += 32) {
-          const double ap = A[row][p], aq = A[row][q];
-          A[row][p] = c * ap - s * aq;
-          A[row][q] = s * ap + c * aq;
-          const double vp = V[row][p], vq = V[row][q];
-          V[row][p] = c * vp - s * vq;
-          V[row][q] = s * vp + c * vq;
-        }
+      for (int e = tid; e < n * h; e += 256) {
+        const int row = e / h, l = e % h;
+        const int u = pp[l], v = qq[l];
+        const double c = cs_c[l], s = cs_s[l];
+        const double vu = V[row][u], vv = V[row][v];
+        V[row][u] = c * vu - s * vv;
+        V[row][v] = s * vu + c * vv;
       }
       __syncthreads();
     }
