@@ -86,17 +86,28 @@ constexpr bool paley_order() {
          (M % 2 == 0 && kron_prime(M / 2 - 1) && (M / 2 - 1) % 4 == 1);
 }
 
-// o = H_M v
+// o = H_M v. With S = sum of v, row r of a +-1 matrix gives
+// 2 (sum of v over the row's +1 entries) - S, or S - 2 (sum over its -1
+// entries): about M / 2 adds per output instead of M - 1, over whichever set
+// is smaller (the table is a compile-time constant).
 template <int M>
 __device__ __forceinline__ void paley_apply(const float (&v)[M], float (&o)[M]) {
   static_assert(paley_order<M>(), "Paley order");
   constexpr Paley<M> P{};
+  float S = v[0];
+#pragma unroll
+  for (int c = 1; c < M; ++c) S += v[c];
 #pragma unroll
   for (int r = 0; r < M; ++r) {
-    float acc = P.h[r][0] > 0 ? v[0] : -v[0];
+    int npos = 0;
 #pragma unroll
-    for (int c = 1; c < M; ++c) acc = P.h[r][c] > 0 ? acc + v[c] : acc - v[c];
-    o[r] = acc;
+    for (int c = 0; c < M; ++c) npos += P.h[r][c] > 0 ? 1 : 0;
+    const signed char want = 2 * npos <= M ? 1 : -1;   // the smaller set
+    float acc = 0.0f;
+#pragma unroll
+    for (int c = 0; c < M; ++c)
+      if (P.h[r][c] == want) acc += v[c];
+    o[r] = want > 0 ? fmaf(2.0f, acc, -S) : fmaf(-2.0f, acc, S);
   }
 }
 
