@@ -399,7 +399,9 @@ def test_tile_codes_rejects_minus8(rw):
                                    (32, 4096, 4096), (5, 192, 100), (31, 1088, 4000),
                                    (8, 16384, 4096), (2, 64, 16383), (8, 1024, 32768),
                                    (8, 1024, 8192), (16, 1088, 12288), (17, 256, 4096),
-                                   (1, 64, 16400)])
+                                   (1, 64, 16400),
+                                   # the largest K (sums stay exact in fp32: 49 K < 2^24)
+                                   (2, 131072, 40), (130, 131072, 64)])
 def test_w4a4_gemm_tiles(rw, T, K, N):
     say(f"w4a4_gemm_tiles T={T} K={K} N={N}")
     a, qa = _codes7(T + K, T, K)
@@ -441,8 +443,10 @@ def test_w4a4_gemm_tiles_ignores_rows_past_T(rw):
         np.testing.assert_array_equal(acc, O.gemm_int(qa[:T], qw))
 
 
-def test_w4a4_gemm_tiles_extremes(rw):
-    T, K, N = 40, 16384, 72
+@pytest.mark.parametrize("T,K,N", [(40, 16384, 72), (8, 131072, 48), (128, 131072, 128)])
+def test_w4a4_gemm_tiles_extremes(rw, T, K, N):
+    """All codes at +-7: every sum is +-49 K, exact up to the largest K."""
+    say(f"w4a4_gemm_tiles extremes T={T} K={K} N={N}")
     qa = np.full((T, K), -7)
     for wv, expect in ((-7, 49 * K), (7, -49 * K)):
         qw = np.full((N, K), wv)
