@@ -22,8 +22,8 @@ Sources (web pages; cited as [key, section]):
   and GEMM quantization), SpinQuant "MOTIVATION" (symmetric quantizer),
   FlatQuant "Preliminaries" (signed b-bit grid, Y = (XH)(H^T W^T)).
 
-Readings where the pages are silent or ambiguous are listed in DESIGN.md;
-the ones that shape code here are restated next to the code.
+Where the pages are silent or ambiguous, the reading taken is stated next to
+the code it shapes.
 
 Pins: every function below is pinned by ``tests/test_oracle_pins.py`` against
 something other than itself (worked example, closed forms, library routines,
