@@ -235,7 +235,7 @@ template <int FW, int FT, int WW, int WT, int S, bool I32OUT>
 __global__ void __launch_bounds__(64 * WW * WT)
 gemm6_lds_kernel(const uint8_t* __restrict__ at, const float* __restrict__ s_a,
                  const uint8_t* __restrict__ wt, const float* __restrict__ s_w,
-                 void* __restrict__ y, int T, int K, int N) {
+                 void* __restrict__ y, int T, int K, int N, int rt) {
   constexpr int NW = WW * WT;
   constexpr int TW = WW * FW * 32, TT = WT * FT * 32;
   constexpr int NRB = WW * FW + WT * FT;      // 32-row blocks of the workgroup (W, then A)
@@ -257,9 +257,24 @@ gemm6_lds_kernel(const uint8_t* __restrict__ at, const float* __restrict__ s_a,
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ww = wave % WW, wq = wave / WW;
   const int nwt = (N + TW - 1) / TW, ntt = (T + TT - 1) / TT, nb = nwt * ntt;
-  int b = blockIdx.x;
-  if ((nb & 7) == 0) b = (b & 7) * (nb >> 3) + (b >> 3);
-  const int n0 = (b / ntt) * TW, t0 = (b % ntt) * TT;
+  // Workgroups are dispatched to the 8 XCDs round robin (b mod 8). With rt > 0
+  // the tile grid is cut into 8 rectangles, rt along T by 8 / rt along N, and
+  // XCD x takes rectangle x, so its L2 fetches only that rectangle's A and W
+  // rows; rt = 0 gives each XCD a run of consecutive tiles instead.
+  int tb, nbk;
+  {
+    int b = blockIdx.x;
+    if (rt > 0) {
+      const int x = b & 7, l = b >> 3, rtt = ntt / rt, rnn = nwt / (8 / rt);
+      tb = (x % rt) * rtt + l % rtt;
+      nbk = (x / rt) * rnn + l / rtt;
+    } else {
+      if ((nb & 7) == 0) b = (b & 7) * (nb >> 3) + (b >> 3);
+      tb = b % ntt;
+      nbk = b / ntt;
+    }
+  }
+  const int n0 = nbk * TW, t0 = tb * TT;
   const int KT = K >> 6, KS = KT >> 1;  // k-tiles, stages
 
   // Copy i of a stage moves bytes [1024 i, 1024 i + 1024) of the stage: row
@@ -616,15 +631,31 @@ hipError_t launch_cfg(const uint8_t* a, const float* s_a, const uint8_t* w, cons
   return hipGetLastError();
 }
 
+// rt for gemm6_lds_kernel: the split of the tile grid into 8 XCD rectangles
+// (rt along T, 8 / rt along N) with the fewest A and W rows per XCD, or 0
+// when no split divides the grid evenly
+inline int xcd_regions(int64_t ntt, int64_t nwt, int64_t TT, int64_t TW) {
+  int best = 0;
+  int64_t cost = 0;
+  for (int rt = 1; rt <= 8; rt *= 2) {
+    const int rn = 8 / rt;
+    if (ntt % rt || nwt % rn) continue;
+    const int64_t c = (ntt / rt) * TT + (nwt / rn) * TW;
+    if (best == 0 || c < cost) best = rt, cost = c;
+  }
+  return best;
+}
+
 template <int FW, int FT, int WW, int WT, int S, bool I32>
 hipError_t launch_lds(const uint8_t* a, const float* s_a, const uint8_t* w, const float* s_w,
                       void* y, int64_t T, int64_t K, int64_t N, hipStream_t s) {
   constexpr int64_t TW = WW * FW * 32, TT = WT * FT * 32;
-  const int64_t nb = ((N + TW - 1) / TW) * ((T + TT - 1) / TT);
+  const int64_t nwt = (N + TW - 1) / TW, ntt = (T + TT - 1) / TT, nb = nwt * ntt;
   if (nb > 0x7FFFFFFF || K < 128 || K % 128) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((gemm6_lds_kernel<FW, FT, WW, WT, S, I32>), dim3(static_cast<unsigned>(nb)),
                      dim3(64 * WW * WT), 0, s, a, s_a, w, s_w, y, static_cast<int>(T),
-                     static_cast<int>(K), static_cast<int>(N));
+                     static_cast<int>(K), static_cast<int>(N),
+                     xcd_regions(ntt, nwt, TT, TW));
   return hipGetLastError();
 }
 
