@@ -401,7 +401,12 @@ def test_tile_codes_rejects_minus8(rw):
                                    (8, 1024, 8192), (16, 1088, 12288), (17, 256, 4096),
                                    (1, 64, 16400),
                                    # the largest K (sums stay exact in fp32: 49 K < 2^24)
-                                   (2, 131072, 40), (130, 131072, 64)])
+                                   (2, 131072, 40), (130, 131072, 64),
+                                   # each split of the tile grid into 8 XCD rectangles
+                                   # (rt along T = 1, 8, 4, 2 with ragged edges; 4 on
+                                   # the large-block variant)
+                                   (256, 384, 1024), (1024, 256, 128), (1024, 640, 256),
+                                   (1000, 640, 1000), (8192, 256, 4096)])
 def test_w4a4_gemm_tiles(rw, T, K, N):
     say(f"w4a4_gemm_tiles T={T} K={K} N={N}")
     a, qa = _codes7(T + K, T, K)
