@@ -603,14 +603,38 @@ hipError_t run_yproj(const uint16_t* x, int64_t T, int D, int P, int S, int r, c
   return hipGetLastError();
 }
 
+// z = the sum of the projection's S D-part partials, in part order from zero
+// (the order the lift's own sum takes), written over part 0 so that the lift
+// reads one partial: its workgroups, one per (64 tokens, D part), would
+// otherwise each re-read all S partials of their tokens. Thread c owns float4
+// chunk c of every part; it reads them all before it writes part 0's.
+__global__ void __launch_bounds__(256)
+zsum_kernel(float* __restrict__ Zpart, int64_t n4, int S) {
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (c >= n4) return;
+  float4* zp4 = reinterpret_cast<float4*>(Zpart);
+  float4 z = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int p0 = 0; p0 < S; p0 += 8) {
+    float4 zp[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) zp[q] = zp4[static_cast<int64_t>(min(p0 + q, S - 1)) * n4 + c];
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (p0 + q < S) {
+        z.x += zp[q].x; z.y += zp[q].y; z.z += zp[q].z; z.w += zp[q].w;
+      }
+  }
+  zp4[c] = z;
+}
+
 template <int RP, int RK>
-hipError_t run_lift(const uint16_t* x, int64_t T, int D, int P, int S, int r, const float* Zpart,
-                    const uint16_t* QH, const uint16_t* QL, const void* addend, void* out, bool of32,
-                    hipStream_t s) {
+hipError_t run_lift(const uint16_t* x, int64_t T, int D, int P, int S, int SZ, int r,
+                    const float* Zpart, const uint16_t* QH, const uint16_t* QL, const void* addend,
+                    void* out, bool of32, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>((T + TPW - 1) / TPW), S);
 #define RW4_LIFT(OF, AD)                                                                          \
   if (of32 == OF && (addend != nullptr) == AD) {                                                  \
-    hipLaunchKernelGGL((lift_kernel<RP, RK, OF, AD>), grid, dim3(LNW * 64), 0, s, x, T, D, P, S,  \
+    hipLaunchKernelGGL((lift_kernel<RP, RK, OF, AD>), grid, dim3(LNW * 64), 0, s, x, T, D, P, SZ, \
                        r, Zpart, QH, QL, addend, out);                                            \
     return hipGetLastError();                                                                     \
   }
@@ -730,7 +754,7 @@ hipError_t launch_align_mfma(const uint16_t* x, void* out, int out_f32, const fl
 }
 
 hipError_t launch_lift(const uint16_t* x, void* out, int out_f32, const void* addend, int64_t T,
-                       int64_t D, int64_t r, const void* basis, bool with_p, const float* Zpart,
+                       int64_t D, int64_t r, const void* basis, bool with_p, float* Zpart,
                        hipStream_t s) {
   if (T == 0) return hipSuccess;
   const AlignBasis a = align_basis(basis, D, r, with_p);
@@ -738,9 +762,21 @@ hipError_t launch_lift(const uint16_t* x, void* out, int out_f32, const void* ad
   const int ri = static_cast<int>(r);
   const int S = align_parts_count(D);
   const bool of32 = out_f32 != 0;
+  // from 16 D parts on, the partials are summed once (in place) for all
+  // workgroups: S^2 T RK floats of L2 reads become S T RK
+  int SZ = S;
+  if (S >= 16) {
+    const int64_t n4 = T * rk_of(r) / 4;
+    hipLaunchKernelGGL(zsum_kernel, dim3(static_cast<unsigned>((n4 + 255) / 256)), dim3(256), 0, s,
+                       Zpart, n4, S);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    SZ = 1;
+  }
   switch (a.RP) {
 #define RW4_L(V, K) \
-  case V: return run_lift<V, K>(x, T, Di, kPart, S, ri, Zpart, a.QH, a.QL, addend, out, of32, s);
+  case V:           \
+    return run_lift<V, K>(x, T, Di, kPart, S, SZ, ri, Zpart, a.QH, a.QL, addend, out, of32, s);
     RW4_L(16, 32) RW4_L(32, 32) RW4_L(48, 64) RW4_L(64, 64) RW4_L(80, 96) RW4_L(96, 96)
     RW4_L(112, 128) RW4_L(128, 128)
 #undef RW4_L

@@ -78,7 +78,7 @@ hipError_t launch_align_small(const uint16_t* x, void* out, int out_f32, const v
                               float* Zs, hipStream_t s);
 // unfused lift out = x + Q z (+ addend), fp32 or bf16 out
 hipError_t launch_lift(const uint16_t* x, void* out, int out_f32, const void* addend, int64_t T,
-                       int64_t D, int64_t r, const void* basis, bool with_p, const float* Zpart,
+                       int64_t D, int64_t r, const void* basis, bool with_p, float* Zpart,
                        hipStream_t s);
 
 // Fused lift + [Walsh-Hadamard] + INT4 quantization into FP6 tiles, after
