@@ -73,7 +73,9 @@ __device__ __forceinline__ void lift_waves(int lw, int lane, int64_t t0, int64_t
   __builtin_amdgcn_s_setprio(3);
   const int i16 = lane & 15;                    // A row (column d0 + i16); B, C column (token)
   const int g = lane >> 4;
-  const int dw = lw * (D / 8);
+  // the wave's eighth of the columns, rotated by workgroup so that the
+  // workgroups of an XCD do not all stream the same lines of A at once
+  const int dw = ((lw + static_cast<int>(blockIdx.x)) & 7) * (D / 8);
   v8bf qa[2][QB][KK], qb[2][QB][KK];
   auto loadq = [&](int buf, int grp) {
 #pragma unroll
