@@ -179,8 +179,22 @@ yproj_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int r,
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * YTPW;
-  const int part = blockIdx.y;
+  // workgroups go to the XCDs round robin in launch order (x fastest). From
+  // 16 D parts on (when the grid divides by 8), XCD k takes a contiguous run
+  // of (token block, part) pairs in part-major order, so its L2 fetches only
+  // a few parts of Q^T instead of all of it (2 MiB at D = 8192, r = 64)
+  int64_t bx = blockIdx.x;
+  int part = blockIdx.y;
+  {
+    const int64_t nb = static_cast<int64_t>(gridDim.x) * gridDim.y;
+    if ((nb & 7) == 0 && gridDim.y >= 16) {
+      const int64_t b = blockIdx.x + static_cast<int64_t>(gridDim.x) * blockIdx.y;
+      const int64_t q = (b & 7) * (nb >> 3) + (b >> 3);
+      bx = q % gridDim.x;
+      part = static_cast<int>(q / gridDim.x);
+    }
+  }
+  const int64_t t0 = bx * YTPW;
   const int dbeg = part * P;
   const int dend = min(D, dbeg + P);
   const int nds = (dend - dbeg) / 64;                 // whole double steps in this part
