@@ -276,7 +276,11 @@ def test_respin_align_identity_cases(rw):
 @pytest.mark.parametrize("T,D,r", [(37, 4096, 32), (2048, 4096, 32), (9, 256, 8), (70, 1024, 64),
                                    (13, 2048, 40), (5, 4096, 128), (11, 8192, 64), (6, 576, 16),
                                    # short batches (up to 16 tokens) take the D-parallel path
-                                   (1, 4096, 32), (16, 8192, 128), (17, 4096, 32), (8, 320, 4)])
+                                   (1, 4096, 32), (16, 8192, 128), (17, 4096, 32), (8, 320, 4),
+                                   # 16 and 32 D parts over several 64-token blocks with a
+                                   # ragged tail: the partials summed once before the lift,
+                                   # the projection's workgroups dealt part-major
+                                   (200, 8192, 64), (70, 16384, 32)])
 @pytest.mark.parametrize("odt", ["f32", "bf16"])
 @pytest.mark.parametrize("add", [False, True])
 def test_respin_align_prepared(rw, T, D, r, odt, add):
