@@ -561,10 +561,11 @@ def test_rotated_linear_flags(rw, T, D, N, flags):
 # the prepared basis gives the same results bit for bit; the fused prologue's
 # geometry changes with D (lane bits of a row), r (32 or 64 padded), and the
 # transform flag (without it the lift operand is Q itself); D = 8192 runs the
-# unfused path on the same basis layout
+# unfused path on the same basis layout (short and multi-block batches)
 @pytest.mark.parametrize("T,D,N,r,flags", [(45, 512, 128, 16, 3), (61, 1024, 64, 48, 3),
                                            (200, 2048, 96, 64, 3), (9, 4096, 64, 64, 1),
-                                           (70, 256, 64, 8, 1), (3, 8192, 64, 64, 3)])
+                                           (70, 256, 64, 8, 1), (3, 8192, 64, 64, 3),
+                                           (100, 8192, 64, 64, 3)])
 def test_rotated_linear_prepared(rw, T, D, N, r, flags):
     say(f"rotated_linear_prepared T={T} D={D} N={N} r={r} flags={flags}")
     t = torch()
