@@ -163,7 +163,13 @@ def structured_rows(rw, torch, dev, timed, with_oracle):
     # flops each (p = r + 16)
     import workloads as W
     D, r, iters = 4096, 32, 4
-    Tg = torch.from_numpy(W.gen_lowrank_transition(11, D, r)).to(dev)
+    # a transition whose deviation from the identity has rank r: I + Q0 (M0 - I) Q0^T
+    # for a seeded (Q0, M0), assembled on the device (a timing input only)
+    Q0, M0 = (torch.from_numpy(v).to(dev).double() for v in
+              W.gen_basis(11, D, r, stream="transition", skew_std=0.3))
+    Tg = (torch.eye(D, dtype=torch.float64, device=dev)
+          + Q0 @ (M0 - torch.eye(r, dtype=torch.float64, device=dev)) @ Q0.T).float()
+    del Q0, M0
     ws = torch.empty((rw.respin_construct_workspace_size(D, r),), dtype=torch.uint8, device=dev)
     ms = timed(lambda: rw.respin_construct(Tg, r, iters, workspace=ws), n=5)
     p = r + 16
@@ -173,7 +179,7 @@ def structured_rows(rw, torch, dev, timed, with_oracle):
            "frac_fp64": flops / (ms * 1e-3) / 1e12 / PEAK_FP64_TFLOPS}
     if with_oracle:
         import oracle as O
-        Ts = W.gen_lowrank_transition(11, 1024, r)
+        Ts = O.t_hat(*W.gen_basis(11, 1024, r, stream="transition", skew_std=0.3))
         t0 = time.perf_counter()
         O.construct_basis(Ts, r)
         rec["oracle_s_at_D1024"] = time.perf_counter() - t0

@@ -27,9 +27,11 @@ the code it shapes.
 
 Pins: every function below is pinned by ``tests/test_oracle_pins.py`` against
 something other than itself (worked example, closed forms, library routines,
-invariants, brute force).  ``silu_gate`` is pinned only by closed-form
+invariants, brute force); ``residual`` against the dense T_hat and a case that
+tells one bf16 rounding from two.  ``silu_gate`` is pinned only by closed-form
 identities of SiLU; the pages give no SiLU value ("parity unpinned" against
-the pages).
+the pages).  A decoder layer is not an oracle function: the layer tests feed
+each oracle stage the GPU's own previous stage.
 """
 from __future__ import annotations
 
@@ -39,7 +41,7 @@ __all__ = [
     "bf16_to_f64", "f64_to_bf16", "align", "align_dense", "t_hat", "construct_basis", "fwht",
     "hadamard",
     "quant_sym", "quant_int4", "pack_int4", "unpack_int4", "gemm_int", "gemm_int_loop",
-    "epilogue", "silu_gate", "prep_weight", "prequant", "rotated_linear", "residual", "layer",
+    "epilogue", "silu_gate", "prep_weight", "prequant", "rotated_linear", "residual",
     "quadratic_character", "jacobsthal", "paley_hadamard", "hadamard_kron", "head_hadamard",
     "FLAG_ALIGN", "FLAG_FWHT", "FLAG_SWIGLU", "FLAG_KRON_SHIFT", "FLAG_HEADS_SHIFT",
 ]
@@ -428,24 +430,9 @@ def rotated_linear(x_bits: np.ndarray, flags: int, wq: np.ndarray, s_w: np.ndarr
 
 
 def residual(x_bits: np.ndarray, Q, M, addend_bits: np.ndarray) -> np.ndarray:
-    """bf16(align(x) + addend): the aligned skip plus the block output, one rounding."""
+    """bf16(align(x) + addend): the aligned skip plus the block output, one rounding.
+
+    The alignment acts on the residual stream [RSQ framework flowchart: the
+    transition sits on the skip connection between two blocks]; the block
+    output joins after it, and the sum is rounded to bf16 once, from float64."""
     return f64_to_bf16(align(bf16_to_f64(x_bits), Q, M) + bf16_to_f64(addend_bits))
-
-
-def layer(x0_bits, basis, wq: dict, s_w: dict, D: int):
-    """One decoder layer's quantized data path on bf16 input bits.
-
-    qkv = L(x0); o = L(V part of qkv) (each token attends only to itself);
-    x1 = bf16(align1(x0) + o); gu = L(x1); d = L_down(FWHT(SiLU(g) * u));
-    x2 = bf16(align2(x1) + d).  Returns every stage."""
-    (Q1, M1), (Q2, M2) = basis
-    st = {}
-    st["qkv"] = rotated_linear(x0_bits, 0, wq["qkv"], s_w["qkv"])
-    v_bits = st["qkv"]["y"][:, 2 * D:3 * D]
-    st["o"] = rotated_linear(v_bits, 0, wq["o"], s_w["o"])
-    st["x1"] = residual(x0_bits, Q1, M1, st["o"]["y"])
-    st["gate_up"] = rotated_linear(st["x1"], 0, wq["gate_up"], s_w["gate_up"])
-    st["down"] = rotated_linear(st["gate_up"]["y"], FLAG_SWIGLU | FLAG_FWHT, wq["down"],
-                                s_w["down"])
-    st["x2"] = residual(st["x1"], Q2, M2, st["down"]["y"])
-    return st

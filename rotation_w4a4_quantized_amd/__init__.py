@@ -504,14 +504,17 @@ def prep_weight(W, rotate: bool, bits: int = 4, m: int = 1, signs=None):
     return tiles, s_w, codes, src
 
 
-def layer(x0, aligns, weights, D: int, ws=None):
+def layer(x0, aligns, weights, D: int, dbg_down=None):
     """One decoder layer's quantized path (each token attends only to itself):
     qkv = L(x0); o = L(V part of qkv); x1 = bf16(align1(x0) + o);
     gu = L(x1); d = L_down(FWHT(SiLU(g) * u)); x2 = bf16(align2(x1) + d).
     ``aligns``: ((basis1, r1), (basis2, r2)), each alignment's basis from
     ``respin_prepare_basis`` (prepared once per layer) with its rank.
-    ``weights``: name -> (tiles, s_w) for qkv, o, gate_up, down. Returns a dict
-    of every stage's output tensor."""
+    ``weights``: name -> (tiles, s_w) for qkv, o, gate_up, down.
+    ``dbg_down``: optional fp32 [T][D_ffn] that receives the down projection's
+    pre-quant values. Returns a dict of every stage's output tensor, plus
+    "down_ws", the down projection's workspace (its activation tiles and
+    scales, see ``workspace_views``)."""
     torch = _torch()
     (B1, r1), (B2, r2) = aligns
     st = {}
@@ -519,7 +522,8 @@ def layer(x0, aligns, weights, D: int, ws=None):
     st["o"], _ = rotated_linear(st["qkv"][:, 2 * D:3 * D], *weights["o"], flags=0)
     st["x1"] = respin_align_prepared(x0, B1, r1, addend=st["o"], out_dtype=torch.bfloat16)
     st["gate_up"], _ = rotated_linear(st["x1"], *weights["gate_up"], flags=0)
-    st["down"], _ = rotated_linear(st["gate_up"], *weights["down"], flags=RW4_SWIGLU | RW4_FWHT)
+    st["down"], st["down_ws"] = rotated_linear(st["gate_up"], *weights["down"],
+                                               flags=RW4_SWIGLU | RW4_FWHT, dbg_prequant=dbg_down)
     st["x2"] = respin_align_prepared(st["x1"], B2, r2, addend=st["down"],
                                      out_dtype=torch.bfloat16)
     return st

@@ -6,8 +6,15 @@
 // int8 in registers and fed to v_mfma_i32_32x32x32_i8. The widening keeps each
 // nibble in the HIGH half of its byte ((w << 4) & 0xF0F0F0F0 for the even
 // elements, w & 0xF0F0F0F0 for the odd ones): each int8 then equals 16 * code,
-// every product carries a factor 256, and the int32 sum is shifted right by 8
-// at the end (exact: |sum| <= 64 K * 256 < 2^31 for K <= 131072). The widened
+// every product carries a factor 256, and the int32 sum S' = 256 S is shifted
+// right by 8 at the end. Each product of two codes lies in [-56, 64] (-8 * -8
+// is the only one above 49), so S lies in [-56 K, 64 K]. For K < 131072, 256 S
+// stays inside int32; at K = 131072 the single value S = 64 K = 2^23 (every
+// code -8 in both rows) gives 256 S = 2^31, which int32 cannot hold: the
+// accumulator then reads -2^31 (wrapped) or 2^31 - 1 (saturated). Neither can
+// be 256 S for an S in range (-2^23 is below -56 K, and 2^31 - 1 is no
+// multiple of 256), so unscale() maps both to 2^23 and every result is exact
+// for K <= 131072. The widened
 // bytes of a lane are in the order 0,2,4,6,1,3,5,7,... of its codes; both
 // operands use the same order, so each MFMA still pairs equal k.
 //
@@ -28,6 +35,11 @@ namespace gemm {
 constexpr int BKB = 128;    // packed bytes per k-step (256 codes), one barrier each
 constexpr int PITCH = 144;  // LDS row pitch (bytes): 128 + 16 keeps 16-lane b128 reads conflict-free
 constexpr int KSUB = BKB / 32;  // 64-code sub-steps per k-step (two MFMAs each)
+
+// the integer sum S from the accumulator of 256 S (the header comment above)
+__device__ __forceinline__ int unscale(int acc) {
+  return (acc == INT32_MIN || acc == INT32_MAX) ? (1 << 23) : (acc >> 8);
+}
 
 __device__ __forceinline__ void widen(const uint4 p, v4i& m0, v4i& m1) {
   const uint32_t H = 0xF0F0F0F0u;
@@ -213,7 +225,7 @@ gemm_kernel(const uint8_t* __restrict__ a, const float* __restrict__ s_a,
           uint16_t o[4];
 #pragma unroll
           for (int c = 0; c < 4; ++c)
-            o[c] = f32_to_bf16((static_cast<float>(acc[i][j][4 * q + c] >> 8) * sa) * swv[c]);
+            o[c] = f32_to_bf16((static_cast<float>(unscale(acc[i][j][4 * q + c])) * sa) * swv[c]);
           *reinterpret_cast<uint2*>(&stage[tt * SP + nn]) =
               make_uint2(o[0] | (static_cast<uint32_t>(o[1]) << 16), o[2] | (static_cast<uint32_t>(o[3]) << 16));
         }
@@ -254,7 +266,7 @@ gemm_kernel(const uint8_t* __restrict__ a, const float* __restrict__ s_a,
           const int n = n0 + (ww * BW + i) * 32 + 8 * q + 4 * (lane >> 5);
           int vals[4];
 #pragma unroll
-          for (int c = 0; c < 4; ++c) vals[c] = acc[i][j][4 * q + c] >> 8;
+          for (int c = 0; c < 4; ++c) vals[c] = unscale(acc[i][j][4 * q + c]);
           int* yp = static_cast<int*>(y) + static_cast<int64_t>(t) * N + n;
           if (n + 3 < N && (N & 3) == 0) {
             *reinterpret_cast<int4*>(yp) = make_int4(vals[0], vals[1], vals[2], vals[3]);

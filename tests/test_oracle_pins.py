@@ -326,6 +326,43 @@ def test_align_full_rank_is_conjugated_rotation():
     np.testing.assert_allclose(O.align(x, Qo, Mo), x @ (Qo @ Mo @ Qo.T).T, atol=1e-12)
 
 
+# ---------------------------------------------------------------- residual add
+def test_residual_against_dense_transition():
+    """bf16(T_hat x + addend): brute force through the dense T_hat (float64),
+    one rounding (f64_to_bf16 is pinned against torch below); the addend joins
+    after the alignment, not before it."""
+    Q, M = _basis(64, 8, skew=0.3)
+    rng = np.random.default_rng(21)
+    xb = W.gen_x(21, 6, 64, 2, 30.0)
+    ab = W.f32_to_bf16_bits(rng.standard_normal((6, 64)).astype(np.float32))
+    x, a = O.bf16_to_f64(xb), O.bf16_to_f64(ab)
+    got = O.residual(xb, Q, M, ab)
+    np.testing.assert_array_equal(got, O.f64_to_bf16(x @ O.t_hat(Q, M).T + a))
+    assert not np.array_equal(got, O.f64_to_bf16((x + a) @ O.t_hat(Q, M).T))
+    # M = I: the skip passes unchanged and the sum is the exact bf16 add
+    np.testing.assert_array_equal(O.residual(xb, Q, np.eye(8), ab), O.f64_to_bf16(x + a))
+
+
+def test_residual_rounds_once():
+    """D = r = 2, Q = I, M a rotation by theta: the aligned value of x = (c, 0)
+    is c cos(theta) = 1 + 2^-8 - 2^-16, just under the midpoint of the bf16
+    neighbours 1 and 1 + 2^-7. With the addend 2^-9 the exact sum lies above
+    that midpoint, so one rounding gives 1 + 2^-7 (bits 0x3F81); rounding the
+    alignment to bf16 first (1) and then the sum 1 + 2^-9 gives 1 (0x3F80)."""
+    c = 1.0 + 2.0 ** -7
+    cos = (1.0 + 2.0 ** -8 - 2.0 ** -16) / c
+    sin = np.sqrt(1.0 - cos * cos)
+    M = np.array([[cos, -sin], [sin, cos]])
+    xb = O.f64_to_bf16(np.array([[c, 0.0]]))
+    ab = O.f64_to_bf16(np.array([[2.0 ** -9, 0.0]]))
+    assert O.bf16_to_f64(xb)[0, 0] == c and O.bf16_to_f64(ab)[0, 0] == 2.0 ** -9
+    got = O.residual(xb, np.eye(2), M, ab)
+    assert got[0, 0] == 0x3F81
+    twice = O.f64_to_bf16(O.bf16_to_f64(O.f64_to_bf16(O.align(O.bf16_to_f64(xb), np.eye(2), M)))
+                          + O.bf16_to_f64(ab))
+    assert twice[0, 0] == 0x3F80
+
+
 # ---------------------------------------------------------------- quantizer
 def test_quant_worked_example():
     g = load("quant_example.txt")

@@ -146,15 +146,6 @@ def gen_basis(key: int, D: int, r: int, stream: str = "basis",
     return Qm.astype(np.float32), M.astype(np.float32)
 
 
-def gen_lowrank_transition(key: int, D: int, r: int, skew_std: float = 0.3) -> np.ndarray:
-    """fp32 [D][D]: I + Q0 (M0 - I) Q0^T for a seeded (Q0, M0) of rank r, i.e. a
-    transition whose deviation from the identity has rank r exactly."""
-    Q0, M0 = gen_basis(key, D, r, stream="transition", skew_std=skew_std)
-    Q0 = Q0.astype(np.float64)
-    M0 = M0.astype(np.float64)
-    return (np.eye(D) + Q0 @ (M0 - np.eye(r)) @ Q0.T).astype(np.float32)
-
-
 def gen_hadamard_transition(key: int, D: int, n_big: int, big=(0.3, 1.0),
                             small: float = 0.01) -> np.ndarray:
     """fp32 [D][D] synthetic residual transition near the identity, of the kind
