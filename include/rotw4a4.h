@@ -21,7 +21,9 @@
  * Conventions shared by every entry point
  *   - Every pointer is a DEVICE pointer (HIP global memory on the current
  *     device) unless stated otherwise. The caller owns every buffer; the
- *     library never allocates or frees device memory.
+ *     library never allocates or frees device memory. Its one device array
+ *     of its own is the scratch of rotated_linear_prepared_noalloc (a static
+ *     object of the library's code, one per GPU).
  *   - Matrices are row-major. Activations are [T][D] (token rows).
  *   - bf16 is IEEE-754 binary32's upper 16 bits; conversions to bf16 round to
  *     nearest, ties to even.
@@ -37,7 +39,8 @@
  *   - T = 0 is a valid empty call: once the sizes, dtypes and flags are
  *     valid it returns RW4_OK without inspecting any pointer or launching.
  *   - The library holds no state between calls and is thread-safe; calls that
- *     write overlapping buffers must be ordered by the caller.
+ *     write overlapping buffers must be ordered by the caller. (The scratch
+ *     of rotated_linear_prepared_noalloc is the one exception: see there.)
  *   - Floating point is IEEE: no fast-math; fp32 division is correctly
  *     rounded; denormals are kept.
  */
@@ -363,6 +366,31 @@ rw4_status rotated_linear_prepared(const void* x, int64_t ldx, int64_t T, int64_
 /* bytes of workspace rotated_linear_prepared needs; 0 on bad input */
 size_t rotated_linear_prepared_workspace_size(int64_t T, int64_t D, int64_t r, unsigned flags);
 
+/*
+ * rotated_linear_prepared_noalloc -- for callers that cannot allocate device
+ * memory (code under HIP graph capture, serving loops or harnesses that forbid
+ * allocation): rotated_linear_prepared with the same arguments minus the
+ * workspace, and the same results bit for bit. Its scratch is a device array
+ * of RW4_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held from the
+ * library's first use on that GPU until the process ends; the call allocates
+ * and frees nothing.
+ *   - Sizes whose workspace (rotated_linear_prepared_workspace_size) exceeds
+ *     RW4_NOALLOC_SCRATCH_BYTES return RW4_ERR_UNSUPPORTED before any launch
+ *     (e.g. T = 4096 tokens at D = 16384; the 70B-shaped linear does not fit).
+ *   - Every call on a GPU uses that GPU's one array: calls that overlap on one
+ *     GPU (other streams, other host threads) race and must be ordered by the
+ *     caller. The array keeps the last call's contents; none of it needs to
+ *     start at zero.
+ *   - The activation tiles and scales stay in the library's array (there is
+ *     no workspace to read them from).
+ * Other arguments, constraints and errors: those of rotated_linear_prepared.
+ */
+#define RW4_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+rw4_status rotated_linear_prepared_noalloc(const void* x, int64_t ldx, int64_t T, int64_t D,
+                                           const void* basis, int64_t r, unsigned flags,
+                                           const uint8_t* w, const float* s_w, int64_t N, void* y,
+                                           float* dbg_prequant, void* stream);
+
 /* n rounded up to a multiple of 256 (workspace offsets) */
 size_t rw4_align256(size_t n);
 
@@ -372,7 +400,7 @@ const char* rw4_status_string(rw4_status s);
 /* ABI version of this header (bumped on any signature change) */
 int rw4_abi_version(void);
 
-#define RW4_ABI_VERSION 8
+#define RW4_ABI_VERSION 9
 
 #ifdef __cplusplus
 }

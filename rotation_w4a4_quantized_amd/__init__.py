@@ -21,7 +21,8 @@ __all__ = [
     "rotated_linear_prepared_workspace_size",
     "w4a4_tiles_size", "w4a4_tile_codes", "w4a4_gemm_tiles", "prep_weight", "layer",
     "quant_act_sym", "RW4_ABITS", "RW4_KRON", "RW4_HEADS", "hadamard_transform", "head_hadamard",
-    "respin_construct", "respin_construct_workspace_size",
+    "respin_construct", "respin_construct_workspace_size", "rotated_linear_prepared_noalloc",
+    "NOALLOC_SCRATCH_BYTES",
 ]
 
 RW4_ALIGN, RW4_FWHT, RW4_SWIGLU = 1, 2, 4
@@ -55,7 +56,7 @@ EXPORTS = ("respin_align", "respin_align_workspace_size", "fwht", "quant_act_int
            "rotated_linear_prepared", "rotated_linear_prepared_workspace_size",
            "respin_align_prepared", "respin_align_prepared_workspace_size",
            "hadamard_transform", "head_hadamard", "respin_construct",
-           "respin_construct_workspace_size", "rw4_align256",
+           "respin_construct_workspace_size", "rotated_linear_prepared_noalloc", "rw4_align256",
            "rw4_status_string", "rw4_abi_version")
 
 
@@ -97,6 +98,8 @@ def lib() -> ctypes.CDLL:
     L.respin_prepare_basis.argtypes = [vp, vp, i64, i64, vp, sz, vp]
     L.rotated_linear_prepared.argtypes = [vp, i64, i64, i64, vp, i64, u32, vp, vp, i64, vp, vp,
                                           sz, vp, vp]
+    L.rotated_linear_prepared_noalloc.argtypes = [vp, i64, i64, i64, vp, i64, u32, vp, vp, i64,
+                                                  vp, vp, vp]
     L.rotated_linear_prepared_workspace_size.argtypes = [i64, i64, i64, u32]
     L.rotated_linear_prepared_workspace_size.restype = sz
     L.respin_align_prepared.argtypes = [vp, vp, i32, vp, vp, i64, i64, i64, vp, sz, vp]
@@ -115,7 +118,8 @@ def lib() -> ctypes.CDLL:
     for f in ("respin_align", "fwht", "quant_act_int4", "quant_act_sym", "w4a4_gemm",
               "w4a4_tile_codes",
               "w4a4_gemm_tiles", "rotated_linear", "respin_prepare_basis",
-              "rotated_linear_prepared", "respin_align_prepared", "hadamard_transform",
+              "rotated_linear_prepared", "rotated_linear_prepared_noalloc",
+              "respin_align_prepared", "hadamard_transform",
               "head_hadamard", "respin_construct"):
         getattr(L, f).restype = i32
     _lib = L
@@ -478,6 +482,36 @@ def rotated_linear_prepared(x, w, s_w, flags: int, basis=None, r: int = 0, out=N
                                        _p(dbg_prequant), _stream())
     _check("rotated_linear_prepared", st)
     return out, workspace
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # RW4_NOALLOC_SCRATCH_BYTES of include/rotw4a4.h
+
+
+def rotated_linear_prepared_noalloc(x, w, s_w, flags: int, basis=None, r: int = 0, out=None,
+                                    dbg_prequant=None):
+    """``rotated_linear_prepared`` without a workspace: the library's own
+    per-GPU scratch array holds the intermediates, and the call allocates no
+    device memory (``out`` must then be given). Calls that overlap on one GPU
+    race. Returns y."""
+    torch = _torch()
+    _rows(x)
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bf16")
+    T = x.shape[0]
+    D = x.shape[1] // 2 if flags & RW4_SWIGLU else x.shape[1]
+    N = s_w.shape[0]
+    if w.numel() * w.element_size() < w4a4_tiles_size(N, D):
+        raise ValueError("w: weight tile buffer too small for [N][D]")
+    r = r if flags & RW4_ALIGN else 0
+    if r and basis.numel() * basis.element_size() < respin_basis_size(D, r):
+        raise ValueError("basis: buffer too small for (D, r)")
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    st = lib().rotated_linear_prepared_noalloc(_p(x), x.stride(0), T, D,
+                                               _p(basis) if r else None, r, flags, _p(w),
+                                               _p(s_w), N, _p(out), _p(dbg_prequant), _stream())
+    _check("rotated_linear_prepared_noalloc", st)
+    return out
 
 
 def workspace_views(workspace, T: int, D: int):

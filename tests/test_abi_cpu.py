@@ -22,7 +22,7 @@ def _declared():
 def test_library_built_and_loads():
     assert os.path.exists(rw.library_path), "build the HIP library first"
     L = rw.lib()
-    assert L.rw4_abi_version() == 8
+    assert L.rw4_abi_version() == 9
 
 
 def test_exports_every_declared_symbol():
@@ -327,3 +327,22 @@ def test_rotated_linear_validation():
     assert _rl(x=ODD) == MIS
     assert _rl(T=0) == 0
     assert _rl(T=0, x=NUL, w=NUL, sw=NUL, y=NUL) == 0
+
+
+# rotated_linear_prepared_noalloc(x, ldx, T, D, basis, r, flags, w, s_w, N, y, dbg, stream):
+# sizes past the library's scratch and invalid arguments are refused on the host
+E = ctypes.c_void_p(0x50000)
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((A, 8192, 8192, 8192, B, 64, 3, C, Dp, 64, E, NUL, NUL), UNS),       # needs > the scratch
+    ((A, 4096, 4, 4096, B, 32, 3 | (1 << 31), C, Dp, 64, E, NUL, NUL), INV),  # unknown flag
+    ((A, 4096, 4, 100, B, 32, 3, C, Dp, 64, E, NUL, NUL), UNS),           # D not a power of two
+    ((A, 4096, -1, 4096, B, 32, 3, C, Dp, 64, E, NUL, NUL), INV),         # negative T
+    ((A, 4096, 0, 4096, B, 32, 3, C, Dp, 64, E, NUL, NUL), 0),            # T = 0: nothing launched
+])
+def test_noalloc_validation(args, expect):
+    L = rw.lib()
+    assert L.rotated_linear_prepared_noalloc(*args) == expect
+    if expect == UNS and args[2] == 8192:
+        assert L.rotated_linear_prepared_workspace_size(8192, 8192, 64, 3) > rw.NOALLOC_SCRATCH_BYTES
