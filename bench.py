@@ -68,14 +68,45 @@ def traffic_bytes():
     return rec.get("bytes_per_launch")
 
 
+def _host_threads():
+    """(cores this process may run on, BLAS threads numpy uses)."""
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        blas = max(int(i.get("num_threads", 1)) for i in info) if info else 1
+    except Exception:
+        blas = None
+    return cores, blas
+
+
+def gpu_clocks():
+    """Current and maximum shader / memory clocks as amd-smi reports them right
+    after the timed runs (best effort: None when the tool is unavailable)."""
+    import subprocess
+    try:
+        p = subprocess.run(["amd-smi", "metric", "--clock", "--json"], capture_output=True,
+                           text=True, timeout=20)
+        if p.returncode != 0:
+            return None
+        rec = json.loads(p.stdout)
+        rec = rec[0] if isinstance(rec, list) else rec
+        clk = rec.get("clock", rec)
+        out = {}
+        for key in ("gfx_0", "mem_0"):
+            c = clk.get(key) if isinstance(clk, dict) else None
+            if isinstance(c, dict):
+                out[key] = {k: (v.get("value") if isinstance(v, dict) else v)
+                            for k, v in c.items() if k in ("clk", "max_clk", "min_clk")}
+        return out or None
+    except Exception:
+        return None
+
+
 def cpu_baseline(wl, inp, seconds):
     """The oracle, as it stands, on a bounded token sample of the same workload."""
     import oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max(int(i.get("num_threads", 1)) for i in threadpool_info()) if threadpool_info() else 1
-    except Exception:
-        threads = 1
+    cores, threads = _host_threads()
     Q, M = inp["basis"][0]
     qw, s_w, _ = O.prep_weight(inp["W"]["lin"], rotate=True)      # offline, untimed
     sample = 128
@@ -88,10 +119,61 @@ def cpu_baseline(wl, inp, seconds):
         t_total += time.perf_counter() - t0
         done += rows.shape[0]
         i += 1
-    return {"value": done / t_total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": done / t_total, "unit": "tokens/s", "cores": cores, "blas_threads": threads,
+            "kind": "oracle",
             "sample": f"{done} tokens of the same workload in {sample}-token batches "
                       f"(float64 align+FWHT, fp32 quant, float64-BLAS integer GEMM), "
                       f"{t_total:.1f} s"}
+
+
+def _oracle_layer(O, x_bits, basis, wq, sw, D):
+    """One decoder layer's chain through the oracle's stages (each token attends
+    only to itself): qkv, o on the V third, the first residual alignment, gate+up,
+    the gated down projection behind the transform, the second residual."""
+    (Q1, M1), (Q2, M2) = basis
+    qkv = O.rotated_linear(x_bits, 0, wq["qkv"], sw["qkv"])["y"]
+    o = O.rotated_linear(np.ascontiguousarray(qkv[:, 2 * D:3 * D]), 0, wq["o"], sw["o"])["y"]
+    x1 = O.residual(x_bits, Q1, M1, o)
+    gu = O.rotated_linear(x1, 0, wq["gate_up"], sw["gate_up"])["y"]
+    d = O.rotated_linear(gu, O.FLAG_SWIGLU | O.FLAG_FWHT, wq["down"], sw["down"])["y"]
+    return O.residual(x1, Q2, M2, d)
+
+
+def cpu_baseline_configs(seconds):
+    """The oracle on the other workloads, each on a bounded token sample of its
+    own inputs (weights prepared untimed): the decode layer (T = 8) and the
+    prefill layer (T = 4096) through the layer chain, the 70B-shaped linear
+    through the unit."""
+    import oracle as O
+    import workloads as W
+    cores, threads = _host_threads()
+    out = {}
+    for cid, sample in ((2, 8), (3, 32), (4, 16)):
+        wl = W.CONFIGS[cid]
+        inp = W.workload_inputs(wl)
+        wq, sw = {}, {}
+        for lin in wl.linears:
+            q, s_, _ = O.prep_weight(inp["W"][lin.name], rotate=lin.rotate)
+            wq[lin.name], sw[lin.name] = q, s_
+        del inp["W"]
+        done, t_total, i = 0, 0.0, 0
+        while t_total < seconds and done < wl.T * 8:
+            r0 = (i * sample) % wl.T
+            rows = inp["x"][r0:r0 + sample]
+            t0 = time.perf_counter()
+            if wl.is_layer:
+                _oracle_layer(O, rows, inp["basis"], wq, sw, wl.D)
+            else:
+                Q, M = inp["basis"][0]
+                O.rotated_linear(rows, O.FLAG_ALIGN | O.FLAG_FWHT, wq["lin"], sw["lin"], Q, M)
+            t_total += time.perf_counter() - t0
+            done += rows.shape[0]
+            i += 1
+        out[wl.name] = {"value": done / t_total, "unit": "tokens/s", "cores": cores,
+                        "blas_threads": threads, "kind": "oracle",
+                        "sample": f"{done} tokens in {sample}-token batches, {t_total:.1f} s"}
+        del wq, sw, inp
+    return out
 
 
 def structured_rows(rw, torch, dev, timed, with_oracle):
@@ -134,8 +216,9 @@ def structured_rows(rw, torch, dev, timed, with_oracle):
     dec = {}
     for name, K, N in (("qkv", 4096, 12288), ("o", 4096, 4096), ("gate_up", 4096, 32768),
                        ("down", 16384, 4096)):
-        wbytes = N * K * 3 // 4
-        nset = min(24, max(2, -(-(320 << 20) // wbytes)))   # >= 320 MiB of weights in rotation
+        wbytes = N * K // 2                      # algorithmic: INT4 codes
+        fp6_bytes = N * K * 3 // 4               # what the kernel streams (FP6 tiles)
+        nset = min(24, max(2, -(-(320 << 20) // fp6_bytes)))   # >= 320 MiB of tiles in rotation
         Tdec = 8
         codes_w = [torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, generator=g).to(dev) & 0x77
                    for _ in range(nset)]
@@ -153,8 +236,10 @@ def structured_rows(rw, torch, dev, timed, with_oracle):
             rw.w4a4_gemm_tiles(at, sa, wt[i], sw, Tdec, K, N, out=yd)
         ms = timed(call, n=2 * nset)
         gbs = wbytes / (ms * 1e-3) / 1e9
-        dec[name] = {"K": K, "N": N, "us": ms * 1e3, "weight_bytes": wbytes, "GB/s": gbs,
-                     "frac_hbm": gbs / PEAK_HBM_GBS}
+        dec[name] = {"K": K, "N": N, "us": ms * 1e3, "weight_bytes_int4": wbytes, "GB/s": gbs,
+                     "frac_hbm": gbs / PEAK_HBM_GBS,
+                     "fp6_tile_bytes_streamed": fp6_bytes,
+                     "GB/s_fp6_streamed": fp6_bytes / (ms * 1e-3) / 1e9}
         del wt
     out["decode_gemm_T8"] = dec
 
@@ -424,10 +509,55 @@ def main():
     align_unprep_ms = timed(lambda: rw.respin_align(s0["x"], Qg, Mg, out=tmp, workspace=aws))
     pws = torch.empty((rw.respin_align_prepared_workspace_size(T, D, r),), dtype=torch.uint8,
                       device=dev)
-    align_ms = timed(lambda: rw.respin_align_prepared(s0["x"], s0["basis"], r, out=tmp,
-                                                      workspace=pws))
-    fwht_ms = timed(lambda: rw.fwht(tmp, out=tmp))
-    quant_ms = timed(lambda: rw.quant_act_int4(tmp, codes_t, sa_t))
+    # warm: one buffer set, replayed (it stays in the 256 MB last-level cache)
+    align_warm_ms = timed(lambda: rw.respin_align_prepared(s0["x"], s0["basis"], r, out=tmp,
+                                                           workspace=pws))
+    fwht_warm_ms = timed(lambda: rw.fwht(tmp, out=tmp))
+    quant_warm_ms = timed(lambda: rw.quant_act_int4(tmp, codes_t, sa_t))
+    del tmp, codes_t, sa_t
+    # cold: every call on the next of NC buffer sets (bf16 x, fp32 rows, codes,
+    # scales: 52 MiB a set, 520 MiB in rotation), so that a set has left the
+    # last-level cache before it comes round again
+    NC = 10
+    cold = [{"x": sets[i % nb]["x"], "f": torch.empty((T, D), dtype=torch.float32, device=dev),
+             "c": torch.empty((T, D // 2), dtype=torch.uint8, device=dev),
+             "s": torch.empty((T,), dtype=torch.float32, device=dev)} for i in range(NC)]
+    for c in cold:
+        c["f"].normal_()
+    ctr = [0]
+
+    def rot(fn):
+        def call():
+            c = cold[ctr[0] % NC]
+            ctr[0] += 1
+            fn(c)
+        return call
+    align_ms = timed(rot(lambda c: rw.respin_align_prepared(c["x"], s0["basis"], r, out=c["f"],
+                                                             workspace=pws)), n=2 * NC)
+    fwht_ms = timed(rot(lambda c: rw.fwht(c["f"], out=c["f"])), n=2 * NC)
+    quant_ms = timed(rot(lambda c: rw.quant_act_int4(c["f"], c["c"], c["s"])), n=2 * NC)
+    del cold
+
+    # the packed-INT4 GEMM (int8 matrix cores, nibbles widened in registers) at
+    # the same shape, on the same codes (packed rows of the weight, activation
+    # codes from the unit's own quantizer), eight operand sets rotated as above
+    codes_w0 = rw.quant_act_int4(rw.fwht(torch.from_numpy(inp["W"]["lin"]).to(dev)))[0]
+    i8sets = [{"a": rw.quant_act_int4(sets[i % nb]["x"])[0], "w": codes_w0.clone(),
+               "sa": torch.rand(T, device=dev), "sw": torch.rand(N, device=dev)}
+              for i in range(nb)]
+    del codes_w0
+    for i in range(args.warmup):
+        q = i8sets[i % nb]
+        rw.w4a4_gemm(q["a"], q["sa"], q["w"], q["sw"], out=sets[i % nb]["y"])
+    torch.cuda.synchronize()
+    ga.record()
+    for i in range(args.steps):
+        q = i8sets[i % nb]
+        rw.w4a4_gemm(q["a"], q["sa"], q["w"], q["sw"], out=sets[i % nb]["y"])
+    gb.record()
+    torch.cuda.synchronize()
+    gemm_i8_ms = ga.elapsed_time(gb) / args.steps
+    del i8sets
 
     rows = structured_rows(rw, torch, dev, timed, not args.no_cpu_baseline)
     configs = config_rows(rw, torch, dev, timed)
@@ -444,10 +574,14 @@ def main():
     stage_bytes = {"align": T * 6 * D + 4 * D * r + 4 * r * r, "fwht": T * 8 * D,
                    "quant": T * (4 * D + D // 2 + 4)}
     stage_ms = {"align": align_ms, "fwht": fwht_ms, "quant": quant_ms}
+    warm_ms = {"align": align_warm_ms, "fwht": fwht_warm_ms, "quant": quant_warm_ms}
     bw = {}
     for k, nbytes in stage_bytes.items():
         gbs = nbytes / (stage_ms[k] * 1e-3) / 1e9
-        bw[k] = {"bytes": nbytes, "GB/s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS}
+        bw[k] = {"bytes": nbytes, "us": stage_ms[k] * 1e3, "GB/s": gbs,
+                 "frac_hbm": gbs / PEAK_HBM_GBS, "cache": "cold (10 buffer sets rotated)",
+                 "us_warm": warm_ms[k] * 1e3,
+                 "frac_hbm_warm": nbytes / (warm_ms[k] * 1e-3) / 1e9 / PEAK_HBM_GBS}
     align_flop = T * (4 * D * r + 2 * r * r)
     bw["align"]["TFLOP/s"] = align_flop / (align_ms * 1e-3) / 1e12
     bw["align"]["frac_fp32"] = bw["align"]["TFLOP/s"] / PEAK_FP32_TFLOPS
@@ -475,11 +609,16 @@ def main():
                      "frac": achieved / PEAK_FP6_TFLOPS,
                      "frac_of_int8_peak": achieved / PEAK_I8_TOPS, "traffic": traffic,
                      "avg_launch_us": gemm_ms * 1e3, "ops_per_launch": gemm_ops},
+        "gemm_int8_packed": {"kernel": "w4a4_gemm (gemm_kernel, packed INT4 rows, int8 MFMA)",
+                             "avg_launch_us": gemm_i8_ms * 1e3,
+                             "TOP/s": gemm_ops / (gemm_i8_ms * 1e-3) / 1e12,
+                             "frac_of_int8_peak": gemm_ops / (gemm_i8_ms * 1e-3) / 1e12 / PEAK_I8_TOPS},
         "step_launch": "one captured HIP graph of the K steps" if graph is not None
                        else "eager launches",
         "eager_ms_per_step": eager_ms_per_step,
-        "stages_us": {"step_events": step_ms_ev * 1e3, "align": align_ms * 1e3,
-                      "fwht": fwht_ms * 1e3, "quant": quant_ms * 1e3, "gemm": gemm_ms * 1e3,
+        "stages_us": {"step_events": step_ms_ev * 1e3, "align_cold": align_ms * 1e3,
+                      "fwht_cold": fwht_ms * 1e3, "quant_cold": quant_ms * 1e3,
+                      "gemm": gemm_ms * 1e3, "gemm_int8_packed": gemm_i8_ms * 1e3,
                       "basis_prep": basis_ms * 1e3,
                       "align_with_basis_prep": align_unprep_ms * 1e3,
                       "step_with_basis_prep": unprepared_ms * 1e3},
@@ -487,8 +626,10 @@ def main():
         "structured_transforms": rows,
         "configs": configs,
     }
+    out["gpu_clocks_after_run"] = gpu_clocks()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+        out["cpu_baseline_other_configs"] = cpu_baseline_configs(args.cpu_seconds / 2)
     print(json.dumps(out), flush=True)
 
 
