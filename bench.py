@@ -48,6 +48,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 256 MiB device copy (counter calibration)")
+    p.add_argument("--profile-step", action="store_true",
+                   help="only the unit's steps, the GEMM, the cold stages and the 256 MiB "
+                        "calibration copy (short runs under a profiler)")
     return p.parse_args()
 
 
@@ -90,6 +93,8 @@ def gpu_clocks():
         if p.returncode != 0:
             return None
         rec = json.loads(p.stdout)
+        if isinstance(rec, dict) and "gpu_data" in rec:
+            rec = rec["gpu_data"]
         rec = rec[0] if isinstance(rec, list) else rec
         clk = rec.get("clock", rec)
         out = {}
@@ -558,6 +563,18 @@ def main():
     torch.cuda.synchronize()
     gemm_i8_ms = ga.elapsed_time(gb) / args.steps
     del i8sets
+
+    if args.profile_step:
+        src = torch.empty((256 << 20,), dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_step": wl.name, "ms_per_step": ms_per_step,
+                          "gemm_us": gemm_ms * 1e3, "gemm_int8_packed_us": gemm_i8_ms * 1e3,
+                          "align_cold_us": align_ms * 1e3, "fwht_cold_us": fwht_ms * 1e3,
+                          "quant_cold_us": quant_ms * 1e3}), flush=True)
+        return
 
     rows = structured_rows(rw, torch, dev, timed, not args.no_cpu_baseline)
     configs = config_rows(rw, torch, dev, timed)
