@@ -241,11 +241,27 @@ def structured_rows(rw, torch, dev, timed, with_oracle):
             rw.w4a4_gemm_tiles(at, sa, wt[i], sw, Tdec, K, N, out=yd)
         ms = timed(call, n=2 * nset)
         gbs = wbytes / (ms * 1e-3) / 1e9
+        # the same product on packed INT4 rows (w4a4_gemm: the weight-streaming
+        # int8 kernel at T <= 16), weights rotated the same way
+        nset4 = min(24, max(2, -(-(320 << 20) // wbytes)))
+        pw = [torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, generator=g).to(dev) & 0x77
+              for _ in range(nset4)]
+        pa = torch.randint(0, 256, (Tdec, K // 2), dtype=torch.uint8, generator=g).to(dev) & 0x77
+        cnt4 = [0]
+
+        def call4():
+            i = cnt4[0] % nset4
+            cnt4[0] += 1
+            rw.w4a4_gemm(pa, sa, pw[i], sw, out=yd)
+        ms4 = timed(call4, n=2 * nset4)
+        gbs4 = wbytes / (ms4 * 1e-3) / 1e9
         dec[name] = {"K": K, "N": N, "us": ms * 1e3, "weight_bytes_int4": wbytes, "GB/s": gbs,
                      "frac_hbm": gbs / PEAK_HBM_GBS,
                      "fp6_tile_bytes_streamed": fp6_bytes,
-                     "GB/s_fp6_streamed": fp6_bytes / (ms * 1e-3) / 1e9}
-        del wt
+                     "GB/s_fp6_streamed": fp6_bytes / (ms * 1e-3) / 1e9,
+                     "packed_int4_us": ms4 * 1e3, "packed_int4_GB/s": gbs4,
+                     "packed_int4_frac_hbm": gbs4 / PEAK_HBM_GBS}
+        del wt, pw
     out["decode_gemm_T8"] = dec
 
     # offline construction of (Q, R_sub) at the prefill shape (D = 4096, r = 32,
@@ -290,11 +306,11 @@ def config_rows(rw, torch, dev, timed):
     gd = torch.Generator(device=dev).manual_seed(11)
     out = {}
 
-    def weight(N, K, rotate):
+    def weight(N, K, rotate, packed=False):
         Wf = torch.randn((N, K), generator=gd, device=dev).mul_(0.02)
-        tl, s, _, _ = rw.prep_weight(Wf, rotate)
+        tl, s, codes, _ = rw.prep_weight(Wf, rotate)
         del Wf
-        return tl, s
+        return (codes, s) if packed else (tl, s)
 
     def basis_pair(key, D, r):
         Q, M = W.gen_basis(key, D, r)
@@ -327,18 +343,23 @@ def config_rows(rw, torch, dev, timed):
     shapes = {"qkv": (3 * D, D, False), "o": (D, D, False), "gate_up": (8 * D, D, False),
               "down": (D, 4 * D, True)}
     sets = [{k: weight(N, K, rot) for k, (N, K, rot) in shapes.items()} for _ in range(2)]
+    psets = [{k: weight(N, K, rot, True) for k, (N, K, rot) in shapes.items()} for _ in range(3)]
     wbytes = sum(N * K // 2 for N, K, _ in shapes.values())          # INT4 codes
     lops = sum(2.0 * N * K for N, K, _ in shapes.values())            # per token
     aligns = tuple((rw.respin_prepare_basis(*basis_pair(k, D, 32)), 32) for k in (21, 22))
-    for name, T in (("layer_decode_T8", 8), ("layer_prefill_T4096", 4096)):
+    # the decode layer on packed INT4 weight rows (RW4_WPACKED, three sets: 402 MB)
+    # and on FP6 tiles (two sets: 402 MB); the prefill layer on FP6 tiles
+    for name, T, packed in (("layer_decode_T8", 8, True), ("layer_decode_T8_fp6_tiles", 8, False),
+                            ("layer_prefill_T4096", 4096, False)):
         x0 = torch.randn((T, D), generator=gd, device=dev).to(torch.bfloat16)
         cnt = [0]
+        ws_sets = psets if packed else sets
 
         def call():
-            i = cnt[0] % len(sets)
+            i = cnt[0] % len(ws_sets)
             cnt[0] += 1
-            rw.layer(x0, aligns, sets[i], D)
-        ms = timed(call, n=4 if T > 8 else 20)
+            rw.layer(x0, aligns, ws_sets[i], D, packed=packed)
+        ms = timed(call, n=4 if T > 8 else 24)
         rec = {"T": T, "D": D, "us": ms * 1e3, "tokens_per_s": T / (ms * 1e-3),
                "gemm_ops": lops * T, "TOPS": lops * T / (ms * 1e-3) / 1e12}
         if T <= 32:
@@ -348,7 +369,7 @@ def config_rows(rw, torch, dev, timed):
         else:
             rec["frac_int8"] = rec["TOPS"] / PEAK_I8_TOPS
         out[name] = rec
-    del sets
+    del sets, psets
     return out
 
 

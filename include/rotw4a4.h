@@ -69,9 +69,10 @@ typedef enum rw4_dtype { RW4_BF16 = 0, RW4_F32 = 1, RW4_I32 = 2 } rw4_dtype;
    (b = 2, 3 or 4; 0 in that field means 4). With RW4_FWHT, RW4_KRON(m)
    (m = 12, 20, 28) makes the transform H_{2^n} (x) H_m over D = 2^n m (see
    hadamard_transform). RW4_HEADS(k) selects the transform across heads,
-   H_{n_h} (x) I with n_h = 2^k (see head_hadamard), instead of RW4_FWHT. */
+   H_{n_h} (x) I with n_h = 2^k (see head_hadamard), instead of RW4_FWHT.
+   RW4_WPACKED: the weights are packed INT4 rows instead of FP6 tiles. */
 enum { RW4_ALIGN = 1, RW4_FWHT = 2, RW4_SWIGLU = 4, RW4_ABITS_SHIFT = 8, RW4_KRON_SHIFT = 16,
-       RW4_HEADS_SHIFT = 24 };
+       RW4_HEADS_SHIFT = 24, RW4_WPACKED = 1 << 29 };
 #define RW4_ABITS(b) ((unsigned)(b) << RW4_ABITS_SHIFT)
 #define RW4_KRON(m) ((unsigned)(m) << RW4_KRON_SHIFT)
 #define RW4_HEADS(k) ((unsigned)(k) << RW4_HEADS_SHIFT)
@@ -219,21 +220,29 @@ rw4_status w4a4_gemm_tiles(const uint8_t* a, const float* s_a, const uint8_t* w,
  *            hadamard_transform (D = 2^n m, m = 12, 20, 28, D <= 16384).
  *          RW4_HEADS(k): the transform across 2^k heads of head_hadamard
  *            instead (no FWHT, ALIGN or SWIGLU; D <= 16384).
+ *          RW4_WPACKED: w holds the weight codes as packed INT4 rows
+ *            (uint8 [N][D/2], the layout of w4a4_gemm) instead of FP6 tiles;
+ *            the activation codes are then packed INT4 rows too and the
+ *            product runs as w4a4_gemm (int8 matrix cores; for T <= 16 its
+ *            weight-streaming kernel, the decode format). Results are the
+ *            same codes, scales and outputs bit for bit as with FP6 tiles of
+ *            the same weight codes.
  *          flags = 0: quantize x as is. ALIGN and SWIGLU are exclusive.
  *   x        bf16, T rows of D (or 2D with SWIGLU) values, row stride ldx
  *            elements (ldx >= width, ldx % 8 == 0)
  *   Q, M, r  as respin_align (ignored without RW4_ALIGN)
- *   w, s_w   weight codes as FP6 tiles of [N][D] (w4a4_tile_codes) and fp32
+ *   w, s_w   weight codes as FP6 tiles of [N][D] (w4a4_tile_codes; no code
+ *            -8) or, with RW4_WPACKED, as packed INT4 rows [N][D/2], and fp32
  *            scales [N]; the weights must already carry the inverse of every
  *            rotation applied here (e.g. rows Hadamard-transformed along K
- *            when RW4_FWHT is set) and hold no code -8
+ *            when RW4_FWHT is set)
  *   y        bf16 [T][N]
  *   workspace device memory of at least rotated_linear_workspace_size(T, D,
  *            r, flags) bytes, 256-byte aligned. After the call it holds the
  *            activation codes as FP6 tiles of [T][D] at offset 0
- *            (w4a4_tiles_size(T, D) bytes) and the per-token scales fp32 [T]
- *            at offset rw4_align256(w4a4_tiles_size(T, D)); the rest is
- *            internal.
+ *            (w4a4_tiles_size(T, D) bytes; with RW4_WPACKED packed INT4 rows
+ *            [T][D/2] there) and the per-token scales fp32 [T] at offset
+ *            rw4_align256(w4a4_tiles_size(T, D)); the rest is internal.
  *   dbg_prequant nullable fp32 [T][D]: if given, receives the fp32 values that
  *            were quantized (for stage-wise checking).
  * Constraints: D a power of two, 64 <= D <= 32768, or with RW4_KRON(m)
@@ -400,7 +409,7 @@ const char* rw4_status_string(rw4_status s);
 /* ABI version of this header (bumped on any signature change) */
 int rw4_abi_version(void);
 
-#define RW4_ABI_VERSION 9
+#define RW4_ABI_VERSION 10
 
 #ifdef __cplusplus
 }

@@ -13,7 +13,7 @@ import os
 from typing import Optional, Tuple
 
 __all__ = [
-    "RW4_ALIGN", "RW4_FWHT", "RW4_SWIGLU", "Rw4Error", "lib", "library_path",
+    "RW4_ALIGN", "RW4_FWHT", "RW4_SWIGLU", "RW4_WPACKED", "Rw4Error", "lib", "library_path",
     "respin_align", "fwht", "quant_act_int4", "w4a4_gemm", "rotated_linear",
     "rotated_linear_workspace_size", "respin_align_workspace_size", "workspace_views",
     "respin_basis_size", "respin_prepare_basis", "rotated_linear_prepared",
@@ -26,6 +26,7 @@ __all__ = [
 ]
 
 RW4_ALIGN, RW4_FWHT, RW4_SWIGLU = 1, 2, 4
+RW4_WPACKED = 1 << 29     # weights as packed INT4 rows [N][K/2] instead of FP6 tiles
 
 
 def RW4_ABITS(bits: int) -> int:
@@ -367,6 +368,13 @@ def w4a4_gemm_tiles(a, s_a, w, s_w, T: int, K: int, N: int, out=None, out_dtype=
     return out
 
 
+def _check_weights(w, N: int, D: int, flags: int):
+    need = N * D // 2 if flags & RW4_WPACKED else w4a4_tiles_size(N, D)
+    if w.numel() * w.element_size() < need:
+        raise ValueError("w: weight buffer too small for [N][D] (packed INT4 rows with "
+                         "RW4_WPACKED, FP6 tiles otherwise)")
+
+
 def rotated_linear_workspace_size(T: int, D: int, r: int, flags: int) -> int:
     return int(lib().rotated_linear_workspace_size(T, D, r, flags))
 
@@ -388,8 +396,7 @@ def rotated_linear(x, w, s_w, flags: int, Q=None, M=None, out=None, workspace=No
     T = x.shape[0]
     D = x.shape[1] // 2 if flags & RW4_SWIGLU else x.shape[1]
     N = s_w.shape[0]
-    if w.numel() * w.element_size() < w4a4_tiles_size(N, D):
-        raise ValueError("w: weight tile buffer too small for [N][D]")
+    _check_weights(w, N, D, flags)
     r = Q.shape[1] if (flags & RW4_ALIGN) and Q is not None else 0
     need = rotated_linear_workspace_size(T, D, r, flags)
     if workspace is None:
@@ -466,8 +473,7 @@ def rotated_linear_prepared(x, w, s_w, flags: int, basis=None, r: int = 0, out=N
     T = x.shape[0]
     D = x.shape[1] // 2 if flags & RW4_SWIGLU else x.shape[1]
     N = s_w.shape[0]
-    if w.numel() * w.element_size() < w4a4_tiles_size(N, D):
-        raise ValueError("w: weight tile buffer too small for [N][D]")
+    _check_weights(w, N, D, flags)
     r = r if flags & RW4_ALIGN else 0
     if r and basis.numel() * basis.element_size() < respin_basis_size(D, r):
         raise ValueError("basis: buffer too small for (D, r)")
@@ -500,8 +506,7 @@ def rotated_linear_prepared_noalloc(x, w, s_w, flags: int, basis=None, r: int = 
     T = x.shape[0]
     D = x.shape[1] // 2 if flags & RW4_SWIGLU else x.shape[1]
     N = s_w.shape[0]
-    if w.numel() * w.element_size() < w4a4_tiles_size(N, D):
-        raise ValueError("w: weight tile buffer too small for [N][D]")
+    _check_weights(w, N, D, flags)
     r = r if flags & RW4_ALIGN else 0
     if r and basis.numel() * basis.element_size() < respin_basis_size(D, r):
         raise ValueError("basis: buffer too small for (D, r)")
@@ -514,13 +519,15 @@ def rotated_linear_prepared_noalloc(x, w, s_w, flags: int, basis=None, r: int = 
     return out
 
 
-def workspace_views(workspace, T: int, D: int):
-    """(activation tiles, flat uint8, and scales fp32 [T]) inside a rotated_linear workspace."""
+def workspace_views(workspace, T: int, D: int, packed: bool = False):
+    """(activation codes, scales fp32 [T]) inside a rotated_linear workspace: the
+    codes as FP6 tiles (flat uint8), or as packed INT4 rows uint8 [T][D/2] for a
+    call with RW4_WPACKED."""
     n = w4a4_tiles_size(T, D)
     off = int(lib().rw4_align256(n))
-    tiles = workspace[:n]
+    codes = workspace[:T * D // 2].view(T, D // 2) if packed else workspace[:n]
     scales = workspace[off: off + 4 * T].view(_torch().float32)
-    return tiles, scales
+    return codes, scales
 
 
 def prep_weight(W, rotate: bool, bits: int = 4, m: int = 1, signs=None):
@@ -538,13 +545,15 @@ def prep_weight(W, rotate: bool, bits: int = 4, m: int = 1, signs=None):
     return tiles, s_w, codes, src
 
 
-def layer(x0, aligns, weights, D: int, dbg_down=None):
+def layer(x0, aligns, weights, D: int, dbg_down=None, packed: bool = False):
     """One decoder layer's quantized path (each token attends only to itself):
     qkv = L(x0); o = L(V part of qkv); x1 = bf16(align1(x0) + o);
     gu = L(x1); d = L_down(FWHT(SiLU(g) * u)); x2 = bf16(align2(x1) + d).
     ``aligns``: ((basis1, r1), (basis2, r2)), each alignment's basis from
     ``respin_prepare_basis`` (prepared once per layer) with its rank.
-    ``weights``: name -> (tiles, s_w) for qkv, o, gate_up, down.
+    ``weights``: name -> (tiles, s_w) for qkv, o, gate_up, down; with
+    ``packed`` (codes, s_w), the packed INT4 rows (RW4_WPACKED: the decode
+    format).
     ``dbg_down``: optional fp32 [T][D_ffn] that receives the down projection's
     pre-quant values. Returns a dict of every stage's output tensor, plus
     "down_ws", the down projection's workspace (its activation tiles and
@@ -552,12 +561,14 @@ def layer(x0, aligns, weights, D: int, dbg_down=None):
     torch = _torch()
     (B1, r1), (B2, r2) = aligns
     st = {}
-    st["qkv"], _ = rotated_linear(x0, *weights["qkv"], flags=0)
-    st["o"], _ = rotated_linear(st["qkv"][:, 2 * D:3 * D], *weights["o"], flags=0)
+    wf = RW4_WPACKED if packed else 0
+    st["qkv"], _ = rotated_linear(x0, *weights["qkv"], flags=wf)
+    st["o"], _ = rotated_linear(st["qkv"][:, 2 * D:3 * D], *weights["o"], flags=wf)
     st["x1"] = respin_align_prepared(x0, B1, r1, addend=st["o"], out_dtype=torch.bfloat16)
-    st["gate_up"], _ = rotated_linear(st["x1"], *weights["gate_up"], flags=0)
+    st["gate_up"], _ = rotated_linear(st["x1"], *weights["gate_up"], flags=wf)
     st["down"], st["down_ws"] = rotated_linear(st["gate_up"], *weights["down"],
-                                               flags=RW4_SWIGLU | RW4_FWHT, dbg_prequant=dbg_down)
+                                               flags=RW4_SWIGLU | RW4_FWHT | wf,
+                                               dbg_prequant=dbg_down)
     st["x2"] = respin_align_prepared(st["x1"], B2, r2, addend=st["down"],
                                      out_dtype=torch.bfloat16)
     return st

@@ -33,7 +33,8 @@ inline int abits(unsigned flags) {
   return b == 0 ? 4 : b;
 }
 constexpr unsigned kFlagMask = RW4_ALIGN | RW4_FWHT | RW4_SWIGLU | (0xFu << RW4_ABITS_SHIFT) |
-                               (0xFFu << RW4_KRON_SHIFT) | (0x1Fu << RW4_HEADS_SHIFT);
+                               (0xFFu << RW4_KRON_SHIFT) | (0x1Fu << RW4_HEADS_SHIFT) |
+                               static_cast<unsigned>(RW4_WPACKED);
 inline int kron_m(unsigned flags) { return static_cast<int>((flags >> RW4_KRON_SHIFT) & 0xFFu); }
 inline int heads_lg(unsigned flags) { return static_cast<int>((flags >> RW4_HEADS_SHIFT) & 0x1Fu); }
 
@@ -108,7 +109,14 @@ rw4_status run_linear(const void* x, int64_t ldx, int64_t T, int64_t D, const vo
                       void* y, void* workspace, float* dbg, hipStream_t s) {
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint8_t* codes = ws;
+  // packed INT4 weights: the activation codes are packed rows [T][D/2] (they
+  // fit the tile area) and the product runs on the packed-row GEMM
+  const bool pk = (flags & RW4_WPACKED) != 0;
   float* s_a = reinterpret_cast<float*>(ws + rw4_align256(rw4::tiles_bytes(T, D)));
+  auto gemm = [&]() {
+    return pk ? rw4::launch_gemm(codes, s_a, w, s_w, y, false, T, D, N, s)
+              : rw4::launch_gemm_tiles(codes, s_a, w, s_w, y, false, T, D, N, s);
+  };
   const void* src = x;
   int in = (flags & RW4_SWIGLU) ? rw4::IN_SWIGLU : rw4::IN_BF16;
   int64_t ld = ldx;
@@ -130,9 +138,9 @@ rw4_status run_linear(const void* x, int64_t ldx, int64_t T, int64_t D, const vo
     if (fused) {
       // lift + transform + quantization on chip
       if (rw4::launch_lift_fwht_quant(xb, T, D, r, basis, Zpart, (flags & RW4_FWHT) != 0, codes,
-                                      s_a, dbg, s, abits(flags)) != hipSuccess)
+                                      s_a, dbg, s, abits(flags), pk) != hipSuccess)
         return RW4_ERR_HIP;
-      return hip_status(rw4::launch_gemm_tiles(codes, s_a, w, s_w, y, false, T, D, N, s));
+      return hip_status(gemm());
     }
     if (!rw4::align_small(T, D) &&
         rw4::launch_lift(xb, tmp, 1, nullptr, T, D, r, basis, with_p(D, r), Zpart, s) != hipSuccess)
@@ -148,14 +156,14 @@ rw4_status run_linear(const void* x, int64_t ldx, int64_t T, int64_t D, const vo
     const int64_t B = D / A;
     const double c = m ? static_cast<double>(D) : static_cast<double>(A);
     e = rw4::launch_kron(src, in, ld, T, A, B, m, nullptr,
-                         static_cast<float>(1.0 / __builtin_sqrt(c)), nullptr, codes, true, s_a,
+                         static_cast<float>(1.0 / __builtin_sqrt(c)), nullptr, codes, !pk, s_a,
                          dbg, abits(flags), s);
   } else {
-    e = rw4::launch_row(src, in, ld, T, D, (flags & RW4_FWHT) != 0, nullptr, codes, true, s_a, dbg,
+    e = rw4::launch_row(src, in, ld, T, D, (flags & RW4_FWHT) != 0, nullptr, codes, !pk, s_a, dbg,
                         s, abits(flags));
   }
   if (e != hipSuccess) return RW4_ERR_HIP;
-  return hip_status(rw4::launch_gemm_tiles(codes, s_a, w, s_w, y, false, T, D, N, s));
+  return hip_status(gemm());
 }
 
 }  // namespace

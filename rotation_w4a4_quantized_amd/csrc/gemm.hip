@@ -281,6 +281,111 @@ gemm_kernel(const uint8_t* __restrict__ a, const float* __restrict__ s_a,
   }
 }
 
+// ----------------------------------------------------------------------------
+// Decode products (T <= 16 tokens): the weights stream once from HBM as packed
+// INT4 rows (0.5 bytes per code), so the kernel is bound by that stream. A
+// workgroup owns 16 weight rows; its NWV waves split K into steps of 256 codes
+// (128 bytes of every row, whole cache lines) and take steps w, w + NWV, ...
+// Lane l holds row l % 16 and the 32-byte quarter l / 16 of each 128-byte
+// step as two 16-byte loads, PD steps in flight. Each 16-byte load widens
+// (16 * code, as above) into the operands of two v_mfma_i32_16x16x64_i8 with
+// weight rows as the A operand and tokens as the B operand; token rows past T
+// load nothing and hold zero. The waves' partial sums (all of the form 256 S,
+// added modulo 2^32) are summed through LDS in wave order, then unscaled.
+constexpr int kDecRows = 16;
+
+template <int NWV, int PD, bool I32OUT>
+__global__ void __launch_bounds__(64 * NWV)
+gemm_decode_kernel(const uint8_t* __restrict__ a, const float* __restrict__ s_a,
+                   const uint8_t* __restrict__ w, const float* __restrict__ s_w,
+                   void* __restrict__ y, int T, int K, int N) {
+  __shared__ uint32_t red[NWV][4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n0 = blockIdx.x * kDecRows;
+  const int KB = K / 2;                       // bytes per row
+  const int nstep = (KB + 127) / 128;         // 128-byte steps (the last may be partial)
+  const int i = lane & 15, g = lane >> 4;
+  // rows past N re-read the last row (their sums are never stored); tokens past
+  // T load nothing
+  const uint8_t* wrow = w + static_cast<int64_t>(min(n0 + i, N - 1)) * KB;
+  const uint8_t* arow = a + static_cast<int64_t>(min(i, T - 1)) * KB;
+  const bool tok = i < T;
+  v4i acc = {0, 0, 0, 0};
+  uint4 wv[PD][2], av[PD][2];
+  // all loads unconditional: quarters past the end of K read the row's first
+  // 16 bytes (K >= 32) and are masked to zero
+  auto load = [&](int u, int st) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int off = st * 128 + 64 * h + 16 * g;  // this lane's 16 bytes of the row
+      const bool ok = st < nstep && off + 16 <= KB;
+      const int o = ok ? off : 0;                   // masked: the row's first 16 bytes
+      uint4 vw = *reinterpret_cast<const uint4*>(wrow + o);
+      uint4 va = *reinterpret_cast<const uint4*>(arow + o);
+      const uint32_t mw = ok ? 0xFFFFFFFFu : 0u;
+      const uint32_t ma = ok && tok ? 0xFFFFFFFFu : 0u;
+      vw.x &= mw; vw.y &= mw; vw.z &= mw; vw.w &= mw;
+      va.x &= ma; va.y &= ma; va.z &= ma; va.w &= ma;
+      wv[u][h] = vw;
+      av[u][h] = va;
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < PD; ++u) load(u, wave + NWV * u);
+  for (int st0 = wave; st0 < nstep; st0 += NWV * PD) {
+#pragma unroll
+    for (int u = 0; u < PD; ++u) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        v4i w0, w1, a0, a1;
+        widen(wv[u][h], w0, w1);
+        widen(av[u][h], a0, a1);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(w0, a0, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(w1, a1, acc, 0, 0, 0);
+      }
+      load(u, st0 + NWV * (u + PD));          // steps past the end load masked zeros
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_sleep(1);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) red[wave][v][lane] = static_cast<uint32_t>(acc[v]);
+  __syncthreads();
+  if (threadIdx.x >= 256) return;
+  // thread (v, l): weight row 4 (l / 16) + v of the block, token l % 16
+  const int v = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int t = l & 15;
+  const int n = n0 + 4 * (l >> 4) + v;
+  if (t >= T || n >= N) return;
+  uint32_t sum = 0;
+#pragma unroll
+  for (int ww = 0; ww < NWV; ++ww) sum += red[ww][v][l];
+  const int S = unscale(static_cast<int>(sum));
+  if constexpr (I32OUT) {
+    static_cast<int32_t*>(y)[static_cast<int64_t>(t) * N + n] = S;
+  } else {
+    static_cast<uint16_t*>(y)[static_cast<int64_t>(t) * N + n] =
+        f32_to_bf16((static_cast<float>(S) * s_a[t]) * s_w[n]);
+  }
+}
+
+template <int NWV, int PD>
+hipError_t launch_decode(const uint8_t* a, const float* s_a, const uint8_t* w, const float* s_w,
+                         void* y, bool i32_out, int64_t T, int64_t K, int64_t N, hipStream_t s) {
+  const int64_t nb = (N + kDecRows - 1) / kDecRows;
+  if (nb > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  if (i32_out)
+    hipLaunchKernelGGL((gemm_decode_kernel<NWV, PD, true>), dim3(static_cast<unsigned>(nb)),
+                       dim3(64 * NWV), 0, s, a, s_a, w, s_w, y, static_cast<int>(T),
+                       static_cast<int>(K), static_cast<int>(N));
+  else
+    hipLaunchKernelGGL((gemm_decode_kernel<NWV, PD, false>), dim3(static_cast<unsigned>(nb)),
+                       dim3(64 * NWV), 0, s, a, s_a, w, s_w, y, static_cast<int>(T),
+                       static_cast<int>(K), static_cast<int>(N));
+  return hipGetLastError();
+}
+
 template <int NWW, int NWT, int BW, int BT>
 hipError_t launch_cfg(const uint8_t* a, const float* s_a, const uint8_t* w, const float* s_w,
                       void* y, bool i32_out, int64_t T, int64_t K, int64_t N, hipStream_t s) {
@@ -302,6 +407,17 @@ hipError_t launch_cfg(const uint8_t* a, const float* s_a, const uint8_t* w, cons
 hipError_t launch_gemm(const uint8_t* a, const float* s_a, const uint8_t* w, const float* s_w,
                        void* y, bool i32_out, int64_t T, int64_t K, int64_t N, hipStream_t s) {
   if (T == 0) return hipSuccess;
+  if (T <= gemm::kDecRows) {
+    // weight streaming: fewer waves per workgroup as the workgroups multiply.
+    // Measured at T = 8 (weights rotated past the last-level cache): 16 waves
+    // with one step in flight for up to 256 workgroups (4096 x 4096: 4.2 us;
+    // 16384 x 4096: 10.1 us), 4 waves with two in flight beyond (4096 x 12288:
+    // 8.8 us; 4096 x 32768: 20.5 us); more steps in flight were slower.
+    const int64_t nb = (N + gemm::kDecRows - 1) / gemm::kDecRows;
+    if (nb <= 256) return gemm::launch_decode<16, 1>(a, s_a, w, s_w, y, i32_out, T, K, N, s);
+    if (nb <= 512) return gemm::launch_decode<8, 2>(a, s_a, w, s_w, y, i32_out, T, K, N, s);
+    return gemm::launch_decode<4, 2>(a, s_a, w, s_w, y, i32_out, T, K, N, s);
+  }
   return gemm::launch_cfg<2, 2, 2, 2>(a, s_a, w, s_w, y, i32_out, T, K, N, s);
 }
 

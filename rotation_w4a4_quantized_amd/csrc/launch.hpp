@@ -81,14 +81,15 @@ hipError_t launch_lift(const uint16_t* x, void* out, int out_f32, const void* ad
                        int64_t D, int64_t r, const void* basis, bool with_p, float* Zpart,
                        hipStream_t s);
 
-// Fused lift + [Walsh-Hadamard] + INT4 quantization into FP6 tiles, after
-// launch_yproj: per token, u = [H x / sqrt(D)] + P z (P = H Q / sqrt(D) with
-// the transform, Q without), codes of u. Needs a basis prepared with P.
+// Fused lift + [Walsh-Hadamard] + INT4 quantization into FP6 tiles (or packed
+// INT4 rows [T][D/2] when packed), after launch_yproj: per token,
+// u = [H x / sqrt(D)] + P z (P = H Q / sqrt(D) with the transform, Q
+// without), codes of u. Needs a basis prepared with P.
 bool lfq_supported(int64_t D, int64_t r);
 hipError_t launch_lift_fwht_quant(const uint16_t* x, int64_t T, int64_t D, int64_t r,
                                   const void* basis, const float* Zpart, bool do_fwht,
                                   uint8_t* tiles, float* s_a, float* dbg, hipStream_t s,
-                                  int bits = 4);
+                                  int bits = 4, bool packed = false);
 
 // W4A4 GEMM, bf16 (dequantized) or raw int32 output.
 hipError_t launch_gemm(const uint8_t* a, const float* s_a, const uint8_t* w, const float* s_w,

@@ -1,5 +1,6 @@
 // Fused prologue of the rotated linear: alignment lift + Walsh-Hadamard
-// transform + per-token INT4 quantization, written as FP6 operand tiles.
+// transform + per-token INT4 quantization, written as FP6 operand tiles (or as
+// packed INT4 rows for the packed-weight GEMM).
 //
 // Per token (ReSpinQuant paper notes, key design 3; "QuaRot 与 SpinQuant"
 // §2.2; "Infra Quant II", QuaRot Method):
@@ -140,7 +141,7 @@ __device__ __forceinline__ void lift_waves(int lw, int lane, int64_t t0, int64_t
   lds_barrier();  // 2: A z in LDS
 }
 
-template <int N, int RK, bool FW, bool DBG>
+template <int N, int RK, bool FW, bool DBG, bool PK>
 __global__ void __launch_bounds__(kThreads)
 lfq_kernel(const uint16_t* __restrict__ x, int64_t T, const float* __restrict__ Zpart, int S,
            const uint16_t* __restrict__ PH, const uint16_t* __restrict__ PL,
@@ -306,8 +307,20 @@ lfq_kernel(const uint16_t* __restrict__ x, int64_t T, const float* __restrict__ 
 #pragma unroll
         for (int e = 0; e < 32; ++e) q[e] = rq.code(u[s][e]);
       }
-      const v6u_t w = pack_fp6_32(q);
-      store_fields32(tiles, t, 32 * c, D, Field12{w[0], w[1], w[2]}, Field12{w[3], w[4], w[5]});
+      if constexpr (PK) {
+        // packed INT4 row: element 2j in the low nibble of byte j
+        uint32_t wd[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          wd[j] = 0;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) wd[j] |= nib(static_cast<int>(q[8 * j + e])) << (4 * e);
+        }
+        *reinterpret_cast<uint4*>(tiles + t * (D / 2) + 16 * c) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+      } else {
+        const v6u_t w = pack_fp6_32(q);
+        store_fields32(tiles, t, 32 * c, D, Field12{w[0], w[1], w[2]}, Field12{w[3], w[4], w[5]});
+      }
       if constexpr (DBG) {
         float4* o = reinterpret_cast<float4*>(dbg + t * D + 32 * c);
 #pragma unroll
@@ -320,31 +333,33 @@ lfq_kernel(const uint16_t* __restrict__ x, int64_t T, const float* __restrict__ 
 
 template <int N, int RK>
 hipError_t launch_n(const uint16_t* x, int64_t T, const float* Zpart, int S, const uint16_t* PH,
-                    const uint16_t* PL, bool fw, uint8_t* tiles, float* s_a, float* dbg,
+                    const uint16_t* PL, bool fw, bool pk, uint8_t* tiles, float* s_a, float* dbg,
                     float qmax, hipStream_t s) {
   const float norm = static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(1 << N)));
   const dim3 grid(static_cast<unsigned>((T + kTok - 1) / kTok));
-#define RW4_LFQ(F, G)                                                                           \
-  if (fw == F && (dbg != nullptr) == G) {                                                       \
-    hipLaunchKernelGGL((lfq_kernel<N, RK, F, G>), grid, dim3(kThreads), 0, s, x, T, Zpart, S,   \
-                       PH, PL, tiles, s_a, dbg, norm, qmax);                                    \
-    return hipGetLastError();                                                                   \
+#define RW4_LFQ(F, G, K)                                                                          \
+  if (fw == F && (dbg != nullptr) == G && pk == K) {                                              \
+    hipLaunchKernelGGL((lfq_kernel<N, RK, F, G, K>), grid, dim3(kThreads), 0, s, x, T, Zpart, S,  \
+                       PH, PL, tiles, s_a, dbg, norm, qmax);                                      \
+    return hipGetLastError();                                                                     \
   }
-  RW4_LFQ(true, false) RW4_LFQ(true, true) RW4_LFQ(false, false) RW4_LFQ(false, true)
+  RW4_LFQ(true, false, false) RW4_LFQ(true, true, false) RW4_LFQ(false, false, false)
+  RW4_LFQ(false, true, false) RW4_LFQ(true, false, true) RW4_LFQ(true, true, true)
+  RW4_LFQ(false, false, true) RW4_LFQ(false, true, true)
 #undef RW4_LFQ
   return hipErrorInvalidValue;
 }
 
 template <int RK>
 hipError_t launch_rk(int n, const uint16_t* x, int64_t T, const float* Zpart, int S,
-                     const uint16_t* PH, const uint16_t* PL, bool fw, uint8_t* tiles, float* s_a,
-                     float* dbg, float qmax, hipStream_t s) {
+                     const uint16_t* PH, const uint16_t* PL, bool fw, bool pk, uint8_t* tiles,
+                     float* s_a, float* dbg, float qmax, hipStream_t s) {
   switch (n) {
-    case 8: return launch_n<8, RK>(x, T, Zpart, S, PH, PL, fw, tiles, s_a, dbg, qmax, s);
-    case 9: return launch_n<9, RK>(x, T, Zpart, S, PH, PL, fw, tiles, s_a, dbg, qmax, s);
-    case 10: return launch_n<10, RK>(x, T, Zpart, S, PH, PL, fw, tiles, s_a, dbg, qmax, s);
-    case 11: return launch_n<11, RK>(x, T, Zpart, S, PH, PL, fw, tiles, s_a, dbg, qmax, s);
-    case 12: return launch_n<12, RK>(x, T, Zpart, S, PH, PL, fw, tiles, s_a, dbg, qmax, s);
+    case 8: return launch_n<8, RK>(x, T, Zpart, S, PH, PL, fw, pk, tiles, s_a, dbg, qmax, s);
+    case 9: return launch_n<9, RK>(x, T, Zpart, S, PH, PL, fw, pk, tiles, s_a, dbg, qmax, s);
+    case 10: return launch_n<10, RK>(x, T, Zpart, S, PH, PL, fw, pk, tiles, s_a, dbg, qmax, s);
+    case 11: return launch_n<11, RK>(x, T, Zpart, S, PH, PL, fw, pk, tiles, s_a, dbg, qmax, s);
+    case 12: return launch_n<12, RK>(x, T, Zpart, S, PH, PL, fw, pk, tiles, s_a, dbg, qmax, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -361,7 +376,7 @@ bool lfq_supported(int64_t D, int64_t r) {
 hipError_t launch_lift_fwht_quant(const uint16_t* x, int64_t T, int64_t D, int64_t r,
                                   const void* basis, const float* Zpart, bool do_fwht,
                                   uint8_t* tiles, float* s_a, float* dbg, hipStream_t s,
-                                  int bits) {
+                                  int bits, bool packed) {
   if (T == 0) return hipSuccess;
   if (!lfq_supported(D, r) || bits < 2 || bits > 4) return hipErrorInvalidValue;
   const float qmax = static_cast<float>((1 << (bits - 1)) - 1);
@@ -373,8 +388,10 @@ hipError_t launch_lift_fwht_quant(const uint16_t* x, int64_t T, int64_t D, int64
   if (S != (D + 511) / 512) return hipErrorInvalidValue;  // the lift waves' part count
   int n = 0;
   while ((int64_t(1) << n) < D) ++n;
-  if (a.RK == 32) return launch_rk<32>(n, x, T, Zpart, S, PH, PL, do_fwht, tiles, s_a, dbg, qmax, s);
-  if (a.RK == 64) return launch_rk<64>(n, x, T, Zpart, S, PH, PL, do_fwht, tiles, s_a, dbg, qmax, s);
+  if (a.RK == 32)
+    return launch_rk<32>(n, x, T, Zpart, S, PH, PL, do_fwht, packed, tiles, s_a, dbg, qmax, s);
+  if (a.RK == 64)
+    return launch_rk<64>(n, x, T, Zpart, S, PH, PL, do_fwht, packed, tiles, s_a, dbg, qmax, s);
   return hipErrorInvalidValue;
 }
 

@@ -22,7 +22,7 @@ def _declared():
 def test_library_built_and_loads():
     assert os.path.exists(rw.library_path), "build the HIP library first"
     L = rw.lib()
-    assert L.rw4_abi_version() == 9
+    assert L.rw4_abi_version() == 10
 
 
 def test_exports_every_declared_symbol():
@@ -276,7 +276,10 @@ def test_structured_transform_validation():
     assert _rl(D=28 * 16, ldx=28 * 16, flags=2 | (16 << 16), r=0) == UNS
     assert _rl(D=4096, ldx=4096, flags=H5 | 1, r=0) == INV
     assert _rl(D=4096, ldx=4096, flags=(15 << 24), r=0) == UNS
-    assert _rl(D=4096, ldx=4096, flags=(1 << 29), r=0) == INV   # unknown bit
+    assert _rl(D=4096, ldx=4096, flags=(1 << 30), r=0) == INV   # unknown bit
+    # packed INT4 weights: same workspace (packed codes fit the tile area)
+    assert (L.rotated_linear_prepared_workspace_size(64, 4096, 32, 3 | (1 << 29))
+            == L.rotated_linear_prepared_workspace_size(64, 4096, 32, 3))
 
 
 def test_construct_validation():

@@ -366,8 +366,12 @@ def _codes(seed, rows, K):
     return rng.integers(0, 256, (rows, K // 2), dtype=np.uint8)   # every byte is two valid codes
 
 
+# T <= 16 takes the weight-streaming decode kernel (K steps of 256 codes with
+# a partial last step, ragged N, fewer waves as the workgroups multiply)
 @pytest.mark.parametrize("T,K,N", [(1, 32, 1), (64, 256, 256), (300, 512, 384), (129, 4096, 130),
-                                   (17, 16384, 64), (8, 4096, 12288), (257, 96, 1000)])
+                                   (17, 16384, 64), (8, 4096, 12288), (257, 96, 1000),
+                                   (16, 96, 70), (9, 160, 33), (3, 32, 17), (8, 16384, 4096),
+                                   (16, 4096, 4100), (1, 4128, 9000), (8, 4096, 32768)])
 def test_w4a4_gemm(rw, T, K, N):
     say(f"w4a4_gemm T={T} K={K} N={N}")
     a = _codes(T + K, T, K)
@@ -550,8 +554,9 @@ def _check_unit(rw, xb, Q, M, flags, codes_w, s_w, qw, sw_h, rows=None):
     y, ws = rw.rotated_linear(dev(xb), codes_w, s_w, flags, dev(Q) if Q is not None else None,
                               dev(M) if M is not None else None, dbg_prequant=dbg)
     _sync()
-    tiles_g, sa_g = (host(v) for v in rw.workspace_views(ws, T, D))
-    codes_g = F.untile(tiles_g, T, D)
+    packed = bool(flags & rw.RW4_WPACKED)
+    codes_ws, sa_g = (host(v) for v in rw.workspace_views(ws, T, D, packed))
+    codes_g = O.unpack_int4(codes_ws) if packed else F.untile(codes_ws, T, D)
     pre = host(dbg)
     y = host(y)
     sel = np.arange(T) if rows is None else rows
@@ -685,6 +690,33 @@ def test_rotated_linear_without_dump(rw, T, flags, bits):
         tg, sg = (host(v) for v in rw.workspace_views(ws, T, D))
         np.testing.assert_array_equal(sg, sd)
         np.testing.assert_array_equal(F.untile(tg, T, D), F.untile(td, T, D))
+
+
+# Packed INT4 weight rows (RW4_WPACKED: the survey's weight layout, the decode
+# format): the activation codes are packed rows too and the product runs on the
+# packed-row GEMM (weight-streaming kernel for T <= 16). Every stage against
+# the oracle, and the outputs bit-identical to the FP6-tile path on the same
+# weight codes.
+@pytest.mark.parametrize("T,D,N,r,flags,bits", [
+    (8, 4096, 4096, 32, 3, 4), (77, 4096, 512, 32, 3, 4), (8, 16384, 64, 0, 6, 4),
+    (9, 8192, 64, 64, 3, 4), (13, 4096, 96, 32, 1, 3), (16, 640, 64, 16, 3 | (20 << 16), 4)])
+def test_rotated_linear_packed(rw, T, D, N, r, flags, bits):
+    say(f"rotated_linear packed weights T={T} D={D} N={N} r={r} flags={flags:#x} bits={bits}")
+    m = (flags >> 16) & 0xFF
+    width = 2 * D if flags & 4 else D
+    xb = W.gen_x(T + D + bits, T, width, 4, 30.0)
+    Q, M = W.gen_basis(T + r, D, r) if flags & 1 else (None, None)
+    Wf = W.gen_weight(N + D, N, D, 0.02)
+    tiles, s_w, codes, src = rw.prep_weight(dev(Wf), bool(flags & 2), bits, m if m else 1)
+    q_w, s_wh = O.quant_sym(host(src), bits)
+    np.testing.assert_array_equal(host(codes), O.pack_int4(q_w))
+    np.testing.assert_array_equal(host(s_w), s_wh)
+    fl = flags | rw.RW4_ABITS(bits)
+    y_p = _check_unit(rw, xb, Q, M, fl | rw.RW4_WPACKED, codes, s_w, q_w, s_wh)
+    y_t, _ = rw.rotated_linear(dev(xb), tiles, s_w, fl, dev(Q) if r else None,
+                               dev(M) if r else None)
+    _sync()
+    np.testing.assert_array_equal(y_p, host(y_t))
 
 
 # lower code widths [RSQ 实验: W3A3]: 3-bit weights and activations through the
@@ -843,24 +875,24 @@ def test_empty_batches(rw):
 
 
 # ---------------------------------------------------------------- decoder layer
-def _layer_check(rw, cid):
+def _layer_check(rw, cid, packed=False):
     wl = W.CONFIGS[cid]
-    say(f"layer {wl.name}")
+    say(f"layer {wl.name} packed={packed}")
     t = torch()
     D, T, F_ = wl.D, wl.T, wl.ffn
     inp = W.workload_inputs(wl)
     weights, qws, sws = {}, {}, {}
     for lin in wl.linears:
         tl, s, c, src = rw.prep_weight(dev(inp["W"][lin.name]), lin.rotate)
-        weights[lin.name] = (tl, s)
+        weights[lin.name] = (c if packed else tl, s)
         qws[lin.name] = O.unpack_int4(host(c))
         sws[lin.name] = host(s)
         del src, c
     aligns = [(rw.respin_prepare_basis(dev(Q), dev(M)), Q.shape[1]) for Q, M in inp["basis"]]
     dbg = t.empty((T, F_), dtype=t.float32, device="cuda")
-    st = rw.layer(dev(inp["x"]), aligns, weights, D, dbg_down=dbg)
+    st = rw.layer(dev(inp["x"]), aligns, weights, D, dbg_down=dbg, packed=packed)
     _sync()
-    down_tiles, down_sa = (host(v) for v in rw.workspace_views(st.pop("down_ws"), T, F_))
+    down_codes, down_sa = (host(v) for v in rw.workspace_views(st.pop("down_ws"), T, F_, packed))
     g = {k: host(v) for k, v in st.items()}
     pre_down = host(dbg)
     del st, dbg
@@ -890,12 +922,13 @@ def _layer_check(rw, cid):
     del ref_pre
     q, s = O.quant_int4(pre_down)
     np.testing.assert_array_equal(down_sa, s)
-    np.testing.assert_array_equal(F.untile(down_tiles, T, F_), q)
+    np.testing.assert_array_equal(O.unpack_int4(down_codes) if packed else F.untile(down_codes, T, F_), q)
     _check_gemm_out(g["down"], q, s, qws["down"], sws["down"])
 
 
-def test_layer_decode_config2(rw):
-    _layer_check(rw, 2)
+@pytest.mark.parametrize("packed", [False, True])
+def test_layer_decode_config2(rw, packed):
+    _layer_check(rw, 2, packed)
 
 
 @pytest.mark.timeout(900)
