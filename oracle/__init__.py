@@ -28,10 +28,11 @@ the code it shapes.
 Pins: every function below is pinned by ``tests/test_oracle_pins.py`` against
 something other than itself (worked example, closed forms, library routines,
 invariants, brute force); ``residual`` against the dense T_hat and a case that
-tells one bf16 rounding from two.  ``silu_gate`` is pinned only by closed-form
-identities of SiLU; the pages give no SiLU value ("parity unpinned" against
-the pages).  A decoder layer is not an oracle function: the layer tests feed
-each oracle stage the GPU's own previous stage.
+tells one bf16 rounding from two.  The pages give no SiLU value; ``silu_gate``
+is pinned against SciPy's logistic function (``scipy.special.expit``, a
+library routine) and the closed forms SiLU(0) = 0 and SiLU(g) - SiLU(-g) = g.
+A decoder layer is not an oracle function: the layer tests feed each oracle
+stage the GPU's own previous stage.
 """
 from __future__ import annotations
 
