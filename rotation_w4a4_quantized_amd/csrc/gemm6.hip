@@ -32,6 +32,8 @@
 // In both, workgroups are renumbered so that each XCD works on a contiguous
 // band of weight tiles, and the bf16 epilogue is staged in LDS so that rows
 // are written with 16-byte stores.
+#include <atomic>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -207,9 +209,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane(
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_cptr)p)));
 }
-// 16 bytes per lane: lds + 16 lane <- g (per-lane address)
-__device__ __forceinline__ void lds_copy16(const void* g, const void* lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr(lds))
+// 16 bytes per lane: lds + 16 lane <- base + off (wave-uniform base, per-lane
+// 32-bit offset)
+__device__ __forceinline__ void lds_copy16(const void* base, uint32_t off, const void* lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
+               "s"(lds_addr(lds))
                : "memory");
 }
 // 4 bytes per lane: lds + 4 lane <- g (per-lane address)
@@ -254,7 +258,8 @@ gemm6_lds_kernel(const uint8_t* __restrict__ at, const float* __restrict__ s_a,
   __shared__ __attribute__((aligned(16))) uint8_t L3[S > 3 ? STAGE : 16];
   __shared__ __attribute__((aligned(16))) float sc[I32OUT ? 4 : TW + TT];  // s_w block | s_a block
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ww = wave % WW, wq = wave / WW;
   const int nwt = (N + TW - 1) / TW, ntt = (T + TT - 1) / TT, nb = nwt * ntt;
   // Workgroups are dispatched to the 8 XCDs round robin (b mod 8). With rt > 0
@@ -280,23 +285,28 @@ gemm6_lds_kernel(const uint8_t* __restrict__ at, const float* __restrict__ s_a,
   // Copy i of a stage moves bytes [1024 i, 1024 i + 1024) of the stage: row
   // block i / 3, third i % 3 of its two consecutive k-tiles (3072 contiguous
   // bytes in the tile layout). The stage buffer keeps that order.
-  const uint8_t* src[LPW];
+  // The copies address the block's first W and A rows (wave-uniform bases) plus
+  // a per-lane 32-bit offset: at most 8 row blocks of K / 64 tiles, which for
+  // K <= 131072 stays below 2^25.
+  const uint8_t* const wb = wt + static_cast<int64_t>(n0 >> 5) * KT * kTileBytes;
+  const uint8_t* const ab = at + static_cast<int64_t>(t0 >> 5) * KT * kTileBytes;
+  bool isw[LPW];
+  uint32_t src[LPW];
   int dst[LPW];
 #pragma unroll
   for (int m = 0; m < LPW; ++m) {
     int i = wave + NW * m;
     if (i >= NI) i -= NW;
     const int rb = i / 3;
-    const uint8_t* row = rb < WW * FW
-        ? wt + static_cast<int64_t>((n0 >> 5) + rb) * KT * kTileBytes
-        : at + static_cast<int64_t>((t0 >> 5) + rb - WW * FW) * KT * kTileBytes;
-    src[m] = row + (i % 3) * 1024 + lane * 16;
+    isw[m] = rb < WW * FW;
+    src[m] = static_cast<uint32_t>(isw[m] ? rb : rb - WW * FW) * KT * kTileBytes +
+             (i % 3) * 1024 + lane * 16;
     dst[m] = i * 1024;
   }
   auto fetch = [&](uint8_t* L, int st) {
+    const int64_t so = static_cast<int64_t>(st) * (2 * kTileBytes);
 #pragma unroll
-    for (int m = 0; m < LPW; ++m)
-      lds_copy16(src[m] + static_cast<int64_t>(st) * (2 * kTileBytes), L + dst[m]);
+    for (int m = 0; m < LPW; ++m) lds_copy16(isw[m] ? wb + so : ab + so, src[m], L + dst[m]);
   };
   // the block's scales go first, so the first stage wait covers them
   if constexpr (!I32OUT) {
@@ -631,6 +641,22 @@ hipError_t launch_cfg(const uint8_t* a, const float* s_a, const uint8_t* w, cons
   return hipGetLastError();
 }
 
+// compute units of the current device (256 on MI355X), read once per device
+inline int device_cus() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cache[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 // rt for gemm6_lds_kernel: the split of the tile grid into 8 XCD rectangles
 // (rt along T, 8 / rt along N) with the fewest A and W rows per XCD, or 0
 // when no split divides the grid evenly
@@ -682,17 +708,27 @@ hipError_t launch_gemm_tiles(const uint8_t* a, const float* s_a, const uint8_t* 
                              int64_t N, hipStream_t s) {
   if (T == 0 || N == 0) return hipSuccess;
   if (K % 128 == 0 && T >= 128) {
-    // 256 x 128 blocks of eight waves for large products (one workgroup per
-    // CU, three quarters of the L2-to-CU operand traffic of 128 x 128
-    // blocks), 128 x 128 blocks of four waves (two workgroups per CU)
-    // otherwise. (256 x 256 blocks halve the traffic but leave half of the
-    // CUs idle at T = 2048: 37.9 us against 28.4.)
+    // Eight-wave blocks of 256 x 256 or 256 x 128 outputs (one workgroup per
+    // CU) for large products, four-wave 128 x 128 blocks (two per CU)
+    // otherwise. A 256 x 256 block moves two thirds of the operand bytes per
+    // MFMA of a 256 x 128 one, and a full wave of them (one per CU) takes
+    // about 16/9 of the time of a full wave of 256 x 128 blocks (K = 4096:
+    // 48.4 us against 27.2); the shape with fewer such weighted waves is
+    // taken, which picks 256 x 128 for 2048 x 4096 outputs (one wave against
+    // one of 256 x 256 blocks on half the CUs) and 256 x 256 from 3072 x 4096
+    // or 2048 x 8192 up.
     const bool big = T >= 2048 && N >= 4096;
+    const int64_t cus = g6::device_cus();
+    const int64_t w2 = ((T + 255) / 256 * ((N + 255) / 256) + cus - 1) / cus;
+    const int64_t w1 = ((T + 255) / 256 * ((N + 127) / 128) + cus - 1) / cus;
+    const bool huge = big && 16 * w2 < 9 * w1;
     if (i32_out)
-      return big ? g6::launch_lds<2, 2, 4, 2, 3, true>(a, s_a, w, s_w, y, T, K, N, s)
-                 : g6::launch_lds<2, 2, 2, 2, 3, true>(a, s_a, w, s_w, y, T, K, N, s);
-    return big ? g6::launch_lds<2, 2, 4, 2, 3, false>(a, s_a, w, s_w, y, T, K, N, s)
-               : g6::launch_lds<2, 2, 2, 2, 3, false>(a, s_a, w, s_w, y, T, K, N, s);
+      return huge  ? g6::launch_lds<2, 4, 4, 2, 3, true>(a, s_a, w, s_w, y, T, K, N, s)
+             : big ? g6::launch_lds<2, 2, 4, 2, 3, true>(a, s_a, w, s_w, y, T, K, N, s)
+                   : g6::launch_lds<2, 2, 2, 2, 3, true>(a, s_a, w, s_w, y, T, K, N, s);
+    return huge  ? g6::launch_lds<2, 4, 4, 2, 3, false>(a, s_a, w, s_w, y, T, K, N, s)
+           : big ? g6::launch_lds<2, 2, 4, 2, 3, false>(a, s_a, w, s_w, y, T, K, N, s)
+                 : g6::launch_lds<2, 2, 2, 2, 3, false>(a, s_a, w, s_w, y, T, K, N, s);
   }
   // decode products: up to 16 tokens and N <= 16384 on 16-row workgroups,
   // with fewer waves per workgroup as their number grows (measured at T = 8:

@@ -478,7 +478,11 @@ def test_tile_codes_rejects_minus8(rw):
                                    # (rt along T = 1, 8, 4, 2 with ragged edges; 4 on
                                    # the large-block variant)
                                    (256, 384, 1024), (1024, 256, 128), (1024, 640, 256),
-                                   (1000, 640, 1000), (8192, 256, 4096)])
+                                   (1000, 640, 1000), (8192, 256, 4096),
+                                   # 256 x 256 blocks (chosen where they take fewer
+                                   # weighted waves): ragged T and N, an even XCD split,
+                                   # a grid no split divides
+                                   (3000, 512, 4100), (2048, 384, 8192), (2304, 256, 5000)])
 def test_w4a4_gemm_tiles(rw, T, K, N):
     say(f"w4a4_gemm_tiles T={T} K={K} N={N}")
     a, qa = _codes7(T + K, T, K)
