@@ -285,65 +285,91 @@ gemm_kernel(const uint8_t* __restrict__ a, const float* __restrict__ s_a,
 // Decode products (T <= 16 tokens): the weights stream once from HBM as packed
 // INT4 rows (0.5 bytes per code), so the kernel is bound by that stream. A
 // workgroup owns 16 weight rows; its NWV waves split K into steps of 256 codes
-// (128 bytes of every row, whole cache lines) and take steps w, w + NWV, ...
-// Lane l holds row l % 16 and the 32-byte quarter l / 16 of each 128-byte
-// step as two 16-byte loads, PD steps in flight. Each 16-byte load widens
+// (128 bytes of every row, whole cache lines), wave w taking steps w, w + NWV,
+// ..., and issues the loads of SPW of its steps at once (a round), none past
+// the end of K. Lane l holds row l % 16 and the 32-byte quarter l / 16 of each
+// step as two 16-byte loads. When the T activation rows fit (ALDS bytes), the
+// workgroup copies them into LDS once, while its first weight round is in
+// flight, instead of every wave loading them from L2 for every step (measured
+// at T = 8, 4096 -> 32768: 15.0 against 20.1 us). Each 16-byte load widens
 // (16 * code, as above) into the operands of two v_mfma_i32_16x16x64_i8 with
 // weight rows as the A operand and tokens as the B operand; token rows past T
-// load nothing and hold zero. The waves' partial sums (all of the form 256 S,
-// added modulo 2^32) are summed through LDS in wave order, then unscaled.
+// hold zero. The waves' partial sums (all of the form 256 S, added modulo 2^32)
+// are summed through LDS in wave order, then unscaled.
 constexpr int kDecRows = 16;
+constexpr int kDecLds = 32768;  // activation bytes (T * K / 2) staged in LDS at most
 
-template <int NWV, int PD, bool I32OUT>
+template <int NWV, int SPW, bool ALDS, bool I32OUT>
 __global__ void __launch_bounds__(64 * NWV)
 gemm_decode_kernel(const uint8_t* __restrict__ a, const float* __restrict__ s_a,
                    const uint8_t* __restrict__ w, const float* __restrict__ s_w,
                    void* __restrict__ y, int T, int K, int N) {
   __shared__ uint32_t red[NWV][4][64];
+  __shared__ __attribute__((aligned(16))) uint8_t al[ALDS ? kDecLds : 16];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n0 = blockIdx.x * kDecRows;
   const int KB = K / 2;                       // bytes per row
   const int nstep = (KB + 127) / 128;         // 128-byte steps (the last may be partial)
   const int i = lane & 15, g = lane >> 4;
-  // rows past N re-read the last row (their sums are never stored); tokens past
-  // T load nothing
+  // rows past N re-read the last row (their sums are never stored); token rows
+  // past T read the last token and are zeroed
   const uint8_t* wrow = w + static_cast<int64_t>(min(n0 + i, N - 1)) * KB;
-  const uint8_t* arow = a + static_cast<int64_t>(min(i, T - 1)) * KB;
-  const bool tok = i < T;
-  v4i acc = {0, 0, 0, 0};
-  uint4 wv[PD][2], av[PD][2];
-  // all loads unconditional: quarters past the end of K read the row's first
-  // 16 bytes (K >= 32) and are masked to zero
-  auto load = [&](int u, int st) {
+  const int arow = min(i, T - 1) * KB;
+  const uint32_t mtok = i < T ? 0xFFFFFFFFu : 0u;
+  uint4 wv[SPW][2];
+  // lane's 16 bytes of step st, half h; quarters past the end of K read the
+  // row's first 16 bytes (K >= 32) and are masked to zero
+  auto offs = [&](int st, int h, uint32_t& m) {
+    const int off = st * 128 + 64 * h + 16 * g;
+    const bool ok = off + 16 <= KB;
+    m = ok ? 0xFFFFFFFFu : 0u;
+    return ok ? off : 0;
+  };
+  auto load = [&](int s0) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int off = st * 128 + 64 * h + 16 * g;  // this lane's 16 bytes of the row
-      const bool ok = st < nstep && off + 16 <= KB;
-      const int o = ok ? off : 0;                   // masked: the row's first 16 bytes
-      uint4 vw = *reinterpret_cast<const uint4*>(wrow + o);
-      uint4 va = *reinterpret_cast<const uint4*>(arow + o);
-      const uint32_t mw = ok ? 0xFFFFFFFFu : 0u;
-      const uint32_t ma = ok && tok ? 0xFFFFFFFFu : 0u;
-      vw.x &= mw; vw.y &= mw; vw.z &= mw; vw.w &= mw;
-      va.x &= ma; va.y &= ma; va.z &= ma; va.w &= ma;
-      wv[u][h] = vw;
-      av[u][h] = va;
+    for (int u = 0; u < SPW; ++u) {
+      const int st = s0 + wave + NWV * u;
+      if (st < nstep) {  // uniform
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          uint32_t m;
+          const int o = offs(st, h, m);
+          wv[u][h] = *reinterpret_cast<const uint4*>(wrow + o);
+        }
+      }
     }
   };
+  load(0);
+  if constexpr (ALDS) {
+    const int nbytes = T * KB;  // a multiple of 16 (K % 32 == 0)
+    for (int o = threadIdx.x * 16; o < nbytes; o += 64 * NWV * 16)
+      *reinterpret_cast<uint4*>(al + o) = *reinterpret_cast<const uint4*>(a + o);
+    __syncthreads();
+  }
+  v4i acc = {0, 0, 0, 0};
+  for (int s0 = 0; s0 < nstep; s0 += NWV * SPW) {
+    if (s0 > 0) load(s0);
 #pragma unroll
-  for (int u = 0; u < PD; ++u) load(u, wave + NWV * u);
-  for (int st0 = wave; st0 < nstep; st0 += NWV * PD) {
+    for (int u = 0; u < SPW; ++u) {
+      const int st = s0 + wave + NWV * u;
+      if (st < nstep) {
 #pragma unroll
-    for (int u = 0; u < PD; ++u) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        v4i w0, w1, a0, a1;
-        widen(wv[u][h], w0, w1);
-        widen(av[u][h], a0, a1);
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(w0, a0, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(w1, a1, acc, 0, 0, 0);
+        for (int h = 0; h < 2; ++h) {
+          uint32_t m;
+          const int o = offs(st, h, m);
+          uint4 va = ALDS ? *reinterpret_cast<const uint4*>(al + arow + o)
+                          : *reinterpret_cast<const uint4*>(a + arow + o);
+          uint4 vw = wv[u][h];
+          const uint32_t ma = m & mtok;
+          vw.x &= m; vw.y &= m; vw.z &= m; vw.w &= m;
+          va.x &= ma; va.y &= ma; va.z &= ma; va.w &= ma;
+          v4i w0, w1, a0, a1;
+          widen(vw, w0, w1);
+          widen(va, a0, a1);
+          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(w0, a0, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(w1, a1, acc, 0, 0, 0);
+        }
       }
-      load(u, st0 + NWV * (u + PD));          // steps past the end load masked zeros
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -370,20 +396,22 @@ gemm_decode_kernel(const uint8_t* __restrict__ a, const float* __restrict__ s_a,
   }
 }
 
-template <int NWV, int PD>
+template <int NWV, int SPW>
 hipError_t launch_decode(const uint8_t* a, const float* s_a, const uint8_t* w, const float* s_w,
                          void* y, bool i32_out, int64_t T, int64_t K, int64_t N, hipStream_t s) {
   const int64_t nb = (N + kDecRows - 1) / kDecRows;
   if (nb > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  if (i32_out)
-    hipLaunchKernelGGL((gemm_decode_kernel<NWV, PD, true>), dim3(static_cast<unsigned>(nb)),
-                       dim3(64 * NWV), 0, s, a, s_a, w, s_w, y, static_cast<int>(T),
-                       static_cast<int>(K), static_cast<int>(N));
-  else
-    hipLaunchKernelGGL((gemm_decode_kernel<NWV, PD, false>), dim3(static_cast<unsigned>(nb)),
-                       dim3(64 * NWV), 0, s, a, s_a, w, s_w, y, static_cast<int>(T),
-                       static_cast<int>(K), static_cast<int>(N));
-  return hipGetLastError();
+  const bool alds = T * (K / 2) <= kDecLds;
+#define RW4_DEC(AL, I)                                                                           \
+  if (alds == AL && i32_out == I) {                                                              \
+    hipLaunchKernelGGL((gemm_decode_kernel<NWV, SPW, AL, I>), dim3(static_cast<unsigned>(nb)),    \
+                       dim3(64 * NWV), 0, s, a, s_a, w, s_w, y, static_cast<int>(T),             \
+                       static_cast<int>(K), static_cast<int>(N));                                \
+    return hipGetLastError();                                                                    \
+  }
+  RW4_DEC(true, false) RW4_DEC(true, true) RW4_DEC(false, false) RW4_DEC(false, true)
+#undef RW4_DEC
+  return hipErrorInvalidValue;
 }
 
 template <int NWW, int NWT, int BW, int BT>
@@ -408,15 +436,15 @@ hipError_t launch_gemm(const uint8_t* a, const float* s_a, const uint8_t* w, con
                        void* y, bool i32_out, int64_t T, int64_t K, int64_t N, hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (T <= gemm::kDecRows) {
-    // weight streaming: fewer waves per workgroup as the workgroups multiply.
-    // Measured at T = 8 (weights rotated past the last-level cache): 16 waves
-    // with one step in flight for up to 256 workgroups (4096 x 4096: 4.2 us;
-    // 16384 x 4096: 10.1 us), 4 waves with two in flight beyond (4096 x 12288:
-    // 8.8 us; 4096 x 32768: 20.5 us); more steps in flight were slower.
+    // weight streaming. Measured at T = 8 (weights rotated past the last-level
+    // cache): up to 256 workgroups (N <= 4096), 16 waves with one step each
+    // per round (4096 x 4096: 4.0 us); K beyond 4096 codes, 16 waves with four
+    // steps each (16384 x 4096: 9.8 us); otherwise 8 waves with two steps each
+    // (4096 x 12288: 7.7 us; 4096 x 32768: 15.0 us).
     const int64_t nb = (N + gemm::kDecRows - 1) / gemm::kDecRows;
+    if (K > 4096) return gemm::launch_decode<16, 4>(a, s_a, w, s_w, y, i32_out, T, K, N, s);
     if (nb <= 256) return gemm::launch_decode<16, 1>(a, s_a, w, s_w, y, i32_out, T, K, N, s);
-    if (nb <= 512) return gemm::launch_decode<8, 2>(a, s_a, w, s_w, y, i32_out, T, K, N, s);
-    return gemm::launch_decode<4, 2>(a, s_a, w, s_w, y, i32_out, T, K, N, s);
+    return gemm::launch_decode<8, 2>(a, s_a, w, s_w, y, i32_out, T, K, N, s);
   }
   return gemm::launch_cfg<2, 2, 2, 2>(a, s_a, w, s_w, y, i32_out, T, K, N, s);
 }
