@@ -243,6 +243,10 @@ yproj_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int r,
         bl[u][c][1] = ld8(QtL + qo + 8);
       }
     }
+    // every load of the batch (and, in the first, of x) is issued before the
+    // first product: left alone, the scheduler interleaves them with the
+    // MFMAs to save registers and the wave waits for memory once per pair
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < DPW; ++u)
 #pragma unroll
@@ -323,10 +327,25 @@ lift_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int S, int 
 
   // 1. every load of the lift, issued up front and unconditional (a wave past
   // the part's end re-reads its last double step and stores nothing; tokens
-  // past T re-read the last token). Block b of the double step covers columns
-  // 16g + 4b + v for lane group g, so A's row i = 4g' + v of block b is column
-  // 16g' + 4b + v. Each thread also fetches 4 consecutive z entries of every
-  // D part (TPW * RK / 4 float4 chunks over the workgroup).
+  // past T re-read the last token). With one z chunk per thread (RK = 32),
+  // each thread fetches 4 consecutive z entries of the first eight D parts
+  // (TPW * RK / 4 float4 chunks over the workgroup) first, then its Q and x. Block b of the double step covers
+  // columns 16g + 4b + v for lane group g, so A's row i = 4g' + v of block b is
+  // column 16g' + 4b + v.
+  constexpr int ZC = TPW * RK / 4;                     // float4 chunks of z
+  constexpr int ZPT = (ZC + NT - 1) / NT;              // chunks per thread
+  // with more than one chunk per thread the early z loads cost more registers
+  // than the round trip they save (the compiler then serializes single loads)
+  constexpr bool ZPRE = ZPT == 1;
+  float4 zp0[8];
+  if constexpr (ZPRE) {
+    const int c = min(tid, ZC - 1);
+    const int64_t trow = min(t0 + (4 * c) / RK, T - 1);
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      zp0[q] = *reinterpret_cast<const float4*>(
+          Zpart + (static_cast<int64_t>(min(q, S - 1)) * T + trow) * RK + (4 * c) % RK);
+  }
   v8bf qh[4][KQ], ql[4][KQ];
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
@@ -346,16 +365,28 @@ lift_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int S, int 
     xv[tb][0] = px[0];
     xv[tb][1] = px[1];
   }
+  // the scheduler keeps every load above ahead of the first use (left alone,
+  // it waits for the Q and x loads before issuing the z loads)
+  if constexpr (ZPRE) __builtin_amdgcn_sched_barrier(0);
   // 2. z = sum over D parts (fixed order), its bf16 split into LDS
-  constexpr int ZC = TPW * RK / 4;                     // float4 chunks of z
-  for (int c = tid; c < ZC; c += NT) {
+#pragma unroll
+  for (int u = 0; u < ZPT; ++u) {
+    const int c = tid + u * NT;
+    if (c >= ZC) break;
     const int tt = (4 * c) / RK;
     const int i = (4 * c) % RK;
     const int64_t trow = min(t0 + tt, T - 1);
-    // the parts in blocks of 8, each block's loads issued together
-    // (unconditional, clamped, masked) and added in part order
+    // the parts in blocks of 8 (the first loaded above), each block's loads
+    // issued together (unconditional, clamped, masked) and added in part order
     float4 z = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    for (int p0 = 0; p0 < S; p0 += 8) {
+    if constexpr (ZPRE) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (q < S) {
+          z.x += zp0[q].x; z.y += zp0[q].y; z.z += zp0[q].z; z.w += zp0[q].w;
+        }
+    }
+    for (int p0 = ZPRE ? 8 : 0; p0 < S; p0 += 8) {
       float4 zp[8];
 #pragma unroll
       for (int q = 0; q < 8; ++q)
