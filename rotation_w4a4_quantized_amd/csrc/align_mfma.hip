@@ -518,27 +518,32 @@ asmall_proj_kernel(const uint16_t* __restrict__ x, int T, int D, int RP, int RK,
   // thread tid stages column d0 + tid of every token; the loads are
   // unconditional (clamped token and column, masked values), so that they
   // are all in flight before the first use
-  uint16_t xr[kSmallT];
-#pragma unroll
-  for (int t = 0; t < kSmallT; ++t) xr[t] = x[static_cast<int64_t>(min(t, T - 1)) * D + dc];
-  float xv[kSmallT];
-#pragma unroll
-  for (int t = 0; t < kSmallT; ++t) xv[t] = col && t < T ? bf16_to_f32(xr[t]) : 0.0f;
-#pragma unroll
-  for (int t = 0; t < kSmallT; ++t) xs[t][tid] = xv[t];
-  for (int i0 = 0; i0 < RK; i0 += 32) {
-    // rows i0 .. i0 + 31 of Q' for this chunk, one column per thread
-    uint16_t hr[32], lr[32];
+  // rows i0 .. i0 + 31 of Q' for this chunk, one column per thread; the first
+  // block's loads go out ahead of x's, so that the thread waits for memory once
+  uint16_t hr[32], lr[32];
+  auto loadq = [&](int i0) {
 #pragma unroll
     for (int k = 0; k < 32; ++k) {
       const int64_t o = static_cast<int64_t>(min(i0 + k, RP - 1)) * D + dc;
       hr[k] = QtH[o];
       lr[k] = QtL[o];
     }
+  };
+  loadq(0);
+  uint16_t xr[kSmallT];
+#pragma unroll
+  for (int t = 0; t < kSmallT; ++t) xr[t] = x[static_cast<int64_t>(min(t, T - 1)) * D + dc];
+  for (int i0 = 0; i0 < RK; i0 += 32) {
+    if (i0 > 0) loadq(i0);
     float qv[32];
 #pragma unroll
     for (int k = 0; k < 32; ++k)
       qv[k] = col && i0 + k < RP ? bf16_to_f32(hr[k]) + bf16_to_f32(lr[k]) : 0.0f;
+    if (i0 == 0) {
+      // x goes to LDS only now, so that no use of it comes before the Q' loads
+#pragma unroll
+      for (int t = 0; t < kSmallT; ++t) xs[t][tid] = col && t < T ? bf16_to_f32(xr[t]) : 0.0f;
+    }
     __syncthreads();                                 // previous block's readers are done
 #pragma unroll
     for (int k = 0; k < 32; ++k) qs[k][tid] = qv[k];
@@ -568,6 +573,38 @@ asmall_lift_kernel(const uint16_t* __restrict__ x, int T, int D, int RK, int C,
                    void* __restrict__ out) {
   __shared__ float zs[kSmallT][kPrepRmax + 1];
   const int tid = threadIdx.x;
+  constexpr int TPT = (kSmallT + 256 / kSmallLift - 1) / (256 / kSmallLift);  // tokens per thread
+  const int tt0 = tid / kSmallLift;
+  // the thread's column of x (and of the addend) for its tokens, loaded first
+  // (unconditional: clamped token and column, unused past T), so that these
+  // loads overlap the z loads instead of following the stores one by one
+  const int dl = min(blockIdx.x * kSmallLift + (tid & (kSmallLift - 1)), D - 1);
+  uint16_t xr[TPT];
+  float ar[TPT];
+#pragma unroll
+  for (int u = 0; u < TPT; ++u) {
+    const int64_t off = static_cast<int64_t>(min(tt0 + u * (256 / kSmallLift), T - 1)) * D + dl;
+    xr[u] = x[off];
+    if constexpr (ADD) {
+      if constexpr (OF32) ar[u] = static_cast<const float*>(addend)[off];
+      else ar[u] = bf16_to_f32(static_cast<const uint16_t*>(addend)[off]);
+    } else {
+      ar[u] = 0.0f;
+    }
+  }
+  // the first 32 values of the thread's row of Q (RK is a multiple of 32), also
+  // independent of z
+  const uint4* qh = reinterpret_cast<const uint4*>(QH + static_cast<int64_t>(dl) * RK);
+  const uint4* ql = reinterpret_cast<const uint4*>(QL + static_cast<int64_t>(dl) * RK);
+  uint4 hv[4], lv[4];
+  auto loadrow = [&](int i0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      hv[j] = qh[i0 / 8 + j];
+      lv[j] = ql[i0 / 8 + j];
+    }
+  };
+  loadrow(0);
   // z: every partial of a thread's entries loaded at once, summed in chunk order
   for (int o = tid; o < T * RK; o += 256) {
     const int t = o / RK, i = o % RK;
@@ -585,21 +622,12 @@ asmall_lift_kernel(const uint16_t* __restrict__ x, int T, int D, int RK, int C,
   __syncthreads();
   const int d = blockIdx.x * kSmallLift + (tid & (kSmallLift - 1));
   if (d >= D) return;
-  // the thread's row of Q in blocks of 32 values (RK is a multiple of 32)
-  const uint4* qh = reinterpret_cast<const uint4*>(QH + static_cast<int64_t>(d) * RK);
-  const uint4* ql = reinterpret_cast<const uint4*>(QL + static_cast<int64_t>(d) * RK);
-  constexpr int TPT = (kSmallT + 256 / kSmallLift - 1) / (256 / kSmallLift);  // tokens per thread
-  const int tt0 = tid / kSmallLift;
+  // the thread's row of Q in blocks of 32 values
   float corr[TPT];
 #pragma unroll
   for (int u = 0; u < TPT; ++u) corr[u] = 0.0f;
   for (int i0 = 0; i0 < RK; i0 += 32) {
-    uint4 hv[4], lv[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      hv[j] = qh[i0 / 8 + j];
-      lv[j] = ql[i0 / 8 + j];
-    }
+    if (i0 > 0) loadrow(i0);
     float q[32];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -623,14 +651,8 @@ asmall_lift_kernel(const uint16_t* __restrict__ x, int T, int D, int RK, int C,
     const int t = tt0 + u * (256 / kSmallLift);
     if (t >= T) break;
     const int64_t off = static_cast<int64_t>(t) * D + d;
-    const float xv = bf16_to_f32(x[off]);
-    float av = 0.0f;
-    if constexpr (ADD) {
-      if constexpr (OF32) av = static_cast<const float*>(addend)[off];
-      else av = bf16_to_f32(static_cast<const uint16_t*>(addend)[off]);
-    }
-    float acc = xv + corr[u];
-    if constexpr (ADD) acc += av;
+    float acc = bf16_to_f32(xr[u]) + corr[u];
+    if constexpr (ADD) acc += ar[u];
     if constexpr (OF32) static_cast<float*>(out)[off] = acc;
     else static_cast<uint16_t*>(out)[off] = f32_to_bf16(acc);
   }
