@@ -147,7 +147,7 @@ __device__ __forceinline__ void unpack4(float (&q)[4], const Raw4<IN>& r, bool u
     if constexpr (IN == IN_SWIGLU) {
       const float u[4] = {bf16lo(r.a.z), bf16hi(r.a.z), bf16lo(r.a.w), bf16hi(r.a.w)};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) q[e] = q[e] / (1.0f + expf(-q[e])) * u[e];
+      for (int e = 0; e < 4; ++e) q[e] = silu_mul(q[e], u[e]);
     }
   }
   if (use_signs) {

@@ -166,7 +166,7 @@ __device__ __forceinline__ void load_row_raw(float (&v)[EPT], const void* x, int
         for (int i = 0; i < EPT; ++i) u[i] = bf16_to_f32(pu[i]);
       }
 #pragma unroll
-      for (int i = 0; i < EPT; ++i) v[i] = g[i] / (1.0f + expf(-g[i])) * u[i];
+      for (int i = 0; i < EPT; ++i) v[i] = silu_mul(g[i], u[i]);
     } else {
 #pragma unroll
       for (int i = 0; i < EPT; ++i) v[i] = g[i];
@@ -353,7 +353,7 @@ __device__ __forceinline__ void load_group(float (&q)[G], const void* x, int64_t
       float u[G];
       unpack(p + D, u);
 #pragma unroll
-      for (int i = 0; i < G; ++i) q[i] = q[i] / (1.0f + expf(-q[i])) * u[i];
+      for (int i = 0; i < G; ++i) q[i] = silu_mul(q[i], u[i]);
     }
   }
 }
