@@ -31,16 +31,24 @@ def _operands(rw, T, D, N, r, flags, key):
     return xb, tiles, s_w, codes, basis, Q, M
 
 
+PK = 1 << 29  # RW4_WPACKED: packed INT4 weight rows (the decode format)
+
+
 # two calls in a row on one GPU, the second smaller than the first (the scratch
 # keeps the first call's contents), then a third on the unfused alignment path
-# and a gated one
+# and a gated one; and the decode shapes on packed INT4 weight rows
 @pytest.mark.parametrize("seq", [((2048, 4096, 4096, 32, 3), (77, 4096, 512, 32, 3),
-                                  (9, 8192, 256, 64, 3), (300, 16384, 128, 0, 6))])
+                                  (9, 8192, 256, 64, 3), (300, 16384, 128, 0, 6)),
+                                 ((8, 4096, 12288, 32, 3 | PK), (3, 4096, 640, 32, 3 | PK),
+                                  (8, 16384, 4096, 0, 6 | PK))])
 def test_noalloc_matches_workspace_entry(rw, seq):
     t = torch()
     for i, (T, D, N, r, flags) in enumerate(seq):
         say(f"noalloc call {i}: T={T} D={D} N={N} r={r} flags={flags}")
         xb, tiles, s_w, codes, basis, Q, M = _operands(rw, T, D, N, r, flags, 100 + i)
+        packed = bool(flags & PK)
+        if packed:
+            tiles = codes  # the weight operand of the call
         x = dev(xb)
         d_ref = t.empty((T, D), dtype=t.float32, device="cuda")
         y_ref, ws = rw.rotated_linear_prepared(x, tiles, s_w, flags, basis, r, dbg_prequant=d_ref)
@@ -59,9 +67,9 @@ def test_noalloc_matches_workspace_entry(rw, seq):
         ref_pre = O.prequant(O.bf16_to_f64(xb), flags, Q, M)
         assert normwise(pre, ref_pre) <= FP32_TOL
         q, s = O.quant_int4(pre)
-        tiles_a, s_a = (host(v) for v in rw.workspace_views(ws, T, D))
+        acts, s_a = (host(v) for v in rw.workspace_views(ws, T, D, packed))
         np.testing.assert_array_equal(s_a, s)
-        np.testing.assert_array_equal(F.untile(tiles_a, T, D), q)
+        np.testing.assert_array_equal(O.unpack_int4(acts) if packed else F.untile(acts, T, D), q)
         nbad, worst = bf16_rel(host(y_na), O.epilogue(O.gemm_int(q, O.unpack_int4(host(codes))),
                                                       s, host(s_w)))
         assert nbad == 0, worst
