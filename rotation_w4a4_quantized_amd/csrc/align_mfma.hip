@@ -200,7 +200,9 @@ yproj_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int r,
   const int nds = (dend - dbeg) / 64;                 // whole double steps in this part
   const int g = lane >> 4;
   const int tl = lane & 15;
-  constexpr int NBC = (RP / 16) % 2 == 0 ? 2 : 1;     // basis blocks per load batch (divides RP/16)
+  // basis blocks per load batch (divides RP/16): all of them up to RP = 64, so
+  // that the whole projection waits for memory once
+  constexpr int NBC = RP <= 64 ? RP / 16 : ((RP / 16) % 2 == 0 ? 2 : 1);
 
   // loads are unconditional: double steps past the part's end re-read its last
   // one and their x is zeroed; tokens past T re-read the last token
@@ -299,8 +301,12 @@ yproj_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int r,
 // 512-column part of 64 tokens keeps two waves per SIMD busy.
 constexpr int LNW = 8;
 
+// All of Q's k-chunks are loaded up front for RK <= 64 (with RK = 64 the
+// second chunk used to be reloaded for every token block, each load waited
+// for in turn: 169.7 us at T = D = 8192); that needs more than the 128
+// registers of four waves per SIMD, so RK = 64 runs with two.
 template <int RP, int RK, bool OF32, bool ADD>
-__global__ void __launch_bounds__(LNW * 64) __attribute__((amdgpu_waves_per_eu(4, 8)))
+__global__ void __launch_bounds__(LNW * 64) __attribute__((amdgpu_waves_per_eu(RK > 32 ? 2 : 4, 8)))
 lift_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int S, int r,
             const float* __restrict__ Zpart, const uint16_t* __restrict__ QH,
             const uint16_t* __restrict__ QL, const void* __restrict__ addend,
@@ -320,7 +326,7 @@ lift_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int S, int 
   const int nds = (dend - dbeg) / 64;
   const int g = lane >> 4;
   const int tl = lane & 15;
-  constexpr int KQ = 1;                               // Q k-chunks loaded up front
+  constexpr int KQ = RK <= 64 ? RK / 32 : 1;          // Q k-chunks loaded up front
   const bool live = wave < nds;                       // this wave's double step exists
   const int d0 = dbeg + 64 * (live ? wave : nds - 1);
   static_assert(TPW * RK % (4 * NT) == 0 || TPW * RK < 4 * NT, "z chunks");
