@@ -359,6 +359,24 @@ rw4_status respin_align_prepared(const void* x, void* out, rw4_dtype out_dt, con
 size_t respin_align_prepared_workspace_size(int64_t T, int64_t D, int64_t r);
 
 /*
+ * respin_align_project_prepared -- the first half of respin_align_prepared for
+ * short batches: the projection z = (M - I) Q^T x ["ReSpinQuant" paper notes,
+ * key design 3], left in `z` for rotated_linear_prepared_residual, which
+ * finishes the alignment inside a product's epilogue.
+ *   x      bf16 [T][D], 1 <= T <= 16, D <= 16384
+ *   basis  prepared for (D, r) by respin_prepare_basis; 256-byte aligned
+ *   z, z_bytes: respin_align_project_size(T, D, r) bytes of device memory,
+ *          256-byte aligned; its layout is internal (per-chunk partial sums)
+ * Constraints: those of respin_basis_size; larger T is RW4_ERR_UNSUPPORTED.
+ * Asynchronous on `stream`; argument errors come before any launch.
+ */
+rw4_status respin_align_project_prepared(const void* x, int64_t T, int64_t D, const void* basis,
+                                         int64_t r, void* z, size_t z_bytes, void* stream);
+
+/* bytes of z respin_align_project_prepared writes; 0 when unsupported */
+size_t respin_align_project_size(int64_t T, int64_t D, int64_t r);
+
+/*
  * rotated_linear_prepared -- rotated_linear with the alignment's basis
  * prepared by respin_prepare_basis(Q, M, D, r) instead of (Q, M): same
  * arguments, same results bit for bit, same workspace contents after the
@@ -371,6 +389,32 @@ rw4_status rotated_linear_prepared(const void* x, int64_t ldx, int64_t T, int64_
                                    const uint8_t* w, const float* s_w, int64_t N, void* y,
                                    void* workspace, size_t ws_bytes, float* dbg_prequant,
                                    void* stream);
+
+/*
+ * rotated_linear_prepared_residual -- rotated_linear_prepared for short
+ * batches on packed INT4 weights whose product also finishes a residual
+ * alignment of the layer: in a decoder layer the alignment sits on the skip
+ * connection and the block's output joins after it ["ReSpinQuant" paper
+ * notes, key design 2-3], so the product that makes the block output can add
+ * it to the aligned skip input directly.
+ *   x .. dbg_prequant  as rotated_linear_prepared; flags must hold
+ *          RW4_WPACKED and 1 <= T <= 16; y receives the bf16 [T][N] output
+ *   res_x  bf16 [T][N], the skip input (N is the alignment's width D)
+ *   res_basis, res_r: the alignment's prepared basis (respin_prepare_basis)
+ *   res_z, res_z_bytes: respin_align_project_prepared(res_x, T, N, res_basis,
+ *          res_r, ...) written before this call on the same stream
+ *   res_out bf16 [T][N], must alias none of x, y, res_x:
+ *          res_out = bf16(res_x + Q z + y), the same bits as
+ *          respin_align_prepared(res_x, res_out, RW4_BF16, res_basis, y, ...)
+ * Asynchronous on `stream`; argument errors come before any launch.
+ */
+rw4_status rotated_linear_prepared_residual(const void* x, int64_t ldx, int64_t T, int64_t D,
+                                            const void* basis, int64_t r, unsigned flags,
+                                            const uint8_t* w, const float* s_w, int64_t N, void* y,
+                                            void* workspace, size_t ws_bytes, float* dbg_prequant,
+                                            const void* res_x, const void* res_basis,
+                                            int64_t res_r, const void* res_z, size_t res_z_bytes,
+                                            void* res_out, void* stream);
 
 /* bytes of workspace rotated_linear_prepared needs; 0 on bad input */
 size_t rotated_linear_prepared_workspace_size(int64_t T, int64_t D, int64_t r, unsigned flags);
@@ -409,7 +453,7 @@ const char* rw4_status_string(rw4_status s);
 /* ABI version of this header (bumped on any signature change) */
 int rw4_abi_version(void);
 
-#define RW4_ABI_VERSION 10
+#define RW4_ABI_VERSION 11
 
 #ifdef __cplusplus
 }

@@ -22,7 +22,8 @@ __all__ = [
     "w4a4_tiles_size", "w4a4_tile_codes", "w4a4_gemm_tiles", "prep_weight", "layer",
     "quant_act_sym", "RW4_ABITS", "RW4_KRON", "RW4_HEADS", "hadamard_transform", "head_hadamard",
     "respin_construct", "respin_construct_workspace_size", "rotated_linear_prepared_noalloc",
-    "NOALLOC_SCRATCH_BYTES",
+    "NOALLOC_SCRATCH_BYTES", "respin_align_project_prepared", "respin_align_project_size",
+    "rotated_linear_prepared_residual",
 ]
 
 RW4_ALIGN, RW4_FWHT, RW4_SWIGLU = 1, 2, 4
@@ -57,7 +58,9 @@ EXPORTS = ("respin_align", "respin_align_workspace_size", "fwht", "quant_act_int
            "rotated_linear_prepared", "rotated_linear_prepared_workspace_size",
            "respin_align_prepared", "respin_align_prepared_workspace_size",
            "hadamard_transform", "head_hadamard", "respin_construct",
-           "respin_construct_workspace_size", "rotated_linear_prepared_noalloc", "rw4_align256",
+           "respin_construct_workspace_size", "rotated_linear_prepared_noalloc",
+           "respin_align_project_prepared", "respin_align_project_size",
+           "rotated_linear_prepared_residual", "rw4_align256",
            "rw4_status_string", "rw4_abi_version")
 
 
@@ -101,6 +104,11 @@ def lib() -> ctypes.CDLL:
                                           sz, vp, vp]
     L.rotated_linear_prepared_noalloc.argtypes = [vp, i64, i64, i64, vp, i64, u32, vp, vp, i64,
                                                   vp, vp, vp]
+    L.respin_align_project_prepared.argtypes = [vp, i64, i64, vp, i64, vp, sz, vp]
+    L.respin_align_project_size.argtypes = [i64, i64, i64]
+    L.respin_align_project_size.restype = sz
+    L.rotated_linear_prepared_residual.argtypes = [vp, i64, i64, i64, vp, i64, u32, vp, vp, i64,
+                                                   vp, vp, sz, vp, vp, vp, i64, vp, sz, vp, vp]
     L.rotated_linear_prepared_workspace_size.argtypes = [i64, i64, i64, u32]
     L.rotated_linear_prepared_workspace_size.restype = sz
     L.respin_align_prepared.argtypes = [vp, vp, i32, vp, vp, i64, i64, i64, vp, sz, vp]
@@ -120,7 +128,8 @@ def lib() -> ctypes.CDLL:
               "w4a4_tile_codes",
               "w4a4_gemm_tiles", "rotated_linear", "respin_prepare_basis",
               "rotated_linear_prepared", "rotated_linear_prepared_noalloc",
-              "respin_align_prepared", "hadamard_transform",
+              "respin_align_prepared", "respin_align_project_prepared",
+              "rotated_linear_prepared_residual", "hadamard_transform",
               "head_hadamard", "respin_construct"):
         getattr(L, f).restype = i32
     _lib = L
@@ -234,6 +243,29 @@ def respin_align_prepared(x, basis, r: int, out=None, addend=None, out_dtype=Non
                                      _stream())
     _check("respin_align_prepared", st)
     return out
+
+
+def respin_align_project_size(T: int, D: int, r: int) -> int:
+    return int(lib().respin_align_project_size(T, D, r))
+
+
+def respin_align_project_prepared(x, basis, r: int, z=None):
+    """The projection half of ``respin_align_prepared`` for short batches
+    (1 <= T <= 16): z for ``rotated_linear_prepared_residual``. Returns z."""
+    torch = _torch()
+    _contig(x)
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bf16")
+    T, D = x.shape
+    if basis.numel() * basis.element_size() < respin_basis_size(D, r):
+        raise ValueError("basis: buffer too small for (D, r)")
+    need = respin_align_project_size(T, D, r)
+    if z is None:
+        z = torch.empty((max(need, 256),), dtype=torch.uint8, device=x.device)
+    st = lib().respin_align_project_prepared(_p(x), T, D, _p(basis), r, _p(z),
+                                             z.numel() * z.element_size(), _stream())
+    _check("respin_align_project_prepared", st)
+    return z
 
 
 def fwht(x, out=None):
@@ -490,6 +522,42 @@ def rotated_linear_prepared(x, w, s_w, flags: int, basis=None, r: int = 0, out=N
     return out, workspace
 
 
+def rotated_linear_prepared_residual(x, w, s_w, flags: int, res_x, res_basis, res_r: int, res_z,
+                                     basis=None, r: int = 0, out=None, res_out=None,
+                                     workspace=None, dbg_prequant=None):
+    """``rotated_linear_prepared`` (packed INT4 weights, 1 <= T <= 16) whose
+    product also finishes the residual alignment of ``res_x`` (projection
+    ``res_z`` from ``respin_align_project_prepared``): res_out = bf16(res_x +
+    Q z + y), bit for bit ``respin_align_prepared(res_x, ..., addend=y)``.
+    Returns (y, res_out, workspace)."""
+    torch = _torch()
+    _rows(x)
+    _contig(res_x)
+    if x.dtype != torch.bfloat16 or res_x.dtype != torch.bfloat16:
+        raise TypeError("x and res_x must be bf16")
+    T = x.shape[0]
+    D = x.shape[1] // 2 if flags & RW4_SWIGLU else x.shape[1]
+    N = s_w.shape[0]
+    if tuple(res_x.shape) != (T, N):
+        raise ValueError("res_x must be [T][N]")
+    _check_weights(w, N, D, flags)
+    r = r if flags & RW4_ALIGN else 0
+    need = rotated_linear_prepared_workspace_size(T, D, r, flags)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    if res_out is None:
+        res_out = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    st = lib().rotated_linear_prepared_residual(
+        _p(x), x.stride(0), T, D, _p(basis) if r else None, r, flags, _p(w), _p(s_w), N,
+        _p(out), _p(workspace), workspace.numel() * workspace.element_size(), _p(dbg_prequant),
+        _p(res_x), _p(res_basis), res_r, _p(res_z), res_z.numel() * res_z.element_size(),
+        _p(res_out), _stream())
+    _check("rotated_linear_prepared_residual", st)
+    return out, res_out, workspace
+
+
 NOALLOC_SCRATCH_BYTES = 64 << 20   # RW4_NOALLOC_SCRATCH_BYTES of include/rotw4a4.h
 
 
@@ -562,6 +630,21 @@ def layer(x0, aligns, weights, D: int, dbg_down=None, packed: bool = False):
     (B1, r1), (B2, r2) = aligns
     st = {}
     wf = RW4_WPACKED if packed else 0
+    T = x0.shape[0]
+    if packed and 1 <= T <= 16:
+        # short batches: each alignment's projection runs ahead, and the
+        # product that makes the residual's addend finishes the alignment in
+        # its epilogue (the same bits as the sequence below)
+        z1 = respin_align_project_prepared(x0, B1, r1)
+        st["qkv"], _ = rotated_linear(x0, *weights["qkv"], flags=wf)
+        st["o"], st["x1"], _ = rotated_linear_prepared_residual(
+            st["qkv"][:, 2 * D:3 * D], *weights["o"], wf, x0, B1, r1, z1)
+        z2 = respin_align_project_prepared(st["x1"], B2, r2)
+        st["gate_up"], _ = rotated_linear(st["x1"], *weights["gate_up"], flags=wf)
+        st["down"], st["x2"], st["down_ws"] = rotated_linear_prepared_residual(
+            st["gate_up"], *weights["down"], RW4_SWIGLU | RW4_FWHT | wf, st["x1"], B2, r2, z2,
+            dbg_prequant=dbg_down)
+        return st
     st["qkv"], _ = rotated_linear(x0, *weights["qkv"], flags=wf)
     st["o"], _ = rotated_linear(st["qkv"][:, 2 * D:3 * D], *weights["o"], flags=wf)
     st["x1"] = respin_align_prepared(x0, B1, r1, addend=st["o"], out_dtype=torch.bfloat16)

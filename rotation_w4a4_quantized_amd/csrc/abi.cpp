@@ -106,7 +106,8 @@ rw4_status check_linear(const void* x, int64_t ldx, int64_t T, int64_t D, int64_
 // the unit after validation; basis prepared for (D, r) when r > 0
 rw4_status run_linear(const void* x, int64_t ldx, int64_t T, int64_t D, const void* basis,
                       int64_t r, unsigned flags, const uint8_t* w, const float* s_w, int64_t N,
-                      void* y, void* workspace, float* dbg, hipStream_t s) {
+                      void* y, void* workspace, float* dbg, hipStream_t s,
+                      const rw4::GemmResidual* res = nullptr) {
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint8_t* codes = ws;
   // packed INT4 weights: the activation codes are packed rows [T][D/2] (they
@@ -114,6 +115,9 @@ rw4_status run_linear(const void* x, int64_t ldx, int64_t T, int64_t D, const vo
   const bool pk = (flags & RW4_WPACKED) != 0;
   float* s_a = reinterpret_cast<float*>(ws + rw4_align256(rw4::tiles_bytes(T, D)));
   auto gemm = [&]() {
+    if (res)
+      return rw4::launch_gemm_residual(codes, s_a, w, s_w, static_cast<uint16_t*>(y), *res, T, D,
+                                       N, s);
     return pk ? rw4::launch_gemm(codes, s_a, w, s_w, y, false, T, D, N, s)
               : rw4::launch_gemm_tiles(codes, s_a, w, s_w, y, false, T, D, N, s);
   };
@@ -383,6 +387,58 @@ rw4_status respin_align_prepared(const void* x, void* out, rw4_dtype out_dt, con
     return RW4_ERR_HIP;
   return hip_status(rw4::launch_lift(xb, out, out_dt == RW4_F32, addend, T, D, r, basis,
                                      with_p(D, r), Zpart, s));
+}
+
+size_t respin_align_project_size(int64_t T, int64_t D, int64_t r) {
+  if (T < 1 || D < 1 || r < 1 || !rw4::align_small(T, D) || respin_basis_size(D, r) == 0) return 0;
+  return rw4::align_zpart_bytes(T, D, r);
+}
+
+rw4_status respin_align_project_prepared(const void* x, int64_t T, int64_t D, const void* basis,
+                                         int64_t r, void* z, size_t z_bytes, void* stream) {
+  if (T < 0 || D < 1 || r < 1) return RW4_ERR_INVALID_ARG;
+  if (respin_basis_size(D, r) == 0) return RW4_ERR_UNSUPPORTED;
+  if (T == 0) return RW4_OK;
+  if (!rw4::align_small(T, D)) return RW4_ERR_UNSUPPORTED;
+  if (!x || !basis) return RW4_ERR_INVALID_ARG;
+  if (!al16(x)) return RW4_ERR_MISALIGNED;
+  if (reinterpret_cast<uintptr_t>(basis) & 255u) return RW4_ERR_INVALID_ARG;
+  if (!z || (reinterpret_cast<uintptr_t>(z) & 255u) || z_bytes < respin_align_project_size(T, D, r))
+    return RW4_ERR_WORKSPACE;
+  return hip_status(rw4::launch_align_small_project(static_cast<const uint16_t*>(x), T, D, r,
+                                                    basis, with_p(D, r), static_cast<float*>(z),
+                                                    strm(stream)));
+}
+
+rw4_status rotated_linear_prepared_residual(const void* x, int64_t ldx, int64_t T, int64_t D,
+                                            const void* basis, int64_t r, unsigned flags,
+                                            const uint8_t* w, const float* s_w, int64_t N, void* y,
+                                            void* workspace, size_t ws_bytes, float* dbg_prequant,
+                                            const void* res_x, const void* res_basis,
+                                            int64_t res_r, const void* res_z, size_t res_z_bytes,
+                                            void* res_out, void* stream) {
+  rw4_status st = check_linear(x, ldx, T, D, r, flags, w, s_w, N, y, dbg_prequant);
+  if (st != RW4_OK || T == 0) return st;
+  if (!(flags & RW4_WPACKED) || T > 16) return RW4_ERR_UNSUPPORTED;
+  if (res_r < 1) return RW4_ERR_INVALID_ARG;
+  if (respin_align_project_size(T, N, res_r) == 0) return RW4_ERR_UNSUPPORTED;
+  if (!res_x || !res_basis || !res_out) return RW4_ERR_INVALID_ARG;
+  if (!al16(res_x) || !al16(res_out)) return RW4_ERR_MISALIGNED;
+  if (reinterpret_cast<uintptr_t>(res_basis) & 255u) return RW4_ERR_INVALID_ARG;
+  if (res_out == res_x || res_out == y || res_out == x) return RW4_ERR_INVALID_ARG;
+  if (!res_z || (reinterpret_cast<uintptr_t>(res_z) & 255u) ||
+      res_z_bytes < respin_align_project_size(T, N, res_r))
+    return RW4_ERR_WORKSPACE;
+  const int64_t re = (flags & RW4_ALIGN) ? r : 0;
+  if (re > 0 && (!basis || (reinterpret_cast<uintptr_t>(basis) & 255u))) return RW4_ERR_INVALID_ARG;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return RW4_ERR_WORKSPACE;
+  if (ws_bytes < call_ws_bytes(T, D, re)) return RW4_ERR_WORKSPACE;
+  const rw4::AlignBasis a = rw4::align_basis(res_basis, N, res_r, with_p(N, res_r));
+  const rw4::GemmResidual res{static_cast<const uint16_t*>(res_x), a.QH, a.QL,
+                              static_cast<const float*>(res_z), a.RK, rw4::align_small_chunks(N),
+                              static_cast<uint16_t*>(res_out)};
+  return run_linear(x, ldx, T, D, basis, re, flags, w, s_w, N, y, workspace, dbg_prequant,
+                    strm(stream), &res);
 }
 
 size_t rotated_linear_prepared_workspace_size(int64_t T, int64_t D, int64_t r, unsigned flags) {

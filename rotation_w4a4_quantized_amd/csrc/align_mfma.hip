@@ -785,6 +785,19 @@ hipError_t launch_yproj(const uint16_t* x, int64_t T, int64_t D, int64_t r, cons
 
 bool align_small(int64_t T, int64_t D) { return T >= 1 && T <= kSmallT && D <= kSmallMaxD; }
 
+int align_small_chunks(int64_t D) { return static_cast<int>((D + kSmallChunk - 1) / kSmallChunk); }
+
+hipError_t launch_align_small_project(const uint16_t* x, int64_t T, int64_t D, int64_t r,
+                                      const void* basis, bool with_p, float* Zs, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (!align_small(T, D) || D % 64 != 0 || r < 1 || r > kPrepRmax) return hipErrorInvalidValue;
+  const AlignBasis a = align_basis(basis, D, r, with_p);
+  hipLaunchKernelGGL(asmall_proj_kernel, dim3(static_cast<unsigned>(align_small_chunks(D))),
+                     dim3(256), 0, s, x, static_cast<int>(T), static_cast<int>(D), a.RP, a.RK,
+                     a.QtH, a.QtL, Zs);
+  return hipGetLastError();
+}
+
 hipError_t launch_align_small(const uint16_t* x, void* out, int out_f32, const void* addend,
                               int64_t T, int64_t D, int64_t r, const void* basis, bool with_p,
                               float* Zs, hipStream_t s) {

@@ -299,13 +299,16 @@ gemm_kernel(const uint8_t* __restrict__ a, const float* __restrict__ s_a,
 constexpr int kDecRows = 16;
 constexpr int kDecLds = 32768;  // activation bytes (T * K / 2) staged in LDS at most
 
-template <int NWV, int SPW, bool ALDS, bool I32OUT>
+constexpr int kResRmax = 128;   // basis width (RK) a residual epilogue takes at most
+
+template <int NWV, int SPW, bool ALDS, bool I32OUT, bool RES>
 __global__ void __launch_bounds__(64 * NWV)
 gemm_decode_kernel(const uint8_t* __restrict__ a, const float* __restrict__ s_a,
                    const uint8_t* __restrict__ w, const float* __restrict__ s_w,
-                   void* __restrict__ y, int T, int K, int N) {
+                   void* __restrict__ y, int T, int K, int N, GemmResidual res) {
   __shared__ uint32_t red[NWV][4][64];
   __shared__ __attribute__((aligned(16))) uint8_t al[ALDS ? kDecLds : 16];
+  __shared__ float zsm[RES ? kDecRows : 1][RES ? kResRmax + 1 : 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n0 = blockIdx.x * kDecRows;
   const int KB = K / 2;                       // bytes per row
@@ -340,6 +343,41 @@ gemm_decode_kernel(const uint8_t* __restrict__ a, const float* __restrict__ s_a,
     }
   };
   load(0);
+  // an epilogue thread's output (token et, row en) is known now: its skip
+  // value and the first 32 values of its basis row load with the weights
+  const int ev = threadIdx.x >> 6, el = threadIdx.x & 63;
+  const int et = el & 15, en = n0 + 4 * (el >> 4) + ev;
+  const bool eact = RES && threadIdx.x < 256 && et < T && en < N;
+  uint4 eqh[4], eql[4];
+  uint16_t exr = 0;
+  if constexpr (RES) {
+    const int64_t row = static_cast<int64_t>(eact ? en : 0) * res.RK;
+    const uint4* qh = reinterpret_cast<const uint4*>(res.QH + row);
+    const uint4* ql = reinterpret_cast<const uint4*>(res.QL + row);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      eqh[j] = qh[j];
+      eql[j] = ql[j];
+    }
+    exr = res.x[static_cast<int64_t>(eact ? et : 0) * N + (eact ? en : 0)];
+  }
+  if constexpr (RES) {
+    // z of the T tokens: the projection's chunk partials summed in chunk
+    // order from zero, as the short-batch lift sums them
+    for (int o = threadIdx.x; o < T * res.RK; o += 64 * NWV) {
+      const int t = o / res.RK, i = o % res.RK;
+      float z = 0.0f;
+      for (int c0 = 0; c0 < res.C; c0 += 16) {
+        float zp[16];
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+          zp[c] = res.Zs[(static_cast<int64_t>(min(c0 + c, res.C - 1)) * T + t) * res.RK + i];
+#pragma unroll
+        for (int c = 0; c < 16; ++c) z += c0 + c < res.C ? zp[c] : 0.0f;
+      }
+      zsm[t][i] = z;
+    }
+  }
   if constexpr (ALDS) {
     const int nbytes = T * KB;  // a multiple of 16 (K % 32 == 0)
     for (int o = threadIdx.x * 16; o < nbytes; o += 64 * NWV * 16)
@@ -388,30 +426,89 @@ gemm_decode_kernel(const uint8_t* __restrict__ a, const float* __restrict__ s_a,
 #pragma unroll
   for (int ww = 0; ww < NWV; ++ww) sum += red[ww][v][l];
   const int S = unscale(static_cast<int>(sum));
+  const int64_t off = static_cast<int64_t>(t) * N + n;
   if constexpr (I32OUT) {
-    static_cast<int32_t*>(y)[static_cast<int64_t>(t) * N + n] = S;
+    static_cast<int32_t*>(y)[off] = S;
   } else {
-    static_cast<uint16_t*>(y)[static_cast<int64_t>(t) * N + n] =
-        f32_to_bf16((static_cast<float>(S) * s_a[t]) * s_w[n]);
+    const uint16_t yb = f32_to_bf16((static_cast<float>(S) * s_a[t]) * s_w[n]);
+    static_cast<uint16_t*>(y)[off] = yb;
+    if constexpr (RES) {
+      // x + Q z with Q = Qh + Ql in fp32 and the FMAs in basis order (the
+      // short-batch lift's arithmetic), then the block output, one rounding
+      const uint4* qh = reinterpret_cast<const uint4*>(res.QH + static_cast<int64_t>(n) * res.RK);
+      const uint4* ql = reinterpret_cast<const uint4*>(res.QL + static_cast<int64_t>(n) * res.RK);
+      float corr = 0.0f;
+      // basis values i0 .. i0 + 31 in fp32 (hi + lo), FMAs in basis order; the
+      // first 32 come from the registers loaded at the start
+      auto chunk = [&](const uint4 (&hv)[4], const uint4 (&lv)[4], int i0) {
+        float q[32];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t hw[4] = {hv[j].x, hv[j].y, hv[j].z, hv[j].w};
+          const uint32_t lw[4] = {lv[j].x, lv[j].y, lv[j].z, lv[j].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            q[8 * j + 2 * e] = bf16lo(hw[e]) + bf16lo(lw[e]);
+            q[8 * j + 2 * e + 1] = bf16hi(hw[e]) + bf16hi(lw[e]);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 32; ++i) corr = fmaf(q[i], zsm[t][i0 + i], corr);
+      };
+      chunk(eqh, eql, 0);
+      for (int i0 = 32; i0 < res.RK; i0 += 32) {
+        uint4 hv[4], lv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          hv[j] = qh[i0 / 8 + j];
+          lv[j] = ql[i0 / 8 + j];
+        }
+        chunk(hv, lv, i0);
+      }
+      float acc = bf16_to_f32(exr) + corr;
+      acc += bf16_to_f32(yb);
+      res.out[off] = f32_to_bf16(acc);
+    }
   }
 }
 
-template <int NWV, int SPW>
+template <int NWV, int SPW, bool RES = false>
 hipError_t launch_decode(const uint8_t* a, const float* s_a, const uint8_t* w, const float* s_w,
-                         void* y, bool i32_out, int64_t T, int64_t K, int64_t N, hipStream_t s) {
+                         void* y, bool i32_out, int64_t T, int64_t K, int64_t N, hipStream_t s,
+                         const GemmResidual& res = GemmResidual{}) {
   const int64_t nb = (N + kDecRows - 1) / kDecRows;
   if (nb > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  if (RES && (i32_out || res.RK > kResRmax || res.RK % 32 != 0)) return hipErrorInvalidValue;
   const bool alds = T * (K / 2) <= kDecLds;
 #define RW4_DEC(AL, I)                                                                           \
   if (alds == AL && i32_out == I) {                                                              \
-    hipLaunchKernelGGL((gemm_decode_kernel<NWV, SPW, AL, I>), dim3(static_cast<unsigned>(nb)),    \
-                       dim3(64 * NWV), 0, s, a, s_a, w, s_w, y, static_cast<int>(T),             \
-                       static_cast<int>(K), static_cast<int>(N));                                \
+    hipLaunchKernelGGL((gemm_decode_kernel<NWV, SPW, AL, I, RES>),                                \
+                       dim3(static_cast<unsigned>(nb)), dim3(64 * NWV), 0, s, a, s_a, w, s_w, y,  \
+                       static_cast<int>(T), static_cast<int>(K), static_cast<int>(N), res);      \
     return hipGetLastError();                                                                    \
   }
-  RW4_DEC(true, false) RW4_DEC(true, true) RW4_DEC(false, false) RW4_DEC(false, true)
+  RW4_DEC(true, false) RW4_DEC(false, false)
+  if constexpr (!RES) {
+    RW4_DEC(true, true) RW4_DEC(false, true)
+  }
 #undef RW4_DEC
   return hipErrorInvalidValue;
+}
+
+// the decode shapes of launch_gemm, with the residual epilogue
+template <bool RES>
+hipError_t launch_decode_any(const uint8_t* a, const float* s_a, const uint8_t* w,
+                             const float* s_w, void* y, bool i32_out, int64_t T, int64_t K,
+                             int64_t N, hipStream_t s, const GemmResidual& res) {
+  // weight streaming. Measured at T = 8 (weights rotated past the last-level
+  // cache): up to 256 workgroups (N <= 4096), 16 waves with one step each
+  // per round (4096 x 4096: 4.0 us); K beyond 4096 codes, 16 waves with four
+  // steps each (16384 x 4096: 9.8 us); otherwise 8 waves with two steps each
+  // (4096 x 12288: 7.7 us; 4096 x 32768: 15.0 us).
+  const int64_t nb = (N + kDecRows - 1) / kDecRows;
+  if (K > 4096) return launch_decode<16, 4, RES>(a, s_a, w, s_w, y, i32_out, T, K, N, s, res);
+  if (nb <= 256) return launch_decode<16, 1, RES>(a, s_a, w, s_w, y, i32_out, T, K, N, s, res);
+  return launch_decode<8, 2, RES>(a, s_a, w, s_w, y, i32_out, T, K, N, s, res);
 }
 
 template <int NWW, int NWT, int BW, int BT>
@@ -435,18 +532,17 @@ hipError_t launch_cfg(const uint8_t* a, const float* s_a, const uint8_t* w, cons
 hipError_t launch_gemm(const uint8_t* a, const float* s_a, const uint8_t* w, const float* s_w,
                        void* y, bool i32_out, int64_t T, int64_t K, int64_t N, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  if (T <= gemm::kDecRows) {
-    // weight streaming. Measured at T = 8 (weights rotated past the last-level
-    // cache): up to 256 workgroups (N <= 4096), 16 waves with one step each
-    // per round (4096 x 4096: 4.0 us); K beyond 4096 codes, 16 waves with four
-    // steps each (16384 x 4096: 9.8 us); otherwise 8 waves with two steps each
-    // (4096 x 12288: 7.7 us; 4096 x 32768: 15.0 us).
-    const int64_t nb = (N + gemm::kDecRows - 1) / gemm::kDecRows;
-    if (K > 4096) return gemm::launch_decode<16, 4>(a, s_a, w, s_w, y, i32_out, T, K, N, s);
-    if (nb <= 256) return gemm::launch_decode<16, 1>(a, s_a, w, s_w, y, i32_out, T, K, N, s);
-    return gemm::launch_decode<8, 2>(a, s_a, w, s_w, y, i32_out, T, K, N, s);
-  }
+  if (T <= gemm::kDecRows)
+    return gemm::launch_decode_any<false>(a, s_a, w, s_w, y, i32_out, T, K, N, s, GemmResidual{});
   return gemm::launch_cfg<2, 2, 2, 2>(a, s_a, w, s_w, y, i32_out, T, K, N, s);
+}
+
+hipError_t launch_gemm_residual(const uint8_t* a, const float* s_a, const uint8_t* w,
+                                const float* s_w, uint16_t* y, const GemmResidual& res, int64_t T,
+                                int64_t K, int64_t N, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (T > gemm::kDecRows) return hipErrorInvalidValue;
+  return gemm::launch_decode_any<true>(a, s_a, w, s_w, y, false, T, K, N, s, res);
 }
 
 }  // namespace rw4

@@ -76,6 +76,11 @@ bool align_small(int64_t T, int64_t D);
 hipError_t launch_align_small(const uint16_t* x, void* out, int out_f32, const void* addend,
                               int64_t T, int64_t D, int64_t r, const void* basis, bool with_p,
                               float* Zs, hipStream_t s);
+// the short-batch projection alone: Zs[c][t][i] for the align_small_chunks(D)
+// 256-column chunks c (align_zpart_bytes(T, D, r) bytes)
+int align_small_chunks(int64_t D);
+hipError_t launch_align_small_project(const uint16_t* x, int64_t T, int64_t D, int64_t r,
+                                      const void* basis, bool with_p, float* Zs, hipStream_t s);
 // unfused lift out = x + Q z (+ addend), fp32 or bf16 out
 hipError_t launch_lift(const uint16_t* x, void* out, int out_f32, const void* addend, int64_t T,
                        int64_t D, int64_t r, const void* basis, bool with_p, float* Zpart,
@@ -94,6 +99,22 @@ hipError_t launch_lift_fwht_quant(const uint16_t* x, int64_t T, int64_t D, int64
 // W4A4 GEMM, bf16 (dequantized) or raw int32 output.
 hipError_t launch_gemm(const uint8_t* a, const float* s_a, const uint8_t* w, const float* s_w,
                        void* y, bool i32_out, int64_t T, int64_t K, int64_t N, hipStream_t s);
+
+// A residual alignment finished in a short-batch product's epilogue:
+// out = bf16((x + Q z) + y) with y the product's bf16 output, bit for bit what
+// the short-batch lift gives with y as its addend.
+struct GemmResidual {
+  const uint16_t* x;   // bf16 [T][N], the skip input
+  const uint16_t* QH;  // the prepared basis' bf16 hi/lo rows of Q, [N][RK]
+  const uint16_t* QL;
+  const float* Zs;     // the short-batch projection of x, [C][T][RK]
+  int RK, C;
+  uint16_t* out;       // bf16 [T][N]
+};
+// packed INT4 rows, 1 <= T <= 16, bf16 output y plus the residual
+hipError_t launch_gemm_residual(const uint8_t* a, const float* s_a, const uint8_t* w,
+                                const float* s_w, uint16_t* y, const GemmResidual& res, int64_t T,
+                                int64_t K, int64_t N, hipStream_t s);
 
 // FP6 operand tiles (layout in common.hpp): rows padded to a multiple of 256.
 int64_t tiles_rows(int64_t R);

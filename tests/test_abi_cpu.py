@@ -22,7 +22,7 @@ def _declared():
 def test_library_built_and_loads():
     assert os.path.exists(rw.library_path), "build the HIP library first"
     L = rw.lib()
-    assert L.rw4_abi_version() == 10
+    assert L.rw4_abi_version() == 11
 
 
 def test_exports_every_declared_symbol():
@@ -242,6 +242,44 @@ def test_respin_align_prepared_validation():
     assert _rap(ws=ctypes.c_void_p(0x40010)) == WSE
     assert _rap(T=0, ws=NUL) == 0
     assert _rap(T=0, x=NUL, out=NUL, basis=NUL, ws=NUL) == 0   # empty call: no pointer read
+
+
+def _proj(x=A, T=8, D=4096, basis=B, r=32, z=C, zb=1 << 20):
+    return rw.lib().respin_align_project_prepared(x, T, D, basis, r, z, zb, NUL)
+
+
+def _rlr(x=A, T=8, D=4096, flags=(1 << 29), N=4096, y=B, ws=C, wsb=1 << 22, rx=Dp,
+         rbasis=ctypes.c_void_p(0x50000), rr=32, rz=ctypes.c_void_p(0x60000), rzb=1 << 20,
+         rout=ctypes.c_void_p(0x70000)):
+    return rw.lib().rotated_linear_prepared_residual(x, D, T, D, NUL, 0, flags, Dp, A, N, y, ws,
+                                                     wsb, NUL, rx, rbasis, rr, rz, rzb, rout, NUL)
+
+
+def test_residual_entries_validation():
+    L = rw.lib()
+    # the projection of short batches only: sized like respin_align's parts
+    assert L.respin_align_project_size(8, 4096, 32) == L.rw4_align256(16 * 8 * 32 * 4)
+    assert L.respin_align_project_size(17, 4096, 32) == 0      # past 16 tokens
+    assert L.respin_align_project_size(8, 1000, 32) == 0
+    assert _proj(T=17) == UNS and _proj(r=6) == UNS
+    assert _proj(x=NUL) == INV and _proj(basis=NUL) == INV and _proj(r=0) == INV
+    assert _proj(x=ODD) == MIS
+    assert _proj(basis=ctypes.c_void_p(0x20010)) == INV
+    assert _proj(z=NUL) == WSE and _proj(zb=100) == WSE
+    assert _proj(z=ctypes.c_void_p(0x30010)) == WSE
+    assert _proj(T=0, x=NUL, basis=NUL, z=NUL) == 0
+    # the residual product: packed weights, short batches, N = the alignment's D
+    assert _rlr(flags=0) == UNS                     # FP6 tiles
+    assert _rlr(T=17) == UNS
+    assert _rlr(N=1000) == UNS                      # no alignment of width 1000
+    assert _rlr(rr=0) == INV
+    assert _rlr(rx=NUL) == INV and _rlr(rbasis=NUL) == INV and _rlr(rout=NUL) == INV
+    assert _rlr(rx=ODD) == MIS and _rlr(rout=ODD) == MIS
+    assert _rlr(rbasis=ctypes.c_void_p(0x50010)) == INV
+    assert _rlr(rout=Dp) == INV and _rlr(rout=B) == INV   # aliases res_x, y
+    assert _rlr(rz=NUL) == WSE and _rlr(rzb=100) == WSE
+    assert _rlr(ws=NUL) == WSE
+    assert _rlr(T=0) == 0
 
 
 def test_structured_transform_validation():

@@ -930,6 +930,40 @@ def _layer_check(rw, cid, packed=False):
     _check_gemm_out(g["down"], q, s, qws["down"], sws["down"])
 
 
+# the product that finishes a residual alignment (short batches, packed
+# weights): the same bits as the product and the aligned residual computed
+# apart; decode shapes (o and down projections), ragged token counts, both
+# basis widths, the gated input, an alignment narrower than 4096
+@pytest.mark.parametrize("T,Din,N,rr,flags", [(8, 4096, 4096, 32, 0), (3, 4096, 4096, 32, 0),
+                                              (16, 4096, 4096, 64, 0), (1, 512, 1024, 8, 0),
+                                              (8, 16384, 4096, 32, 6), (5, 16384, 4096, 64, 6)])
+def test_rotated_linear_residual(rw, T, Din, N, rr, flags):
+    say(f"rotated_linear_prepared_residual T={T} D={Din} N={N} r={rr} flags={flags}")
+    t = torch()
+    fl = flags | rw.RW4_WPACKED
+    xb = W.gen_x(700 + T, T, 2 * Din if flags & O.FLAG_SWIGLU else Din, 8, 80.0)
+    Wf = W.gen_weight(701, N, Din, 0.02)
+    _, s_w, codes, _ = rw.prep_weight(dev(Wf), bool(flags & O.FLAG_FWHT))
+    res_x = dev(W.gen_x(702 + T, T, N, 8, 80.0))
+    Q, M = W.gen_basis(703, N, rr)
+    B = rw.respin_prepare_basis(dev(Q), dev(M))
+    z = rw.respin_align_project_prepared(res_x, B, rr)
+    d_fused = t.empty((T, Din), dtype=t.float32, device="cuda")
+    y, res_out, ws = rw.rotated_linear_prepared_residual(dev(xb), codes, s_w, fl, res_x, B, rr, z,
+                                                         dbg_prequant=d_fused)
+    d_ref = t.empty((T, Din), dtype=t.float32, device="cuda")
+    y_ref, ws_ref = rw.rotated_linear_prepared(dev(xb), codes, s_w, fl, dbg_prequant=d_ref)
+    res_ref = rw.respin_align_prepared(res_x, B, rr, addend=y_ref, out_dtype=t.bfloat16)
+    _sync()
+    np.testing.assert_array_equal(host(y), host(y_ref))
+    np.testing.assert_array_equal(host(res_out), host(res_ref))
+    np.testing.assert_array_equal(host(d_fused), host(d_ref))
+    for a, b in zip(rw.workspace_views(ws, T, Din, True), rw.workspace_views(ws_ref, T, Din, True)):
+        np.testing.assert_array_equal(host(a), host(b))
+    # and the aligned residual against the oracle, as the layer tests check it
+    _check_residual(rw, host(res_x), host(y), B, rr, Q, M, host(res_out))
+
+
 @pytest.mark.parametrize("packed", [False, True])
 def test_layer_decode_config2(rw, packed):
     _layer_check(rw, 2, packed)
