@@ -391,6 +391,29 @@ rw4_status rotated_linear_prepared(const void* x, int64_t ldx, int64_t T, int64_
                                    void* stream);
 
 /*
+ * rotated_linear_prepared_project -- rotated_linear_prepared for short
+ * batches that also writes the alignment projection of its own input x for
+ * another prepared basis (respin_align_project_prepared(x, T, D, proj_basis,
+ * proj_r, proj_z, ...), the same bytes): in a decoder layer the skip input
+ * of a residual point is also the input of the next quantized linear, so
+ * the projection and the quantizer read the same rows, in one launch when
+ * D = 4096 ["ReSpinQuant" paper notes, key design 3].
+ *   x .. dbg_prequant  as rotated_linear_prepared; flags may not hold
+ *          RW4_ALIGN, RW4_SWIGLU or the structured transforms; ldx == D;
+ *          1 <= T <= 16
+ *   proj_basis, proj_r: prepared for (D, proj_r) by respin_prepare_basis
+ *   proj_z, proj_z_bytes: respin_align_project_size(T, D, proj_r) bytes,
+ *          256-byte aligned
+ * Asynchronous on `stream`; argument errors come before any launch.
+ */
+rw4_status rotated_linear_prepared_project(const void* x, int64_t ldx, int64_t T, int64_t D,
+                                           const void* basis, int64_t r, unsigned flags,
+                                           const uint8_t* w, const float* s_w, int64_t N, void* y,
+                                           void* workspace, size_t ws_bytes, float* dbg_prequant,
+                                           const void* proj_basis, int64_t proj_r, void* proj_z,
+                                           size_t proj_z_bytes, void* stream);
+
+/*
  * rotated_linear_prepared_residual -- rotated_linear_prepared for short
  * batches on packed INT4 weights whose product also finishes a residual
  * alignment of the layer: in a decoder layer the alignment sits on the skip
@@ -453,7 +476,7 @@ const char* rw4_status_string(rw4_status s);
 /* ABI version of this header (bumped on any signature change) */
 int rw4_abi_version(void);
 
-#define RW4_ABI_VERSION 11
+#define RW4_ABI_VERSION 12
 
 #ifdef __cplusplus
 }

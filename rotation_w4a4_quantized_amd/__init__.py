@@ -23,7 +23,7 @@ __all__ = [
     "quant_act_sym", "RW4_ABITS", "RW4_KRON", "RW4_HEADS", "hadamard_transform", "head_hadamard",
     "respin_construct", "respin_construct_workspace_size", "rotated_linear_prepared_noalloc",
     "NOALLOC_SCRATCH_BYTES", "respin_align_project_prepared", "respin_align_project_size",
-    "rotated_linear_prepared_residual",
+    "rotated_linear_prepared_residual", "rotated_linear_prepared_project",
 ]
 
 RW4_ALIGN, RW4_FWHT, RW4_SWIGLU = 1, 2, 4
@@ -60,7 +60,7 @@ EXPORTS = ("respin_align", "respin_align_workspace_size", "fwht", "quant_act_int
            "hadamard_transform", "head_hadamard", "respin_construct",
            "respin_construct_workspace_size", "rotated_linear_prepared_noalloc",
            "respin_align_project_prepared", "respin_align_project_size",
-           "rotated_linear_prepared_residual", "rw4_align256",
+           "rotated_linear_prepared_residual", "rotated_linear_prepared_project", "rw4_align256",
            "rw4_status_string", "rw4_abi_version")
 
 
@@ -109,6 +109,8 @@ def lib() -> ctypes.CDLL:
     L.respin_align_project_size.restype = sz
     L.rotated_linear_prepared_residual.argtypes = [vp, i64, i64, i64, vp, i64, u32, vp, vp, i64,
                                                    vp, vp, sz, vp, vp, vp, i64, vp, sz, vp, vp]
+    L.rotated_linear_prepared_project.argtypes = [vp, i64, i64, i64, vp, i64, u32, vp, vp, i64,
+                                                  vp, vp, sz, vp, vp, i64, vp, sz, vp]
     L.rotated_linear_prepared_workspace_size.argtypes = [i64, i64, i64, u32]
     L.rotated_linear_prepared_workspace_size.restype = sz
     L.respin_align_prepared.argtypes = [vp, vp, i32, vp, vp, i64, i64, i64, vp, sz, vp]
@@ -129,7 +131,8 @@ def lib() -> ctypes.CDLL:
               "w4a4_gemm_tiles", "rotated_linear", "respin_prepare_basis",
               "rotated_linear_prepared", "rotated_linear_prepared_noalloc",
               "respin_align_prepared", "respin_align_project_prepared",
-              "rotated_linear_prepared_residual", "hadamard_transform",
+              "rotated_linear_prepared_residual", "rotated_linear_prepared_project",
+              "hadamard_transform",
               "head_hadamard", "respin_construct"):
         getattr(L, f).restype = i32
     _lib = L
@@ -558,6 +561,34 @@ def rotated_linear_prepared_residual(x, w, s_w, flags: int, res_x, res_basis, re
     return out, res_out, workspace
 
 
+def rotated_linear_prepared_project(x, w, s_w, flags: int, proj_basis, proj_r: int, out=None,
+                                    proj_z=None, workspace=None, dbg_prequant=None):
+    """``rotated_linear_prepared`` (1 <= T <= 16, contiguous x, no alignment
+    in the unit) that also writes ``respin_align_project_prepared(x,
+    proj_basis, proj_r)``. Returns (y, proj_z, workspace)."""
+    torch = _torch()
+    _contig(x)
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bf16")
+    T, D = x.shape
+    N = s_w.shape[0]
+    _check_weights(w, N, D, flags)
+    need = rotated_linear_prepared_workspace_size(T, D, 0, flags)
+    if workspace is None:
+        workspace = torch.empty((max(need, 256),), dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    if proj_z is None:
+        proj_z = torch.empty((max(respin_align_project_size(T, D, proj_r), 256),),
+                             dtype=torch.uint8, device=x.device)
+    st = lib().rotated_linear_prepared_project(
+        _p(x), x.stride(0), T, D, None, 0, flags, _p(w), _p(s_w), N, _p(out), _p(workspace),
+        workspace.numel() * workspace.element_size(), _p(dbg_prequant), _p(proj_basis), proj_r,
+        _p(proj_z), proj_z.numel() * proj_z.element_size(), _stream())
+    _check("rotated_linear_prepared_project", st)
+    return out, proj_z, workspace
+
+
 NOALLOC_SCRATCH_BYTES = 64 << 20   # RW4_NOALLOC_SCRATCH_BYTES of include/rotw4a4.h
 
 
@@ -632,15 +663,15 @@ def layer(x0, aligns, weights, D: int, dbg_down=None, packed: bool = False):
     wf = RW4_WPACKED if packed else 0
     T = x0.shape[0]
     if packed and 1 <= T <= 16:
-        # short batches: each alignment's projection runs ahead, and the
-        # product that makes the residual's addend finishes the alignment in
-        # its epilogue (the same bits as the sequence below)
-        z1 = respin_align_project_prepared(x0, B1, r1)
-        st["qkv"], _ = rotated_linear(x0, *weights["qkv"], flags=wf)
+        # short batches: each alignment's projection runs with the quantizer
+        # of the same input, and the product that makes the residual's addend
+        # finishes the alignment in its epilogue (the same bits as the
+        # sequence below)
+        st["qkv"], z1, _ = rotated_linear_prepared_project(x0, *weights["qkv"], wf, B1, r1)
         st["o"], st["x1"], _ = rotated_linear_prepared_residual(
             st["qkv"][:, 2 * D:3 * D], *weights["o"], wf, x0, B1, r1, z1)
-        z2 = respin_align_project_prepared(st["x1"], B2, r2)
-        st["gate_up"], _ = rotated_linear(st["x1"], *weights["gate_up"], flags=wf)
+        st["gate_up"], z2, _ = rotated_linear_prepared_project(st["x1"], *weights["gate_up"], wf,
+                                                               B2, r2)
         st["down"], st["x2"], st["down_ws"] = rotated_linear_prepared_residual(
             st["gate_up"], *weights["down"], RW4_SWIGLU | RW4_FWHT | wf, st["x1"], B2, r2, z2,
             dbg_prequant=dbg_down)

@@ -104,10 +104,17 @@ rw4_status check_linear(const void* x, int64_t ldx, int64_t T, int64_t D, int64_
 }
 
 // the unit after validation; basis prepared for (D, r) when r > 0
+// the short-batch projection of the unit's own input for another basis
+struct SideProj {
+  const void* basis;
+  int64_t r;
+  float* z;
+};
+
 rw4_status run_linear(const void* x, int64_t ldx, int64_t T, int64_t D, const void* basis,
                       int64_t r, unsigned flags, const uint8_t* w, const float* s_w, int64_t N,
                       void* y, void* workspace, float* dbg, hipStream_t s,
-                      const rw4::GemmResidual* res = nullptr) {
+                      const rw4::GemmResidual* res = nullptr, const SideProj* sp = nullptr) {
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint8_t* codes = ws;
   // packed INT4 weights: the activation codes are packed rows [T][D/2] (they
@@ -162,6 +169,20 @@ rw4_status run_linear(const void* x, int64_t ldx, int64_t T, int64_t D, const vo
     e = rw4::launch_kron(src, in, ld, T, A, B, m, nullptr,
                          static_cast<float>(1.0 / __builtin_sqrt(c)), nullptr, codes, !pk, s_a,
                          dbg, abits(flags), s);
+  } else if (sp) {
+    // the quantizer and the side projection read the same rows: one launch
+    // when the shapes allow, else the projection and then the quantizer
+    const rw4::AlignBasis pb = rw4::align_basis(sp->basis, D, sp->r, with_p(D, sp->r));
+    const uint16_t* xb = static_cast<const uint16_t*>(src);
+    if (in == rw4::IN_BF16 && rw4::quant_project_fused(T, D)) {
+      e = rw4::launch_quant_project(xb, ld, T, D, (flags & RW4_FWHT) != 0, codes, !pk, s_a, dbg,
+                                    abits(flags), pb, sp->z, s);
+    } else {
+      e = rw4::launch_align_small_project(xb, T, D, sp->r, sp->basis, with_p(D, sp->r), sp->z, s);
+      if (e == hipSuccess)
+        e = rw4::launch_row(src, in, ld, T, D, (flags & RW4_FWHT) != 0, nullptr, codes, !pk, s_a,
+                            dbg, s, abits(flags));
+    }
   } else {
     e = rw4::launch_row(src, in, ld, T, D, (flags & RW4_FWHT) != 0, nullptr, codes, !pk, s_a, dbg,
                         s, abits(flags));
@@ -408,6 +429,31 @@ rw4_status respin_align_project_prepared(const void* x, int64_t T, int64_t D, co
   return hip_status(rw4::launch_align_small_project(static_cast<const uint16_t*>(x), T, D, r,
                                                     basis, with_p(D, r), static_cast<float*>(z),
                                                     strm(stream)));
+}
+
+rw4_status rotated_linear_prepared_project(const void* x, int64_t ldx, int64_t T, int64_t D,
+                                           const void* basis, int64_t r, unsigned flags,
+                                           const uint8_t* w, const float* s_w, int64_t N, void* y,
+                                           void* workspace, size_t ws_bytes, float* dbg_prequant,
+                                           const void* proj_basis, int64_t proj_r, void* proj_z,
+                                           size_t proj_z_bytes, void* stream) {
+  rw4_status st = check_linear(x, ldx, T, D, r, flags, w, s_w, N, y, dbg_prequant);
+  if (st != RW4_OK || T == 0) return st;
+  // the unit's input is the projected x itself: no alignment or gate in the
+  // unit, a plain power-of-two transform at most, contiguous rows
+  if ((flags & (RW4_ALIGN | RW4_SWIGLU)) || kron_m(flags) || heads_lg(flags) || ldx != D)
+    return RW4_ERR_UNSUPPORTED;
+  if (proj_r < 1) return RW4_ERR_INVALID_ARG;
+  const size_t zb = respin_align_project_size(T, D, proj_r);
+  if (zb == 0) return RW4_ERR_UNSUPPORTED;
+  if (!proj_basis || (reinterpret_cast<uintptr_t>(proj_basis) & 255u)) return RW4_ERR_INVALID_ARG;
+  if (!proj_z || (reinterpret_cast<uintptr_t>(proj_z) & 255u) || proj_z_bytes < zb)
+    return RW4_ERR_WORKSPACE;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return RW4_ERR_WORKSPACE;
+  if (ws_bytes < call_ws_bytes(T, D, 0)) return RW4_ERR_WORKSPACE;
+  const SideProj sp{proj_basis, proj_r, static_cast<float*>(proj_z)};
+  return run_linear(x, ldx, T, D, basis, 0, flags, w, s_w, N, y, workspace, dbg_prequant,
+                    strm(stream), nullptr, &sp);
 }
 
 rw4_status rotated_linear_prepared_residual(const void* x, int64_t ldx, int64_t T, int64_t D,

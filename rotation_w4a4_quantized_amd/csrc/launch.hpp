@@ -76,6 +76,14 @@ bool align_small(int64_t T, int64_t D);
 hipError_t launch_align_small(const uint16_t* x, void* out, int out_f32, const void* addend,
                               int64_t T, int64_t D, int64_t r, const void* basis, bool with_p,
                               float* Zs, hipStream_t s);
+// the quantizer of rows of a short batch (bf16 [T][4096], optional FWHT,
+// packed or tiled codes) and, in the same launch, the short-batch projection
+// of the same rows for the prepared basis pb into Zs
+bool quant_project_fused(int64_t T, int64_t D);
+hipError_t launch_quant_project(const uint16_t* x, int64_t ldx, int64_t T, int64_t D,
+                                bool do_fwht, uint8_t* codes, bool tiled, float* scales,
+                                float* dbg, int bits, const AlignBasis& pb, float* Zs,
+                                hipStream_t s);
 // the short-batch projection alone: Zs[c][t][i] for the align_small_chunks(D)
 // 256-column chunks c (align_zpart_bytes(T, D, r) bytes)
 int align_small_chunks(int64_t D);

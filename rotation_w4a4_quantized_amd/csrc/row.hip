@@ -17,6 +17,7 @@
 // code = clamp(rint(fl32(v / step)), -2^(b-1), 2^(b-1) - 1); symmetric absmax
 // keeps every code in [-(2^(b-1) - 1), 2^(b-1) - 1]. Codes are stored as INT4
 // nibbles (element 2j in the low nibble) or FP6 tile fields, whatever b.
+#include "align_small.hpp"
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -228,11 +229,12 @@ __device__ __forceinline__ void store_tiled(uint8_t* tiles, int64_t row, int64_t
   }
 }
 
+// one row block (ROWS rows) of row_kernel, block index blk
 template <int N, int E, int IN, bool FW, bool QOUT, bool TILED>
-__global__ void __launch_bounds__(1024)
-row_kernel(const void* __restrict__ x, int64_t ldx, int64_t T, float* __restrict__ yf,
-           uint8_t* __restrict__ codes, float* __restrict__ scales, float* __restrict__ dbg,
-           float norm, float qmax) {
+__device__ __forceinline__ void row_body(int64_t blk, const void* __restrict__ x, int64_t ldx,
+                                         int64_t T, float* __restrict__ yf,
+                                         uint8_t* __restrict__ codes, float* __restrict__ scales,
+                                         float* __restrict__ dbg, float norm, float qmax) {
   constexpr int D = 1 << N;
   constexpr int EPT = 1 << E;
   constexpr int P = D >> E;                         // threads per row
@@ -245,10 +247,6 @@ row_kernel(const void* __restrict__ x, int64_t ldx, int64_t T, float* __restrict
   const int tid = threadIdx.x;
   const int rl = tid / P;
   const int t = tid % P;
-  // tiled output: give each XCD (workgroups go to XCDs round-robin) a
-  // contiguous band of rows, so a tile's 32 rows are written through one L2
-  int64_t blk = blockIdx.x;
-  if (TILED && (gridDim.x & 7) == 0) blk = (blk & 7) * (gridDim.x >> 3) + (blk >> 3);
   const int64_t row = blk * ROWS + rl;
   const bool active = row < T;
 
@@ -298,6 +296,37 @@ row_kernel(const void* __restrict__ x, int64_t ldx, int64_t T, float* __restrict
       store_codes<EPT>(codes + row * (D / 2) + t * (EPT / 2), v, s);
     if (dbg) store_f32<EPT>(dbg + row * D + t * EPT, v);
   }
+}
+
+template <int N, int E, int IN, bool FW, bool QOUT, bool TILED>
+__global__ void __launch_bounds__(1024)
+row_kernel(const void* __restrict__ x, int64_t ldx, int64_t T, float* __restrict__ yf,
+           uint8_t* __restrict__ codes, float* __restrict__ scales, float* __restrict__ dbg,
+           float norm, float qmax) {
+  // tiled output: give each XCD (workgroups go to XCDs round-robin) a
+  // contiguous band of rows, so a tile's 32 rows are written through one L2
+  int64_t blk = blockIdx.x;
+  if (TILED && (gridDim.x & 7) == 0) blk = (blk & 7) * (gridDim.x >> 3) + (blk >> 3);
+  row_body<N, E, IN, FW, QOUT, TILED>(blk, x, ldx, T, yf, codes, scales, dbg, norm, qmax);
+}
+
+// The quantizer of a short batch (one 256-thread workgroup per row, D = 4096:
+// 16 values per thread) and, beside it in the same launch, the short-batch
+// alignment projection of the same rows for another basis (one 256-thread
+// workgroup per 256-column chunk): workgroups 0 .. nq - 1 quantize, the rest
+// project. Neither waits for the other; one launch instead of two.
+template <bool FW, bool TILED>
+__global__ void __launch_bounds__(256)
+quant_proj_kernel(const uint16_t* __restrict__ x, int64_t ldx, int64_t T, uint8_t* __restrict__ codes,
+                  float* __restrict__ scales, float* __restrict__ dbg, float norm, float qmax,
+                  int nq, int RP, int RK, const uint16_t* __restrict__ QtH,
+                  const uint16_t* __restrict__ QtL, float* __restrict__ Zs) {
+  if (static_cast<int>(blockIdx.x) < nq)
+    row_body<12, 4, IN_BF16, FW, true, TILED>(blockIdx.x, x, ldx, T, nullptr, codes, scales, dbg,
+                                             norm, qmax);
+  else
+    asmall_proj_body(static_cast<int>(blockIdx.x) - nq, x, static_cast<int>(T), 4096, RP, RK, QtH,
+                     QtL, Zs);
 }
 
 // ---------------------------------------------------------------- one wave per row
@@ -533,6 +562,29 @@ hipError_t launch_row(const void* x, int in_mode, int64_t ldx, int64_t T, int64_
   RW4_SEL(IN_SWIGLU, true, true, true) RW4_SEL(IN_SWIGLU, false, true, true)
   RW4_SEL(IN_BF16, false, true, true) RW4_SEL(IN_F32, false, true, true)
 #undef RW4_SEL
+  return hipErrorInvalidValue;
+}
+
+bool quant_project_fused(int64_t T, int64_t D) { return T >= 1 && T <= kSmallT && D == 4096; }
+
+hipError_t launch_quant_project(const uint16_t* x, int64_t ldx, int64_t T, int64_t D,
+                                bool do_fwht, uint8_t* codes, bool tiled, float* scales,
+                                float* dbg, int bits, const AlignBasis& pb, float* Zs,
+                                hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (!quant_project_fused(T, D) || bits < 2 || bits > 4) return hipErrorInvalidValue;
+  const float qmax = static_cast<float>((1 << (bits - 1)) - 1);
+  const float norm = static_cast<float>(1.0 / 64.0);   // 1 / sqrt(4096)
+  const dim3 grid(static_cast<unsigned>(T + D / kSmallChunk));
+#define RW4_QP(FW, TL)                                                                           \
+  if (do_fwht == FW && tiled == TL) {                                                            \
+    hipLaunchKernelGGL((quant_proj_kernel<FW, TL>), grid, dim3(256), 0, s, x, ldx, T, codes,    \
+                       scales, dbg, norm, qmax, static_cast<int>(T), pb.RP, pb.RK, pb.QtH,      \
+                       pb.QtL, Zs);                                                             \
+    return hipGetLastError();                                                                    \
+  }
+  RW4_QP(false, false) RW4_QP(false, true) RW4_QP(true, false) RW4_QP(true, true)
+#undef RW4_QP
   return hipErrorInvalidValue;
 }
 

@@ -22,7 +22,7 @@ def _declared():
 def test_library_built_and_loads():
     assert os.path.exists(rw.library_path), "build the HIP library first"
     L = rw.lib()
-    assert L.rw4_abi_version() == 11
+    assert L.rw4_abi_version() == 12
 
 
 def test_exports_every_declared_symbol():
@@ -280,6 +280,27 @@ def test_residual_entries_validation():
     assert _rlr(rz=NUL) == WSE and _rlr(rzb=100) == WSE
     assert _rlr(ws=NUL) == WSE
     assert _rlr(T=0) == 0
+
+
+def _rlj(x=A, ldx=4096, T=8, D=4096, flags=(1 << 29), N=4096, y=B, ws=C, wsb=1 << 22,
+         pb=ctypes.c_void_p(0x50000), pr=32, pz=ctypes.c_void_p(0x60000), pzb=1 << 20):
+    return rw.lib().rotated_linear_prepared_project(x, ldx, T, D, NUL, 0, flags, Dp, A, N, y, ws,
+                                                    wsb, NUL, pb, pr, pz, pzb, NUL)
+
+
+def test_projecting_unit_validation():
+    assert _rlj() is not None
+    assert _rlj(T=17) == UNS                        # short batches only
+    assert _rlj(flags=(1 << 29) | 1) == UNS         # the unit aligns nothing itself
+    assert _rlj(flags=(1 << 29) | 4, ldx=8192) == UNS
+    assert _rlj(ldx=8192) == UNS                    # contiguous rows
+    assert _rlj(pr=0) == INV and _rlj(pr=6) == UNS
+    assert _rlj(pb=NUL) == INV and _rlj(pb=ctypes.c_void_p(0x50010)) == INV
+    assert _rlj(pz=NUL) == WSE and _rlj(pzb=100) == WSE
+    assert _rlj(pz=ctypes.c_void_p(0x60010)) == WSE
+    assert _rlj(ws=NUL) == WSE and _rlj(wsb=100) == WSE
+    assert _rlj(x=ODD) == MIS
+    assert _rlj(T=0) == 0
 
 
 def test_structured_transform_validation():

@@ -930,6 +930,52 @@ def _layer_check(rw, cid, packed=False):
     _check_gemm_out(g["down"], q, s, qws["down"], sws["down"])
 
 
+# the unit that also projects its own input for an alignment: the same bits
+# as the unit and the projection called apart (one launch at D = 4096, the
+# projection then the quantizer otherwise); packed and tiled weights, the
+# transform in the unit, ragged token counts, both basis widths
+@pytest.mark.parametrize("T,D,N,rr,flags,packed", [(8, 4096, 12288, 32, 0, True),
+                                                   (3, 4096, 4096, 64, 0, True),
+                                                   (16, 4096, 640, 32, 2, False),
+                                                   (1, 4096, 4096, 8, 2, True),
+                                                   (8, 1024, 512, 32, 0, True),
+                                                   (5, 8192, 256, 64, 2, False)])
+def test_rotated_linear_project(rw, T, D, N, rr, flags, packed):
+    say(f"rotated_linear_prepared_project T={T} D={D} N={N} r={rr} flags={flags} packed={packed}")
+    t = torch()
+    fl = flags | (rw.RW4_WPACKED if packed else 0)
+    x = dev(W.gen_x(720 + T, T, D, 8, 80.0))
+    Wf = W.gen_weight(721, N, D, 0.02)
+    tiles, s_w, codes, _ = rw.prep_weight(dev(Wf), bool(flags & O.FLAG_FWHT))
+    w = codes if packed else tiles
+    Q, M = W.gen_basis(722, D, rr)
+    B = rw.respin_prepare_basis(dev(Q), dev(M))
+    d1 = t.empty((T, D), dtype=t.float32, device="cuda")
+    y, z, ws = rw.rotated_linear_prepared_project(x, w, s_w, fl, B, rr, dbg_prequant=d1)
+    d2 = t.empty((T, D), dtype=t.float32, device="cuda")
+    y_ref, ws_ref = rw.rotated_linear_prepared(x, w, s_w, fl, dbg_prequant=d2)
+    z_ref = rw.respin_align_project_prepared(x, B, rr)
+    _sync()
+    n = rw.respin_align_project_size(T, D, rr)
+    np.testing.assert_array_equal(host(y), host(y_ref))
+    np.testing.assert_array_equal(host(d1), host(d2))
+    np.testing.assert_array_equal(host(z)[:n], host(z_ref)[:n])
+    (c1, s1), (c2, s2) = rw.workspace_views(ws, T, D, packed), rw.workspace_views(ws_ref, T, D, packed)
+    np.testing.assert_array_equal(host(s1), host(s2))
+    # the codes of the T rows (tiles pad to 256 rows that nobody writes)
+    dec = (lambda c: host(c)) if packed else (lambda c: F.untile(host(c), T, D))
+    np.testing.assert_array_equal(dec(c1), dec(c2))
+    # the projection finishes into the oracle's alignment: the residual
+    # product on it against respin_align_prepared is checked by the residual
+    # test; here its lift through the residual entry with a zero block output
+    if packed and N == D:
+        zero_x = t.zeros((T, 2 * D if fl & O.FLAG_SWIGLU else D), dtype=t.bfloat16, device="cuda")
+        _, res_out, _ = rw.rotated_linear_prepared_residual(zero_x, w, s_w, fl, x, B, rr, z)
+        res_ref = rw.respin_align_prepared(x, B, rr, out_dtype=t.bfloat16)
+        _sync()
+        np.testing.assert_array_equal(host(res_out), host(res_ref))
+
+
 # the product that finishes a residual alignment (short batches, packed
 # weights): the same bits as the product and the aligned residual computed
 # apart; decode shapes (o and down projections), ragged token counts, both
