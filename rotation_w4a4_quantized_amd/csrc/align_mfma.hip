@@ -493,6 +493,208 @@ lift_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int S, int 
   }
 }
 
+// The lift as a loop over 64-token blocks (RK <= 64, z already summed over
+// the D parts). A grid of G x S workgroups, about one per CU: the workgroup of
+// D part p takes the blocks b, b + G, b + 2G, ... Its slice of Q (the part's
+// 512 rows, bf16 hi/lo) is loaded once and stays in registers, and the next
+// block's z, x and addend are loaded while the current block is multiplied
+// and written, so a CU keeps a block of loads in flight behind its stores
+// instead of waiting for memory once per block (one workgroup per CU fits
+// the registers this takes). z goes through a double-buffered LDS split and
+// the results through the stage above; the arithmetic per output is the
+// lift kernel's, in the same order (the addend joins the fp32 accumulator
+// before the bf16 rounding, as there), so both give the same bits.
+template <int RK, bool OF32, bool ADD>
+__global__ void __launch_bounds__(LNW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+lift_loop_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P,
+                 const float* __restrict__ Z, const uint16_t* __restrict__ QH,
+                 const uint16_t* __restrict__ QL, const uint16_t* __restrict__ addend,
+                 void* __restrict__ out) {
+  static_assert(RK == 32 || RK == 64, "the Q slice is held in registers");
+  static_assert(!(OF32 && ADD), "a bf16 addend joins bf16 outputs only");
+  constexpr int NT = LNW * 64;
+  constexpr int KQ = RK / 32;
+  constexpr int ZC = TPW * RK / 4;  // float4 chunks of one block's z
+  constexpr int ZPT = ZC / NT;
+  static_assert(ZC % NT == 0, "z chunks per thread");
+  __shared__ __attribute__((aligned(16))) uint16_t zh[2][TPW][RK + 8];
+  __shared__ __attribute__((aligned(16))) uint16_t zl[2][TPW][RK + 8];
+  __shared__ __attribute__((aligned(16))) float stage[TB][kPart + 4];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int part = blockIdx.y;
+  const int dbeg = part * P;
+  const int dend = min(D, dbeg + P);
+  const int nds = (dend - dbeg) / 64;
+  const int ncols = dend - dbeg;
+  const int g = lane >> 4;
+  const int tl = lane & 15;
+  const bool live = wave < nds;
+  const int d0 = dbeg + 64 * (live ? wave : nds - 1);
+  const int64_t nb = (T + TPW - 1) / TPW;
+  const int64_t G = gridDim.x;
+  int64_t blk = blockIdx.x;
+  if (blk >= nb) return;
+
+  // loads of block b (tokens past T re-read the last token); unconditional
+  float4 zn[ZPT];
+  uint4 xn[TBW][2], an[TBW][2];
+  auto load_block = [&](int64_t b) {
+#pragma unroll
+    for (int u = 0; u < ZPT; ++u) {
+      const int c = tid + u * NT;
+      const int64_t trow = min(b * TPW + (4 * c) / RK, T - 1);
+      zn[u] = *reinterpret_cast<const float4*>(Z + trow * RK + (4 * c) % RK);
+    }
+#pragma unroll
+    for (int tb = 0; tb < TBW; ++tb) {
+      const int64_t off = min(b * TPW + 16 * tb + tl, T - 1) * D + d0 + 16 * g;
+      const uint4* px = reinterpret_cast<const uint4*>(x + off);
+      xn[tb][0] = px[0];
+      xn[tb][1] = px[1];
+      if constexpr (ADD) {
+        const uint4* pa = reinterpret_cast<const uint4*>(addend + off);
+        an[tb][0] = pa[0];
+        an[tb][1] = pa[1];
+      }
+    }
+  };
+  // z of a block, its bf16 split into LDS buffer q
+  auto put_z = [&](int q) {
+#pragma unroll
+    for (int u = 0; u < ZPT; ++u) {
+      const int c = tid + u * NT;
+      const int tt = (4 * c) / RK;
+      const int i = (4 * c) % RK;
+      const float zz[4] = {zn[u].x, zn[u].y, zn[u].z, zn[u].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint16_t h = f32_to_bf16(zz[e]);
+        zh[q][tt][i + e] = h;
+        zl[q][tt][i + e] = f32_to_bf16(zz[e] - bf16_to_f32(h));
+      }
+    }
+  };
+
+  v8bf qh[4][KQ], ql[4][KQ];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int drow = d0 + 16 * (tl >> 2) + 4 * b + (tl & 3);
+#pragma unroll
+    for (int kk = 0; kk < KQ; ++kk) {
+      const int64_t qo = static_cast<int64_t>(drow) * RK + 32 * kk + 8 * g;
+      qh[b][kk] = ld8(QH + qo);
+      ql[b][kk] = ld8(QL + qo);
+    }
+  }
+  // this thread's store chunks of a 16-token result block: row and column
+  constexpr int CW = OF32 ? 4 : 8;              // values per 16-byte store
+  constexpr int SIT = TB * kPart / CW / NT;     // stores per thread
+  int sr[SIT], sc[SIT];
+#pragma unroll
+  for (int it = 0; it < SIT; ++it) {
+    const int c = tid + it * NT;
+    sr[it] = c / (kPart / CW);
+    const int col = (c % (kPart / CW)) * CW;
+    sc[it] = col < ncols ? col : col % ncols;
+  }
+  load_block(blk);
+  put_z(0);
+  lds_barrier();
+  int q = 0;
+  for (;;) {
+    uint4 xc[TBW][2], ac[TBW][2];
+#pragma unroll
+    for (int tb = 0; tb < TBW; ++tb) {
+      xc[tb][0] = xn[tb][0];
+      xc[tb][1] = xn[tb][1];
+      if constexpr (ADD) {
+        ac[tb][0] = an[tb][0];
+        ac[tb][1] = an[tb][1];
+      }
+    }
+    const int64_t t0 = blk * TPW;
+    const bool more = blk + G < nb;
+    // the next block's loads (the last block's again after the final one)
+    load_block(more ? blk + G : blk);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int tb = 0; tb < TBW; ++tb) {
+      if (live) {
+        v4f acc[4];
+        acc[0] = v4f{bf16lo(xc[tb][0].x), bf16hi(xc[tb][0].x), bf16lo(xc[tb][0].y), bf16hi(xc[tb][0].y)};
+        acc[1] = v4f{bf16lo(xc[tb][0].z), bf16hi(xc[tb][0].z), bf16lo(xc[tb][0].w), bf16hi(xc[tb][0].w)};
+        acc[2] = v4f{bf16lo(xc[tb][1].x), bf16hi(xc[tb][1].x), bf16lo(xc[tb][1].y), bf16hi(xc[tb][1].y)};
+        acc[3] = v4f{bf16lo(xc[tb][1].z), bf16hi(xc[tb][1].z), bf16lo(xc[tb][1].w), bf16hi(xc[tb][1].w)};
+#pragma unroll
+        for (int kk = 0; kk < KQ; ++kk) {
+          const v8bf bh = *reinterpret_cast<const v8bf*>(&zh[q][16 * tb + tl][32 * kk + 8 * g]);
+          const v8bf bl = *reinterpret_cast<const v8bf*>(&zl[q][16 * tb + tl][32 * kk + 8 * g]);
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            acc[b] = mfma(qh[b][kk], bh, acc[b]);
+            acc[b] = mfma(ql[b][kk], bh, acc[b]);
+            acc[b] = mfma(qh[b][kk], bl, acc[b]);
+          }
+        }
+        mfma_drain();
+        if constexpr (ADD) {
+          const uint32_t aw[8] = {ac[tb][0].x, ac[tb][0].y, ac[tb][0].z, ac[tb][0].w,
+                                  ac[tb][1].x, ac[tb][1].y, ac[tb][1].z, ac[tb][1].w};
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            acc[b][0] += bf16lo(aw[2 * b]);
+            acc[b][1] += bf16hi(aw[2 * b]);
+            acc[b][2] += bf16lo(aw[2 * b + 1]);
+            acc[b][3] += bf16hi(aw[2 * b + 1]);
+          }
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          *reinterpret_cast<float4*>(&stage[tl][64 * wave + 16 * g + 4 * b]) =
+              make_float4(acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
+      }
+      lds_barrier();
+      // a fixed number of unconditional stores per thread, so that the wait
+      // for the next block's loads leaves these stores in flight (with a
+      // runtime count the compiler must drain them all first). A row past T
+      // holds exactly row T - 1's values (its x, addend and z loads were
+      // clamped to that token) and rewrites them there; a column past a short
+      // last part rewrites a column of the part.
+#pragma unroll
+      for (int it = 0; it < SIT; ++it) {
+        const int row = sr[it];
+        const int col = sc[it];
+        const int64_t off = min(t0 + 16 * tb + row, T - 1) * D + dbeg + col;
+        if constexpr (OF32) {
+          *reinterpret_cast<float4*>(static_cast<float*>(out) + off) =
+              *reinterpret_cast<const float4*>(&stage[row][col]);
+        } else {
+          const float4 s0 = *reinterpret_cast<const float4*>(&stage[row][col]);
+          const float4 s1 = *reinterpret_cast<const float4*>(&stage[row][col + 4]);
+          const float o[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+          uint32_t w[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            w[i] = f32_to_bf16(o[2 * i]) | (static_cast<uint32_t>(f32_to_bf16(o[2 * i + 1])) << 16);
+          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + off) =
+              make_uint4(w[0], w[1], w[2], w[3]);
+        }
+      }
+      if (tb + 1 < TBW) lds_barrier();
+    }
+    // the next block's z into the other buffer (its last reader was before
+    // the previous iteration's final barrier), then one barrier for both the
+    // stage and z
+    put_z(q ^ 1);
+    lds_barrier();
+    if (!more) break;
+    q ^= 1;
+    blk += G;
+  }
+}
+
 // Short batches (T <= kSmallT tokens, decode): the two steps on the vector
 // ALUs, spread over D instead of over tokens, since a few tokens leave the
 // token-blocked kernels a handful of workgroups that each pull the whole basis
@@ -660,6 +862,27 @@ hipError_t run_lift(const uint16_t* x, int64_t T, int D, int P, int S, int SZ, i
   return hipErrorInvalidValue;
 }
 
+template <int RK>
+hipError_t run_lift_loop(const uint16_t* x, int64_t T, int D, int P, int64_t G, int S,
+                         const float* Z, const uint16_t* QH, const uint16_t* QL,
+                         const void* addend, void* out, bool of32, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(G), S);
+  const uint16_t* ab = static_cast<const uint16_t*>(addend);
+  if (of32)
+    hipLaunchKernelGGL((lift_loop_kernel<RK, true, false>), grid, dim3(LNW * 64), 0, s, x, T, D, P,
+                       Z, QH, QL, ab, out);
+  else if (addend != nullptr) {
+    if constexpr (RK == 64)
+      hipLaunchKernelGGL((lift_loop_kernel<RK, false, true>), grid, dim3(LNW * 64), 0, s, x, T, D,
+                         P, Z, QH, QL, ab, out);
+    else
+      return hipErrorInvalidValue;  // not taken: the one-block kernel serves RK = 32 with addend
+  } else
+    hipLaunchKernelGGL((lift_loop_kernel<RK, false, false>), grid, dim3(LNW * 64), 0, s, x, T, D,
+                       P, Z, QH, QL, ab, out);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 bool align_mfma_supported(int64_t D, int64_t r) { return r > 0 && r <= 128 && D % 64 == 0; }
@@ -792,6 +1015,17 @@ hipError_t launch_lift(const uint16_t* x, void* out, int out_f32, const void* ad
   const int ri = static_cast<int>(r);
   const int S = align_parts_count(D);
   const bool of32 = out_f32 != 0;
+  // the loop form from 16 D parts on, when every workgroup of a grid of about
+  // one per CU gets at least two blocks. Measured against the one-block
+  // kernel: 193.7 -> 152.7 us at T = D = 8192, r = 64 (fp32 out); slower at
+  // 8 parts, where two resident one-block workgroups per CU keep more loads
+  // in flight than one looping workgroup (which also needs the partials
+  // summed first), and with an addend at RK = 32 (its registers for a small
+  // basis slice: 76.8 against 72.2 us at T = 4096, D = 8192)
+  const int64_t nb = (T + TPW - 1) / TPW;
+  const int64_t G = std::max<int64_t>(1, device_cus() / S);
+  const bool loop = S >= 16 && a.RK <= 64 && (addend == nullptr || (a.RK == 64 && !of32)) &&
+                    nb >= 2 * G;
   // from 16 D parts on, the partials are summed once (in place) for all
   // workgroups: S^2 T RK floats of L2 reads become S T RK
   int SZ = S;
@@ -802,6 +1036,11 @@ hipError_t launch_lift(const uint16_t* x, void* out, int out_f32, const void* ad
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     SZ = 1;
+  }
+  if (loop) {
+    if (a.RK == 32)
+      return run_lift_loop<32>(x, T, Di, kPart, G, S, Zpart, a.QH, a.QL, addend, out, of32, s);
+    return run_lift_loop<64>(x, T, Di, kPart, G, S, Zpart, a.QH, a.QL, addend, out, of32, s);
   }
   switch (a.RP) {
 #define RW4_L(V, K) \

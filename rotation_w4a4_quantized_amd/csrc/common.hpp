@@ -32,6 +32,16 @@ __device__ __forceinline__ void mfma_drain() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// this wave's LDS accesses have completed, then a workgroup barrier that the
+// compiler may not move memory accesses across; global loads and stores in
+// flight stay in flight
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt untouched
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // bf16 bits -> fp32 (exact)
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);

@@ -641,22 +641,6 @@ hipError_t launch_cfg(const uint8_t* a, const float* s_a, const uint8_t* w, cons
   return hipGetLastError();
 }
 
-// compute units of the current device (256 on MI355X), read once per device
-inline int device_cus() {
-  constexpr int kMaxDev = 64;
-  static std::atomic<int> cache[kMaxDev];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 256;
-  int n = cache[dev].load(std::memory_order_relaxed);
-  if (n == 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n <= 0)
-      n = 256;
-    cache[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
-
 // rt for gemm6_lds_kernel: the split of the tile grid into 8 XCD rectangles
 // (rt along T, 8 / rt along N) with the fewest A and W rows per XCD, or 0
 // when no split divides the grid evenly
@@ -718,7 +702,7 @@ hipError_t launch_gemm_tiles(const uint8_t* a, const float* s_a, const uint8_t* 
     // one of 256 x 256 blocks on half the CUs) and 256 x 256 from 3072 x 4096
     // or 2048 x 8192 up.
     const bool big = T >= 2048 && N >= 4096;
-    const int64_t cus = g6::device_cus();
+    const int64_t cus = device_cus();
     const int64_t w2 = ((T + 255) / 256 * ((N + 255) / 256) + cus - 1) / cus;
     const int64_t w1 = ((T + 255) / 256 * ((N + 127) / 128) + cus - 1) / cus;
     const bool huge = big && 16 * w2 < 9 * w1;

@@ -43,15 +43,6 @@ constexpr int kChunkPitch = 144;     // bytes per 32-value chunk in the lift buf
 // byte offset of 32-value chunk c in a token's lift buffer
 __device__ __forceinline__ int lift_off(int c) { return c * kChunkPitch; }
 
-// this wave's LDS writes have completed, then a workgroup barrier that the
-// compiler may not move memory accesses across
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt untouched
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // The lift waves of a 16-wave workgroup of kTok tokens (waves 8..15, lw =
 // wave - 8): z of the tokens from the projection's parts (summed in a fixed
 // order, bf16 hi/lo split into zh/zl), then A z on bf16 matrix cores for

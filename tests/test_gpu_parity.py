@@ -310,6 +310,50 @@ def test_respin_align_prepared(rw, T, D, r, odt, add):
     assert normwise(got, want) <= tol
 
 
+# From 16 D parts of 512 columns (D > 7680), batches of at least 2 * floor(256 / S)
+# blocks of 64 tokens (S parts, 256 CUs) take the looping lift when r <= 64
+# (with an addend, 32 < r <= 64): one workgroup per (D part, token stride)
+# keeps its basis slice in registers across blocks. A 64-token slice takes
+# the one-block lift; the rows of both must agree bit for bit, and both the
+# oracle's alignment.
+@pytest.mark.parametrize("T,D,r,odt,add", [
+    (2053, 8192, 64, "f32", False),      # the 70B-shaped prologue's lift, ragged tail
+    (2048, 8192, 32, "f32", False),      # exactly two blocks per workgroup
+    (1100, 16384, 32, "f32", False),     # 32 parts, 18 blocks over 8 strides
+    (2000, 8256, 64, "bf16", False),     # a last part of 64 columns (7 idle waves)
+    (2100, 8192, 48, "bf16", True),      # r padded to 64, bf16 addend
+    (1030, 16384, 64, "bf16", True)])
+def test_respin_align_looping_lift(rw, T, D, r, odt, add):
+    say(f"looping lift T={T} D={D} r={r} out={odt} addend={add}")
+    tt = torch()
+    Q, M = W.gen_basis(D + 7 * r, D, r)
+    xb = W.gen_x(D + T + 3, T, D, 8, 80.0)
+    out_dtype = tt.float32 if odt == "f32" else tt.bfloat16
+    addend = None
+    if add:
+        addend = dev(W.f32_to_bf16_bits(W.bf16_bits_to_f32(W.gen_x(D + T + 4, T, D, 0, 1.0))))
+    basis = rw.respin_prepare_basis(dev(Q), dev(M))
+    xg = dev(xb)
+    out = rw.respin_align_prepared(xg, basis, r, addend=addend, out_dtype=out_dtype)
+    for t0 in range(0, T, 64):
+        t1 = min(T, t0 + 64)
+        # a slice of up to 16 rows would take the short-batch kernels: the tail
+        # is checked inside the last 64 rows (each token's z and lift do not
+        # depend on the other tokens of its block)
+        s0 = t1 - 64 if t1 - t0 <= 16 else t0
+        part = rw.respin_align_prepared(xg[s0:t1].contiguous(), basis, r,
+                                        addend=None if addend is None else addend[s0:t1].contiguous(),
+                                        out_dtype=out_dtype)[t0 - s0:]
+        if not tt.equal(part, out[t0:t1]):
+            bad = (part != out[t0:t1]).nonzero()[:4].tolist()
+            raise AssertionError(f"rows {t0}..{t1}: looping lift differs at {bad}")
+    want = O.align(W.bf16_bits_to_f32(xb), Q, M)
+    if add:
+        want = want + O.bf16_to_f64(host(addend))
+    got = host(out) if odt == "f32" else O.bf16_to_f64(host(out))
+    assert normwise(got, want) <= (FP32_TOL if odt == "f32" else BF16_TOL)
+
+
 @pytest.mark.parametrize("T,D,r", [(33, 4096, 32), (8, 4096, 32), (70, 256, 8)])
 @pytest.mark.parametrize("direct", [False, True])
 def test_respin_align_bf16_residual(rw, T, D, r, direct):
