@@ -132,6 +132,46 @@ def test_fwht_in_place_and_involution(rw):
     assert normwise(host(g), x) <= 2 * FP32_TOL
 
 
+# Long batches of wide rows (many workgroups per CU over the launch): every
+# row equals the same row run in a slice of 256 rows, bit for bit, and the
+# oracle's.
+def _same_as_slices(full, run, xg, T, step=256):
+    tt = torch()
+    for t0 in range(0, T, step):
+        part = run(xg[t0:t0 + step].contiguous())
+        for a, b in zip(part if isinstance(part, tuple) else (part,),
+                        full if isinstance(full, tuple) else (full,)):
+            if not tt.equal(a, b[t0:t0 + step]):
+                raise AssertionError(f"rows {t0}..{t0 + step} differ from the slice's")
+
+
+@pytest.mark.parametrize("T,D,dt", [(1100, 16384, "f32"), (1030, 32768, "bf16")])
+def test_fwht_long_batches(rw, T, D, dt):
+    say(f"fwht long batch T={T} D={D} {dt}")
+    x32 = W.bf16_bits_to_f32(W.gen_x(D + T, T, D, 8, 80.0))
+    xg = dev(W.f32_to_bf16_bits(x32)) if dt == "bf16" else dev(x32)
+    y = rw.fwht(xg)
+    _same_as_slices(y, rw.fwht, xg, T)
+    assert normwise(host(y), O.fwht(x32)) <= FP32_TOL
+
+
+@pytest.mark.parametrize("T,D,dt", [(1100, 16384, "f32"), (2100, 8192, "bf16"), (1030, 32768, "f32")])
+def test_quant_act_int4_long_batches(rw, T, D, dt):
+    say(f"quant_act_int4 long batch T={T} D={D} {dt}")
+    x = _quant_input(T, D, seed=T + D)
+    if dt == "bf16":
+        xb = W.f32_to_bf16_bits(x)
+        xg = dev(xb)
+        x = W.bf16_bits_to_f32(xb)
+    else:
+        xg = dev(x)
+    codes, scales = rw.quant_act_int4(xg)
+    _same_as_slices((codes, scales), rw.quant_act_int4, xg, T)
+    q, s = O.quant_int4(x)
+    np.testing.assert_array_equal(host(scales), s)
+    np.testing.assert_array_equal(host(codes), O.pack_int4(q))
+
+
 # ---------------------------------------------------------------- structured Hadamard
 @pytest.mark.parametrize("T,n,m", [(37, 4, 12), (9, 5, 20), (5, 9, 28), (20, 12, 1), (3, 14, 1),
                                    (2, 1, 12), (4, 0, 28), (6, 8, 20)])
@@ -667,7 +707,10 @@ def test_rotated_linear_config4(rw):
                                          (1, 4096, 4096, 3), (21, 4096, 64, 4 | 2),
                                          (6, 8192, 64, 4 | 2), (9, 2048, 64, 2),
                                          # the down projection's width in the layers
-                                         (8, 16384, 64, 4 | 2), (300, 16384, 128, 4 | 2)])
+                                         (8, 16384, 64, 4 | 2), (300, 16384, 128, 4 | 2),
+                                         # long batches (at D = 8192 the looping lift)
+                                         (1100, 16384, 64, 4 | 2), (2100, 8192, 64, 1 | 2),
+                                         (4100, 4096, 64, 0)])
 def test_rotated_linear_flags(rw, T, D, N, flags):
     say(f"rotated_linear T={T} D={D} N={N} flags={flags}")
     width = 2 * D if flags & 4 else D
