@@ -298,6 +298,140 @@ yproj_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int r,
   }
 }
 
+// The projection as a loop over 64-token blocks from 16 D parts on (RP <= 64):
+// a grid of G x S workgroups, about one per CU; the workgroup of D part p
+// takes the blocks b, b + G, b + 2G, ... Its block of Q' (RP rows of the
+// part, bf16 hi/lo) is loaded once and stays in registers, and the next
+// block's x is loaded while the current one is multiplied, reduced and
+// stored. The products, their order and the reduction are those of
+// yproj_kernel, so both give the same partials. Tokens past T re-read the
+// last token and rewrite its partials with the same bits; every thread
+// issues a fixed number of stores, so the wait for the next block's x leaves
+// them in flight.
+template <int RP>
+__global__ void __launch_bounds__(YNW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+yproj_loop_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P,
+                  const uint16_t* __restrict__ QtH, const uint16_t* __restrict__ QtL,
+                  float* __restrict__ Zpart) {
+  static_assert(RP <= 64 && DPW == 1, "the basis block is held in registers");
+  constexpr int RK = (RP + 31) / 32 * 32;
+  constexpr int NT = YNW * 64;
+  constexpr int NBC = RP / 16;
+  constexpr int ZST = YTPW * RK / NT;                 // partial stores per thread and block
+  static_assert(YTPW * RK % NT == 0, "stores per thread");
+  __shared__ float red[4][YTPW][RP + 1];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int part = blockIdx.y;
+  const int dbeg = part * P;
+  const int dend = min(D, dbeg + P);
+  const int nds = (dend - dbeg) / 64;
+  const int g = lane >> 4;
+  const int tl = lane & 15;
+  const int dsc = wave < nds ? wave : nds - 1;
+  const uint32_t keep = wave < nds ? 0xFFFFFFFFu : 0u;  // a double step past the part is zero
+  const int64_t nb = (T + YTPW - 1) / YTPW;
+  const int64_t G = gridDim.x;
+  int64_t blk = blockIdx.x;
+  if (blk >= nb) return;
+
+  v8bf bh[NBC][2], bl[NBC][2];
+#pragma unroll
+  for (int c = 0; c < NBC; ++c) {
+    const int64_t qo = static_cast<int64_t>(16 * c + tl) * D + dbeg + 64 * dsc + 16 * g;
+    bh[c][0] = ld8(QtH + qo);
+    bh[c][1] = ld8(QtH + qo + 8);
+    bl[c][0] = ld8(QtL + qo);
+    bl[c][1] = ld8(QtL + qo + 8);
+  }
+  uint4 xn[YTBW][2];
+  auto load_x = [&](int64_t b) {
+#pragma unroll
+    for (int tb = 0; tb < YTBW; ++tb) {
+      const int64_t trow = min(b * YTPW + 16 * tb + tl, T - 1);
+      const uint4* px = reinterpret_cast<const uint4*>(x + trow * D + 16 * g + dbeg + 64 * dsc);
+      xn[tb][0] = px[0];
+      xn[tb][1] = px[1];
+    }
+  };
+  v8bf xa[YTBW][2];
+  auto take_x = [&]() {
+#pragma unroll
+    for (int tb = 0; tb < YTBW; ++tb) {
+      uint4 a0 = xn[tb][0], a1 = xn[tb][1];
+      a0.x &= keep; a0.y &= keep; a0.z &= keep; a0.w &= keep;
+      a1.x &= keep; a1.y &= keep; a1.z &= keep; a1.w &= keep;
+      xa[tb][0] = as8(a0);
+      xa[tb][1] = as8(a1);
+    }
+  };
+  load_x(blk);
+  take_x();
+  // the basis block has arrived too (an explicit vmcnt(0)): otherwise its
+  // waits land inside the loop, where they also drain the previous round's
+  // stores
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  for (;;) {
+    const int64_t t0 = blk * YTPW;
+    const bool more = blk + G < nb;
+    load_x(more ? blk + G : blk);
+    __builtin_amdgcn_sched_barrier(0);
+    v4f acc[YTBW][NBC];
+#pragma unroll
+    for (int tb = 0; tb < YTBW; ++tb)
+#pragma unroll
+      for (int c = 0; c < NBC; ++c) acc[tb][c] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int c = 0; c < NBC; ++c)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int tb = 0; tb < YTBW; ++tb) {
+          acc[tb][c] = mfma(xa[tb][h], bh[c][h], acc[tb][c]);
+          acc[tb][c] = mfma(xa[tb][h], bl[c][h], acc[tb][c]);
+        }
+    mfma_drain();
+    if (wave >= 4) {
+#pragma unroll
+      for (int tb = 0; tb < YTBW; ++tb)
+#pragma unroll
+        for (int c = 0; c < NBC; ++c)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) red[wave - 4][16 * tb + 4 * g + v][16 * c + tl] = acc[tb][c][v];
+    }
+    lds_barrier();
+    if (wave < 4) {
+#pragma unroll
+      for (int tb = 0; tb < YTBW; ++tb)
+#pragma unroll
+        for (int c = 0; c < NBC; ++c)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            float& slot = red[wave][16 * tb + 4 * g + v][16 * c + tl];
+            slot = acc[tb][c][v] + slot;
+          }
+    }
+    lds_barrier();
+#pragma unroll
+    for (int k = 0; k < ZST; ++k) {
+      const int o = tid + k * NT;
+      const int t = o / RK;
+      const int i = o % RK;
+      float z = 0.0f;
+      if (i < RP) z = (red[0][t][i] + red[1][t][i]) + (red[2][t][i] + red[3][t][i]);
+      Zpart[(static_cast<int64_t>(part) * T + min(t0 + t, T - 1)) * RK + i] = z;
+    }
+    // every read of red is done before the next block's writes
+    lds_barrier();
+    if (!more) break;
+    // the next block's x, taken here at the end of the round so that the only
+    // path to this wait is the one through this round's stores
+    take_x();
+    blk += G;
+  }
+}
+
 // The lift runs 8 waves per workgroup, one 64-column double step each, so a
 // 512-column part of 64 tokens keeps two waves per SIMD busy.
 constexpr int LNW = 8;
@@ -817,6 +951,17 @@ inline size_t a256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 template <int RP>
 hipError_t run_yproj(const uint16_t* x, int64_t T, int D, int P, int S, int r, const uint16_t* QtH,
                      const uint16_t* QtL, float* Zpart, hipStream_t s) {
+  // the loop form from 16 D parts on, when every workgroup of a grid of about
+  // one per CU gets at least two blocks
+  if constexpr (RP <= 64) {
+    const int64_t nb = (T + YTPW - 1) / YTPW;
+    const int64_t G = std::max<int64_t>(1, device_cus() / S);
+    if (S >= 16 && nb >= 2 * G) {
+      hipLaunchKernelGGL(yproj_loop_kernel<RP>, dim3(static_cast<unsigned>(G), S), dim3(YNW * 64),
+                         0, s, x, T, D, P, QtH, QtL, Zpart);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL(yproj_kernel<RP>, dim3(static_cast<unsigned>((T + YTPW - 1) / YTPW), S), dim3(YNW * 64),
                      0, s, x, T, D, P, r, QtH, QtL, Zpart);
   return hipGetLastError();
