@@ -473,10 +473,11 @@ size_t rw4_align256(size_t n);
 /* static, human-readable name of a status code */
 const char* rw4_status_string(rw4_status s);
 
-/* ABI version of this header (bumped on any signature change) */
+/* ABI version of this header (bumped on any signature change, and when the
+ * layout of a prepared basis changes) */
 int rw4_abi_version(void);
 
-#define RW4_ABI_VERSION 12
+#define RW4_ABI_VERSION 13
 
 #ifdef __cplusplus
 }

@@ -126,6 +126,27 @@ basis_prep_kernel(const float* __restrict__ Q, const float* __restrict__ M, int 
 // orthogonal, H (x + Q z) / sqrt(D) = H x / sqrt(D) + P z.
 constexpr int kBasisFwhtMax = 4096;
 
+// Q' in the order the projection's waves read it: 1 KiB chunks, one per
+// (64-column double step dg, 16-row block c, hi/lo, half h), lane 16 g + t
+// holding Q'[16 c + t][64 dg + 16 g + 8 h .. + 8]. A wave then loads each
+// operand fragment as one contiguous 1 KiB (from L2 a row-major fragment,
+// 16 rows of 64 bytes, reads at about a third of that rate). Same values as
+// Q'h/Q'l, so the same products.
+__global__ void __launch_bounds__(256)
+qtf_kernel(const uint16_t* __restrict__ QtH, const uint16_t* __restrict__ QtL, int D, int RP,
+           uint16_t* __restrict__ QtF) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int lane = static_cast<int>(idx & 63);
+  const int64_t q = idx >> 6;
+  const int h = static_cast<int>(q & 1);
+  const int hl = static_cast<int>((q >> 1) & 1);
+  const int nbc = RP / 16;
+  const int c = static_cast<int>((q >> 2) % nbc);
+  const int64_t dg = (q >> 2) / nbc;
+  const int64_t o = static_cast<int64_t>(16 * c + (lane & 15)) * D + 64 * dg + 16 * (lane >> 4) + 8 * h;
+  *reinterpret_cast<uint4*>(QtF + idx * 8) = *reinterpret_cast<const uint4*>((hl ? QtL : QtH) + o);
+}
+
 __global__ void __launch_bounds__(1024)
 basis_fwht_kernel(const float* __restrict__ Q, int D, int r, int RK, float norm,
                   uint16_t* __restrict__ PH, uint16_t* __restrict__ PL) {
@@ -172,8 +193,7 @@ constexpr int YTPW = YTBW * TB;
 template <int RP>
 __global__ void __launch_bounds__(YNW * 64)
 yproj_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int r,
-             const uint16_t* __restrict__ QtH, const uint16_t* __restrict__ QtL,
-             float* __restrict__ Zpart) {
+             const uint16_t* __restrict__ QtF, float* __restrict__ Zpart) {
   constexpr int RK = (RP + 31) / 32 * 32;
   constexpr int NT = YNW * 64;
   __shared__ float red[4][YTPW][RP + 1];
@@ -237,13 +257,14 @@ yproj_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int r,
     for (int u = 0; u < DPW; ++u) {
       const int ds = wave * DPW + u;
       const int dsc = ds < nds ? ds : nds - 1;
+      const int64_t dg = dbeg / 64 + dsc;
 #pragma unroll
       for (int c = 0; c < NBC; ++c) {
-        const int64_t qo = static_cast<int64_t>(16 * (nb0 + c) + tl) * D + dbeg + 64 * dsc + 16 * g;
-        bh[u][c][0] = ld8(QtH + qo);
-        bh[u][c][1] = ld8(QtH + qo + 8);
-        bl[u][c][0] = ld8(QtL + qo);
-        bl[u][c][1] = ld8(QtL + qo + 8);
+        const uint16_t* f = QtF + (dg * (RP / 16) + nb0 + c) * 4 * 512 + lane * 8;
+        bh[u][c][0] = ld8(f);
+        bh[u][c][1] = ld8(f + 512);
+        bl[u][c][0] = ld8(f + 1024);
+        bl[u][c][1] = ld8(f + 1536);
       }
     }
     // every load of the batch (and, in the first, of x) is issued before the
@@ -311,8 +332,7 @@ yproj_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int r,
 template <int RP>
 __global__ void __launch_bounds__(YNW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 yproj_loop_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P,
-                  const uint16_t* __restrict__ QtH, const uint16_t* __restrict__ QtL,
-                  float* __restrict__ Zpart) {
+                  const uint16_t* __restrict__ QtF, float* __restrict__ Zpart) {
   static_assert(RP <= 64 && DPW == 1, "the basis block is held in registers");
   constexpr int RK = (RP + 31) / 32 * 32;
   constexpr int NT = YNW * 64;
@@ -337,13 +357,14 @@ yproj_loop_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P,
   if (blk >= nb) return;
 
   v8bf bh[NBC][2], bl[NBC][2];
+  const int64_t dg = dbeg / 64 + dsc;
 #pragma unroll
   for (int c = 0; c < NBC; ++c) {
-    const int64_t qo = static_cast<int64_t>(16 * c + tl) * D + dbeg + 64 * dsc + 16 * g;
-    bh[c][0] = ld8(QtH + qo);
-    bh[c][1] = ld8(QtH + qo + 8);
-    bl[c][0] = ld8(QtL + qo);
-    bl[c][1] = ld8(QtL + qo + 8);
+    const uint16_t* f = QtF + (dg * NBC + c) * 4 * 512 + lane * 8;
+    bh[c][0] = ld8(f);
+    bh[c][1] = ld8(f + 512);
+    bl[c][0] = ld8(f + 1024);
+    bl[c][1] = ld8(f + 1536);
   }
   uint4 xn[YTBW][2];
   auto load_x = [&](int64_t b) {
@@ -949,8 +970,8 @@ inline int rk_of(int64_t r) { return static_cast<int>((r + 31) / 32 * 32); }
 inline size_t a256(size_t n) { return (n + 255) & ~static_cast<size_t>(255); }
 
 template <int RP>
-hipError_t run_yproj(const uint16_t* x, int64_t T, int D, int P, int S, int r, const uint16_t* QtH,
-                     const uint16_t* QtL, float* Zpart, hipStream_t s) {
+hipError_t run_yproj(const uint16_t* x, int64_t T, int D, int P, int S, int r, const uint16_t* QtF,
+                     float* Zpart, hipStream_t s) {
   // the loop form from 16 D parts on, when every workgroup of a grid of about
   // one per CU gets at least two blocks
   if constexpr (RP <= 64) {
@@ -958,12 +979,12 @@ hipError_t run_yproj(const uint16_t* x, int64_t T, int D, int P, int S, int r, c
     const int64_t G = std::max<int64_t>(1, device_cus() / S);
     if (S >= 16 && nb >= 2 * G) {
       hipLaunchKernelGGL(yproj_loop_kernel<RP>, dim3(static_cast<unsigned>(G), S), dim3(YNW * 64),
-                         0, s, x, T, D, P, QtH, QtL, Zpart);
+                         0, s, x, T, D, P, QtF, Zpart);
       return hipGetLastError();
     }
   }
   hipLaunchKernelGGL(yproj_kernel<RP>, dim3(static_cast<unsigned>((T + YTPW - 1) / YTPW), S), dim3(YNW * 64),
-                     0, s, x, T, D, P, r, QtH, QtL, Zpart);
+                     0, s, x, T, D, P, r, QtF, Zpart);
   return hipGetLastError();
 }
 
@@ -1044,7 +1065,7 @@ size_t align_zpart_bytes(int64_t T, int64_t D, int64_t r) {
 
 size_t align_basis_bytes(int64_t D, int64_t r, bool with_p) {
   const size_t RP = rp_of(r), RK = rk_of(r), Dz = static_cast<size_t>(D);
-  size_t n = 2 * a256(RP * Dz * 2) + 2 * a256(Dz * RK * 2);
+  size_t n = 2 * a256(RP * Dz * 2) + 2 * a256(Dz * RK * 2) + a256(RP * Dz * 4);
   if (with_p) n += 2 * a256(Dz * RK * 2);
   return n;
 }
@@ -1059,6 +1080,7 @@ AlignBasis align_basis(const void* basis, int64_t D, int64_t r, bool with_p) {
   a.QtL = reinterpret_cast<uint16_t*>(p); p += a256(RP * Dz * 2);
   a.QH = reinterpret_cast<uint16_t*>(p);  p += a256(Dz * RK * 2);
   a.QL = reinterpret_cast<uint16_t*>(p);  p += a256(Dz * RK * 2);
+  a.QtF = reinterpret_cast<uint16_t*>(p); p += a256(RP * Dz * 4);
   a.PH = with_p ? reinterpret_cast<uint16_t*>(p) : nullptr;
   if (with_p) p += a256(Dz * RK * 2);
   a.PL = with_p ? reinterpret_cast<uint16_t*>(p) : nullptr;
@@ -1072,6 +1094,10 @@ hipError_t launch_basis_prep(const float* Q, const float* M, int64_t D, int64_t 
   hipLaunchKernelGGL(basis_prep_kernel, pgrid, dim3(256), 0, s, Q, M, static_cast<int>(D),
                      static_cast<int>(r), a.RP, a.RK, a.QtH, a.QtL, a.QH, a.QL);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(qtf_kernel, dim3(static_cast<unsigned>(D / 64 * (a.RP / 16))), dim3(256), 0, s,
+                     a.QtH, a.QtL, static_cast<int>(D), a.RP, a.QtF);
+  e = hipGetLastError();
   if (e != hipSuccess || !with_p) return e;
   if ((D & (D - 1)) != 0 || D > kBasisFwhtMax) return hipErrorInvalidValue;
   const float norm = static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(D)));
@@ -1088,7 +1114,7 @@ hipError_t launch_yproj(const uint16_t* x, int64_t T, int64_t D, int64_t r, cons
   const int ri = static_cast<int>(r);
   const int S = align_parts_count(D);
   switch (a.RP) {
-#define RW4_Y(V) case V: return run_yproj<V>(x, T, Di, kPart, S, ri, a.QtH, a.QtL, Zpart, s);
+#define RW4_Y(V) case V: return run_yproj<V>(x, T, Di, kPart, S, ri, a.QtF, Zpart, s);
     RW4_Y(16) RW4_Y(32) RW4_Y(48) RW4_Y(64) RW4_Y(80) RW4_Y(96) RW4_Y(112) RW4_Y(128)
 #undef RW4_Y
     default: return hipErrorInvalidValue;

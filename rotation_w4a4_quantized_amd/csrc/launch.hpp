@@ -74,6 +74,7 @@ hipError_t launch_align_mfma(const uint16_t* x, void* out, int out_f32, const fl
 // [D][RK] for the fused prologue (D a power of two <= 4096).
 struct AlignBasis {
   uint16_t* QtH; uint16_t* QtL; uint16_t* QH; uint16_t* QL;
+  uint16_t* QtF;                // Q'h/Q'l again, in the projection's MFMA fragment order
   uint16_t* PH; uint16_t* PL;   // null without P
   int RP, RK;                   // r padded to 16 and to 32
 };

@@ -22,7 +22,7 @@ def _declared():
 def test_library_built_and_loads():
     assert os.path.exists(rw.library_path), "build the HIP library first"
     L = rw.lib()
-    assert L.rw4_abi_version() == 12
+    assert L.rw4_abi_version() == 13
 
 
 def test_exports_every_declared_symbol():
@@ -76,12 +76,13 @@ def test_workspace_size():
 
 def test_basis_size():
     L = rw.lib()
-    # bf16 hi/lo of the projection operand [r padded to 16][D] and of Q [D][r
-    # padded to 32], plus the Hadamard image of Q (hi/lo, [D][r padded to 32])
-    # for D a power of two in [256, 4096] with r <= 64
-    assert L.respin_basis_size(4096, 32) == 6 * (4096 * 32 * 2)
-    assert L.respin_basis_size(8192, 64) == 4 * (8192 * 64 * 2)
-    assert L.respin_basis_size(256, 8) == 2 * (256 * 16 * 2) + 4 * (256 * 32 * 2)
+    # bf16 hi/lo of the projection operand [r padded to 16][D] (twice: rows,
+    # and in the projection's fragment order) and of Q [D][r padded to 32],
+    # plus the Hadamard image of Q (hi/lo, [D][r padded to 32]) for D a power
+    # of two in [256, 4096] with r <= 64
+    assert L.respin_basis_size(4096, 32) == 8 * (4096 * 32 * 2)
+    assert L.respin_basis_size(8192, 64) == 6 * (8192 * 64 * 2)
+    assert L.respin_basis_size(256, 8) == 4 * (256 * 16 * 2) + 4 * (256 * 32 * 2)
     assert L.respin_basis_size(4096, 0) == 0 and L.respin_basis_size(4096, 6) == 0
     assert L.respin_basis_size(4096, 132) == 0 and L.respin_basis_size(1000, 8) == 0
     assert L.respin_basis_size(64, 68) == 0
