@@ -208,11 +208,19 @@ yproj_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int r,
   int part = blockIdx.y;
   {
     const int64_t nb = static_cast<int64_t>(gridDim.x) * gridDim.y;
+    const int64_t b = blockIdx.x + static_cast<int64_t>(gridDim.x) * blockIdx.y;
     if ((nb & 7) == 0 && gridDim.y >= 16) {
-      const int64_t b = blockIdx.x + static_cast<int64_t>(gridDim.x) * blockIdx.y;
       const int64_t q = (b & 7) * (nb >> 3) + (b >> 3);
       bx = q % gridDim.x;
       part = static_cast<int>(q / gridDim.x);
+    } else if ((gridDim.x & 7) == 0) {
+      // fewer parts: XCD k takes the k-th eighth of the token blocks, every
+      // part of them, the band of tokens the fused prologue that follows
+      // gives the same XCD, which then finds those rows of x in its L2
+      const int64_t per = gridDim.x >> 3;
+      const int64_t j = b >> 3;
+      bx = (b & 7) * per + j % per;
+      part = static_cast<int>(j / per);
     }
   }
   const int64_t t0 = bx * YTPW;
