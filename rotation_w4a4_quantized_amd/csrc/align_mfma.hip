@@ -190,13 +190,76 @@ constexpr int TPW = TBW * TB;             // tokens per lift workgroup
 constexpr int YTBW = 4;                   // 16-token blocks per projection workgroup
 constexpr int YTPW = YTBW * TB;
 
+// The projection's reduction over its 8 waves and the partial stores, shared by
+// both projection kernels. Wave w holds, for its 64 columns, the block's
+// partials acc[tb][c][v] = z-part of token 16 tb + 4 g + v, basis index
+// 16 c + t. Waves 4..7 park theirs in red[w - 4], waves 0..3 add theirs
+// (slot = own + parked), and z = (slot 0 + slot 1) + (slot 2 + slot 3).
+// red[w][i][t] holds basis index i, token t (rows padded to 68 words): a lane's
+// four tokens are one 16-byte access, and the 16 lanes of a row group fall on
+// distinct banks. Each thread then forms four consecutive tokens of one
+// basis index (i < RP; zero padding up to RK) and stores them, 4 per group
+// (rows past T rewrite row T - 1 with the same bits).
+constexpr int kRedPitch = YTPW + 4;
+
+template <int RP, bool LB>
+__device__ __forceinline__ void yproj_reduce_store(const v4f (&acc)[YTBW][RP / 16],
+                                                   float (&red)[4][RP][kRedPitch], int wave,
+                                                   int g, int tl, int tid, int part, int64_t T,
+                                                   int64_t t0, float* __restrict__ Zpart) {
+  constexpr int RK = (RP + 31) / 32 * 32;
+  constexpr int NT = YNW * 64;
+  constexpr int NQ = YTPW / 4;                        // token quads of the block
+  static_assert(NQ * RK % NT == 0, "quads per thread");
+  auto bar = [] {
+    if constexpr (LB)
+      lds_barrier();
+    else
+      __syncthreads();
+  };
+  if (wave >= 4) {
+#pragma unroll
+    for (int tb = 0; tb < YTBW; ++tb)
+#pragma unroll
+      for (int c = 0; c < RP / 16; ++c)
+        *reinterpret_cast<v4f*>(&red[wave - 4][16 * c + tl][16 * tb + 4 * g]) = acc[tb][c];
+  }
+  bar();
+  if (wave < 4) {
+#pragma unroll
+    for (int tb = 0; tb < YTBW; ++tb)
+#pragma unroll
+      for (int c = 0; c < RP / 16; ++c) {
+        v4f& slot = *reinterpret_cast<v4f*>(&red[wave][16 * c + tl][16 * tb + 4 * g]);
+        slot = acc[tb][c] + slot;
+      }
+  }
+  bar();
+#pragma unroll
+  for (int k = 0; k < NQ * RK / NT; ++k) {
+    const int o = tid + k * NT;
+    const int i = o % RK;
+    const int q = o / RK;
+    v4f z = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    if (i < RP) {
+      const v4f r0 = *reinterpret_cast<const v4f*>(&red[0][i][4 * q]);
+      const v4f r1 = *reinterpret_cast<const v4f*>(&red[1][i][4 * q]);
+      const v4f r2 = *reinterpret_cast<const v4f*>(&red[2][i][4 * q]);
+      const v4f r3 = *reinterpret_cast<const v4f*>(&red[3][i][4 * q]);
+      z = (r0 + r1) + (r2 + r3);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      Zpart[(static_cast<int64_t>(part) * T + min(t0 + 4 * q + e, T - 1)) * RK + i] = z[e];
+  }
+}
+
 template <int RP>
 __global__ void __launch_bounds__(YNW * 64)
 yproj_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int r,
              const uint16_t* __restrict__ QtF, float* __restrict__ Zpart) {
   constexpr int RK = (RP + 31) / 32 * 32;
-  constexpr int NT = YNW * 64;
-  __shared__ float red[4][YTPW][RP + 1];
+  __shared__ __attribute__((aligned(16))) float red[4][RP][kRedPitch];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -292,39 +355,7 @@ yproj_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int r,
           }
   }
   mfma_drain();
-  // C layout: lane holds rows 4g + v (tokens of block b), column tl (basis index)
-  // waves 4..7 park their sums in red[wave - 4]; waves 0..3 add theirs
-  if (wave >= 4) {
-#pragma unroll
-    for (int b = 0; b < YTBW; ++b)
-#pragma unroll
-      for (int nb = 0; nb < RP / 16; ++nb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) red[wave - 4][16 * b + 4 * g + v][16 * nb + tl] = acc[b][nb][v];
-  }
-  __syncthreads();
-  if (wave < 4) {
-#pragma unroll
-    for (int b = 0; b < YTBW; ++b)
-#pragma unroll
-      for (int nb = 0; nb < RP / 16; ++nb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          float& slot = red[wave][16 * b + 4 * g + v][16 * nb + tl];
-          slot = acc[b][nb][v] + slot;
-        }
-  }
-  __syncthreads();
-  // partial z of this D part for the workgroup's tokens (the operand is
-  // Q (M - I)^T, so the sums are z's parts; the consumers add the parts);
-  // columns past RP (padding up to RK) are zero
-  for (int o = tid; o < YTPW * RK; o += NT) {
-    const int t = o / RK;
-    const int i = o % RK;
-    float z = 0.0f;
-    if (i < RP) z = (red[0][t][i] + red[1][t][i]) + (red[2][t][i] + red[3][t][i]);
-    if (t0 + t < T) Zpart[(static_cast<int64_t>(part) * T + t0 + t) * RK + i] = z;
-  }
+  yproj_reduce_store<RP, false>(acc, red, wave, g, tl, tid, part, T, t0, Zpart);
 }
 
 // The projection as a loop over 64-token blocks from 16 D parts on (RP <= 64):
@@ -345,9 +376,7 @@ yproj_loop_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P,
   constexpr int RK = (RP + 31) / 32 * 32;
   constexpr int NT = YNW * 64;
   constexpr int NBC = RP / 16;
-  constexpr int ZST = YTPW * RK / NT;                 // partial stores per thread and block
-  static_assert(YTPW * RK % NT == 0, "stores per thread");
-  __shared__ float red[4][YTPW][RP + 1];
+  __shared__ __attribute__((aligned(16))) float red[4][RP][kRedPitch];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -421,36 +450,7 @@ yproj_loop_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P,
           acc[tb][c] = mfma(xa[tb][h], bl[c][h], acc[tb][c]);
         }
     mfma_drain();
-    if (wave >= 4) {
-#pragma unroll
-      for (int tb = 0; tb < YTBW; ++tb)
-#pragma unroll
-        for (int c = 0; c < NBC; ++c)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) red[wave - 4][16 * tb + 4 * g + v][16 * c + tl] = acc[tb][c][v];
-    }
-    lds_barrier();
-    if (wave < 4) {
-#pragma unroll
-      for (int tb = 0; tb < YTBW; ++tb)
-#pragma unroll
-        for (int c = 0; c < NBC; ++c)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            float& slot = red[wave][16 * tb + 4 * g + v][16 * c + tl];
-            slot = acc[tb][c][v] + slot;
-          }
-    }
-    lds_barrier();
-#pragma unroll
-    for (int k = 0; k < ZST; ++k) {
-      const int o = tid + k * NT;
-      const int t = o / RK;
-      const int i = o % RK;
-      float z = 0.0f;
-      if (i < RP) z = (red[0][t][i] + red[1][t][i]) + (red[2][t][i] + red[3][t][i]);
-      Zpart[(static_cast<int64_t>(part) * T + min(t0 + t, T - 1)) * RK + i] = z;
-    }
+    yproj_reduce_store<RP, true>(acc, red, wave, g, tl, tid, part, T, t0, Zpart);
     // every read of red is done before the next block's writes
     lds_barrier();
     if (!more) break;
