@@ -148,8 +148,12 @@ rw4_status run_linear(const void* x, int64_t ldx, int64_t T, int64_t D, const vo
     }
     if (fused) {
       // lift + transform + quantization on chip
+      // the product's weights are read ahead into the caches meanwhile
+      // (prefill-linear step: GEMM 27.5 -> 25.0 us, prologue 16.5 -> 18.1 us)
+      const size_t wbytes = pk ? static_cast<size_t>(N) * static_cast<size_t>(D / 2)
+                               : rw4::tiles_bytes(N, D);
       if (rw4::launch_lift_fwht_quant(xb, T, D, r, basis, Zpart, (flags & RW4_FWHT) != 0, codes,
-                                      s_a, dbg, s, abits(flags), pk) != hipSuccess)
+                                      s_a, dbg, s, abits(flags), pk, w, wbytes) != hipSuccess)
         return RW4_ERR_HIP;
       return hip_status(gemm());
     }

@@ -118,10 +118,14 @@ hipError_t launch_lift(const uint16_t* x, void* out, int out_f32, const void* ad
 // u = [H x / sqrt(D)] + P z (P = H Q / sqrt(D) with the transform, Q
 // without), codes of u. Needs a basis prepared with P.
 bool lfq_supported(int64_t D, int64_t r);
+// pre, pre_bytes (optional): the weights of the product that follows; the
+// kernel reads one word of each of their 128-byte lines, so that the product
+// finds them in the caches (it streams from L2 while HBM is otherwise idle)
 hipError_t launch_lift_fwht_quant(const uint16_t* x, int64_t T, int64_t D, int64_t r,
                                   const void* basis, const float* Zpart, bool do_fwht,
                                   uint8_t* tiles, float* s_a, float* dbg, hipStream_t s,
-                                  int bits = 4, bool packed = false);
+                                  int bits = 4, bool packed = false, const void* pre = nullptr,
+                                  size_t pre_bytes = 0);
 
 // W4A4 GEMM, bf16 (dequantized) or raw int32 output.
 hipError_t launch_gemm(const uint8_t* a, const float* s_a, const uint8_t* w, const float* s_w,

@@ -137,7 +137,7 @@ __global__ void __launch_bounds__(kThreads)
 lfq_kernel(const uint16_t* __restrict__ x, int64_t T, const float* __restrict__ Zpart, int S,
            const uint16_t* __restrict__ PH, const uint16_t* __restrict__ PL,
            uint8_t* __restrict__ tiles, float* __restrict__ s_a, float* __restrict__ dbg,
-           float norm, float qmax) {
+           float norm, float qmax, const uint8_t* __restrict__ pre, int64_t pre_lines) {
   constexpr int D = 1 << N;
   constexpr int NCH = D / 32;                   // 32-value chunks per row
   constexpr int NS = NCH > 64 ? NCH / 64 : 1;   // chunks per lane
@@ -183,6 +183,13 @@ lfq_kernel(const uint16_t* __restrict__ x, int64_t T, const float* __restrict__ 
 #pragma unroll
     for (int q = 0; q < 4; ++q) raw[s][q] = p[q];
   }
+  // one word of a 128-byte line of the next product's weights per lane (the
+  // lanes of the grid wrap over the lines), read behind the row: HBM is
+  // otherwise idle while the lift streams from L2, and the product then finds
+  // these lines in the caches. The value is consumed only under a condition
+  // that never holds (pre_lines >= 1), so no wait for it is ever executed.
+  const int64_t pl = ((static_cast<int64_t>(blockIdx.x) * 8 + tok) * 64 + lane) % pre_lines;
+  const uint32_t pfv = *reinterpret_cast<const uint32_t*>(pre + pl * 128);
   lds_barrier();  // 1 (the row is still in flight)
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
@@ -320,18 +327,19 @@ lfq_kernel(const uint16_t* __restrict__ x, int64_t T, const float* __restrict__ 
       }
     }
   }
+  if (pre_lines < 1) s_a[0] = __uint_as_float(pfv);
 }
 
 template <int N, int RK>
 hipError_t launch_n(const uint16_t* x, int64_t T, const float* Zpart, int S, const uint16_t* PH,
                     const uint16_t* PL, bool fw, bool pk, uint8_t* tiles, float* s_a, float* dbg,
-                    float qmax, hipStream_t s) {
+                    float qmax, hipStream_t s, const uint8_t* pre, int64_t pre_lines) {
   const float norm = static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(1 << N)));
   const dim3 grid(static_cast<unsigned>((T + kTok - 1) / kTok));
 #define RW4_LFQ(F, G, K)                                                                          \
   if (fw == F && (dbg != nullptr) == G && pk == K) {                                              \
     hipLaunchKernelGGL((lfq_kernel<N, RK, F, G, K>), grid, dim3(kThreads), 0, s, x, T, Zpart, S,  \
-                       PH, PL, tiles, s_a, dbg, norm, qmax);                                      \
+                       PH, PL, tiles, s_a, dbg, norm, qmax, pre, pre_lines);                      \
     return hipGetLastError();                                                                     \
   }
   RW4_LFQ(true, false, false) RW4_LFQ(true, true, false) RW4_LFQ(false, false, false)
@@ -344,13 +352,14 @@ hipError_t launch_n(const uint16_t* x, int64_t T, const float* Zpart, int S, con
 template <int RK>
 hipError_t launch_rk(int n, const uint16_t* x, int64_t T, const float* Zpart, int S,
                      const uint16_t* PH, const uint16_t* PL, bool fw, bool pk, uint8_t* tiles,
-                     float* s_a, float* dbg, float qmax, hipStream_t s) {
+                     float* s_a, float* dbg, float qmax, hipStream_t s, const uint8_t* pre,
+                     int64_t pl) {
   switch (n) {
-    case 8: return launch_n<8, RK>(x, T, Zpart, S, PH, PL, fw, pk, tiles, s_a, dbg, qmax, s);
-    case 9: return launch_n<9, RK>(x, T, Zpart, S, PH, PL, fw, pk, tiles, s_a, dbg, qmax, s);
-    case 10: return launch_n<10, RK>(x, T, Zpart, S, PH, PL, fw, pk, tiles, s_a, dbg, qmax, s);
-    case 11: return launch_n<11, RK>(x, T, Zpart, S, PH, PL, fw, pk, tiles, s_a, dbg, qmax, s);
-    case 12: return launch_n<12, RK>(x, T, Zpart, S, PH, PL, fw, pk, tiles, s_a, dbg, qmax, s);
+    case 8: return launch_n<8, RK>(x, T, Zpart, S, PH, PL, fw, pk, tiles, s_a, dbg, qmax, s, pre, pl);
+    case 9: return launch_n<9, RK>(x, T, Zpart, S, PH, PL, fw, pk, tiles, s_a, dbg, qmax, s, pre, pl);
+    case 10: return launch_n<10, RK>(x, T, Zpart, S, PH, PL, fw, pk, tiles, s_a, dbg, qmax, s, pre, pl);
+    case 11: return launch_n<11, RK>(x, T, Zpart, S, PH, PL, fw, pk, tiles, s_a, dbg, qmax, s, pre, pl);
+    case 12: return launch_n<12, RK>(x, T, Zpart, S, PH, PL, fw, pk, tiles, s_a, dbg, qmax, s, pre, pl);
     default: return hipErrorInvalidValue;
   }
 }
@@ -367,7 +376,7 @@ bool lfq_supported(int64_t D, int64_t r) {
 hipError_t launch_lift_fwht_quant(const uint16_t* x, int64_t T, int64_t D, int64_t r,
                                   const void* basis, const float* Zpart, bool do_fwht,
                                   uint8_t* tiles, float* s_a, float* dbg, hipStream_t s,
-                                  int bits, bool packed) {
+                                  int bits, bool packed, const void* pre, size_t pre_bytes) {
   if (T == 0) return hipSuccess;
   if (!lfq_supported(D, r) || bits < 2 || bits > 4) return hipErrorInvalidValue;
   const float qmax = static_cast<float>((1 << (bits - 1)) - 1);
@@ -379,10 +388,16 @@ hipError_t launch_lift_fwht_quant(const uint16_t* x, int64_t T, int64_t D, int64
   if (S != (D + 511) / 512) return hipErrorInvalidValue;  // the lift waves' part count
   int n = 0;
   while ((int64_t(1) << n) < D) ++n;
+  // the read-ahead's lines; without weights, the one line read is x's first
+  const bool ra = pre != nullptr && pre_bytes >= 128;
+  const uint8_t* pb = ra ? static_cast<const uint8_t*>(pre) : reinterpret_cast<const uint8_t*>(x);
+  const int64_t pl = ra ? static_cast<int64_t>(pre_bytes / 128) : 1;
   if (a.RK == 32)
-    return launch_rk<32>(n, x, T, Zpart, S, PH, PL, do_fwht, packed, tiles, s_a, dbg, qmax, s);
+    return launch_rk<32>(n, x, T, Zpart, S, PH, PL, do_fwht, packed, tiles, s_a, dbg, qmax, s,
+                         pb, pl);
   if (a.RK == 64)
-    return launch_rk<64>(n, x, T, Zpart, S, PH, PL, do_fwht, packed, tiles, s_a, dbg, qmax, s);
+    return launch_rk<64>(n, x, T, Zpart, S, PH, PL, do_fwht, packed, tiles, s_a, dbg, qmax, s,
+                         pb, pl);
   return hipErrorInvalidValue;
 }
 
