@@ -566,7 +566,11 @@ def test_tile_codes_rejects_minus8(rw):
                                    # 256 x 256 blocks (chosen where they take fewer
                                    # weighted waves): ragged T and N, an even XCD split,
                                    # a grid no split divides
-                                   (3000, 512, 4100), (2048, 384, 8192), (2304, 256, 5000)])
+                                   (3000, 512, 4100), (2048, 384, 8192), (2304, 256, 5000),
+                                   # whole tiles, several per CU (256 x 256 blocks with
+                                   # 2, 3, 8 stages; 256 x 128 blocks with 16)
+                                   (8192, 256, 8192), (4096, 384, 8192), (4096, 1024, 8192),
+                                   (2048, 2048, 12288)])
 def test_w4a4_gemm_tiles(rw, T, K, N):
     say(f"w4a4_gemm_tiles T={T} K={K} N={N}")
     a, qa = _codes7(T + K, T, K)
