@@ -411,15 +411,28 @@ gemm6_lds_kernel(const uint8_t* __restrict__ at, const float* __restrict__ s_a,
     uint16_t* st = reinterpret_cast<uint16_t*>(L0) + wave * 32 * SPW;
     uint16_t* yo = static_cast<uint16_t*>(y);
     const int tl = lane & 31;
+    // every scale this lane needs, read from LDS together (one wait instead
+    // of one per fragment)
+    float4 swv[FW][4];
+    float sav[FT];
+#pragma unroll
+    for (int ii = 0; ii < FW; ++ii)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        swv[ii][q] = *reinterpret_cast<const float4*>(
+            &sc[ww * FW * 32 + 32 * ii + 8 * q + 4 * (lane >> 5)]);
+#pragma unroll
+    for (int j = 0; j < FT; ++j) sav[j] = sc[TW + wq * FT * 32 + 32 * j + tl];
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < FT; ++j) {
-      const float sa = sc[TW + wq * FT * 32 + 32 * j + tl];
+      const float sa = sav[j];
 #pragma unroll
       for (int ii = 0; ii < FW; ++ii)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int nl = 32 * ii + 8 * q + 4 * (lane >> 5);
-          const float4 sw = *reinterpret_cast<const float4*>(&sc[ww * FW * 32 + nl]);
+          const float4 sw = swv[ii][q];
           const float v0 = (acc[ii][j][4 * q + 0] * sa) * sw.x;
           const float v1 = (acc[ii][j][4 * q + 1] * sa) * sw.y;
           const float v2 = (acc[ii][j][4 * q + 2] * sa) * sw.z;
@@ -428,19 +441,29 @@ gemm6_lds_kernel(const uint8_t* __restrict__ at, const float* __restrict__ s_a,
               make_uint2(f32_to_bf16(v0) | (static_cast<uint32_t>(f32_to_bf16(v1)) << 16),
                          f32_to_bf16(v2) | (static_cast<uint32_t>(f32_to_bf16(v3)) << 16));
         }
-      // the wave reads back only what it wrote (LDS accesses of a wave are in order)
-      constexpr int CPR = FW * 4;  // 16-byte chunks per staged row
+      // the wave reads back only what it wrote (LDS accesses of a wave are in
+      // order): all of this row group's chunks first, then their stores
+      constexpr int CPR = FW * 4;          // 16-byte chunks per staged row
+      constexpr int RPJ = 32 * CPR / 64;   // chunks per lane
+      uint4 cv[RPJ];
 #pragma unroll
-      for (int c = lane; c < 32 * CPR; c += 64) {
+      for (int k = 0; k < RPJ; ++k) {
+        const int c = lane + 64 * k;
+        cv[k] = *reinterpret_cast<const uint4*>(&st[(c / CPR) * SPW + (c % CPR) * 8]);
+      }
+#pragma unroll
+      for (int k = 0; k < RPJ; ++k) {
+        const int c = lane + 64 * k;
         const int row = c / CPR, col = (c % CPR) * 8;
         const int t = wt0 + 32 * j + row, n = wn0 + col;
         if (t < T && n < N) {
           uint16_t* o = yo + static_cast<int64_t>(t) * N + n;
           if (n + 8 <= N && (N & 7) == 0) {
-            *reinterpret_cast<uint4*>(o) = *reinterpret_cast<const uint4*>(&st[row * SPW + col]);
+            *reinterpret_cast<uint4*>(o) = cv[k];
           } else {
-            const uint16_t* e = &st[row * SPW + col];
-            for (int k = 0; k < 8 && n + k < N; ++k) o[k] = e[k];
+            const uint32_t wv[4] = {cv[k].x, cv[k].y, cv[k].z, cv[k].w};
+            for (int e = 0; e < 8 && n + e < N; ++e)
+              o[e] = static_cast<uint16_t>(wv[e >> 1] >> (16 * (e & 1)));
           }
         }
       }
