@@ -635,7 +635,7 @@ lift_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int S, int 
           const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(addend) + off);
           o.x += a.x; o.y += a.y; o.z += a.z; o.w += a.w;
         }
-        *reinterpret_cast<float4*>(static_cast<float*>(out) + off) = o;
+        store_stream16(static_cast<float*>(out) + off, o);
       } else {
         const float4 s0 = *reinterpret_cast<const float4*>(&stage[row][col]);
         const float4 s1 = *reinterpret_cast<const float4*>(&stage[row][col + 4]);
@@ -649,7 +649,7 @@ lift_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P, int S, int 
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           w[i] = f32_to_bf16(o[2 * i]) | (static_cast<uint32_t>(f32_to_bf16(o[2 * i + 1])) << 16);
-        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + off) = make_uint4(w[0], w[1], w[2], w[3]);
+        store_stream16(static_cast<uint16_t*>(out) + off, make_uint4(w[0], w[1], w[2], w[3]));
       }
     }
     __syncthreads();
@@ -831,8 +831,8 @@ lift_loop_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P,
         const int col = sc[it];
         const int64_t off = min(t0 + 16 * tb + row, T - 1) * D + dbeg + col;
         if constexpr (OF32) {
-          *reinterpret_cast<float4*>(static_cast<float*>(out) + off) =
-              *reinterpret_cast<const float4*>(&stage[row][col]);
+          store_stream16(static_cast<float*>(out) + off,
+                         *reinterpret_cast<const float4*>(&stage[row][col]));
         } else {
           const float4 s0 = *reinterpret_cast<const float4*>(&stage[row][col]);
           const float4 s1 = *reinterpret_cast<const float4*>(&stage[row][col + 4]);
@@ -841,8 +841,7 @@ lift_loop_kernel(const uint16_t* __restrict__ x, int64_t T, int D, int P,
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             w[i] = f32_to_bf16(o[2 * i]) | (static_cast<uint32_t>(f32_to_bf16(o[2 * i + 1])) << 16);
-          *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + off) =
-              make_uint4(w[0], w[1], w[2], w[3]);
+          store_stream16(static_cast<uint16_t*>(out) + off, make_uint4(w[0], w[1], w[2], w[3]));
         }
       }
       if (tb + 1 < TBW) lds_barrier();

@@ -243,7 +243,7 @@ gemm_kernel(const uint8_t* __restrict__ a, const float* __restrict__ s_a,
       const uint4 v = *reinterpret_cast<const uint4*>(&stage[tt * SP + nn]);
       uint16_t* yp = yb + static_cast<int64_t>(t) * N + n;
       if (n + 7 < N && (N & 7) == 0) {
-        *reinterpret_cast<uint4*>(yp) = v;
+        store_stream16(yp, v);
       } else {
         const uint16_t e[8] = {static_cast<uint16_t>(v.x), static_cast<uint16_t>(v.x >> 16),
                                static_cast<uint16_t>(v.y), static_cast<uint16_t>(v.y >> 16),

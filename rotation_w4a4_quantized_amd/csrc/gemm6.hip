@@ -180,7 +180,7 @@ gemm6_kernel(const uint8_t* __restrict__ at, const float* __restrict__ s_a,
       const uint4 v = *reinterpret_cast<const uint4*>(&stage[row * SP + col]);
       uint16_t* o = yo + static_cast<int64_t>(t) * N + n;
       if (n + 8 <= N && (N & 7) == 0) {
-        *reinterpret_cast<uint4*>(o) = v;
+        store_stream16(o, v);
       } else {
         const uint16_t* e = reinterpret_cast<const uint16_t*>(&stage[row * SP + col]);
         for (int k = 0; k < 8 && n + k < N; ++k) o[k] = e[k];
@@ -459,7 +459,7 @@ gemm6_lds_kernel(const uint8_t* __restrict__ at, const float* __restrict__ s_a,
         if (t < T && n < N) {
           uint16_t* o = yo + static_cast<int64_t>(t) * N + n;
           if (n + 8 <= N && (N & 7) == 0) {
-            *reinterpret_cast<uint4*>(o) = cv[k];
+            store_stream16(o, cv[k]);
           } else {
             const uint32_t wv[4] = {cv[k].x, cv[k].y, cv[k].z, cv[k].w};
             for (int e = 0; e < 8 && n + e < N; ++e)
