@@ -123,7 +123,7 @@ struct Raw4 {
 template <int IN>
 __device__ __forceinline__ void fetch4(Raw4<IN>& r, const void* x, int64_t off, int D) {
   if constexpr (IN == IN_F32) {
-    r.a = *reinterpret_cast<const uint4*>(static_cast<const float*>(x) + off);
+    r.a = load_stream16(static_cast<const float*>(x) + off);
   } else {
     const uint16_t* p = static_cast<const uint16_t*>(x) + off;
     const uint2 g = *reinterpret_cast<const uint2*>(p);
@@ -268,8 +268,7 @@ kron_row_kernel(const void* __restrict__ x, int64_t ldx, int A, int B, int logA,
   if constexpr (OUT == KRON_F32) {
     for (int f = 4 * tid; f < D; f += 4 * kKronThreads) {
       const float4 v = *reinterpret_cast<const float4*>(buf + f);
-      *reinterpret_cast<float4*>(y + row * D + f) =
-          make_float4(v.x * norm, v.y * norm, v.z * norm, v.w * norm);
+      store_stream16(y + row * D + f, make_float4(v.x * norm, v.y * norm, v.z * norm, v.w * norm));
     }
   } else {
     float m = 0.0f;
