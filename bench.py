@@ -48,6 +48,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 256 MiB device copy (counter calibration)")
+    p.add_argument("--profile-configs", action="store_true",
+                   help="only the other configurations (70B-shaped linear, decode and prefill "
+                        "layers; short runs under a profiler)")
     p.add_argument("--profile-step", action="store_true",
                    help="only the unit's steps, the GEMM, the cold stages and the 256 MiB "
                         "calibration copy (short runs under a profiler)")
@@ -373,6 +376,40 @@ def config_rows(rw, torch, dev, timed):
     return out
 
 
+def graph_timed(torch, fn, n=20):
+    """Average device time of one call: n calls captured once in a HIP graph
+    and replayed between two events, so that the host's per-call cost (the
+    Python binding) does not leave the device idle between short kernels;
+    eager back-to-back calls if capture is not possible."""
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    try:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side), torch.cuda.graph(g, stream=side):
+            for _ in range(n):
+                fn()
+        torch.cuda.current_stream().wait_stream(side)
+        g.replay()
+        torch.cuda.synchronize()
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+    except Exception:
+        torch.cuda.synchronize()
+    a.record()
+    for _ in range(n):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -384,6 +421,11 @@ def main():
     import workloads as W
 
     rw.lib()
+    if args.profile_configs:
+        dev = torch.device("cuda:0")
+        rec = config_rows(rw, torch, dev, lambda fn, n=20: graph_timed(torch, fn, n))
+        print(json.dumps({"profile_configs": rec}), flush=True)
+        return
     wl = W.CONFIGS[args.config]
     if wl.is_layer:
         raise SystemExit("bench workloads are the single-linear configs (0, 1, 4)")
@@ -493,37 +535,7 @@ def main():
     sa_t = torch.empty((T,), dtype=torch.float32, device=dev)
 
     def timed(fn, n=20):
-        """Average device time of one call: n calls captured once in a HIP graph
-        and replayed between two events, so that the host's per-call cost (the
-        Python binding) does not leave the device idle between short kernels;
-        eager back-to-back calls if capture is not possible."""
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        try:
-            g = torch.cuda.CUDAGraph()
-            side = torch.cuda.Stream()
-            side.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(side), torch.cuda.graph(g, stream=side):
-                for _ in range(n):
-                    fn()
-            torch.cuda.current_stream().wait_stream(side)
-            g.replay()
-            torch.cuda.synchronize()
-            a.record()
-            g.replay()
-            b.record()
-            torch.cuda.synchronize()
-            return a.elapsed_time(b) / n
-        except Exception:
-            torch.cuda.synchronize()
-        a.record()
-        for _ in range(n):
-            fn()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / n
+        return graph_timed(torch, fn, n)
 
     # the same unit with the basis prepared inside every call (rotated_linear)
     uws = torch.empty((rw.rotated_linear_workspace_size(T, D, r, flags),), dtype=torch.uint8,

@@ -63,9 +63,11 @@ __device__ __forceinline__ void store_stream16(void* p, float4 v) {
 
 // Streaming 16-byte load (the non-temporal hint) for a row's last read: the
 // line is not kept in L2 at the expense of lines that are still to be used.
-// In the row kernels (transform, quantizer, gated input), cold fp32 rows at
+// In the wave-per-row kernel (fp32 rows of 2048-8192 values), cold rows at
 // D = 4096, T = 2048: transform in place 17.1 -> 12.3 us, quantizer
-// 10.3 -> 9.3 us. On the fused prologue's second read of x it was slower.
+// 10.3 -> 9.3 us. Not in the workgroup-per-row kernel (its row kernel in the
+// D = 8192 unit lost 15-30 us of 1260 with it) nor on the fused prologue's
+// second read of x (slower).
 __device__ __forceinline__ uint4 load_stream16(const void* p) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));

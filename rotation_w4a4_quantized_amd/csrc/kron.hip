@@ -123,7 +123,7 @@ struct Raw4 {
 template <int IN>
 __device__ __forceinline__ void fetch4(Raw4<IN>& r, const void* x, int64_t off, int D) {
   if constexpr (IN == IN_F32) {
-    r.a = load_stream16(static_cast<const float*>(x) + off);
+    r.a = *reinterpret_cast<const uint4*>(static_cast<const float*>(x) + off);
   } else {
     const uint16_t* p = static_cast<const uint16_t*>(x) + off;
     const uint2 g = *reinterpret_cast<const uint2*>(p);

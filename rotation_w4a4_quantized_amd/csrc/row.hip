@@ -126,7 +126,7 @@ __device__ __forceinline__ void load_row_raw(float (&v)[EPT], const void* x, int
     if constexpr (EPT >= 4) {
 #pragma unroll
       for (int i = 0; i < EPT / 4; ++i) {
-        const float4 q = load_stream16f(reinterpret_cast<const float4*>(p) + i);
+        const float4 q = reinterpret_cast<const float4*>(p)[i];
         v[4 * i] = q.x; v[4 * i + 1] = q.y; v[4 * i + 2] = q.z; v[4 * i + 3] = q.w;
       }
     } else {
@@ -139,7 +139,7 @@ __device__ __forceinline__ void load_row_raw(float (&v)[EPT], const void* x, int
     if constexpr (EPT >= 8) {
 #pragma unroll
       for (int i = 0; i < EPT / 8; ++i) {
-        const uint4 q = load_stream16(reinterpret_cast<const uint4*>(p) + i);
+        const uint4 q = reinterpret_cast<const uint4*>(p)[i];
         g[8 * i + 0] = bf16lo(q.x); g[8 * i + 1] = bf16hi(q.x);
         g[8 * i + 2] = bf16lo(q.y); g[8 * i + 3] = bf16hi(q.y);
         g[8 * i + 4] = bf16lo(q.z); g[8 * i + 5] = bf16hi(q.z);
@@ -156,7 +156,7 @@ __device__ __forceinline__ void load_row_raw(float (&v)[EPT], const void* x, int
       if constexpr (EPT >= 8) {
 #pragma unroll
         for (int i = 0; i < EPT / 8; ++i) {
-          const uint4 q = load_stream16(reinterpret_cast<const uint4*>(pu) + i);
+          const uint4 q = reinterpret_cast<const uint4*>(pu)[i];
           u[8 * i + 0] = bf16lo(q.x); u[8 * i + 1] = bf16hi(q.x);
           u[8 * i + 2] = bf16lo(q.y); u[8 * i + 3] = bf16hi(q.y);
           u[8 * i + 4] = bf16lo(q.z); u[8 * i + 5] = bf16hi(q.z);
