@@ -239,7 +239,8 @@ template <int FW, int FT, int WW, int WT, int S, bool I32OUT>
 __global__ void __launch_bounds__(64 * WW * WT)
 gemm6_lds_kernel(const uint8_t* __restrict__ at, const float* __restrict__ s_a,
                  const uint8_t* __restrict__ wt, const float* __restrict__ s_w,
-                 void* __restrict__ y, int T, int K, int N, int rt, int sup) {
+                 void* __restrict__ y, int T, int K, int N, int rt, int st_t,
+                 int st_n) {
   constexpr int NW = WW * WT;
   constexpr int TW = WW * FW * 32, TT = WT * FT * 32;
   constexpr int NRB = WW * FW + WT * FT;      // 32-row blocks of the workgroup (W, then A)
@@ -266,15 +267,15 @@ gemm6_lds_kernel(const uint8_t* __restrict__ at, const float* __restrict__ s_a,
   // the tile grid is cut into 8 rectangles, rt along T by 8 / rt along N, and
   // XCD x takes rectangle x, so its L2 fetches only that rectangle's A and W
   // rows; rt = 0 gives each XCD a run of consecutive tiles instead. Inside
-  // its rectangle an XCD takes super-tiles of st_t x st_n tiles (sup =
-  // st_t | st_n << 16, both dividing the rectangle's sides), T-fastest within
-  // and between them, so that the tiles resident at once share few rows.
+  // its rectangle an XCD takes super-tiles of st_t x st_n tiles (dividing the
+  // rectangle's sides), T-fastest within and between them, so that the tiles
+  // resident at once share few rows.
   int tb, nbk;
   {
     int b = blockIdx.x;
     if (rt > 0) {
       const int x = b & 7, l = b >> 3, rtt = ntt / rt, rnn = nwt / (8 / rt);
-      const int st_t = sup & 0xFFFF, st_n = sup >> 16, per = st_t * st_n;
+      const int per = st_t * st_n;
       const int sblk = l / per, w = l % per, nst = rtt / st_t;
       tb = (x % rt) * rtt + (sblk % nst) * st_t + w % st_t;
       nbk = (x / rt) * rnn + (sblk / nst) * st_n + w / st_t;
@@ -684,25 +685,27 @@ inline int xcd_regions(int64_t ntt, int64_t nwt, int64_t TT, int64_t TW) {
   return best;
 }
 
-// The super-tile (st_t | st_n << 16) an XCD walks its rtt x rnn rectangle
-// in: when the rectangle holds more tiles than the XCD runs at once (its
-// CUs, one workgroup each), the st_t x st_n tiles resident together (st_t
-// dividing rtt, st_n = resident / st_t dividing rnn) with the fewest A and W
-// rows; otherwise, or when none divides, the whole T side (the rectangle's
-// tiles T-fastest). On 256 x 256 tiles at 4096 -> 32768, T = 4096 (a 16 x 16
+// The super-tile {st_t, st_n} an XCD walks its rtt x rnn rectangle in: when
+// the rectangle holds more tiles than the XCD runs at once (its CUs' resident
+// workgroups), the st_t x st_n tiles resident together (st_t dividing rtt,
+// st_n = resident / st_t dividing rnn) with the fewest A and W rows;
+// otherwise, or when none divides, the whole T side (the rectangle's tiles
+// T-fastest). On 256 x 256 tiles at 4096 -> 32768, T = 4096 (a 16 x 16
 // rectangle, 32 resident) this takes 4 x 8 super-tiles: 9 instead of
 // 13.5 MiB of operand rows per resident set. Measured on MI355X: prefill
 // layer (T = 4096) 936 -> 910 us, 70B-shaped linear 1279 -> 1253 us.
-inline int xcd_supertile(int64_t rtt, int64_t rnn, int64_t TT, int64_t TW, int64_t resident) {
-  int best = static_cast<int>(rtt) | (1 << 16);
+struct SuperTile { int t, n; };
+inline SuperTile xcd_supertile(int64_t rtt, int64_t rnn, int64_t TT, int64_t TW,
+                               int64_t resident) {
+  SuperTile best{static_cast<int>(rtt), 1};
   if (rtt * rnn <= resident || resident < 1) return best;
   int64_t cost = -1;
-  for (int64_t st = 1; st <= rtt; st *= 2) {
+  for (int64_t st = 1; st <= rtt && st <= resident; st *= 2) {
     if (rtt % st || resident % st) continue;
     const int64_t sn = resident / st;
-    if (sn < 1 || rnn % sn) continue;
+    if (rnn % sn) continue;
     const int64_t c = st * TT + sn * TW;
-    if (cost < 0 || c < cost) cost = c, best = static_cast<int>(st | (sn << 16));
+    if (cost < 0 || c < cost) cost = c, best = SuperTile{static_cast<int>(st), static_cast<int>(sn)};
   }
   return best;
 }
@@ -717,11 +720,11 @@ hipError_t launch_lds(const uint8_t* a, const float* s_a, const uint8_t* w, cons
   // workgroups resident per CU: the 4-wave blocks take 74 KiB of LDS (two per
   // CU), the 8-wave ones 110-146 KiB (one)
   const int64_t resident = device_cus() / 8 * (WW * WT <= 4 ? 2 : 1);
-  const int sup = rt > 0 ? xcd_supertile(ntt / rt, nwt / (8 / rt), TT, TW, resident)
-                         : 1 | (1 << 16);
+  const SuperTile st = rt > 0 ? xcd_supertile(ntt / rt, nwt / (8 / rt), TT, TW, resident)
+                              : SuperTile{1, 1};
   hipLaunchKernelGGL((gemm6_lds_kernel<FW, FT, WW, WT, S, I32>), dim3(static_cast<unsigned>(nb)),
                      dim3(64 * WW * WT), 0, s, a, s_a, w, s_w, y, static_cast<int>(T),
-                     static_cast<int>(K), static_cast<int>(N), rt, sup);
+                     static_cast<int>(K), static_cast<int>(N), rt, st.t, st.n);
   return hipGetLastError();
 }
 
