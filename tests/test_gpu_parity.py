@@ -570,7 +570,11 @@ def test_tile_codes_rejects_minus8(rw):
                                    # whole tiles, several per CU (256 x 256 blocks with
                                    # 2, 3, 8 stages; 256 x 128 blocks with 16)
                                    (8192, 256, 8192), (4096, 384, 8192), (4096, 1024, 8192),
-                                   (2048, 2048, 12288)])
+                                   (2048, 2048, 12288),
+                                   # an XCD's rectangle larger than its resident tiles,
+                                   # walked in super-tiles: 4 x 16 of 128 x 128 blocks
+                                   # (12 x 16 rectangle), 4 x 8 of 256 x 256 (16 x 8)
+                                   (1536, 256, 16384), (4096, 128, 16384)])
 def test_w4a4_gemm_tiles(rw, T, K, N):
     say(f"w4a4_gemm_tiles T={T} K={K} N={N}")
     a, qa = _codes7(T + K, T, K)
