@@ -46,12 +46,20 @@ constexpr int NW = 4;           // waves per workgroup
 // entries of M - I are exact in fp32 (M's diagonal lies well inside [0.5, 2]
 // for the sub-rotations of the pages, so M_ii - 1 is exact by Sterbenz), and
 // Q' is summed in fp32. Columns j >= r are zero padding.
+// Q' is also written in the order the projection's waves read it (QtF): 1 KiB
+// chunks, one per (64-column double step dg, 16-row block c, hi/lo, half h),
+// lane 16 g + t holding Q'[16 c + t][64 dg + 16 g + 8 h .. + 8]. A wave then
+// loads each operand fragment as one contiguous 1 KiB (from L2 a row-major
+// fragment, 16 rows of 64 bytes, reads at about a third of that rate). Same
+// values as Q'h/Q'l, so the same products. (A separate reordering launch
+// cost ~4 us of the basis preparation.)
 constexpr int kPrepRmax = 128;
 
 __global__ void __launch_bounds__(256)
 basis_prep_kernel(const float* __restrict__ Q, const float* __restrict__ M, int D, int r, int RP,
                   int RK, uint16_t* __restrict__ QtH, uint16_t* __restrict__ QtL,
-                  uint16_t* __restrict__ QH, uint16_t* __restrict__ QL) {
+                  uint16_t* __restrict__ QH, uint16_t* __restrict__ QL,
+                  uint16_t* __restrict__ QtF) {
   __shared__ uint16_t th[32][64 + 2];
   __shared__ uint16_t tlo[32][64 + 2];
   __shared__ float qrow[64][kPrepRmax + 1];     // Q rows d0 .. d0 + 63
@@ -116,6 +124,13 @@ basis_prep_kernel(const float* __restrict__ Q, const float* __restrict__ M, int 
     vl.z = tlo[jr][db + 4] | (uint32_t(tlo[jr][db + 5]) << 16); vl.w = tlo[jr][db + 6] | (uint32_t(tlo[jr][db + 7]) << 16);
     *reinterpret_cast<uint4*>(QtH + static_cast<int64_t>(j) * D + d0 + db) = vh;
     *reinterpret_cast<uint4*>(QtL + static_cast<int64_t>(j) * D + d0 + db) = vl;
+    if (d0 + 64 <= D) {  // whole double steps (the projection's parts)
+      const int64_t q = ((static_cast<int64_t>(blockIdx.x) * (RP / 16) + (j >> 4)) * 2) * 2 +
+                        ((db >> 3) & 1);                      // hi; lo is chunk q + 2
+      const int ln = 16 * (db >> 4) + (j & 15);
+      *reinterpret_cast<uint4*>(QtF + (q * 64 + ln) * 8) = vh;
+      *reinterpret_cast<uint4*>(QtF + ((q + 2) * 64 + ln) * 8) = vl;
+    }
   }
 }
 
@@ -125,27 +140,6 @@ basis_prep_kernel(const float* __restrict__ Q, const float* __restrict__ M, int 
 // the FWHT (h = 1, 2, ..., D/2) in fp32. Since H_D / sqrt(D) is symmetric and
 // orthogonal, H (x + Q z) / sqrt(D) = H x / sqrt(D) + P z.
 constexpr int kBasisFwhtMax = 4096;
-
-// Q' in the order the projection's waves read it: 1 KiB chunks, one per
-// (64-column double step dg, 16-row block c, hi/lo, half h), lane 16 g + t
-// holding Q'[16 c + t][64 dg + 16 g + 8 h .. + 8]. A wave then loads each
-// operand fragment as one contiguous 1 KiB (from L2 a row-major fragment,
-// 16 rows of 64 bytes, reads at about a third of that rate). Same values as
-// Q'h/Q'l, so the same products.
-__global__ void __launch_bounds__(256)
-qtf_kernel(const uint16_t* __restrict__ QtH, const uint16_t* __restrict__ QtL, int D, int RP,
-           uint16_t* __restrict__ QtF) {
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  const int lane = static_cast<int>(idx & 63);
-  const int64_t q = idx >> 6;
-  const int h = static_cast<int>(q & 1);
-  const int hl = static_cast<int>((q >> 1) & 1);
-  const int nbc = RP / 16;
-  const int c = static_cast<int>((q >> 2) % nbc);
-  const int64_t dg = (q >> 2) / nbc;
-  const int64_t o = static_cast<int64_t>(16 * c + (lane & 15)) * D + 64 * dg + 16 * (lane >> 4) + 8 * h;
-  *reinterpret_cast<uint4*>(QtF + idx * 8) = *reinterpret_cast<const uint4*>((hl ? QtL : QtH) + o);
-}
 
 __global__ void __launch_bounds__(1024)
 basis_fwht_kernel(const float* __restrict__ Q, int D, int r, int RK, float norm,
@@ -1158,12 +1152,8 @@ hipError_t launch_basis_prep(const float* Q, const float* M, int64_t D, int64_t 
   const AlignBasis a = align_basis(basis, D, r, with_p);
   const dim3 pgrid(static_cast<unsigned>((D + 63) / 64), static_cast<unsigned>(a.RK / 32));
   hipLaunchKernelGGL(basis_prep_kernel, pgrid, dim3(256), 0, s, Q, M, static_cast<int>(D),
-                     static_cast<int>(r), a.RP, a.RK, a.QtH, a.QtL, a.QH, a.QL);
+                     static_cast<int>(r), a.RP, a.RK, a.QtH, a.QtL, a.QH, a.QL, a.QtF);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(qtf_kernel, dim3(static_cast<unsigned>(D / 64 * (a.RP / 16))), dim3(256), 0, s,
-                     a.QtH, a.QtL, static_cast<int>(D), a.RP, a.QtF);
-  e = hipGetLastError();
   if (e != hipSuccess || !with_p) return e;
   if ((D & (D - 1)) != 0 || D > kBasisFwhtMax) return hipErrorInvalidValue;
   const float norm = static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(D)));
