@@ -55,18 +55,20 @@ constexpr int NW = 4;           // waves per workgroup
 // cost ~4 us of the basis preparation.)
 constexpr int kPrepRmax = 128;
 
-__global__ void __launch_bounds__(256)
-basis_prep_kernel(const float* __restrict__ Q, const float* __restrict__ M, int D, int r, int RP,
-                  int RK, uint16_t* __restrict__ QtH, uint16_t* __restrict__ QtL,
-                  uint16_t* __restrict__ QH, uint16_t* __restrict__ QL,
-                  uint16_t* __restrict__ QtF) {
+__device__ __forceinline__ void basis_prep_tile(int bx, int by, const float* __restrict__ Q,
+                                                const float* __restrict__ M, int D, int r, int RP,
+                                                int RK, uint16_t* __restrict__ QtH,
+                                                uint16_t* __restrict__ QtL,
+                                                uint16_t* __restrict__ QH,
+                                                uint16_t* __restrict__ QL,
+                                                uint16_t* __restrict__ QtF) {
   __shared__ uint16_t th[32][64 + 2];
   __shared__ uint16_t tlo[32][64 + 2];
   __shared__ float qrow[64][kPrepRmax + 1];     // Q rows d0 .. d0 + 63
   __shared__ float mi[32][kPrepRmax + 1];       // (M - I) rows j0 .. j0 + 31
   const int tid = threadIdx.x;
-  const int d0 = blockIdx.x * 64;
-  const int j0 = blockIdx.y * 32;
+  const int d0 = bx * 64;
+  const int j0 = by * 32;
   for (int c = tid; c < 64 * r; c += 256) {
     const int dd = c / r, k = c % r;
     qrow[dd][k] = d0 + dd < D ? Q[static_cast<int64_t>(d0 + dd) * r + k] : 0.0f;
@@ -125,13 +127,21 @@ basis_prep_kernel(const float* __restrict__ Q, const float* __restrict__ M, int 
     *reinterpret_cast<uint4*>(QtH + static_cast<int64_t>(j) * D + d0 + db) = vh;
     *reinterpret_cast<uint4*>(QtL + static_cast<int64_t>(j) * D + d0 + db) = vl;
     if (d0 + 64 <= D) {  // whole double steps (the projection's parts)
-      const int64_t q = ((static_cast<int64_t>(blockIdx.x) * (RP / 16) + (j >> 4)) * 2) * 2 +
+      const int64_t q = ((static_cast<int64_t>(bx) * (RP / 16) + (j >> 4)) * 2) * 2 +
                         ((db >> 3) & 1);                      // hi; lo is chunk q + 2
       const int ln = 16 * (db >> 4) + (j & 15);
       *reinterpret_cast<uint4*>(QtF + (q * 64 + ln) * 8) = vh;
       *reinterpret_cast<uint4*>(QtF + ((q + 2) * 64 + ln) * 8) = vl;
     }
   }
+}
+
+__global__ void __launch_bounds__(256)
+basis_prep_kernel(const float* __restrict__ Q, const float* __restrict__ M, int D, int r, int RP,
+                  int RK, uint16_t* __restrict__ QtH, uint16_t* __restrict__ QtL,
+                  uint16_t* __restrict__ QH, uint16_t* __restrict__ QL,
+                  uint16_t* __restrict__ QtF) {
+  basis_prep_tile(blockIdx.x, blockIdx.y, Q, M, D, r, RP, RK, QtH, QtL, QH, QL, QtF);
 }
 
 // Hadamard image of the basis for the fused prologue: P = H_D Q / sqrt(D),
@@ -174,13 +184,12 @@ basis_fwht_kernel(const float* __restrict__ Q, int D, int r, int RK, float norm,
 // the same order as above (h = 1, 2, ..., 2048), so the results are the same
 // bits. One workgroup per column, as above.
 constexpr int kBasisFwhtFast = 4096;
-__global__ void __launch_bounds__(256)
-basis_fwht4096_kernel(const float* __restrict__ Q, int r, int RK, float norm,
-                      uint16_t* __restrict__ PH, uint16_t* __restrict__ PL) {
+__device__ __forceinline__ void basis_fwht4096_col(int j, const float* __restrict__ Q, int r,
+                                                   int RK, float norm, uint16_t* __restrict__ PH,
+                                                   uint16_t* __restrict__ PL) {
   constexpr int D = kBasisFwhtFast;
   __shared__ float col[D + D / 16];             // one pad word per 16 (conflict-free phase 1)
   const int t = threadIdx.x;
-  const int j = blockIdx.x;
   auto at = [](int d) { return d + (d >> 4); };
   auto levels = [](float (&v)[16]) {
 #pragma unroll
@@ -224,6 +233,23 @@ basis_fwht4096_kernel(const float* __restrict__ Q, int r, int RK, float norm,
     PH[static_cast<int64_t>(d) * RK + j] = hi;
     PL[static_cast<int64_t>(d) * RK + j] = f32_to_bf16(w - bf16_to_f32(hi));
   }
+}
+
+// The basis preparation at D = 4096 in one launch: workgroups below the tile
+// count run basis_prep_tile (tile b % gx, b / gx), the rest the Hadamard image
+// of column b - tiles; neither reads what the other writes.
+__global__ void __launch_bounds__(256)
+basis_prep_p4096_kernel(const float* __restrict__ Q, const float* __restrict__ M, int r, int RP,
+                        int RK, int gx, uint16_t* __restrict__ QtH, uint16_t* __restrict__ QtL,
+                        uint16_t* __restrict__ QH, uint16_t* __restrict__ QL,
+                        uint16_t* __restrict__ QtF, float norm, uint16_t* __restrict__ PH,
+                        uint16_t* __restrict__ PL) {
+  const int b = blockIdx.x;
+  const int tiles = gx * (RK / 32);
+  if (b < tiles)
+    basis_prep_tile(b % gx, b / gx, Q, M, kBasisFwhtFast, r, RP, RK, QtH, QtL, QH, QL, QtF);
+  else
+    basis_fwht4096_col(b - tiles, Q, r, RK, norm, PH, PL);
 }
 
 // A D part of 512 columns is 8 double steps of 64 columns; each of the 8
@@ -1150,20 +1176,24 @@ AlignBasis align_basis(const void* basis, int64_t D, int64_t r, bool with_p) {
 hipError_t launch_basis_prep(const float* Q, const float* M, int64_t D, int64_t r, bool with_p,
                              void* basis, hipStream_t s) {
   const AlignBasis a = align_basis(basis, D, r, with_p);
+  const float norm = static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(D)));
+  if (with_p && D == kBasisFwhtFast) {
+    // one launch (15.1 us in two)
+    const int gx = static_cast<int>(D / 64);
+    hipLaunchKernelGGL(basis_prep_p4096_kernel,
+                       dim3(static_cast<unsigned>(gx * (a.RK / 32) + a.RK)), dim3(256), 0, s, Q, M,
+                       static_cast<int>(r), a.RP, a.RK, gx, a.QtH, a.QtL, a.QH, a.QL, a.QtF, norm,
+                       a.PH, a.PL);
+    return hipGetLastError();
+  }
   const dim3 pgrid(static_cast<unsigned>((D + 63) / 64), static_cast<unsigned>(a.RK / 32));
   hipLaunchKernelGGL(basis_prep_kernel, pgrid, dim3(256), 0, s, Q, M, static_cast<int>(D),
                      static_cast<int>(r), a.RP, a.RK, a.QtH, a.QtL, a.QH, a.QL, a.QtF);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !with_p) return e;
   if ((D & (D - 1)) != 0 || D > kBasisFwhtMax) return hipErrorInvalidValue;
-  const float norm = static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(D)));
-  // 12.8 us for the one-level-per-barrier kernel at D = 4096, r = 32
-  if (D == kBasisFwhtFast)
-    hipLaunchKernelGGL(basis_fwht4096_kernel, dim3(static_cast<unsigned>(a.RK)), dim3(256), 0, s,
-                       Q, static_cast<int>(r), a.RK, norm, a.PH, a.PL);
-  else
-    hipLaunchKernelGGL(basis_fwht_kernel, dim3(static_cast<unsigned>(a.RK)), dim3(1024), 0, s, Q,
-                       static_cast<int>(D), static_cast<int>(r), a.RK, norm, a.PH, a.PL);
+  hipLaunchKernelGGL(basis_fwht_kernel, dim3(static_cast<unsigned>(a.RK)), dim3(1024), 0, s, Q,
+                     static_cast<int>(D), static_cast<int>(r), a.RK, norm, a.PH, a.PL);
   return hipGetLastError();
 }
 
