@@ -84,11 +84,12 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// fp32 -> bf16 bits, round to nearest, ties to even (finite inputs)
+// fp32 -> bf16 bits, round to nearest, ties to even: the gfx950 conversion
+// instruction (v_cvt_pk_bf16_f32), one instruction where the integer
+// rounding (add the rounding bias and the tie bit, shift) took three; the
+// same bits for every finite input
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 // the two bf16 halves of a 32-bit word -> fp32 (element 0 = low half)
