@@ -33,7 +33,9 @@ PEAK_HBM_GBS = 8000.0
 PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 vector, TFLOP/s
 PEAK_FP64_TFLOPS = 78.6       # MI355X fp64 vector, TFLOP/s
 METRIC = "rotated W4A4 linear tokens/s; GEMM int8-MFMA TOPS and align/quant GB/s vs peak"
-GEMM_SRC = os.path.join(ROOT, "rotation_w4a4_quantized_amd", "csrc", "gemm6.hip")
+# the GEMM kernel's sources: its file and the headers it compiles in
+GEMM_SRC = [os.path.join(ROOT, "rotation_w4a4_quantized_amd", "csrc", f)
+            for f in ("gemm6.hip", "common.hpp", "launch.hpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "w4a4_gemm_D4096_T2048_traffic.json")
 
 
@@ -57,9 +59,12 @@ def parse():
     return p.parse_args()
 
 
-def _src_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def _src_hash(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_bytes():
